@@ -1,0 +1,266 @@
+"""Plain, slow fp64 CPU oracle for grouped-head attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The HIP library never
+calls it, links it or falls back to it, and it shares no code with the HIP
+path: it imports nothing from ``grouped_head_latent_amd``.
+
+Every function computes the exact definition in float64 on inputs that are
+widened bit-for-bit from bf16 (or fp32).  There is no tiling, no online
+softmax and no reordering: each output row is a two-pass softmax over its
+visible keys followed by one weighted sum, evaluated with numpy matrix
+products as the only library primitive.
+
+Sources (the web pages this build works from):
+  * "Grouped Query Attention (GQA)", Ultralytics glossary, section "How GQA
+    works": a group of query heads shares one key head and one value head;
+    inside each head the computation is unchanged scaled dot-product attention;
+    one group gives MQA, as many groups as query heads gives MHA; the worked
+    example uses causal masking and repeat-interleaves each key/value head to
+    its consecutive group of query heads.
+  * "GTA: Grouped-head latenT Attention" news article, section on the grouped
+    shared attention matrix: heads are split into groups (four per group in the
+    example) and a group computes its attention scores once and hands the same
+    matrix to every head in the group.
+  * "GQLA: Group-Query Latent Attention for Hardware-Adaptive Large Language
+    Model Decoding", section 1 and section 3.1 with Eq. (1) and Figure 2: the
+    latent c^KV is expanded by per-group up-projections W^UK, W^UV with g
+    groups; a shared decoupled RoPE key k^R is concatenated to each group's
+    key; the absorbed path folds W^UK into the query and W^UV into the output so
+    all h_q heads attend straight over the cached latent, and both paths give
+    the same outputs.
+
+Readings where the pages are silent (each is listed in the design doc):
+  * decode / chunked causal alignment is bottom-right: with L keys and s_q new
+    queries, query t sees keys 0 .. L - s_q + t;
+  * head i belongs to group floor(i / (heads per group)) (consecutive heads,
+    as repeat_interleave in the GQA example makes them);
+  * the absorbed path's scale is 1/sqrt(d_h + d^R), the scale of the expanded
+    per-group key [k^C; k^R], passed explicitly by the caller;
+  * the absorbed path's value is the latent c^KV alone (width r_kv); k^R is a
+    key only.
+
+Pinning: every function here is checked by ``tests/test_oracle_pins.py``
+against brute force on tiny inputs, against torch's CPU scaled_dot_product_
+attention in float64, against closed forms (constant V, zero Q, a single key)
+and against the equivalences the pages state (GQA = MHA on repeated K/V, GTA =
+MHA on repeated Q/K, absorbed latent = expanded per-group GQA).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "widen_bf16", "softmax_attention", "gqa_prefill", "gqa_decode",
+    "gta_prefill", "latent_absorb_decode", "absorb_query", "absorb_output",
+    "expand_latent",
+]
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (bf16 is the top half of
+    an IEEE fp32 word)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                      n_visible: np.ndarray, scale: float):
+    """The definition of scaled dot-product attention for a set of query rows
+    that share one key/value head ("How GQA works": unchanged scaled
+    dot-product attention inside each head).
+
+    q: (n, dk) query rows; k: (m, dk); v: (m, dv); n_visible: (n,) integers,
+    row r attends to keys 0 .. n_visible[r]-1 (the causal mask; n_visible = m
+    means no mask).  Returns o (n, dv) and lse (n,) = log sum_u exp(s_u) in
+    natural-log units of the scaled scores.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n_visible = np.asarray(n_visible, dtype=np.int64)
+    n, m = q.shape[0], k.shape[0]
+    if n == 0:
+        return np.zeros((0, v.shape[1])), np.zeros((0,))
+    if np.any(n_visible < 1) or np.any(n_visible > m):
+        raise ValueError("every query row must see between 1 and m keys")
+    # step 1: scores s_u = scale * q . k_u
+    s = scale * (q @ k.T)
+    # causal mask: keys at or beyond n_visible[r] take no weight
+    visible = np.arange(m)[None, :] < n_visible[:, None]
+    s = np.where(visible, s, -np.inf)
+    # step 2: softmax, two passes (max, then exponentials and their sum)
+    mx = np.max(s, axis=1, keepdims=True)
+    p = np.exp(s - mx)
+    z = np.sum(p, axis=1, keepdims=True)
+    # step 3: probability-weighted sum of the value rows
+    o = (p / z) @ v
+    lse = (mx + np.log(z))[:, 0]
+    return o, lse
+
+
+def _group_of(head: int, heads: int, groups: int) -> int:
+    """Consecutive heads share a group: head i -> floor(i / (heads/groups))."""
+    return head // (heads // groups)
+
+
+def gqa_prefill(q, k, v, *, causal: bool = True, scale: float | None = None,
+                heads=None):
+    """Grouped-query attention ("How GQA works").
+
+    q: (B, h_q, S_q, d); k, v: (B, h_kv, S_k, d[v]); h_q % h_kv == 0.
+    Causal rows are aligned bottom-right: query t sees keys
+    0 .. t + (S_k - S_q) (for S_q == S_k that is the usual u <= t).
+    `heads` optionally restricts the evaluation to a list of (b, i) pairs
+    (other rows of the result are left as NaN).
+    Returns o (B, h_q, S_q, dv) and lse (B, h_q, S_q).
+    """
+    B, h_q, S_q, d = q.shape
+    _, h_kv, S_k, _ = k.shape
+    dv = v.shape[3]
+    if h_q % h_kv:
+        raise ValueError("h_q must be a multiple of h_kv")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.full((B, h_q, S_q, dv), np.nan)
+    lse = np.full((B, h_q, S_q), np.nan)
+    if causal:
+        nvis = np.arange(S_q) + (S_k - S_q) + 1
+    else:
+        nvis = np.full(S_q, S_k)
+    pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h_q)]
+    for b, i in pairs:
+        j = _group_of(i, h_q, h_kv)
+        o[b, i], lse[b, i] = softmax_attention(q[b, i], k[b, j], v[b, j], nvis, scale)
+    return o, lse
+
+
+def gqa_decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
+               heads=None):
+    """Decode step of grouped-query attention over a contiguous KV cache.
+
+    q: (B, h_q, s_q, d); k_cache, v_cache: (B, h_kv, L_cap, d); seqlens: (B,)
+    with s_q <= L_b <= L_cap.  The cache of sequence b holds L_b tokens, the
+    last s_q of which are the new queries' own keys, so query t sees keys
+    0 .. L_b - s_q + t.  Slots at or beyond L_b are never read.
+    """
+    B, h_q, s_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.full((B, h_q, s_q, v_cache.shape[3]), np.nan)
+    lse = np.full((B, h_q, s_q), np.nan)
+    pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h_q)]
+    for b, i in pairs:
+        L = int(seqlens[b])
+        if not (s_q <= L <= k_cache.shape[2]):
+            raise ValueError("need s_q <= L_b <= L_cap")
+        j = _group_of(i, h_q, h_kv)
+        nvis = np.arange(s_q) + (L - s_q) + 1
+        o[b, i], lse[b, i] = softmax_attention(q[b, i], k_cache[b, j, :L],
+                                               v_cache[b, j, :L], nvis, scale)
+    return o, lse
+
+
+def gta_prefill(q, k, v, *, causal: bool = True, scale: float | None = None,
+                heads=None):
+    """GTA shared-score attention (GTA article, grouped shared attention
+    matrix): each group has one query/key projection, so one score matrix per
+    group, computed once and applied to the value of every head in the group.
+
+    q, k: (B, n_grp, S, d_qk); v: (B, h, S, d_v); h % n_grp == 0.
+    Returns o (B, h, S, d_v) and lse (B, n_grp, S) (one per shared matrix).
+    """
+    B, n_grp, S, d_qk = q.shape
+    h = v.shape[1]
+    if h % n_grp:
+        raise ValueError("h must be a multiple of n_grp")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_qk)
+    nvis = np.arange(S) + 1 if causal else np.full(S, S)
+    o = np.full((B, h, S, v.shape[3]), np.nan)
+    lse = np.full((B, n_grp, S), np.nan)
+    pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h)]
+    for b, i in pairs:
+        j = _group_of(i, h, n_grp)
+        o[b, i], lse[b, j] = softmax_attention(q[b, j], k[b, j], v[b, i], nvis, scale)
+    return o, lse
+
+
+def latent_absorb_decode(q_lat, q_rope, c_kv, k_rope, seqlens, *, scale: float,
+                         heads=None):
+    """MQA-absorbed latent decode (GQLA section 1 and Figure 2, right): every
+    query head attends directly over the cached latent.
+
+    The score of head i with token u is
+        scale * (q_lat[i] . c_u + q_rope[i] . k_rope_u),
+    i.e. a dot product of the concatenations [q_lat; q_rope] and [c_u; k^R_u]
+    (the expanded key [W^UK c; k^R] of Eq. (1) with W^UK moved onto the
+    query), and the value is the latent c_u itself.
+
+    q_lat: (B, s_q, h_q, r_kv); q_rope: (B, s_q, h_q, d_r);
+    c_kv: (B, L_cap, r_kv); k_rope: (B, L_cap, d_r); seqlens: (B,).
+    Returns o_lat (B, s_q, h_q, r_kv) and lse (B, s_q, h_q).
+    """
+    B, s_q, h_q, r_kv = q_lat.shape
+    o = np.full((B, s_q, h_q, r_kv), np.nan)
+    lse = np.full((B, s_q, h_q), np.nan)
+    pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h_q)]
+    for b, i in pairs:
+        L = int(seqlens[b])
+        if not (s_q <= L <= c_kv.shape[1]):
+            raise ValueError("need s_q <= L_b <= L_cap")
+        qi = np.concatenate([q_lat[b, :, i], q_rope[b, :, i]], axis=1)
+        kb = np.concatenate([c_kv[b, :L], k_rope[b, :L]], axis=1)
+        nvis = np.arange(s_q) + (L - s_q) + 1
+        o[b, :, i], lse[b, :, i] = softmax_attention(qi, kb, c_kv[b, :L], nvis, scale)
+    return o, lse
+
+
+def absorb_query(q_c, w_uk, g: int):
+    """Fold W^UK into the query (GQLA Figure 2, right): for head i in group
+    j = g(i), q~_i = (W^UK_j)^T q^C_i, where W^UK (g*d_h, r_kv) stacks the
+    groups' (d_h, r_kv) blocks as in Eq. (1).
+
+    q_c: (..., h_q, d_h) -> (..., h_q, r_kv).
+    """
+    h_q, d_h = q_c.shape[-2], q_c.shape[-1]
+    out = np.empty(q_c.shape[:-1] + (w_uk.shape[1],))
+    for i in range(h_q):
+        j = _group_of(i, h_q, g)
+        w = w_uk[j * d_h:(j + 1) * d_h]            # (d_h, r_kv)
+        out[..., i, :] = q_c[..., i, :] @ w
+    return out
+
+
+def absorb_output(o_lat, w_uv, g: int, d_h: int):
+    """Apply W^UV after attention (GQLA Figure 2, right): O_i = W^UV_j o_lat_i.
+
+    o_lat: (..., h_q, r_kv) -> (..., h_q, d_h).
+    """
+    h_q = o_lat.shape[-2]
+    out = np.empty(o_lat.shape[:-1] + (d_h,))
+    for i in range(h_q):
+        j = _group_of(i, h_q, g)
+        w = w_uv[j * d_h:(j + 1) * d_h]            # (d_h, r_kv)
+        out[..., i, :] = o_lat[..., i, :] @ w.T
+    return out
+
+
+def expand_latent(c_kv, k_rope, w_uk, w_uv, g: int):
+    """The per-group expanded cache of GQLA's GQA path (section 3.1): for
+    group j, K_j = [c W^UK_j^T ; k^R] (width d_h + d^R) and V_j = c W^UV_j^T
+    (width d_h), from Eq. (1) (k^C = W^UK c, shared k^R concatenated).
+
+    c_kv: (B, L, r_kv); k_rope: (B, L, d_r) -> K (B, g, L, d_h+d_r),
+    V (B, g, L, d_h).
+    """
+    d_h = w_uk.shape[0] // g
+    B, L, _ = c_kv.shape
+    K = np.empty((B, g, L, d_h + k_rope.shape[2]))
+    V = np.empty((B, g, L, d_h))
+    for j in range(g):
+        K[:, j, :, :d_h] = c_kv @ w_uk[j * d_h:(j + 1) * d_h].T
+        K[:, j, :, d_h:] = k_rope
+        V[:, j] = c_kv @ w_uv[j * d_h:(j + 1) * d_h].T
+    return K, V

@@ -1,0 +1,61 @@
+"""Byte and FLOP accounting against the figures the pages print."""
+import json
+import os
+
+import numpy as np
+
+from grouped_head_latent_amd import accounting as acc
+
+G = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def test_gqa_example_values_per_token():
+    for key in ("gqa_example_values_per_token_gqa", "gqa_example_values_per_token_mha"):
+        f = G[key]
+        assert acc.kv_values_per_token(f["kv_heads"], f["head_dim"]) == f["value"]
+
+
+def test_llama31_cache_sizes():
+    f = G["llama31_8b_gqa_bytes_per_token"]
+    per_tok = acc.kv_bytes_per_token(f["layers"], f["kv_heads"], f["head_dim"], f["elem_bytes"])
+    assert per_tok == f["value"]
+    assert per_tok * G["llama31_8b_gqa_bytes_full_context"]["tokens"] == G["llama31_8b_gqa_bytes_full_context"]["value"]
+    mha = acc.kv_bytes_per_token(f["layers"], G["llama31_8b_mha_bytes_per_token"]["kv_heads"], f["head_dim"])
+    assert mha == G["llama31_8b_mha_bytes_per_token"]["value"]
+    assert mha * 131072 == G["llama31_8b_mha_bytes_full_context"]["value"]
+
+
+def test_transgqla_ratio_and_gqla_cache_layouts():
+    f = G["transgqla_llama3_8b_cache_ratio"]
+    ratio = acc.latent_elems_per_token(f["r_kv"], f["d_r"]) / acc.kv_values_per_token(
+        f["baseline_kv_heads"], f["baseline_head_dim"])
+    assert ratio == f["value"]
+    assert acc.gqla_gqa_path_elems_per_token(8, 128, 64) == 2 * 8 * 128 + 64
+
+
+def test_absorb_intensity_and_mtp_doubling():
+    f = G["mla_absorb_intensity_flop_per_byte"]
+    ai = acc.absorb_intensity(f["h_q"], f["r_kv"], f["d_r"], f["s_q"])
+    assert abs(ai - f["value"]) / f["value"] < f["rel_tol"]
+    assert acc.absorb_intensity(128, 512, 64, 2) / ai == G["mtp_doubles_intensity"]["value"]
+
+
+def test_gta_printed_ratios_are_consistent():
+    for key in ("gta_500m_cache_ratio", "gta_500m_small_cache_ratio"):
+        f = G[key]
+        assert abs(f["gta_dims"] / f["mha_dims"] - f["value"]) < 1e-12
+
+
+def test_causal_pair_counts_by_enumeration():
+    for s_q, s_k in [(1, 1), (5, 5), (3, 9), (16, 16)]:
+        brute = sum(1 for t in range(s_q) for u in range(s_k) if u <= t + s_k - s_q)
+        assert acc.causal_pairs(s_q, s_k) == brute
+    L = np.array([4, 9])
+    assert acc.decode_pairs(L, 2) == sum(sum(1 for t in range(2) for u in range(l) if u <= l - 2 + t) for l in L)
+
+
+def test_config_work_figures():
+    # GQA prefill at batch 4, 32 heads, seq 4096, head dim 128, causal
+    assert abs(acc.gqa_prefill_flops(4, 32, 4096, 4096, 128) - 5.4993e11) / 5.4993e11 < 1e-4
+    # GTA prefill at batch 8, 4 groups of 4 heads, seq 2048, dims 64
+    assert abs(acc.gta_prefill_flops(8, 16, 4, 2048, 64, 64) - 4.2971e10) / 4.2971e10 < 1e-4
