@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped-head attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+
+One step is one call of the path over one batch of synthetic input, already
+resident in HBM.  The headline workload is causal GQA prefill at batch 4,
+32 query heads over 8 KV heads, 4096 tokens, head dim 128, bf16 inputs with
+fp32 accumulation; `value` is its algorithmic attention TFLOP/s (the causal
+pair count times 4*d FLOP, whatever the kernel actually executes).  The other
+workloads (GQA decode, GTA shared-score prefill, latent-absorbed decode) are
+timed the same way and reported under "extras".
+
+Rank 0 prints one JSON line.  Only one GPU is used: --gpus above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from grouped_head_latent_amd import accounting as acc  # noqa: E402
+
+PREFILL = dict(B=4, h_q=32, h_kv=8, S=4096, d=128, seed=2)
+DECODE = dict(B=64, h_q=32, h_kv=8, d=128, L_lo=1024, L_hi=32768, seed=3)
+GTA = dict(B=8, h=16, n_grp=4, S=2048, d=64, seed=4)
+LATENT = dict(B=64, h_q=128, r_kv=512, d_r=64, L_lo=8192, L_hi=65536, seed=5, d_h=128)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
+
+
+def time_steps(fn, steps, warmup, torch):
+    """Warm up, then time exactly `steps` calls between two synchronisations
+    with HIP events recorded on the stream the kernels are launched on."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(steps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+# ------------------------------------------------------------------ workloads
+
+def bench_prefill(gha, torch, steps, warmup):
+    c = PREFILL
+    B, h_q, h_kv, S, d = c["B"], c["h_q"], c["h_kv"], c["S"], c["d"]
+    q = to_dev(synth.normal_bf16((B, h_q, S, d), c["seed"], 1), torch)
+    k = to_dev(synth.normal_bf16((B, h_kv, S, d), c["seed"], 2), torch)
+    v = to_dev(synth.normal_bf16((B, h_kv, S, d), c["seed"], 3), torch)
+    o = torch.empty((B, h_q, S, d), dtype=torch.bfloat16, device="cuda")
+    ms, wall = time_steps(lambda: gha.gqa_prefill(q, k, v, causal=True, out=o), steps, warmup, torch)
+    flops = acc.gqa_prefill_flops(B, h_q, S, S, d)
+    return dict(ms=ms, wall=wall, flops=flops, tflops=flops / ms / 1e9,
+                bytes=acc.gqa_prefill_bytes(B, h_q, h_kv, S, S, d))
+
+
+def bench_decode(gha, torch, steps, warmup, s_q):
+    c = DECODE
+    B, h_q, h_kv, d = c["B"], c["h_q"], c["h_kv"], c["d"]
+    L_cap = c["L_hi"]
+    seqlens = synth.uniform_i32(B, c["L_lo"], c["L_hi"], c["seed"], synth.STREAM["seqlens"])
+    kc = to_dev(synth.cache_bf16(B, h_kv, L_cap, d, seqlens, c["seed"], 2), torch)
+    vc = to_dev(synth.cache_bf16(B, h_kv, L_cap, d, seqlens, c["seed"], 3), torch)
+    q = to_dev(synth.normal_bf16((B, h_q, s_q, d), c["seed"], 1), torch)
+    sl = torch.from_numpy(seqlens).cuda()
+    o = torch.empty((B, h_q, s_q, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gha.gqa_decode_workspace_bytes(B, h_q, h_kv, s_q, L_cap, d), dtype=torch.uint8, device="cuda")
+    ms, wall = time_steps(lambda: gha.gqa_decode(q, kc, vc, sl, out=o, workspace=ws), steps, warmup, torch)
+    by = acc.gqa_decode_bytes(seqlens, h_q, h_kv, s_q, d)
+    fl = acc.gqa_decode_flops(seqlens, h_q, s_q, d)
+    del kc, vc
+    return dict(ms=ms, gbps=by / ms / 1e6, tflops=fl / ms / 1e9, bytes=by, flops=fl,
+                sum_L=int(seqlens.sum()))
+
+
+def bench_gta(gha, torch, steps, warmup):
+    c = GTA
+    B, h, g, S, d = c["B"], c["h"], c["n_grp"], c["S"], c["d"]
+    q = to_dev(synth.normal_bf16((B, g, S, d), c["seed"], 1), torch)
+    k = to_dev(synth.normal_bf16((B, g, S, d), c["seed"], 2), torch)
+    v = to_dev(synth.normal_bf16((B, h, S, d), c["seed"], 3), torch)
+    o = torch.empty((B, h, S, d), dtype=torch.bfloat16, device="cuda")
+    ms, wall = time_steps(lambda: gha.gta_shared_score_prefill(q, k, v, out=o), steps, warmup, torch)
+    fl = acc.gta_prefill_flops(B, h, g, S, d, d)
+    return dict(ms=ms, tflops=fl / ms / 1e9, flops=fl)
+
+
+def bench_latent(gha, torch, steps, warmup, s_q):
+    c = LATENT
+    B, h_q, r, dr = c["B"], c["h_q"], c["r_kv"], c["d_r"]
+    L_cap = c["L_hi"]
+    seqlens = synth.uniform_i32(B, c["L_lo"], c["L_hi"], c["seed"], synth.STREAM["seqlens"])
+    cache = to_dev(synth.latent_cache_bf16(B, L_cap, r + dr, seqlens, c["seed"], synth.STREAM["latent"]), torch)
+    q_lat = to_dev(synth.normal_bf16((B, s_q, h_q, r), c["seed"], synth.STREAM["q"], 0.25), torch)
+    q_r = to_dev(synth.normal_bf16((B, s_q, h_q, dr), c["seed"], synth.STREAM["q_rope"]), torch)
+    sl = torch.from_numpy(seqlens).cuda()
+    o = torch.empty((B, s_q, h_q, r), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gha.latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_cap, r), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(c["d_h"] + dr)
+    ms, wall = time_steps(lambda: gha.latent_absorb_decode(q_lat, q_r, cache[..., :r], cache[..., r:], sl,
+                                                           scale=scale, out=o, workspace=ws), steps, warmup, torch)
+    by = acc.latent_decode_bytes(seqlens, h_q, s_q, r, dr)
+    fl = acc.latent_decode_flops(seqlens, h_q, s_q, r, dr)
+    del cache
+    return dict(ms=ms, gbps=by / ms / 1e6, tflops=fl / ms / 1e9, bytes=by, flops=fl,
+                sum_L=int(seqlens.sum()))
+
+
+# ---------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(max_seconds=15.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the headline
+    workload: whole (batch, head) slices of the causal prefill, as many as
+    fit in about `max_seconds`, scaled to TFLOP/s with the same algorithmic
+    count as the GPU figure."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    c = PREFILL
+    B, h_q, h_kv, S, d = c["B"], c["h_q"], c["h_kv"], c["S"], c["d"]
+    G = h_q // h_kv
+    done, t_total = 0, 0.0
+    pairs = [(b, i) for b in range(B) for i in range(h_q)]
+    while done < len(pairs) and t_total < max_seconds:
+        b, i = pairs[done]
+        q = oracle.widen_bf16(synth.normal_bf16_rows((B, h_q, S, d), c["seed"], 1, (b, i)))
+        k = oracle.widen_bf16(synth.normal_bf16_rows((B, h_kv, S, d), c["seed"], 2, (b, i // G)))
+        v = oracle.widen_bf16(synth.normal_bf16_rows((B, h_kv, S, d), c["seed"], 3, (b, i // G)))
+        t0 = time.perf_counter()
+        oracle.gqa_prefill(q[None, None], k[None, None], v[None, None], causal=True)
+        t_total += time.perf_counter() - t0
+        done += 1
+    flops = done * acc.gqa_prefill_flops(1, 1, S, S, d)
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {B * h_q} (batch, head) slices of the causal prefill "
+                      f"(4096 x 4096 x 128 each), fp64 numpy, {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default=None, help="prefill|decode|gta|latent: time one workload")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import grouped_head_latent_amd as gha
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gha.load_library()
+
+    only = args.only
+    extras = {}
+    head = None
+    if only in (None, "prefill"):
+        log("prefill ...")
+        head = bench_prefill(gha, torch, args.steps, args.warmup)
+        log(f"prefill {head['ms']:.4f} ms {head['tflops']:.1f} TFLOP/s")
+    if not args.no_extras or only is not None:
+        if only in (None, "gta"):
+            log("gta ...")
+            extras["gta_prefill"] = bench_gta(gha, torch, args.steps, args.warmup)
+            log(extras["gta_prefill"])
+        if only in (None, "decode"):
+            for s_q in (1, 2):
+                log(f"decode s_q={s_q} ...")
+                extras[f"gqa_decode_sq{s_q}"] = bench_decode(gha, torch, args.steps, args.warmup, s_q)
+                log(extras[f"gqa_decode_sq{s_q}"])
+                torch.cuda.empty_cache()
+        if only in (None, "latent"):
+            for s_q in (1, 2):
+                log(f"latent s_q={s_q} ...")
+                extras[f"latent_decode_sq{s_q}"] = bench_latent(gha, torch, args.steps, args.warmup, s_q)
+                log(extras[f"latent_decode_sq{s_q}"])
+                torch.cuda.empty_cache()
+    for k_, e in extras.items():
+        if "gbps" in e:
+            e["hbm_frac"] = e["gbps"] / acc.PEAK_HBM_GBPS
+        e["mfma_frac"] = e["tflops"] / acc.PEAK_BF16_TFLOPS
+
+    if head is None:
+        print(json.dumps({"extras": extras}))
+        return
+    out = {
+        "metric": "decode HBM GB/s (% of peak) + prefill attention TFLOPS (% of MFMA peak)",
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) rounded to bf16",
+        "config": {"workload": "causal GQA prefill, batch 4, 32 query heads / 8 KV heads, "
+                               "4096 tokens, head dim 128, bf16 in, fp32 accumulate, bf16 out",
+                   "global_batch": PREFILL["B"], "seq_len": PREFILL["S"], "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(head["tflops"], 2), "peak": acc.PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(head["tflops"] / acc.PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu:
+        log("cpu baseline ...")
+        out["cpu_baseline"] = cpu_baseline()
+    if extras:
+        out["extras"] = extras
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+"""Grouped-head attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libgha.so``, whose C ABI is declared in
+``include/gha.h``.  The functions below only marshal arguments: they turn
+torch tensors (device memory) into pointer-and-stride descriptors, allocate
+outputs and workspaces with torch when the caller does not pass them, and call
+the library on torch's current stream.  Every step of the computation runs in
+the library's HIP kernels; there is no fallback of any kind.  If the library
+is missing or cannot be loaded, every call raises.
+
+Entry points (same names as the C ABI):
+  gqa_prefill, gqa_decode, gta_shared_score_prefill, latent_absorb_decode,
+  gqa_decode_workspace_bytes, latent_absorb_decode_workspace_bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "gqa_prefill", "gqa_decode", "gta_shared_score_prefill", "latent_absorb_decode",
+    "gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
+    "GhaError", "library_path", "load_library", "GHA_F32", "GHA_BF16",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgha.so")
+
+GHA_F32, GHA_BF16 = 0, 1
+STATUS = ["GHA_OK", "GHA_ERR_NULL", "GHA_ERR_SHAPE", "GHA_ERR_GROUPING", "GHA_ERR_STRIDE",
+          "GHA_ERR_ALIGN", "GHA_ERR_DTYPE", "GHA_ERR_HEAD_DIM", "GHA_ERR_WORKSPACE", "GHA_ERR_HIP"]
+
+
+class GhaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        name = STATUS[status] if 0 <= status < len(STATUS) else str(status)
+        super().__init__(f"{name}: {detail}")
+
+
+class GhaTensor(ctypes.Structure):
+    """gha_tensor: device pointer plus batch/head/token element strides."""
+    _fields_ = [("ptr", ctypes.c_void_p), ("sb", ctypes.c_int64),
+                ("sh", ctypes.c_int64), ("ss", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgha.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m grouped_head_latent_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F, S, V = ctypes.POINTER(GhaTensor), ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+    lib.gqa_prefill.argtypes = [P, P, P, P, V, I, I, I, I, I, I, I, I, F, I, V]
+    lib.gqa_prefill.restype = I
+    lib.gqa_decode.argtypes = [P, P, P, V, P, V, I, I, I, I, I, I, I, I, I, F, V, S, V]
+    lib.gqa_decode.restype = I
+    lib.gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.gqa_decode_workspace_bytes.restype = S
+    lib.gta_shared_score_prefill.argtypes = [P, P, P, P, V, I, I, I, I, I, I, I, I, F, I, V]
+    lib.gta_shared_score_prefill.restype = I
+    lib.latent_absorb_decode.argtypes = [P, P, P, P, V, P, V, I, I, I, I, I, I, I, I, I, F, V, S, V]
+    lib.latent_absorb_decode.restype = I
+    lib.latent_absorb_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.latent_absorb_decode_workspace_bytes.restype = S
+    lib.gha_status_string.argtypes = [I]
+    lib.gha_status_string.restype = ctypes.c_char_p
+    lib.gha_last_error.argtypes = []
+    lib.gha_last_error.restype = ctypes.c_char_p
+    lib.gha_version.argtypes = []
+    lib.gha_version.restype = I
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise GhaError(status, _lib.gha_last_error().decode())
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GHA_BF16
+    if t.dtype == torch.float32:
+        return GHA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _desc(t, axes=(0, 1, 2)) -> GhaTensor:
+    """Descriptor of a 4-D (or, with axes, 3-D) tensor with a contiguous last
+    axis; `axes` names the tensor axes that are batch, head and token (None
+    for an absent axis, stride 0)."""
+    if t.stride(-1) != 1:
+        raise ValueError("the last axis must be contiguous")
+    st = [0 if a is None else t.stride(a) for a in axes]
+    return GhaTensor(t.data_ptr(), st[0], st[1], st[2])
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _out_code(out_dtype):
+    import torch
+    return GHA_F32 if out_dtype == torch.float32 else GHA_BF16
+
+
+# ------------------------------------------------------------------ wrappers
+
+def gqa_prefill(q, k, v, *, causal: bool = True, scale: float | None = None, out=None,
+                out_dtype=None, return_lse: bool = False, stream=None):
+    """q (B, h_q, S_q, d), k/v (B, h_kv, S_k, d) device tensors (bf16, or fp32
+    for the fp32 path).  Returns o (B, h_q, S_q, d) [and lse (B, h_q, S_q)]."""
+    import torch
+    lib = load_library()
+    B, h_q, S_q, d = q.shape
+    h_kv, S_k = k.shape[1], k.shape[2]
+    out_dtype = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
+    o = out if out is not None else torch.empty((B, h_q, S_q, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, h_q, S_q), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.gqa_prefill(_desc(q), _desc(k), _desc(v), _desc(o), _ptr(lse), B, h_q, h_kv, S_q,
+                           S_k, d, _dtype_code(q), _out_code(o.dtype), float(scale or 0.0),
+                           int(bool(causal)), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def gqa_decode_workspace_bytes(B, h_q, h_kv, s_q, L_max, d) -> int:
+    return int(load_library().gqa_decode_workspace_bytes(B, h_q, h_kv, s_q, L_max, d))
+
+
+def gqa_decode(q, k_cache, v_cache, seqlens, *, L_max: int | None = None,
+               scale: float | None = None, out=None, out_dtype=None, workspace=None,
+               return_lse: bool = False, stream=None):
+    """q (B, h_q, s_q, d); caches (B, h_kv, L_cap, d); seqlens int32 device (B,).
+    L_max: an upper bound on the lengths (default L_cap)."""
+    import torch
+    lib = load_library()
+    B, h_q, s_q, d = q.shape
+    h_kv, L_cap = k_cache.shape[1], k_cache.shape[2]
+    L_max = L_cap if L_max is None else int(L_max)
+    out_dtype = out_dtype or torch.bfloat16
+    o = out if out is not None else torch.empty((B, h_q, s_q, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=q.device) if return_lse else None
+    need = gqa_decode_workspace_bytes(B, h_q, h_kv, s_q, L_max, d)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    _check(lib.gqa_decode(_desc(q), _desc(k_cache), _desc(v_cache), _ptr(seqlens), _desc(o),
+                          _ptr(lse), B, h_q, h_kv, s_q, L_cap, L_max, d, _dtype_code(q),
+                          _out_code(o.dtype), float(scale or 0.0), _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def gta_shared_score_prefill(q, k, v, *, causal: bool = True, scale: float | None = None,
+                             out=None, out_dtype=None, return_lse: bool = False, stream=None):
+    """q, k (B, n_grp, S, d_qk); v (B, h, S, d_v).  Returns o (B, h, S, d_v)
+    [and lse (B, n_grp, S)]."""
+    import torch
+    lib = load_library()
+    B, n_grp, S, d_qk = q.shape
+    h, d_v = v.shape[1], v.shape[3]
+    out_dtype = out_dtype or torch.bfloat16
+    o = out if out is not None else torch.empty((B, h, S, d_v), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, n_grp, S), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.gta_shared_score_prefill(_desc(q), _desc(k), _desc(v), _desc(o), _ptr(lse), B, h,
+                                        n_grp, S, d_qk, d_v, _dtype_code(q), _out_code(o.dtype),
+                                        float(scale or 0.0), int(bool(causal)), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_max, r_kv) -> int:
+    return int(load_library().latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_max, r_kv))
+
+
+def latent_absorb_decode(q_lat, q_rope, c_kv, k_rope, seqlens, *, scale: float,
+                         L_max: int | None = None, out=None, out_dtype=None, workspace=None,
+                         return_lse: bool = False, stream=None):
+    """q_lat (B, s_q, h_q, r_kv), q_rope (B, s_q, h_q, d_r); c_kv (B, L_cap, r_kv),
+    k_rope (B, L_cap, d_r) (may be views of one (B, L_cap, r_kv + d_r) buffer);
+    seqlens int32 device (B,).  Returns o_lat (B, s_q, h_q, r_kv) [and lse
+    (B, s_q, h_q)]."""
+    import torch
+    lib = load_library()
+    B, s_q, h_q, r_kv = q_lat.shape
+    d_r = q_rope.shape[3]
+    L_cap = c_kv.shape[1]
+    L_max = L_cap if L_max is None else int(L_max)
+    out_dtype = out_dtype or torch.bfloat16
+    o = out if out is not None else torch.empty((B, s_q, h_q, r_kv), dtype=out_dtype, device=q_lat.device)
+    lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q_lat.device) if return_lse else None
+    need = latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_max, r_kv)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q_lat.device)
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    # (batch, head, token) axes: q-like tensors are (B, s_q, h_q, .), caches (B, L, .)
+    _check(lib.latent_absorb_decode(
+        _desc(q_lat, (0, 2, 1)), _desc(q_rope, (0, 2, 1)), _desc(c_kv, (0, None, 1)),
+        _desc(k_rope, (0, None, 1)), _ptr(seqlens), _desc(o, (0, 2, 1)), _ptr(lse),
+        B, h_q, s_q, L_cap, L_max, r_kv, d_r, _dtype_code(q_lat), _out_code(o.dtype),
+        float(scale), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return (o, lse) if return_lse else o

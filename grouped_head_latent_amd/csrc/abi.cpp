@@ -1,0 +1,305 @@
+// C ABI of the grouped-head attention library: argument validation, split
+// planning and dispatch.  Every check runs on the host before anything is
+// launched; see include/gha.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/gha.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gha_status fail(gha_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+int elem_size(gha_dtype t) { return t == GHA_F32 ? 4 : 2; }
+
+// A view must be present, non-negative and keep every row 16-byte aligned.
+gha_status check_view(const char* name, const gha_tensor* t, gha_dtype dt, bool use_sb,
+                      bool use_sh, bool use_ss) {
+  if (t == nullptr || t->ptr == nullptr) return fail(GHA_ERR_NULL, "%s: null tensor or pointer", name);
+  if (t->sb < 0 || t->sh < 0 || t->ss < 0) return fail(GHA_ERR_STRIDE, "%s: negative stride", name);
+  const int64_t es = elem_size(dt);
+  if ((reinterpret_cast<uintptr_t>(t->ptr) & 15u) != 0)
+    return fail(GHA_ERR_ALIGN, "%s: pointer not 16-byte aligned", name);
+  if ((use_sb && (t->sb * es) % 16) || (use_sh && (t->sh * es) % 16) || (use_ss && (t->ss * es) % 16))
+    return fail(GHA_ERR_ALIGN, "%s: a stride is not a multiple of 16 bytes", name);
+  return GHA_OK;
+}
+
+gha_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GHA_ERR_HIP, "no HIP device: %s", hipGetErrorString(e));
+  return GHA_OK;
+}
+
+gha_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GHA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  g_err[0] = 0;
+  return GHA_OK;
+}
+
+// Split plan of the GQA decode: aim for about 8192 work-groups so that short
+// and long sequences spread evenly over 256 CUs; splits are whole multiples
+// of 256 keys (four waves x 64 keys).
+void gqa_decode_plan(int B, int h_kv, int n_rb, int L_max, int* split_len, int* n_splits) {
+  const int64_t units = (int64_t)B * h_kv * n_rb;
+  const int64_t want = units >= 8192 ? 1 : (8192 + units - 1) / units;
+  int64_t sl = (L_max + want - 1) / want;
+  sl = (sl + 255) / 256 * 256;
+  if (sl < 256) sl = 256;
+  *split_len = (int)sl;
+  *n_splits = (int)((L_max + sl - 1) / sl);
+}
+
+// Split plan of the latent decode: about 1024 work-groups; each split's
+// partial (64 rows x 512 fp32) should stay small next to the tokens it reads.
+void latent_plan(int B, int n_rb, int L_max, int* split_len, int* n_splits) {
+  const int64_t units = (int64_t)B * n_rb;
+  const int64_t want = units >= 1024 ? 1 : (1024 + units - 1) / units;
+  int64_t sl = (L_max + want - 1) / want;
+  sl = (sl + 255) / 256 * 256;
+  if (sl < 256) sl = 256;
+  *split_len = (int)sl;
+  *n_splits = (int)((L_max + sl - 1) / sl);
+}
+
+int gqa_row_blocks(int h_q, int h_kv, int s_q) { return ((h_q / h_kv) * s_q + 15) / 16; }
+int latent_row_blocks(int h_q, int s_q) { return (h_q * s_q + 63) / 64; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gha_status_string(gha_status s) {
+  switch (s) {
+    case GHA_OK: return "GHA_OK";
+    case GHA_ERR_NULL: return "GHA_ERR_NULL";
+    case GHA_ERR_SHAPE: return "GHA_ERR_SHAPE";
+    case GHA_ERR_GROUPING: return "GHA_ERR_GROUPING";
+    case GHA_ERR_STRIDE: return "GHA_ERR_STRIDE";
+    case GHA_ERR_ALIGN: return "GHA_ERR_ALIGN";
+    case GHA_ERR_DTYPE: return "GHA_ERR_DTYPE";
+    case GHA_ERR_HEAD_DIM: return "GHA_ERR_HEAD_DIM";
+    case GHA_ERR_WORKSPACE: return "GHA_ERR_WORKSPACE";
+    case GHA_ERR_HIP: return "GHA_ERR_HIP";
+  }
+  return "GHA_ERR_UNKNOWN";
+}
+
+const char* gha_last_error(void) { return g_err; }
+
+int gha_version(void) { return 100; }  // 0.1.0
+
+gha_status gqa_prefill(const gha_tensor* q, const gha_tensor* k, const gha_tensor* v,
+                       const gha_tensor* o, float* lse, int B, int h_q, int h_kv, int S_q,
+                       int S_k, int d, gha_dtype in_dtype, gha_dtype out_dtype, float scale,
+                       int causal, void* stream) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || S_q < 1 || S_k < 1)
+    return fail(GHA_ERR_SHAPE, "sizes must be positive (B=%d h_q=%d h_kv=%d S_q=%d S_k=%d)", B, h_q, h_kv, S_q, S_k);
+  if (h_q % h_kv) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
+  if (causal && S_q > S_k) return fail(GHA_ERR_SHAPE, "causal needs S_q <= S_k (got %d > %d)", S_q, S_k);
+  if (d != 64 && d != 128) return fail(GHA_ERR_HEAD_DIM, "head dim %d not in {64, 128}", d);
+  const bool f32in = in_dtype == GHA_F32;
+  if (!((in_dtype == GHA_BF16 && (out_dtype == GHA_BF16 || out_dtype == GHA_F32)) ||
+        (f32in && out_dtype == GHA_F32)))
+    return fail(GHA_ERR_DTYPE, "unsupported in/out dtypes (%d, %d)", (int)in_dtype, (int)out_dtype);
+  gha_status s;
+  if ((s = check_view("q", q, in_dtype, B > 1, h_q > 1, S_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("k", k, in_dtype, B > 1, h_kv > 1, S_k > 1)) != GHA_OK) return s;
+  if ((s = check_view("v", v, in_dtype, B > 1, h_kv > 1, S_k > 1)) != GHA_OK) return s;
+  if ((s = check_view("o", o, out_dtype, B > 1, h_q > 1, S_q > 1)) != GHA_OK) return s;
+  if ((s = check_device()) != GHA_OK) return s;
+
+  gha::PrefillArgs a{};
+  a.q = q->ptr; a.q_sb = q->sb; a.q_sh = q->sh; a.q_ss = q->ss;
+  a.k = k->ptr; a.k_sb = k->sb; a.k_sh = k->sh; a.k_ss = k->ss;
+  a.v = v->ptr; a.v_sb = v->sb; a.v_sh = v->sh; a.v_ss = v->ss;
+  a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
+  a.lse = lse; a.lse_heads = h_q;
+  a.S_q = S_q; a.S_k = S_k; a.h_kv = h_kv; a.group = h_q / h_kv;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+  a.B = B;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (f32in) {
+    a.n_blocks = B;
+    return launched(gha::launch_prefill_f32(a, d, st), "gqa_prefill(f32)");
+  }
+  const int G = a.group;
+  a.heads_per_wg = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
+  a.n_subgroups = G / a.heads_per_wg;
+  const int pos_per_wg = (4 / a.heads_per_wg) * gha::prefill_rows_per_wave();
+  a.n_qblocks = (S_q + pos_per_wg - 1) / pos_per_wg;
+  const int64_t nb = (int64_t)B * h_kv * a.n_subgroups * a.n_qblocks;
+  if (nb > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  a.n_blocks = (int)nb;
+  a.dv_head = d;
+  return launched(gha::launch_prefill_bf16(a, d, d, out_dtype == GHA_F32, false, st), "gqa_prefill");
+}
+
+size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint, int d) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_max_hint < 1 || d < 1 || h_q % h_kv) return 0;
+  const int n_rb = gqa_row_blocks(h_q, h_kv, s_q);
+  int sl, ns;
+  gqa_decode_plan(B, h_kv, n_rb, L_max_hint, &sl, &ns);
+  const size_t rows = (size_t)B * h_kv * n_rb * ns * 16;
+  return rows * (size_t)d * 4 + rows * 4;
+}
+
+gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
+                      const int32_t* seqlens_k, const gha_tensor* o, float* lse, int B, int h_q,
+                      int h_kv, int s_q, int L_cap, int L_max_hint, int d, gha_dtype in_dtype,
+                      gha_dtype out_dtype, float scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
+    return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (h_q % h_kv) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
+  if (L_max_hint > L_cap || s_q > L_max_hint)
+    return fail(GHA_ERR_SHAPE, "need s_q <= L_max_hint <= L_cap (s_q=%d L_max_hint=%d L_cap=%d)", s_q, L_max_hint, L_cap);
+  if (d != 64 && d != 128) return fail(GHA_ERR_HEAD_DIM, "head dim %d not in {64, 128}", d);
+  if (in_dtype != GHA_BF16 || (out_dtype != GHA_BF16 && out_dtype != GHA_F32))
+    return fail(GHA_ERR_DTYPE, "decode takes bf16 inputs and bf16 or f32 outputs");
+  if (seqlens_k == nullptr) return fail(GHA_ERR_NULL, "seqlens_k is null");
+  gha_status s;
+  if ((s = check_view("q", q, in_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("k_cache", k_cache, in_dtype, B > 1, h_kv > 1, true)) != GHA_OK) return s;
+  if ((s = check_view("v_cache", v_cache, in_dtype, B > 1, h_kv > 1, true)) != GHA_OK) return s;
+  if ((s = check_view("o", o, out_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  const size_t need = gqa_decode_workspace_bytes(B, h_q, h_kv, s_q, L_max_hint, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
+  if ((s = check_device()) != GHA_OK) return s;
+
+  gha::DecodeArgs a{};
+  a.q = q->ptr; a.q_sb = q->sb; a.q_sh = q->sh; a.q_ss = q->ss;
+  a.k = k_cache->ptr; a.k_sb = k_cache->sb; a.k_sh = k_cache->sh; a.k_ss = k_cache->ss;
+  a.v = v_cache->ptr; a.v_sb = v_cache->sb; a.v_sh = v_cache->sh; a.v_ss = v_cache->ss;
+  a.seqlens = seqlens_k;
+  a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
+  a.lse = lse;
+  a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.s_q = s_q; a.group = h_q / h_kv;
+  a.rows = a.group * s_q;
+  a.n_rb = gqa_row_blocks(h_q, h_kv, s_q);
+  gqa_decode_plan(B, h_kv, a.n_rb, L_max_hint, &a.split_len, &a.n_splits);
+  const size_t n_part = (size_t)B * h_kv * a.n_rb * a.n_splits * 16;
+  a.ws_o = reinterpret_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + n_part * d;
+  a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+  if ((int64_t)B * h_kv * a.n_rb * a.n_splits > (1LL << 30))
+    return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  return launched(gha::launch_gqa_decode(a, d, out_dtype == GHA_F32, reinterpret_cast<hipStream_t>(stream)),
+                  "gqa_decode");
+}
+
+gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, const gha_tensor* v,
+                                    const gha_tensor* o, float* lse, int B, int h, int n_grp, int S,
+                                    int d_qk, int d_v, gha_dtype in_dtype, gha_dtype out_dtype,
+                                    float scale, int causal, void* stream) {
+  if (B < 1 || h < 1 || n_grp < 1 || S < 1) return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (h % n_grp) return fail(GHA_ERR_GROUPING, "h=%d is not a multiple of n_grp=%d", h, n_grp);
+  const int per = h / n_grp;
+  const int DV = per * d_v;
+  if ((d_qk != 64 && d_qk != 128) || d_v != 64 || (DV != 64 && DV != 128 && DV != 256))
+    return fail(GHA_ERR_HEAD_DIM, "need d_qk in {64,128}, d_v == 64 and (h/n_grp)*d_v in {64,128,256} (d_qk=%d d_v=%d per=%d)", d_qk, d_v, per);
+  if (in_dtype != GHA_BF16 || (out_dtype != GHA_BF16 && out_dtype != GHA_F32))
+    return fail(GHA_ERR_DTYPE, "GTA takes bf16 inputs and bf16 or f32 outputs");
+  gha_status s;
+  if ((s = check_view("q", q, in_dtype, B > 1, n_grp > 1, S > 1)) != GHA_OK) return s;
+  if ((s = check_view("k", k, in_dtype, B > 1, n_grp > 1, S > 1)) != GHA_OK) return s;
+  if ((s = check_view("v", v, in_dtype, B > 1, h > 1, S > 1)) != GHA_OK) return s;
+  if ((s = check_view("o", o, out_dtype, B > 1, h > 1, S > 1)) != GHA_OK) return s;
+  if ((s = check_device()) != GHA_OK) return s;
+
+  gha::PrefillArgs a{};
+  a.q = q->ptr; a.q_sb = q->sb; a.q_sh = q->sh; a.q_ss = q->ss;
+  a.k = k->ptr; a.k_sb = k->sb; a.k_sh = k->sh; a.k_ss = k->ss;
+  a.v = v->ptr; a.v_sb = v->sb; a.v_sh = v->sh; a.v_ss = v->ss;
+  a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
+  a.lse = lse; a.lse_heads = n_grp;
+  a.S_q = S; a.S_k = S; a.h_kv = n_grp; a.group = per;
+  a.heads_per_wg = 1; a.n_subgroups = 1;
+  const int pos_per_wg = 4 * gha::prefill_rows_per_wave();
+  a.n_qblocks = (S + pos_per_wg - 1) / pos_per_wg;
+  a.n_blocks = B * n_grp * a.n_qblocks;
+  a.dv_head = d_v;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d_qk);
+  a.B = B;
+  return launched(gha::launch_prefill_bf16(a, d_qk, DV, out_dtype == GHA_F32, true,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                  "gta_shared_score_prefill");
+}
+
+size_t latent_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_hint, int r_kv) {
+  if (B < 1 || h_q < 1 || s_q < 1 || L_max_hint < 1 || r_kv < 1) return 0;
+  const int n_rb = latent_row_blocks(h_q, s_q);
+  int sl, ns;
+  latent_plan(B, n_rb, L_max_hint, &sl, &ns);
+  const size_t rows = (size_t)B * n_rb * ns * 64;
+  return rows * (size_t)r_kv * 4 + rows * 4;
+}
+
+gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rope,
+                                const gha_tensor* c_kv, const gha_tensor* k_rope,
+                                const int32_t* seqlens_k, const gha_tensor* o_lat, float* lse,
+                                int B, int h_q, int s_q, int L_cap, int L_max_hint, int r_kv,
+                                int d_r, gha_dtype in_dtype, gha_dtype out_dtype, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || h_q < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
+    return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (L_max_hint > L_cap || s_q > L_max_hint)
+    return fail(GHA_ERR_SHAPE, "need s_q <= L_max_hint <= L_cap (s_q=%d L_max_hint=%d L_cap=%d)", s_q, L_max_hint, L_cap);
+  if (r_kv != 512 || d_r != 64) return fail(GHA_ERR_HEAD_DIM, "need r_kv == 512 and d_r == 64 (got %d, %d)", r_kv, d_r);
+  if (!(scale > 0.f)) return fail(GHA_ERR_SHAPE, "scale must be given (> 0) for the absorbed path");
+  if (in_dtype != GHA_BF16 || (out_dtype != GHA_BF16 && out_dtype != GHA_F32))
+    return fail(GHA_ERR_DTYPE, "latent decode takes bf16 inputs and bf16 or f32 outputs");
+  if (seqlens_k == nullptr) return fail(GHA_ERR_NULL, "seqlens_k is null");
+  gha_status s;
+  if ((s = check_view("q_lat", q_lat, in_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("q_rope", q_rope, in_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("c_kv", c_kv, in_dtype, B > 1, false, true)) != GHA_OK) return s;
+  if ((s = check_view("k_rope", k_rope, in_dtype, B > 1, false, true)) != GHA_OK) return s;
+  if ((s = check_view("o_lat", o_lat, out_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  const size_t need = latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_max_hint, r_kv);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
+  if ((s = check_device()) != GHA_OK) return s;
+
+  gha::LatentArgs a{};
+  a.q = q_lat->ptr; a.q_sb = q_lat->sb; a.q_sh = q_lat->sh; a.q_ss = q_lat->ss;
+  a.qr = q_rope->ptr; a.qr_sb = q_rope->sb; a.qr_sh = q_rope->sh; a.qr_ss = q_rope->ss;
+  a.c = c_kv->ptr; a.c_sb = c_kv->sb; a.c_ss = c_kv->ss;
+  a.kr = k_rope->ptr; a.kr_sb = k_rope->sb; a.kr_ss = k_rope->ss;
+  a.seqlens = seqlens_k;
+  a.o = o_lat->ptr; a.o_sb = o_lat->sb; a.o_sh = o_lat->sh; a.o_ss = o_lat->ss;
+  a.lse = lse;
+  a.B = B; a.h_q = h_q; a.s_q = s_q;
+  a.n_rb = latent_row_blocks(h_q, s_q);
+  latent_plan(B, a.n_rb, L_max_hint, &a.split_len, &a.n_splits);
+  const size_t n_part = (size_t)B * a.n_rb * a.n_splits * 64;
+  a.ws_o = reinterpret_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + n_part * r_kv;
+  a.scale = scale;
+  if ((int64_t)B * a.n_rb * a.n_splits > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  return launched(gha::launch_latent_decode(a, out_dtype == GHA_F32, reinterpret_cast<hipStream_t>(stream)),
+                  "latent_absorb_decode");
+}
+
+}  // extern "C"

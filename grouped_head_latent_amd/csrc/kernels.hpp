@@ -1,0 +1,71 @@
+// Launch descriptors shared by the C-ABI layer and the kernels.  Every size
+// and stride here has already been validated on the host.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gha {
+
+struct PrefillArgs {
+  const void* q; int64_t q_sb, q_sh, q_ss;
+  const void* k; int64_t k_sb, k_sh, k_ss;
+  const void* v; int64_t v_sb, v_sh, v_ss;
+  void* o;       int64_t o_sb, o_sh, o_ss;
+  float* lse;         // dense (B, lse_heads, S_q) or null
+  int lse_heads;      // h_q (GQA) or n_grp (GTA)
+  int S_q, S_k;
+  int h_kv;           // GQA: key/value heads; GTA: groups
+  int group;          // GQA: query heads per KV head; GTA: heads per group
+  int heads_per_wg;   // query heads sharing one work-group (1, 2 or 4)
+  int n_subgroups;    // group / heads_per_wg
+  int n_qblocks;      // position blocks per (batch, head set)
+  int n_blocks;       // work-groups with work
+  int dv_head;        // GTA: value width of one head
+  int causal;
+  int B;
+  float scale;
+};
+
+struct DecodeArgs {
+  const void* q; int64_t q_sb, q_sh, q_ss;
+  const void* k; int64_t k_sb, k_sh, k_ss;
+  const void* v; int64_t v_sb, v_sh, v_ss;
+  const int32_t* seqlens;
+  void* o;       int64_t o_sb, o_sh, o_ss;
+  float* lse;         // dense (B, h_q, s_q) or null
+  float* ws_o;        // (units, n_splits, 16, d) fp32 partial outputs
+  float* ws_lse;      // (units, n_splits, 16) fp32 partial log2-sum-exp
+  int B, h_q, h_kv, s_q, group;
+  int rows;           // group * s_q query rows per KV head
+  int n_rb;           // 16-row blocks per KV head
+  int split_len;      // keys per split (multiple of 256)
+  int n_splits;       // splits per unit at L_max_hint
+  float scale;
+};
+
+struct LatentArgs {
+  const void* q; int64_t q_sb, q_sh, q_ss;     // q_lat (B, s_q, h_q, r_kv)
+  const void* qr; int64_t qr_sb, qr_sh, qr_ss; // q_rope (B, s_q, h_q, d_r)
+  const void* c; int64_t c_sb, c_ss;           // c_kv (B, L_cap, r_kv)
+  const void* kr; int64_t kr_sb, kr_ss;        // k_rope (B, L_cap, d_r)
+  const int32_t* seqlens;
+  void* o;       int64_t o_sb, o_sh, o_ss;     // o_lat (B, s_q, h_q, r_kv)
+  float* lse;         // dense (B, s_q, h_q) or null
+  float* ws_o;        // (B, n_rb, n_splits, 64, r_kv)
+  float* ws_lse;      // (B, n_rb, n_splits, 64)
+  int B, h_q, s_q;
+  int n_rb;           // 64-row blocks over s_q * h_q rows
+  int split_len;
+  int n_splits;
+  float scale;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int dqk, int dv, bool out_f32, bool gta,
+                               hipStream_t st);
+hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
+int prefill_rows_per_wave();
+
+hipError_t launch_gqa_decode(const DecodeArgs& a, int d, bool out_f32, hipStream_t st);
+hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st);
+
+}  // namespace gha

@@ -1,0 +1,330 @@
+// Causal grouped-head attention prefill, bf16 inputs, fp32 accumulation, on
+// gfx950 MFMA.  One kernel serves two of the library's operations:
+//
+//  * GQA ("Grouped Query Attention (GQA)", Ultralytics glossary, "How GQA
+//    works"): a group of query heads shares one key/value head.  A work-group
+//    takes up to four query heads of one group and one block of positions, so
+//    every K/V tile staged in LDS is used by all of those heads.
+//  * GTA shared-score attention ("GTA: Grouped-head latenT Attention" news
+//    article, grouped shared attention matrix): a group has one query and one
+//    key, so one score matrix, applied to the value of every head in the
+//    group.  Here the group's head values are treated as one wide value
+//    (heads_per_group * d_v columns), so P is computed once per group and
+//    multiplied into all of the group's heads in the same pass.
+//
+// Per wave: QT tiles of 16 query rows.  Per iteration: 64 keys.
+//   S^T (keys x queries) = K Q^T on MFMA, K from LDS, Q^T resident in VGPRs.
+//   Online softmax on S^T: each lane holds one query column, so the running
+//   max and the rescale factor are per-lane scalars.
+//   O^T (dv x queries) += V^T P^T on MFMA: P^T is the S^T accumulator itself,
+//   converted to bf16 in place; V^T comes from LDS, where the tile was stored
+//   transposed (and its keys permuted to match the accumulator's key order)
+//   when it was staged.
+// K/V tiles are double-buffered in LDS: global loads for tile t+1 are issued
+// before tile t is computed.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace gha {
+
+namespace {
+
+constexpr int KB = 64;  // keys per iteration
+
+// Position of key u (0..63) of a tile inside a V^T row.  The S^T accumulator
+// of lane group g holds keys 16*kt + 4*g + r; the PV contraction step ks takes
+// tiles 2ks and 2ks+1, so group g's eight slots are keys
+// 32ks + {4g..4g+3, 16+4g..16+4g+3}, stored contiguously here.
+__device__ __forceinline__ int vt_pos(int u) {
+  int ks = u >> 5, w = u & 31, half = w >> 4, g = (w & 15) >> 2, r = w & 3;
+  return 32 * ks + 8 * g + 4 * half + r;
+}
+
+template <int DQK, int DV, int QT, bool OUT_F32, bool GTA>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int KP = DQK + 8;   // K row pitch in LDS (elements): 16 B pad
+  constexpr int VP = KB + 8;    // V^T row pitch in LDS (elements): 16 B pad
+  constexpr int K_ELEMS = KB * KP;
+  constexpr int V_ELEMS = DV * VP;
+  constexpr int DS = DQK / 32;  // contraction steps of the score MFMA
+  constexpr int DT = DV / 16;   // 16-wide output column tiles
+  constexpr int K_LOADS = KB * DQK / 8 / 256;   // 16-byte K loads per thread
+  constexpr int V_UNITS = (KB / 4) * (DV / 8);  // (4 keys x 8 columns) units
+  constexpr int V_PER_THREAD = (V_UNITS + 255) / 256;
+  static_assert(K_LOADS >= 1, "tile too small");
+
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (K_ELEMS + V_ELEMS)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 15;  // MFMA row / column index
+  const int lg = lane >> 4;  // MFMA lane group
+
+  // ---- which work this work-group does -----------------------------------
+  const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  if (lid >= (uint32_t)a.n_blocks) return;
+  const int n_qb = a.n_qblocks;
+  const int qb = n_qb - 1 - (int)(lid % n_qb);  // heavy (late) blocks first
+  int rest = (int)(lid / n_qb);
+  const int sg = rest % a.n_subgroups;  rest /= a.n_subgroups;
+  const int kvh = rest % a.h_kv;        // GQA: KV head; GTA: group
+  const int b = rest / a.h_kv;
+
+  const int wph = 4 / a.heads_per_wg;   // waves per head
+  const int pos_per_wg = wph * QT * 16;
+  const int qhead = GTA ? kvh : kvh * a.group + sg * a.heads_per_wg + wave / wph;
+  const int pos0 = qb * pos_per_wg + (wave % wph) * QT * 16;  // this wave's first row
+  const int off = a.S_k - a.S_q;  // bottom-right causal offset
+
+  // keys this work-group must visit, and this wave's own last visible key
+  int k_end = a.S_k;
+  int wave_kmax = a.S_k - 1;
+  if (a.causal) {
+    int last_pos = min(qb * pos_per_wg + pos_per_wg - 1, a.S_q - 1);
+    k_end = min(a.S_k, last_pos + off + 1);
+    wave_kmax = min(a.S_k - 1, min(pos0 + QT * 16 - 1, a.S_q - 1) + off);
+  }
+  const int n_kb = (k_end + KB - 1) / KB;
+
+  const __bf16* qbase = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)qhead * a.q_sh;
+  const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
+  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb +
+                        (int64_t)(GTA ? kvh * a.group : kvh) * a.v_sh;
+
+  // ---- resident Q^T fragments (B operand of the score MFMA) ---------------
+  u32x4 qf[QT][DS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int pos = pos0 + qt * 16 + li;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      if (pos < a.S_q)
+        qf[qt][s] = ld16(qbase + (int64_t)pos * a.q_ss + 32 * s + 8 * lg);
+      else
+        qf[qt][s] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // ---- staging: global -> registers -> LDS --------------------------------
+  u32x4 kreg[K_LOADS];
+  u32x4 vreg[V_PER_THREAD][4];
+
+  auto load_tile = [&](int kb) {
+    const int key0 = kb * KB;
+#pragma unroll
+    for (int i = 0; i < K_LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
+      const int kk = key0 + key;
+      kreg[i] = (kk < a.S_k) ? ld16(kbase + (int64_t)kk * a.k_ss + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_THREAD; ++i) {
+      const int u = tid + 256 * i;
+      if (u < V_UNITS) {
+        const int dchunk = u % (DV / 8), kgrp = u / (DV / 8);
+        const int d = dchunk * 8;
+        const __bf16* vp;
+        if constexpr (GTA) {
+          vp = vbase + (int64_t)(d / a.dv_head) * a.v_sh + (d % a.dv_head);
+        } else {
+          vp = vbase + d;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = key0 + 4 * kgrp + r;
+          vreg[i][r] = (kk < a.S_k) ? ld16(vp + (int64_t)kk * a.v_ss) : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    __bf16* ks = smem + buf * (K_ELEMS + V_ELEMS);
+    __bf16* vs = ks + K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < K_LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
+      st16(ks + key * KP + col, kreg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_THREAD; ++i) {
+      const int u = tid + 256 * i;
+      if (u < V_UNITS) {
+        const int dchunk = u % (DV / 8), kgrp = u / (DV / 8);
+        const int p = vt_pos(4 * kgrp);
+        // 4 keys x 8 columns -> 8 rows (columns) x 4 keys
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          u32x2 lo = {lo_pair(vreg[i][0][w], vreg[i][1][w]), lo_pair(vreg[i][2][w], vreg[i][3][w])};
+          u32x2 hi = {hi_pair(vreg[i][0][w], vreg[i][1][w]), hi_pair(vreg[i][2][w], vreg[i][3][w])};
+          *reinterpret_cast<u32x2*>(vs + (dchunk * 8 + 2 * w) * VP + p) = lo;
+          *reinterpret_cast<u32x2*>(vs + (dchunk * 8 + 2 * w + 1) * VP + p) = hi;
+        }
+      }
+    }
+  };
+
+  // ---- running state -------------------------------------------------------
+  f32x4 oacc[DT][QT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m2[QT], lsum[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) { m2[qt] = kNegInf; lsum[qt] = 0.f; }
+  const float c2 = a.scale * kLog2e;
+
+  if (n_kb > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int kb = 0; kb < n_kb; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < n_kb) load_tile(kb + 1);
+
+    const int key0 = kb * KB;
+    if (key0 <= wave_kmax) {  // wave-uniform: skip tiles wholly above the diagonal
+      const __bf16* ks = smem + buf * (K_ELEMS + V_ELEMS);
+      const __bf16* vs = ks + K_ELEMS;
+
+      // S^T = K Q^T
+      f32x4 sacc[4][QT];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          u32x4 kf = ld16(ks + (16 * kt + li) * KP + 32 * s + 8 * lg);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma_bf16(kf, qf[qt][s], sacc[kt][qt]);
+        }
+      }
+
+      // mask + online softmax (per query column = per lane)
+      const bool need_mask = (key0 + KB > a.S_k) ||
+                             (a.causal && key0 + KB - 1 > pos0 + off);
+      u32x4 pf[QT][2];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int qpos = pos0 + qt * 16 + li;
+        const int kmax = a.causal ? min(qpos + off, a.S_k - 1) : a.S_k - 1;
+        float mx = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (need_mask && key0 + 16 * kt + 4 * lg + r > kmax) sacc[kt][qt][r] = kNegInf;
+            mx = fmaxf(mx, sacc[kt][qt][r]);
+          }
+        mx = group4_max(mx);
+        const float mnew = fmaxf(m2[qt], mx * c2);
+        const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2[qt] - mnew);
+        const float msub = (mnew == kNegInf) ? 0.f : mnew;
+        m2[qt] = mnew;
+        float p[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[kt][r] = fast_exp2(__builtin_fmaf(sacc[kt][qt][r], c2, -msub));
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          pf[qt][k2] = u32x4{pack_bf16(p[2 * k2][0], p[2 * k2][1]), pack_bf16(p[2 * k2][2], p[2 * k2][3]),
+                             pack_bf16(p[2 * k2 + 1][0], p[2 * k2 + 1][1]),
+                             pack_bf16(p[2 * k2 + 1][2], p[2 * k2 + 1][3])};
+        }
+        lsum[qt] = lsum[qt] * alpha + (bf16x8_sum(pf[qt][0]) + bf16x8_sum(pf[qt][1]));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+      }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          u32x4 vf = ld16(vs + (16 * dt + li) * VP + 32 * k2 + 8 * lg);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma_bf16(vf, pf[qt][k2], oacc[dt][qt]);
+        }
+      }
+    }
+
+    if (kb + 1 < n_kb) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise and write --------------------------------------
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qpos = pos0 + qt * 16 + li;
+    const float l = group4_sum(lsum[qt]);
+    if (qpos >= a.S_q) continue;
+    const float inv = 1.f / l;
+    if (a.lse != nullptr && lg == 0) {
+      a.lse[((int64_t)b * a.lse_heads + qhead) * a.S_q + qpos] = (m2[qt] + fast_log2(l)) * kLn2;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 16 * dt + 4 * lg;
+      int64_t obase;
+      if constexpr (GTA) {
+        obase = (int64_t)b * a.o_sb + (int64_t)(kvh * a.group + d / a.dv_head) * a.o_sh +
+                (int64_t)qpos * a.o_ss + (d % a.dv_head);
+      } else {
+        obase = (int64_t)b * a.o_sb + (int64_t)qhead * a.o_sh + (int64_t)qpos * a.o_ss + d;
+      }
+      const f32x4 v = oacc[dt][qt] * inv;
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<f32x4*>((float*)a.o + obase) = v;
+      } else {
+        *reinterpret_cast<u32x2*>((__bf16*)a.o + obase) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      }
+    }
+  }
+}
+
+template <int DQK, int DV, int QT, bool OUT_F32, bool GTA>
+hipError_t launch_one(const PrefillArgs& a, hipStream_t st) {
+  const uint32_t padded = (uint32_t)((a.n_blocks + 7) / 8 * 8);
+  hipLaunchKernelGGL((prefill_bf16_kernel<DQK, DV, QT, OUT_F32, GTA>), dim3(padded), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <bool GTA>
+hipError_t launch_dims(const PrefillArgs& a, int dqk, int dv, bool out_f32, hipStream_t st) {
+#define GHA_CASE(DQ, DVV, QTT)                                                        \
+  if (dqk == DQ && dv == DVV)                                                         \
+    return out_f32 ? launch_one<DQ, DVV, QTT, true, GTA>(a, st)                       \
+                   : launch_one<DQ, DVV, QTT, false, GTA>(a, st);
+  if constexpr (!GTA) {
+    GHA_CASE(128, 128, 2)
+    GHA_CASE(64, 64, 2)
+  } else {
+    GHA_CASE(64, 256, 2)
+    GHA_CASE(64, 128, 2)
+    GHA_CASE(64, 64, 2)
+    GHA_CASE(128, 256, 2)
+    GHA_CASE(128, 128, 2)
+    GHA_CASE(128, 64, 2)
+  }
+#undef GHA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int prefill_rows_per_wave() { return 2 * 16; }
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int dqk, int dv, bool out_f32, bool gta,
+                               hipStream_t st) {
+  return gta ? launch_dims<true>(a, dqk, dv, out_f32, st) : launch_dims<false>(a, dqk, dv, out_f32, st);
+}
+
+}  // namespace gha

@@ -1,0 +1,179 @@
+/* gha.h - C ABI of the grouped-head attention library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Four operations, all exact causal scaled dot-product attention
+ * o = softmax(scale * q k^T) v with fp32 accumulation, differing in which heads
+ * share what:
+ *
+ *   gqa_prefill               grouped-query attention over a whole sequence:
+ *                             consecutive groups of h_q/h_kv query heads share
+ *                             one key head and one value head.  One group is
+ *                             MQA, h_kv == h_q is MHA.  ("Grouped Query
+ *                             Attention (GQA)", Ultralytics glossary, section
+ *                             "How GQA works".)
+ *   gqa_decode                the same for s_q new query tokens per sequence
+ *                             against a contiguous KV cache with per-sequence
+ *                             lengths; split-KV with a log-sum-exp merge.
+ *   gta_shared_score_prefill  GTA's grouped shared attention matrix: heads are
+ *                             split into groups, each group has one query/key
+ *                             pair and so one score matrix, which is applied
+ *                             to the value of every head in the group.  ("GTA:
+ *                             Grouped-head latenT Attention" news article,
+ *                             grouped shared attention matrix mechanism.)
+ *   latent_absorb_decode      the absorbed (MQA-like) path of MLA/GQLA: every
+ *                             query head attends straight over the cached
+ *                             latent c^KV (width r_kv) plus the shared RoPE key
+ *                             k^R (width d_r); the value is the latent itself.
+ *                             ("GQLA: Group-Query Latent Attention ...",
+ *                             section 1, section 3.1 Eq. (1), Figure 2 right.)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are described by gha_tensor: a device pointer plus element strides
+ * for the batch, head and token axes.  The feature (last) axis must be
+ * contiguous, and ptr and every stride must keep each row 16-byte aligned
+ * (GHA_ERR_ALIGN otherwise).  Strides may be any non-negative values, so
+ * (B, H, S, D), (B, S, H, D) and views into larger buffers are all accepted.
+ *
+ * Element types: GHA_BF16 inputs with GHA_BF16 or GHA_F32 outputs everywhere;
+ * GHA_F32 inputs (with GHA_F32 outputs) for gqa_prefill only.
+ *
+ * Causal alignment is bottom-right: with S_k keys and S_q queries, query t
+ * sees keys 0 .. t + (S_k - S_q).  For prefill with S_q == S_k that is the
+ * usual u <= t; for decode, seqlens_k[b] counts the cache including the s_q
+ * new tokens, so query t of sequence b sees keys 0 .. L_b - s_q + t.
+ *
+ * Outputs: o has the query's batch/head/token indexing with the value width;
+ * lse (optional, may be NULL) receives log(sum_u exp(scale * q.k_u)) in
+ * natural-log units, fp32, densely packed as documented per call.
+ *
+ * Ownership and errors: the caller owns every buffer (device memory, e.g.
+ * from torch).  The library never allocates, frees or synchronises; it
+ * enqueues kernels on `stream` (a hipStream_t, NULL for the default stream)
+ * and returns.  Every argument is checked on the host before anything is
+ * launched; on any error nothing is launched or written, the status says what
+ * class of error it was and gha_last_error() (thread-local) gives the detail.
+ * A failed launch returns GHA_ERR_HIP.  Results are deterministic: the split
+ * plan depends only on the arguments and no atomics are used.
+ */
+#ifndef GHA_H_
+#define GHA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GHA_OK = 0,
+  GHA_ERR_NULL = 1,      /* a required pointer is NULL */
+  GHA_ERR_SHAPE = 2,     /* a size is out of range or inconsistent */
+  GHA_ERR_GROUPING = 3,  /* h_q % h_kv != 0, or h % n_grp != 0 */
+  GHA_ERR_STRIDE = 4,    /* a negative stride */
+  GHA_ERR_ALIGN = 5,     /* a row is not 16-byte aligned */
+  GHA_ERR_DTYPE = 6,     /* unsupported input/output element types */
+  GHA_ERR_HEAD_DIM = 7,  /* unsupported head / latent width */
+  GHA_ERR_WORKSPACE = 8, /* workspace missing or too small */
+  GHA_ERR_HIP = 9        /* no usable device, or a launch failed */
+} gha_status;
+
+typedef enum { GHA_F32 = 0, GHA_BF16 = 1 } gha_dtype;
+
+/* A strided view: element (b, h, s, c) lives at ptr[b*sb + h*sh + s*ss + c]. */
+typedef struct {
+  void* ptr;
+  int64_t sb, sh, ss;
+} gha_tensor;
+
+/* Grouped-query attention over a sequence ("How GQA works": a group of
+ * consecutive query heads shares one key head and one value head; inside each
+ * head the computation is ordinary scaled dot-product attention).
+ *   q (B, h_q, S_q, d), k (B, h_kv, S_k, d), v (B, h_kv, S_k, d),
+ *   o (B, h_q, S_q, d); lse NULL or dense fp32 (B, h_q, S_q).
+ * Query head i reads key/value head i / (h_q / h_kv).
+ * Requires 1 <= S_q <= S_k when causal; d in {64, 128};
+ * in/out: BF16/BF16, BF16/F32 or F32/F32.  scale <= 0 means 1/sqrt(d). */
+gha_status gqa_prefill(const gha_tensor* q, const gha_tensor* k, const gha_tensor* v,
+                       const gha_tensor* o, float* lse,
+                       int B, int h_q, int h_kv, int S_q, int S_k, int d,
+                       gha_dtype in_dtype, gha_dtype out_dtype,
+                       float scale, int causal, void* stream);
+
+/* One decode step of grouped-query attention against a contiguous KV cache
+ * (the GQLA page's section 1: each generated token reads the whole cached
+ * history).
+ *   q (B, h_q, s_q, d); k_cache, v_cache (B, h_kv, L_cap, d);
+ *   seqlens_k: device int32 (B,), s_q <= seqlens_k[b] <= L_cap, counting the
+ *   s_q new tokens, whose keys are the last s_q cached;
+ *   o (B, h_q, s_q, d); lse NULL or dense fp32 (B, h_q, s_q).
+ * L_max_hint: an upper bound on max_b seqlens_k[b] (<= L_cap); it sizes the
+ * split plan, and lengths above it are a precondition violation.
+ * d == 128 or 64; in BF16, out BF16 or F32.  scale <= 0 means 1/sqrt(d).
+ * workspace: device memory of at least gqa_decode_workspace_bytes(...) bytes
+ * (the split partials); its contents on entry do not matter. */
+gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache,
+                      const gha_tensor* v_cache, const int32_t* seqlens_k,
+                      const gha_tensor* o, float* lse,
+                      int B, int h_q, int h_kv, int s_q, int L_cap, int L_max_hint,
+                      int d, gha_dtype in_dtype, gha_dtype out_dtype, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint, int d);
+
+/* GTA shared-score attention (GTA news article, grouped shared attention
+ * matrix: a group computes its attention scores once and every head of the
+ * group uses that same matrix).
+ *   q, k (B, n_grp, S, d_qk): one query and one key per group;
+ *   v (B, h, S, d_v), o (B, h, S, d_v): per head; head i is in group
+ *   i / (h / n_grp); lse NULL or dense fp32 (B, n_grp, S), one per group.
+ * Requires h % n_grp == 0, d_qk in {64, 128}, d_v == 64,
+ * (h / n_grp) * d_v in {64, 128, 256}; in BF16, out BF16 or F32.
+ * scale <= 0 means 1/sqrt(d_qk). */
+gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k,
+                                    const gha_tensor* v, const gha_tensor* o, float* lse,
+                                    int B, int h, int n_grp, int S, int d_qk, int d_v,
+                                    gha_dtype in_dtype, gha_dtype out_dtype,
+                                    float scale, int causal, void* stream);
+
+/* Absorbed latent decode (GQLA section 1 and Figure 2, right: with W^UK folded
+ * into the query and W^UV into the output, all h_q heads attend directly over
+ * the cache of r_kv + d_r elements per token, which serves as the one shared
+ * key and value).
+ *   q_lat (B, s_q, h_q, r_kv): the absorbed query (W^UK_g(i))^T q^C_i;
+ *   q_rope (B, s_q, h_q, d_r): the per-head RoPE query;
+ *   c_kv (B, L_cap, r_kv) and k_rope (B, L_cap, d_r): the cache (their head
+ *   stride is ignored; they may be two views of one (B, L_cap, r_kv + d_r)
+ *   buffer);
+ *   seqlens_k: device int32 (B,), s_q <= seqlens_k[b] <= L_cap;
+ *   o_lat (B, s_q, h_q, r_kv): softmax-weighted latent, before W^UV;
+ *   lse NULL or dense fp32 (B, s_q, h_q).
+ * For gha_tensor the (sb, sh, ss) strides are always batch, head, token:
+ * for q_lat laid out (B, s_q, h_q, r_kv) contiguously, sh = r_kv and
+ * ss = h_q * r_kv.
+ * The score of head i and token u is scale * (q_lat_i . c_u + q_rope_i . k^R_u);
+ * scale must be given (> 0): the expanded head width d_h is not an argument
+ * (1/sqrt(d_h + d_r) reproduces the expanded per-group path).
+ * r_kv == 512, d_r == 64; in BF16, out BF16 or F32.
+ * workspace: at least latent_absorb_decode_workspace_bytes(...) bytes. */
+gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rope,
+                                const gha_tensor* c_kv, const gha_tensor* k_rope,
+                                const int32_t* seqlens_k, const gha_tensor* o_lat,
+                                float* lse, int B, int h_q, int s_q, int L_cap,
+                                int L_max_hint, int r_kv, int d_r,
+                                gha_dtype in_dtype, gha_dtype out_dtype, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+size_t latent_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_hint,
+                                            int r_kv);
+
+/* Status name, thread-local detail of the last error, library version. */
+const char* gha_status_string(gha_status s);
+const char* gha_last_error(void);
+int gha_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GHA_H_ */

@@ -114,3 +114,25 @@ def normal_bf16_rows(shape, seed: int, stream: int, index, stddev: float = 1.0) 
     for ax, i in enumerate(index):
         flat = flat * shape[ax] + int(i)
     return normal_bf16(shape[n_lead:], seed, stream, stddev, offset=flat * inner)
+
+
+def cache_bf16(B: int, H: int, L_cap: int, d: int, seqlens, seed: int, stream: int) -> np.ndarray:
+    """A contiguous (B, H, L_cap, d) bf16 KV cache: slots [0, L_b) of sequence b
+    hold the stream's values for the full-shape tensor (so any slice can be
+    regenerated alone); every slot at or beyond L_b is NaN, so a kernel that
+    reads past a sequence's length poisons its output."""
+    out = np.full((B, H, L_cap, d), BF16_NAN, dtype=np.uint16)
+    for b in range(B):
+        L = int(seqlens[b])
+        for h in range(H):
+            out[b, h, :L] = normal_bf16((L, d), seed, stream, offset=((b * H + h) * L_cap) * d)
+    return out
+
+
+def latent_cache_bf16(B: int, L_cap: int, width: int, seqlens, seed: int, stream: int) -> np.ndarray:
+    """A (B, L_cap, width) bf16 latent cache, NaN beyond each sequence's length."""
+    out = np.full((B, L_cap, width), BF16_NAN, dtype=np.uint16)
+    for b in range(B):
+        L = int(seqlens[b])
+        out[b, :L] = normal_bf16((L, width), seed, stream, offset=b * L_cap * width)
+    return out

@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/gha.h declares, and rejects bad arguments before touching a device.
+No kernel is launched here; fake (but aligned) pointers only reach the
+argument checks, which fail first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_head_latent_amd as gha
+from grouped_head_latent_amd import GhaTensor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gha.library_path()):
+        from grouped_head_latent_amd import build
+        build.build()
+    return gha.load_library()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "gha.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"gqa_prefill", "gqa_decode", "gta_shared_score_prefill", "latent_absorb_decode",
+            "gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
+            "gha_status_string", "gha_last_error", "gha_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.gha_version() >= 100
+    assert lib.gha_status_string(3) == b"GHA_ERR_GROUPING"
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def T(ptr=FAKE, sb=1 << 20, sh=1 << 14, ss=128):
+    return GhaTensor(ptr, sb, sh, ss)
+
+
+def prefill(lib, **kw):
+    a = dict(q=T(), k=T(), v=T(), o=T(), lse=None, B=1, h_q=8, h_kv=2, S_q=16, S_k=16, d=128,
+             i=gha.GHA_BF16, o_t=gha.GHA_BF16, scale=0.0, causal=1)
+    a.update(kw)
+    return lib.gqa_prefill(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                           ctypes.byref(a["o"]), a["lse"], a["B"], a["h_q"], a["h_kv"], a["S_q"],
+                           a["S_k"], a["d"], a["i"], a["o_t"], a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h_kv=3), 3),                      # 8 % 3 != 0
+    (dict(d=96), 7),                        # unsupported head dim
+    (dict(S_q=17, S_k=16), 2),              # causal with S_q > S_k
+    (dict(B=0), 2),
+    (dict(i=gha.GHA_F32, o_t=gha.GHA_BF16), 6),
+    (dict(q=T(ptr=0)), 1),
+    (dict(k=T(ptr=FAKE + 2)), 5),           # misaligned pointer
+    (dict(v=T(ss=100)), 5),                 # 200-byte rows: not 16-byte multiples
+    (dict(o=T(sh=-1)), 4),
+])
+def test_prefill_rejects_bad_arguments(lib, kw, status):
+    assert prefill(lib, **kw) == status
+    assert len(lib.gha_last_error()) > 0
+
+
+def decode(lib, **kw):
+    a = dict(q=T(), k=T(), v=T(), seq=FAKE, o=T(), B=2, h_q=32, h_kv=8, s_q=1, L_cap=4096,
+             L_max=4096, d=128, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.gqa_decode(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                          ctypes.c_void_p(a["seq"]) if a["seq"] else None, ctypes.byref(a["o"]), None,
+                          a["B"], a["h_q"], a["h_kv"], a["s_q"], a["L_cap"], a["L_max"], a["d"],
+                          gha.GHA_BF16, gha.GHA_BF16, 0.0,
+                          ctypes.c_void_p(a["ws"]) if a["ws"] else None, a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h_kv=5), 3),
+    (dict(L_max=8192), 2),                  # hint above capacity
+    (dict(s_q=3, L_max=2, L_cap=2), 2),     # s_q above the longest sequence
+    (dict(seq=0), 1),
+    (dict(ws=0), 8),
+    (dict(ws_bytes=16), 8),
+    (dict(d=256), 7),
+])
+def test_decode_rejects_bad_arguments(lib, kw, status):
+    assert decode(lib, **kw) == status
+
+
+def test_workspace_sizes_cover_the_split_plan(lib):
+    assert lib.gqa_decode_workspace_bytes(64, 32, 8, 1, 32768, 128) > 0
+    assert lib.gqa_decode_workspace_bytes(64, 32, 7, 1, 32768, 128) == 0
+    n = lib.latent_absorb_decode_workspace_bytes(64, 128, 2, 65536, 512)
+    assert n > 0 and n % (4 * 513) == 0
+
+
+def latent(lib, **kw):
+    a = dict(r_kv=512, d_r=64, scale=0.07, L_max=1024, L_cap=1024, s_q=1)
+    a.update(kw)
+    return lib.latent_absorb_decode(ctypes.byref(T(ss=512 * 128)), ctypes.byref(T(ss=64 * 128)),
+                                    ctypes.byref(T(ss=576)), ctypes.byref(T(ptr=FAKE + 1024, ss=576)),
+                                    ctypes.c_void_p(FAKE), ctypes.byref(T(ss=512 * 128)), None, 2, 128,
+                                    a["s_q"], a["L_cap"], a["L_max"], a["r_kv"], a["d_r"], gha.GHA_BF16,
+                                    gha.GHA_BF16, a["scale"], ctypes.c_void_p(FAKE), 16, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(r_kv=256), 7), (dict(d_r=32), 7), (dict(scale=0.0), 2), (dict(L_max=2048), 2),
+])
+def test_latent_rejects_bad_arguments(lib, kw, status):
+    assert latent(lib, **kw) == status
+
+
+def test_latent_rejects_small_workspace(lib):
+    assert latent(lib) == 8
+
+
+def gta(lib, **kw):
+    a = dict(h=16, n_grp=4, d_qk=64, d_v=64)
+    a.update(kw)
+    return lib.gta_shared_score_prefill(ctypes.byref(T()), ctypes.byref(T()), ctypes.byref(T()),
+                                        ctypes.byref(T()), None, 1, a["h"], a["n_grp"], 64, a["d_qk"],
+                                        a["d_v"], gha.GHA_BF16, gha.GHA_BF16, 0.0, 1, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_grp=3), 3), (dict(d_v=128), 7), (dict(h=32, n_grp=4), 7), (dict(d_qk=96), 7),
+])
+def test_gta_rejects_bad_arguments(lib, kw, status):
+    assert gta(lib, **kw) == status
+
+
+def test_valid_call_without_device_reports_hip_error(lib):
+    """On a host with no GPU a well-formed call must fail cleanly with
+    GHA_ERR_HIP (never crash).  Skipped where a device exists, since the fake
+    pointers would then reach a kernel."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present")
+    assert prefill(lib) == 9
+    assert b"device" in lib.gha_last_error()

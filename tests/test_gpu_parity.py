@@ -1,0 +1,331 @@
+"""GPU parity: every entry point of the C ABI against the fp64 oracle on the
+same seeded inputs.  Each case prints its name first so a failure is easy to
+place.  Tolerances: fp32 inputs 1e-5 max abs; bf16 inputs with fp32
+accumulation 1e-2 max / 1e-3 mean abs (fp32 outputs), plus half a bf16 ulp of
+the reference for bf16 outputs."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_cases import (bf16_to_torch, cache_bits, latent_cache_bits, tolerance_ok,
+                             widen)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gha_lib():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import grouped_head_latent_amd as gha
+    gha.load_library()
+    return gha
+
+
+def gen(shape, seed, stream):
+    return synth.normal_bf16(shape, seed, stream)
+
+
+def check(name, got, ref, bf16_out=False, **kw):
+    ok, mx, mean = tolerance_ok(got, ref, bf16_out=bf16_out, **kw)
+    say(f"{name}: max_abs={mx:.3e} mean_abs={mean:.3e}")
+    assert ok, f"{name}: max_abs={mx:.3e} mean_abs={mean:.3e}"
+
+
+# ----------------------------------------------------------------- fp32 path
+
+def test_tiny_gqa_fp32_matches_oracle_and_repeated_heads(gha_lib):
+    """Worked GQA example shapes: batch 1, 8 query heads, 2 KV heads, 16
+    tokens, head dim 64, fp32, causal, seed 0."""
+    say("tiny fp32 GQA (1, 8/2, 16, 64)")
+    q = synth.normal_f32((1, 8, 16, 64), 0, synth.STREAM["q"])
+    k = synth.normal_f32((1, 2, 16, 64), 0, synth.STREAM["k"])
+    v = synth.normal_f32((1, 2, 16, 64), 0, synth.STREAM["v"])
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    o, lse = gha_lib.gqa_prefill(dq, dk, dv, causal=True, return_lse=True)
+    o_mha = gha_lib.gqa_prefill(dq, dk.repeat_interleave(4, dim=1).contiguous(),
+                                dv.repeat_interleave(4, dim=1).contiguous(), causal=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.gqa_prefill(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64))
+    err = np.abs(o.cpu().numpy() - ref).max()
+    say(f"fp32 max_abs={err:.3e}")
+    assert err <= 1e-5
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-5
+    assert torch.equal(o, o_mha)
+
+
+@pytest.mark.parametrize("B,h_q,h_kv,S,d", [(2, 4, 2, 150, 128), (1, 2, 1, 65, 64)])
+def test_fp32_prefill_ragged(gha_lib, B, h_q, h_kv, S, d):
+    say(f"fp32 prefill B={B} h={h_q}/{h_kv} S={S} d={d}")
+    q = synth.normal_f32((B, h_q, S, d), 7, 1)
+    k = synth.normal_f32((B, h_kv, S, d), 7, 2)
+    v = synth.normal_f32((B, h_kv, S, d), 7, 3)
+    o = gha_lib.gqa_prefill(*(torch.from_numpy(x).cuda() for x in (q, k, v)))
+    ref, _ = oracle.gqa_prefill(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64))
+    assert np.abs(o.cpu().numpy() - ref).max() <= 1e-5
+
+
+# ------------------------------------------------------------- bf16 prefill
+
+PREFILL_CASES = [
+    # B, h_q, h_kv, S_q, S_k, d, causal
+    (2, 8, 2, 200, 200, 128, True),   # ragged tail, 4 heads per group
+    (1, 4, 1, 130, 130, 128, True),   # MQA
+    (1, 4, 4, 97, 97, 128, True),     # MHA
+    (2, 4, 2, 77, 77, 64, True),      # 2 heads per group, d=64
+    (1, 6, 3, 64, 64, 64, True),      # 2 heads per group, one exact tile
+    (1, 8, 2, 1, 1, 128, True),       # one token
+    (1, 8, 2, 70, 300, 128, True),    # chunked prefill: bottom-right causal
+    (1, 8, 2, 90, 150, 128, False),   # no mask
+]
+
+
+@pytest.mark.parametrize("B,h_q,h_kv,S_q,S_k,d,causal", PREFILL_CASES)
+def test_gqa_prefill_bf16(gha_lib, B, h_q, h_kv, S_q, S_k, d, causal):
+    say(f"bf16 prefill B={B} h={h_q}/{h_kv} S_q={S_q} S_k={S_k} d={d} causal={causal}")
+    qb, kb, vb = gen((B, h_q, S_q, d), 8, 1), gen((B, h_kv, S_k, d), 8, 2), gen((B, h_kv, S_k, d), 8, 3)
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    o32, lse = gha_lib.gqa_prefill(q, k, v, causal=causal, out_dtype=torch.float32, return_lse=True)
+    o16 = gha_lib.gqa_prefill(q, k, v, causal=causal)
+    ref, ref_lse = oracle.gqa_prefill(widen(qb), widen(kb), widen(vb), causal=causal)
+    check("o fp32", o32.cpu().numpy(), ref)
+    check("o bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("lse", lse.cpu().numpy(), ref_lse)
+
+
+def test_gqa_prefill_strided_bshd_layout(gha_lib):
+    """(B, S, H, D) memory order passed through the strides."""
+    say("bf16 prefill BSHD strides")
+    B, h_q, h_kv, S, d = 2, 8, 2, 100, 128
+    qb, kb, vb = gen((B, S, h_q, d), 9, 1), gen((B, S, h_kv, d), 9, 2), gen((B, S, h_kv, d), 9, 3)
+    q, k, v = (bf16_to_torch(x).transpose(1, 2) for x in (qb, kb, vb))
+    o = gha_lib.gqa_prefill(q, k, v, out_dtype=torch.float32)
+    ref, _ = oracle.gqa_prefill(*(widen(x).transpose(0, 2, 1, 3) for x in (qb, kb, vb)))
+    check("bshd", o.cpu().numpy(), ref)
+
+
+def test_prefill_invariants(gha_lib):
+    """Constant V gives exactly-normalised rows; row 0 returns v_0; two runs
+    are bitwise equal."""
+    say("prefill invariants")
+    B, h_q, h_kv, S, d = 1, 8, 2, 129, 128
+    q, k = bf16_to_torch(gen((B, h_q, S, d), 10, 1)), bf16_to_torch(gen((B, h_kv, S, d), 10, 2))
+    ones = torch.ones((B, h_kv, S, d), dtype=torch.bfloat16, device="cuda")
+    o = gha_lib.gqa_prefill(q, k, ones, out_dtype=torch.float32)
+    assert (o - 1).abs().max().item() <= 1e-2
+    v = bf16_to_torch(gen((B, h_kv, S, d), 10, 3))
+    o1 = gha_lib.gqa_prefill(q, k, v, out_dtype=torch.float32)
+    o2 = gha_lib.gqa_prefill(q, k, v, out_dtype=torch.float32)
+    assert torch.equal(o1, o2)
+    for i in range(h_q):
+        assert torch.allclose(o1[0, i, 0], v[0, i // 4, 0].float(), atol=0, rtol=0)
+
+
+def test_gqa_prefill_full_size_sampled(gha_lib):
+    """Batch 4, 32 query heads over 8 KV heads, 4096 tokens, head dim 128, in
+    the launch configuration the benchmark times; the oracle evaluates every
+    row of four sampled (batch, head) pairs."""
+    B, h_q, h_kv, S, d = 4, 32, 8, 4096, 128
+    say(f"full-size prefill {B}x{h_q}/{h_kv}x{S}x{d}")
+    qb, kb, vb = gen((B, h_q, S, d), 2, 1), gen((B, h_kv, S, d), 2, 2), gen((B, h_kv, S, d), 2, 3)
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    o = gha_lib.gqa_prefill(q, k, v, out_dtype=torch.float32)
+    o16 = gha_lib.gqa_prefill(q, k, v)
+    pairs = [(0, 0), (1, 13), (2, 22), (3, 31)]
+    ref, _ = oracle.gqa_prefill(widen(qb), widen(kb), widen(vb), heads=pairs)
+    o = o.cpu().numpy()
+    o16 = o16.float().cpu().numpy()
+    for b, i in pairs:
+        check(f"full prefill (b={b}, head={i})", o[b, i], ref[b, i])
+        check(f"full prefill bf16 (b={b}, head={i})", o16[b, i], ref[b, i], bf16_out=True)
+
+
+# ------------------------------------------------------------------- decode
+
+def decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, seed):
+    qb = gen((B, h_q, s_q, d), seed, 1)
+    kb = cache_bits(B, h_kv, L_cap, d, seqlens, seed, 2)
+    vb = cache_bits(B, h_kv, L_cap, d, seqlens, seed, 3)
+    return qb, kb, vb
+
+
+DECODE_CASES = [
+    # B, h_q, h_kv, s_q, L_cap, seqlens, d
+    (3, 32, 8, 1, 1100, [1, 700, 1100], 128),
+    (3, 32, 8, 2, 1100, [2, 333, 1099], 128),
+    (2, 8, 1, 2, 600, [64, 599], 128),      # MQA: 16 rows in one block
+    (2, 16, 1, 1, 300, [5, 300], 128),      # 16 heads per group
+    (2, 32, 1, 1, 300, [257, 299], 128),    # 32 rows: two row blocks
+    (2, 4, 4, 1, 260, [256, 260], 128),     # MHA
+    (2, 8, 2, 2, 500, [3, 480], 64),        # head dim 64
+]
+
+
+@pytest.mark.parametrize("B,h_q,h_kv,s_q,L_cap,seqlens,d", DECODE_CASES)
+def test_gqa_decode(gha_lib, B, h_q, h_kv, s_q, L_cap, seqlens, d):
+    say(f"decode B={B} h={h_q}/{h_kv} s_q={s_q} L_cap={L_cap} L={seqlens} d={d}")
+    seqlens = np.array(seqlens, dtype=np.int32)
+    qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, 12)
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    sl = torch.from_numpy(seqlens).cuda()
+    o32, lse = gha_lib.gqa_decode(q, k, v, sl, out_dtype=torch.float32, return_lse=True)
+    o16 = gha_lib.gqa_decode(q, k, v, sl)
+    ref, ref_lse = oracle.gqa_decode(widen(qb), widen(kb), widen(vb), seqlens)
+    check("decode fp32", o32.cpu().numpy(), ref)
+    check("decode bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("decode lse", lse.cpu().numpy(), ref_lse)
+
+
+def test_gqa_decode_single_key_returns_value(gha_lib):
+    say("decode L=1")
+    B, h_q, h_kv, d = 2, 8, 2, 128
+    qb, kb, vb = decode_case(B, h_q, h_kv, 1, 64, [1, 1], d, 13)
+    o = gha_lib.gqa_decode(*(bf16_to_torch(x) for x in (qb, kb, vb)),
+                           torch.ones(B, dtype=torch.int32, device="cuda"), out_dtype=torch.float32)
+    ref = np.repeat(widen(vb)[:, :, :1], 4, axis=1)
+    assert np.abs(o.cpu().numpy() - ref).max() <= 1e-6
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_gqa_decode_full_size_sampled(gha_lib, s_q):
+    """Batch 64, 32/8 heads, head dim 128, lengths uniform in [1024, 32768],
+    cache capacity 32768 with NaN beyond each length."""
+    B, h_q, h_kv, d, L_cap = 64, 32, 8, 128, 32768
+    say(f"full-size decode s_q={s_q}")
+    seqlens = synth.uniform_i32(B, 1024, 32768, 3, synth.STREAM["seqlens"])
+    qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, 3)
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    del kb, vb
+    o = gha_lib.gqa_decode(q, k, v, torch.from_numpy(seqlens).cuda(), out_dtype=torch.float32).cpu().numpy()
+    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 17, 40]:
+        kh = k[b].view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = v[b].view(torch.int16).cpu().numpy().view(np.uint16)
+        # the oracle gets host-generated values: regenerate this sequence's slice
+        L = int(seqlens[b])
+        k_ref = np.stack([synth.normal_bf16((L, d), 3, 2, offset=((b * h_kv + j) * L_cap) * d) for j in range(h_kv)])
+        v_ref = np.stack([synth.normal_bf16((L, d), 3, 3, offset=((b * h_kv + j) * L_cap) * d) for j in range(h_kv)])
+        assert np.array_equal(kh[:, :L], k_ref) and np.array_equal(vh[:, :L], v_ref)
+        ref, _ = oracle.gqa_decode(widen(qb[b:b + 1]), widen(k_ref)[None], widen(v_ref)[None],
+                                   np.array([L]))
+        check(f"full decode b={b} L={L}", o[b:b + 1], ref)
+
+
+# ---------------------------------------------------------------------- GTA
+
+GTA_CASES = [
+    # B, h, n_grp, S, d_qk, d_v
+    (2, 16, 4, 300, 64, 64),
+    (1, 8, 4, 129, 64, 64),
+    (1, 4, 4, 70, 64, 64),
+    (1, 8, 2, 100, 128, 64),
+]
+
+
+@pytest.mark.parametrize("B,h,n_grp,S,d_qk,d_v", GTA_CASES)
+def test_gta_shared_score(gha_lib, B, h, n_grp, S, d_qk, d_v):
+    say(f"GTA B={B} h={h} groups={n_grp} S={S} d_qk={d_qk} d_v={d_v}")
+    qb, kb, vb = gen((B, n_grp, S, d_qk), 14, 1), gen((B, n_grp, S, d_qk), 14, 2), gen((B, h, S, d_v), 14, 3)
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    o, lse = gha_lib.gta_shared_score_prefill(q, k, v, out_dtype=torch.float32, return_lse=True)
+    o16 = gha_lib.gta_shared_score_prefill(q, k, v)
+    ref, ref_lse = oracle.gta_prefill(widen(qb), widen(kb), widen(vb))
+    check("gta fp32", o.cpu().numpy(), ref)
+    check("gta bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("gta lse", lse.cpu().numpy(), ref_lse)
+
+
+def test_gta_full_size_sampled(gha_lib):
+    """Batch 8, 16 heads in 4 groups of 4, 2048 tokens, dims 64."""
+    B, h, n_grp, S, d = 8, 16, 4, 2048, 64
+    say("full-size GTA")
+    qb, kb, vb = gen((B, n_grp, S, d), 4, 1), gen((B, n_grp, S, d), 4, 2), gen((B, h, S, d), 4, 3)
+    o = gha_lib.gta_shared_score_prefill(*(bf16_to_torch(x) for x in (qb, kb, vb)),
+                                         out_dtype=torch.float32).cpu().numpy()
+    pairs = [(0, 0), (0, 3), (3, 6), (7, 15)]
+    ref, _ = oracle.gta_prefill(widen(qb), widen(kb), widen(vb), heads=pairs)
+    for b, i in pairs:
+        check(f"full GTA (b={b}, head={i})", o[b, i], ref[b, i])
+
+
+# ------------------------------------------------------------------- latent
+
+def latent_inputs(B, s_q, h_q, L_cap, seqlens, seed, g=8, d_h=128):
+    q_c = gen((B, s_q, h_q, d_h), seed, synth.STREAM["q_c"])
+    q_r = gen((B, s_q, h_q, 64), seed, synth.STREAM["q_rope"])
+    cache = latent_cache_bits(B, L_cap, 576, seqlens, seed, synth.STREAM["latent"])
+    w_uk = widen(synth.normal_bf16((g * d_h, 512), seed, synth.STREAM["w_uk"], 0.02))
+    w_uv = widen(synth.normal_bf16((g * d_h, 512), seed, synth.STREAM["w_uv"], 0.02))
+    # absorbed query, made on the host in fp64 and rounded to bf16 (the input
+    # the kernel and the oracle both receive)
+    q_lat = synth.round_bf16(oracle.absorb_query(widen(q_c), w_uk, g).astype(np.float32))
+    return q_c, q_r, cache, w_uk, w_uv, q_lat
+
+
+LATENT_CASES = [
+    # B, h_q, s_q, L_cap, seqlens
+    (2, 128, 1, 700, [1, 700]),
+    (2, 128, 2, 600, [2, 555]),
+    (1, 16, 1, 300, [299]),
+    (2, 96, 2, 400, [37, 400]),
+]
+
+
+@pytest.mark.parametrize("B,h_q,s_q,L_cap,seqlens", LATENT_CASES)
+def test_latent_absorb_decode(gha_lib, B, h_q, s_q, L_cap, seqlens):
+    say(f"latent B={B} h_q={h_q} s_q={s_q} L_cap={L_cap} L={seqlens}")
+    seqlens = np.array(seqlens, dtype=np.int32)
+    g = 8 if h_q % 8 == 0 else 1
+    q_c, q_r, cache, w_uk, w_uv, q_lat = latent_inputs(B, s_q, h_q, L_cap, seqlens, 15, g=g)
+    dcache = bf16_to_torch(cache)
+    scale = 1 / math.sqrt(128 + 64)
+    o32, lse = gha_lib.latent_absorb_decode(bf16_to_torch(q_lat), bf16_to_torch(q_r), dcache[..., :512],
+                                            dcache[..., 512:], torch.from_numpy(seqlens).cuda(),
+                                            scale=scale, out_dtype=torch.float32, return_lse=True)
+    o16 = gha_lib.latent_absorb_decode(bf16_to_torch(q_lat), bf16_to_torch(q_r), dcache[..., :512],
+                                       dcache[..., 512:], torch.from_numpy(seqlens).cuda(), scale=scale)
+    c = widen(cache)
+    ref, ref_lse = oracle.latent_absorb_decode(widen(q_lat), widen(q_r), c[..., :512], c[..., 512:],
+                                               seqlens, scale=scale)
+    check("latent fp32", o32.cpu().numpy(), ref)
+    check("latent bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("latent lse", lse.cpu().numpy(), ref_lse)
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_latent_full_size_sampled_and_expanded_path(gha_lib, s_q):
+    """h_q 128, r_kv 512, RoPE 64, batch 64, lengths uniform in [8192, 65536],
+    W^UK/W^UV per 8 groups ~ N(0, 0.02).  o_lat is checked against the
+    absorbed oracle on sampled sequences, and W^UV o_lat (host, fp64) against
+    the expanded per-group GQA oracle (GQLA: the two paths are equal)."""
+    B, h_q, L_cap, g, d_h = 64, 128, 65536, 8, 128
+    say(f"full-size latent s_q={s_q}")
+    seqlens = synth.uniform_i32(B, 8192, 65536, 5, synth.STREAM["seqlens"])
+    q_c, q_r, cache, w_uk, w_uv, q_lat = latent_inputs(B, s_q, h_q, L_cap, seqlens, 5)
+    dcache = bf16_to_torch(cache)
+    scale = 1 / math.sqrt(d_h + 64)
+    o = gha_lib.latent_absorb_decode(bf16_to_torch(q_lat), bf16_to_torch(q_r), dcache[..., :512],
+                                     dcache[..., 512:], torch.from_numpy(seqlens).cuda(), scale=scale,
+                                     out_dtype=torch.float32).cpu().numpy()
+    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 30]:
+        L = int(seqlens[b])
+        c = widen(cache[b:b + 1, :L])
+        ref, _ = oracle.latent_absorb_decode(widen(q_lat[b:b + 1]), widen(q_r[b:b + 1]), c[..., :512],
+                                             c[..., 512:], np.array([L]), scale=scale)
+        check(f"full latent b={b} L={L}", o[b:b + 1], ref)
+        # expanded per-group GQA path from the un-absorbed query
+        K, V = oracle.expand_latent(c[..., :512], c[..., 512:], w_uk, w_uv, g)
+        qf = np.concatenate([widen(q_c[b:b + 1]), widen(q_r[b:b + 1])], -1).transpose(0, 2, 1, 3)
+        O_exp, _ = oracle.gqa_decode(qf, K, V, np.array([L]), scale=scale)
+        O_gpu = oracle.absorb_output(o[b:b + 1], w_uv, g, d_h)
+        check(f"expanded path b={b}", O_gpu, O_exp.transpose(0, 2, 1, 3))
