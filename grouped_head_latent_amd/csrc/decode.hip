@@ -69,27 +69,40 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_split_kernel(DecodeArgs a) 
 #pragma unroll
   for (int e = 0; e < 8; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m2 = kNegInf, lsum = 0.f;
+  wait_vmem_all();
 
-  for (int k0 = start + wave * CH; k0 < end; k0 += 4 * CH) {
-    // ---- loads: K in score-tile order, V as 8-key x 8-feature blocks ----
+  // Loads are clamped to the last key of the split instead of branched on:
+  // keys at or past `end` are masked to -inf below, so they get zero weight.
+  // With head dim 64, lanes li >= 8 feed MFMA rows whose outputs are
+  // discarded; they re-read a valid chunk.
+  const int vcol = 8 * (li % NCH);
+  u32x4 kf[4][DS];
+  u32x4 vr[2][8];
+  auto load_k = [&](int k0) {
     // score tile t, row i  <->  key k0 + 32*(t/2) + 8*(i/4) + 4*(t%2) + i%4
-    u32x4 kf[4][DS];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int key = k0 + 32 * (t >> 1) + 8 * (li >> 2) + 4 * (t & 1) + (li & 3);
+      const int key = min(k0 + 32 * (t >> 1) + 8 * (li >> 2) + 4 * (t & 1) + (li & 3), end - 1);
 #pragma unroll
-      for (int s = 0; s < DS; ++s)
-        kf[t][s] = (key < end) ? ld16(kbase + (int64_t)key * a.k_ss + 32 * s + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < DS; ++s) kf[t][s] = ld16(kbase + (int64_t)key * a.k_ss + 32 * s + 8 * lg);
     }
-    u32x4 vr[2][8];
+  };
+  auto load_v = [&](int k0) {
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk)
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        const int key = k0 + 32 * hk + 8 * lg + tt;
-        vr[hk][tt] = (key < end && li < NCH) ? ld16(vbase + (int64_t)key * a.v_ss + 8 * li)
-                                             : u32x4{0u, 0u, 0u, 0u};
+        const int key = min(k0 + 32 * hk + 8 * lg + tt, end - 1);
+        vr[hk][tt] = ld16(vbase + (int64_t)key * a.v_ss + vcol);
       }
+  };
+
+  // Pipeline per wave: K(c) was loaded during the previous chunk's P.V;
+  // V(c) is loaded while S(c) and its softmax run.
+  int k0 = start + wave * CH;
+  if (k0 < end) load_k(k0);
+  for (; k0 < end; k0 += 4 * CH) {
+    load_v(k0);
 
     // ---- S^T = K Q^T ------------------------------------------------------
     f32x4 sacc[4];
@@ -99,6 +112,8 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_split_kernel(DecodeArgs a) 
 #pragma unroll
       for (int s = 0; s < DS; ++s) sacc[t] = mfma_bf16(kf[t][s], qf[s], sacc[t]);
     }
+    if (k0 + 4 * CH < end) load_k(k0 + 4 * CH);
+
     // lane group lg, tile t, element r  <->  key k0 + 32*(t/2) + 8*lg + 4*(t%2) + r
     float mx = kNegInf;
 #pragma unroll
@@ -109,11 +124,16 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_split_kernel(DecodeArgs a) 
         if (key >= end || key > kvis) sacc[t][r] = kNegInf;
         mx = fmaxf(mx, sacc[t][r]);
       }
-    mx = group4_max(mx);
-    const float mnew = fmaxf(m2, mx * c2);
-    const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2 - mnew);
-    const float msub = (mnew == kNegInf) ? 0.f : mnew;
-    m2 = mnew;
+    const float mx2 = group4_max(mx) * c2;
+    if (wave_any(mx2 > m2 + kRescaleSlack)) {
+      const float mnew = fmaxf(m2, mx2);
+      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2 - mnew);
+      m2 = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) oacc[e] *= alpha;
+    }
+    const float msub = (m2 == kNegInf) ? 0.f : m2;
     float p[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -125,9 +145,7 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_split_kernel(DecodeArgs a) 
       pfs[hk] = u32x4{pack_bf16(p[2 * hk][0], p[2 * hk][1]), pack_bf16(p[2 * hk][2], p[2 * hk][3]),
                       pack_bf16(p[2 * hk + 1][0], p[2 * hk + 1][1]),
                       pack_bf16(p[2 * hk + 1][2], p[2 * hk + 1][3])};
-    lsum = lsum * alpha + (bf16x8_sum(pfs[0]) + bf16x8_sum(pfs[1]));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) oacc[e] *= alpha;
+    lsum += bf16x8_sum(pfs[0]) + bf16x8_sum(pfs[1]);
 
     // ---- O^T += V^T P^T ---------------------------------------------------
 #pragma unroll

@@ -51,15 +51,47 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 (the four lane groups
-// that hold one MFMA column).
-__device__ __forceinline__ float group4_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+// that hold one MFMA column), with gfx950's permlane swaps.
+// v_permlane16_swap a, b exchanges the odd 16-lane rows of a with the even
+// rows of b; applied to two copies of x it leaves, per lane, x in one
+// register and x of lane l^16 in the other (v_permlane32_swap likewise for
+// l^32), so the max or sum of the two registers is the pair reduction.
+// Written as inline asm because the compiler builtin exposes only the first
+// of the two results; the s_nop pads cover the VALU-write-to-permlane
+// hazard, since the hazard checker does not look inside inline asm.
+__device__ __forceinline__ void permlane16_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
-__device__ __forceinline__ float group4_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+__device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
+__device__ __forceinline__ float xor16_max(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane16_swap(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane32_swap(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane16_swap(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane32_swap(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float group4_max(float x) { return xor32_max(xor16_max(x)); }
+__device__ __forceinline__ float group4_sum(float x) { return xor32_sum(xor16_sum(x)); }
+
+// An MFMA A operand of all-ones bf16: multiplying it into P^T sums P over the
+// contraction (key) axis in every output row, i.e. the softmax normaliser of
+// exactly the bf16 probabilities that the P.V product consumes.
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 
 // Interleave the low (or high) bf16 halves of two words: result = (a.x, b.x).
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
@@ -68,6 +100,23 @@ __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
+
+// Wait until every vector-memory load issued so far has landed (vmcnt = 0,
+// other counters untouched).  Kernels call it once after loading their
+// resident query fragments: otherwise the first MFMA of the main loop waits
+// on vmcnt(0) every iteration, i.e. on the prefetch of the next tile too.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// True in every lane if any lane's predicate holds (wave-uniform branch).
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Online softmax with a lazily updated running maximum.  Scores are kept in
+// log2 units (score * scale * log2 e).  The running maximum m only moves when
+// a tile's maximum exceeds it by more than kRescaleSlack, so most tiles skip
+// rescaling the output accumulator; probabilities are then at most
+// 2^kRescaleSlack, far inside fp32 and bf16 range.  The result is the same
+// softmax: numerator and normaliser share whatever m was used.
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -76,12 +76,10 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
     for (int i = 0; i < LOADS; ++i) {
       const int c = tid + 256 * i;
       const int key = c / (DL / 8), col = (c % (DL / 8)) * 8;
-      const int kk = k0 + key;
-      if (kk < end)
-        stg[i] = (col < RKV) ? ld16(cbase + (int64_t)kk * a.c_ss + col)
-                             : ld16(rbase + (int64_t)kk * a.kr_ss + (col - RKV));
-      else
-        stg[i] = u32x4{0u, 0u, 0u, 0u};
+      // clamped, not branched: tokens at or past `end` are masked to -inf
+      const int kk = min(k0 + key, end - 1);
+      stg[i] = (col < RKV) ? ld16(cbase + (int64_t)kk * a.c_ss + col)
+                           : ld16(rbase + (int64_t)kk * a.kr_ss + (col - RKV));
     }
   };
   auto store_tile = [&](int buf) {
@@ -103,6 +101,7 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   const int n_t = (end - start + TKEYS - 1) / TKEYS;
   load_tile(start);
   store_tile(0);
+  wait_vmem_all();
   __syncthreads();
 
   for (int it = 0; it < n_t; ++it) {
@@ -130,11 +129,18 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
         if (key >= end || key > kvis) sacc[t][r] = kNegInf;
         mx = fmaxf(mx, sacc[t][r]);
       }
-    mx = group4_max(mx);
-    const float mnew = fmaxf(m2, mx * c2);
-    const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2 - mnew);
-    const float msub = (mnew == kNegInf) ? 0.f : mnew;
-    m2 = mnew;
+    const float mx2 = group4_max(mx) * c2;
+    if (wave_any(mx2 > m2 + kRescaleSlack)) {
+      const float mnew = fmaxf(m2, mx2);
+      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2 - mnew);
+      m2 = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int dg = 0; dg < 4; ++dg)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[dg][e] *= alpha;
+    }
+    const float msub = (m2 == kNegInf) ? 0.f : m2;
     float p[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -142,11 +148,7 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
       for (int r = 0; r < 4; ++r) p[t][r] = fast_exp2(__builtin_fmaf(sacc[t][r], c2, -msub));
     const u32x4 pf = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
                       pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
-    lsum = lsum * alpha + bf16x8_sum(pf);
-#pragma unroll
-    for (int dg = 0; dg < 4; ++dg)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) oacc[dg][e] *= alpha;
+    lsum += bf16x8_sum(pf);
 
     // O^T += C^T P^T: lane reads tokens 8*lg .. 8*lg+7, features 128*dg + 8*li .. +7
 #pragma unroll
@@ -189,12 +191,16 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   if (lg == 0) a.ws_lse[pidx] = lfull > 0.f ? m2 + fast_log2(lfull) : kNegInf;
 }
 
+// Merge the splits of 4 query rows per work-group (64 threads per row, 8
+// features per thread): each split s holds its normalised output O_s and its
+// log2-sum-exp l_s; the result is sum_s 2^(l_s - M) O_s / sum_s 2^(l_s - M).
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
-  const int unit = blockIdx.x;  // b * n_rb + rb
+  const int unit = blockIdx.x / 16;  // b * n_rb + rb
   const int rb = unit % a.n_rb, b = unit / a.n_rb;
   const int tid = threadIdx.x;
-  const int row = tid >> 2, quarter = tid & 3;
+  const int row = (blockIdx.x % 16) * 4 + (tid >> 6);
+  const int f = (tid & 63) * 8;
   const int R = rb * 64 + row;
   if (R >= a.s_q * a.h_q) return;
   const int L = a.seqlens[b];
@@ -204,28 +210,30 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
   const int64_t base = (int64_t)unit * a.n_splits * 64 + row;
   float M = kNegInf;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_lse[base + (int64_t)s * 64]);
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int s = 0; s < ns; ++s) {
     const float ls = a.ws_lse[base + (int64_t)s * 64];
-    den += (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
+    const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
+    den += w;
+    const float* src = a.ws_o + (base + (int64_t)s * 64) * RKV + f;
+    acc0 += w * *reinterpret_cast<const f32x4*>(src);
+    acc1 += w * *reinterpret_cast<const f32x4*>(src + 4);
   }
   const float inv = 1.f / den;
+  acc0 *= inv;
+  acc1 *= inv;
   const int tq = R / a.h_q, head = R % a.h_q;
-  const int64_t obase = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh + (int64_t)tq * a.o_ss;
-  for (int f = quarter * 4; f < RKV; f += 16) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ns; ++s) {
-      const float ls = a.ws_lse[base + (int64_t)s * 64];
-      const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
-      acc += w * *reinterpret_cast<const f32x4*>(a.ws_o + (base + (int64_t)s * 64) * RKV + f);
-    }
-    acc *= inv;
-    if constexpr (OUT_F32)
-      *reinterpret_cast<f32x4*>((float*)a.o + obase + f) = acc;
-    else
-      *reinterpret_cast<u32x2*>((__bf16*)a.o + obase + f) = u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+  const int64_t obase = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh + (int64_t)tq * a.o_ss + f;
+  if constexpr (OUT_F32) {
+    *reinterpret_cast<f32x4*>((float*)a.o + obase) = acc0;
+    *reinterpret_cast<f32x4*>((float*)a.o + obase + 4) = acc1;
+  } else {
+    *reinterpret_cast<u32x4*>((__bf16*)a.o + obase) =
+        u32x4{pack_bf16(acc0[0], acc0[1]), pack_bf16(acc0[2], acc0[3]), pack_bf16(acc1[0], acc1[1]),
+              pack_bf16(acc1[2], acc1[3])};
   }
-  if (a.lse != nullptr && quarter == 0)
+  if (a.lse != nullptr && (tid & 63) == 0)
     a.lse[((int64_t)b * a.s_q + tq) * a.h_q + head] = (M + fast_log2(den)) * kLn2;
 }
 
@@ -238,9 +246,9 @@ hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t s
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (out_f32)
-    hipLaunchKernelGGL(latent_merge_kernel<true>, dim3(a.B * a.n_rb), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(latent_merge_kernel<true>, dim3(a.B * a.n_rb * 16), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(latent_merge_kernel<false>, dim3(a.B * a.n_rb), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(latent_merge_kernel<false>, dim3(a.B * a.n_rb * 16), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

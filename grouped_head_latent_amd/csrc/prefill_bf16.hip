@@ -48,10 +48,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int V_ELEMS = DV * VP;
   constexpr int DS = DQK / 32;  // contraction steps of the score MFMA
   constexpr int DT = DV / 16;   // 16-wide output column tiles
-  constexpr int K_LOADS = KB * DQK / 8 / 256;   // 16-byte K loads per thread
-  constexpr int V_UNITS = (KB / 4) * (DV / 8);  // (4 keys x 8 columns) units
+  constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
+  constexpr int K_LOADS = KB * KCH / 256;       // 16-byte K loads per thread
+  constexpr int K_ROWSTEP = 256 / KCH;          // rows between a thread's K loads
+  constexpr int VCH = DV / 8;                   // 8-column chunks per V row
+  constexpr int V_UNITS = (KB / 4) * VCH;       // (4 keys x 8 columns) units
   constexpr int V_PER_THREAD = (V_UNITS + 255) / 256;
-  static_assert(K_LOADS >= 1, "tile too small");
+  static_assert(K_LOADS >= 1 && KB * KCH % 256 == 0, "tile staging");
 
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (K_ELEMS + V_ELEMS)];
 
@@ -96,92 +99,108 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   u32x4 qf[QT][DS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const int pos = pos0 + qt * 16 + li;
+    const int pos = min(pos0 + qt * 16 + li, a.S_q - 1);  // rows past S_q are never written
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      if (pos < a.S_q)
-        qf[qt][s] = ld16(qbase + (int64_t)pos * a.q_ss + 32 * s + 8 * lg);
-      else
-        qf[qt][s] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int s = 0; s < DS; ++s) qf[qt][s] = ld16(qbase + (int64_t)pos * a.q_ss + 32 * s + 8 * lg);
   }
 
   // ---- staging: global -> registers -> LDS --------------------------------
+  // Each thread loads K rows k_row + K_ROWSTEP*i (16 bytes each) and, per V
+  // unit, 4 consecutive keys x 8 columns of V, which it transposes into V^T.
+  // Tiles wholly inside the sequence use plain strided addresses; the tail
+  // tile clamps rows to the last key (their scores are masked to -inf).
+  const int k_row = tid / KCH, k_col = (tid % KCH) * 8;
+  const __bf16* kthr = kbase + (int64_t)k_row * a.k_ss + k_col;
+  const int64_t k_rowstep = (int64_t)K_ROWSTEP * a.k_ss;
+  const __bf16* vthr[V_PER_THREAD];
+  int v_dchunk[V_PER_THREAD], v_kgrp[V_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < V_PER_THREAD; ++i) {
+    const int u = min(tid + 256 * i, V_UNITS - 1);
+    v_dchunk[i] = u % VCH;
+    v_kgrp[i] = u / VCH;
+    const int d = v_dchunk[i] * 8;
+    const __bf16* vp = GTA ? vbase + (int64_t)(d / a.dv_head) * a.v_sh + (d % a.dv_head) : vbase + d;
+    vthr[i] = vp + (int64_t)(4 * v_kgrp[i]) * a.v_ss;
+  }
+
   u32x4 kreg[K_LOADS];
   u32x4 vreg[V_PER_THREAD][4];
 
   auto load_tile = [&](int kb) {
     const int key0 = kb * KB;
+    const int64_t koff = (int64_t)key0 * a.k_ss, voff = (int64_t)key0 * a.v_ss;
+    if (key0 + KB <= a.S_k) {
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
-      const int kk = key0 + key;
-      kreg[i] = (kk < a.S_k) ? ld16(kbase + (int64_t)kk * a.k_ss + col) : u32x4{0u, 0u, 0u, 0u};
-    }
+      for (int i = 0; i < K_LOADS; ++i) kreg[i] = ld16(kthr + koff + i * k_rowstep);
 #pragma unroll
-    for (int i = 0; i < V_PER_THREAD; ++i) {
-      const int u = tid + 256 * i;
-      if (u < V_UNITS) {
-        const int dchunk = u % (DV / 8), kgrp = u / (DV / 8);
-        const int d = dchunk * 8;
-        const __bf16* vp;
-        if constexpr (GTA) {
-          vp = vbase + (int64_t)(d / a.dv_head) * a.v_sh + (d % a.dv_head);
-        } else {
-          vp = vbase + d;
-        }
+      for (int i = 0; i < V_PER_THREAD; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vreg[i][r] = ld16(vthr[i] + voff + r * a.v_ss);
+    } else {
+#pragma unroll
+      for (int i = 0; i < K_LOADS; ++i) {
+        const int kk = min(key0 + k_row + K_ROWSTEP * i, a.S_k - 1);
+        kreg[i] = ld16(kbase + (int64_t)kk * a.k_ss + k_col);
+      }
+#pragma unroll
+      for (int i = 0; i < V_PER_THREAD; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int kk = key0 + 4 * kgrp + r;
-          vreg[i][r] = (kk < a.S_k) ? ld16(vp + (int64_t)kk * a.v_ss) : u32x4{0u, 0u, 0u, 0u};
+          const int kk = min(key0 + 4 * v_kgrp[i] + r, a.S_k - 1);
+          vreg[i][r] = ld16(vthr[i] + (int64_t)(kk - 4 * v_kgrp[i]) * a.v_ss);
         }
-      }
     }
   };
 
+  // V^T rows are 64 keys (128 B) + 16 B pad; the 16-byte column unit of row d
+  // is XOR-swizzled by (d >> 4) & 7, so that the 16 lanes writing one key
+  // group to 16 different rows land in distinct banks while the MFMA-side
+  // reads (16 consecutive rows, one unit) stay conflict-free.
   auto store_tile = [&](int buf) {
     __bf16* ks = smem + buf * (K_ELEMS + V_ELEMS);
     __bf16* vs = ks + K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
-      st16(ks + key * KP + col, kreg[i]);
-    }
+    for (int i = 0; i < K_LOADS; ++i) st16(ks + (k_row + K_ROWSTEP * i) * KP + k_col, kreg[i]);
 #pragma unroll
     for (int i = 0; i < V_PER_THREAD; ++i) {
-      const int u = tid + 256 * i;
-      if (u < V_UNITS) {
-        const int dchunk = u % (DV / 8), kgrp = u / (DV / 8);
-        const int p = vt_pos(4 * kgrp);
+      if (tid + 256 * i < V_UNITS) {
+        const int p = vt_pos(4 * v_kgrp[i]);
+        const int sw = (v_dchunk[i] >> 1) & 7;
+        const int pp = (((p >> 3) ^ sw) << 3) | (p & 7);
+        __bf16* vrow = vs + (v_dchunk[i] * 8) * VP + pp;
         // 4 keys x 8 columns -> 8 rows (columns) x 4 keys
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           u32x2 lo = {lo_pair(vreg[i][0][w], vreg[i][1][w]), lo_pair(vreg[i][2][w], vreg[i][3][w])};
           u32x2 hi = {hi_pair(vreg[i][0][w], vreg[i][1][w]), hi_pair(vreg[i][2][w], vreg[i][3][w])};
-          *reinterpret_cast<u32x2*>(vs + (dchunk * 8 + 2 * w) * VP + p) = lo;
-          *reinterpret_cast<u32x2*>(vs + (dchunk * 8 + 2 * w + 1) * VP + p) = hi;
+          *reinterpret_cast<u32x2*>(vrow + (2 * w) * VP) = lo;
+          *reinterpret_cast<u32x2*>(vrow + (2 * w + 1) * VP) = hi;
         }
       }
     }
   };
 
   // ---- running state -------------------------------------------------------
-  f32x4 oacc[DT][QT];
+  // oacc[dt][qt]: O^T tile; lacc[qt]: the normaliser, from the ones-MFMA
+  f32x4 oacc[DT][QT], lacc[QT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int qt = 0; qt < QT; ++qt) {
+    lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m2[QT], lsum[QT];
+    for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m2[QT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) { m2[qt] = kNegInf; lsum[qt] = 0.f; }
+  for (int qt = 0; qt < QT; ++qt) m2[qt] = kNegInf;
   const float c2 = a.scale * kLog2e;
+  const u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
 
   if (n_kb > 0) {
     load_tile(0);
     store_tile(0);
   }
+  wait_vmem_all();
   __syncthreads();
 
   for (int kb = 0; kb < n_kb; ++kb) {
@@ -193,18 +212,22 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       const __bf16* ks = smem + buf * (K_ELEMS + V_ELEMS);
       const __bf16* vs = ks + K_ELEMS;
 
-      // S^T = K Q^T
+      // S^T = K Q^T: per contraction step, read the four key tiles' fragments
+      // first so several LDS reads are in flight per MFMA chain
       f32x4 sacc[4][QT];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          u32x4 kf = ld16(ks + (16 * kt + li) * KP + 32 * s + 8 * lg);
+      for (int s = 0; s < DS; ++s) {
+        u32x4 kf[4];
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma_bf16(kf, qf[qt][s], sacc[kt][qt]);
-        }
+        for (int kt = 0; kt < 4; ++kt) kf[kt] = ld16(ks + (16 * kt + li) * KP + 32 * s + 8 * lg);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma_bf16(kf[kt], qf[qt][s], sacc[kt][qt]);
       }
 
       // mask + online softmax (per query column = per lane)
@@ -213,21 +236,33 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       u32x4 pf[QT][2];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const int qpos = pos0 + qt * 16 + li;
-        const int kmax = a.causal ? min(qpos + off, a.S_k - 1) : a.S_k - 1;
-        float mx = kNegInf;
+        if (need_mask) {
+          const int qpos = pos0 + qt * 16 + li;
+          const int kmax = a.causal ? min(qpos + off, a.S_k - 1) : a.S_k - 1;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+          for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (need_mask && key0 + 16 * kt + 4 * lg + r > kmax) sacc[kt][qt][r] = kNegInf;
-            mx = fmaxf(mx, sacc[kt][qt][r]);
-          }
-        mx = group4_max(mx);
-        const float mnew = fmaxf(m2[qt], mx * c2);
-        const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2[qt] - mnew);
-        const float msub = (mnew == kNegInf) ? 0.f : mnew;
-        m2[qt] = mnew;
+            for (int r = 0; r < 4; ++r)
+              if (key0 + 16 * kt + 4 * lg + r > kmax) sacc[kt][qt][r] = kNegInf;
+        }
+        float mx = fmaxf(fmaxf(sacc[0][qt][0], sacc[0][qt][1]), sacc[0][qt][2]);
+        mx = fmaxf(fmaxf(mx, sacc[0][qt][3]), sacc[1][qt][0]);
+        mx = fmaxf(fmaxf(mx, sacc[1][qt][1]), sacc[1][qt][2]);
+        mx = fmaxf(fmaxf(mx, sacc[1][qt][3]), sacc[2][qt][0]);
+        mx = fmaxf(fmaxf(mx, sacc[2][qt][1]), sacc[2][qt][2]);
+        mx = fmaxf(fmaxf(mx, sacc[2][qt][3]), sacc[3][qt][0]);
+        mx = fmaxf(fmaxf(mx, sacc[3][qt][1]), sacc[3][qt][2]);
+        mx = fmaxf(mx, sacc[3][qt][3]);
+        const float mx2 = group4_max(mx) * c2;
+        if (wave_any(mx2 > m2[qt] + kRescaleSlack)) {
+          const float mnew = fmaxf(m2[qt], mx2);
+          const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2[qt] - mnew);
+          m2[qt] = mnew;
+          lacc[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+        }
+        const float msub = (m2[qt] == kNegInf) ? 0.f : m2[qt];
         float p[4][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -239,17 +274,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
                              pack_bf16(p[2 * k2 + 1][0], p[2 * k2 + 1][1]),
                              pack_bf16(p[2 * k2 + 1][2], p[2 * k2 + 1][3])};
         }
-        lsum[qt] = lsum[qt] * alpha + (bf16x8_sum(pf[qt][0]) + bf16x8_sum(pf[qt][1]));
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
       }
 
-      // O^T += V^T P^T
+      // O^T += V^T P^T, and the normaliser += 1^T P^T
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          u32x4 vf = ld16(vs + (16 * dt + li) * VP + 32 * k2 + 8 * lg);
+        for (int qt = 0; qt < QT; ++qt) lacc[qt] = mfma_bf16(ones, pf[qt][k2], lacc[qt]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int unit = (4 * k2 + lg) ^ (dt & 7);
+          u32x4 vf = ld16(vs + (16 * dt + li) * VP + 8 * unit);
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma_bf16(vf, pf[qt][k2], oacc[dt][qt]);
         }
@@ -264,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int qpos = pos0 + qt * 16 + li;
-    const float l = group4_sum(lsum[qt]);
+    const float l = lacc[qt][0];
     if (qpos >= a.S_q) continue;
     const float inv = 1.f / l;
     if (a.lse != nullptr && lg == 0) {
