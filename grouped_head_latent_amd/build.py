@@ -27,9 +27,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
 
 
-def _compile(src: str, extra=()) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra=(), objdir=None) -> str:
+    objdir = objdir or OBJDIR
+    os.makedirs(objdir, exist_ok=True)
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [HIPCC, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -38,20 +39,24 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, save_temps: bool = False) -> str:
-    """Compile every source and link libgha.so; returns its path."""
+def build(verbose: bool = False, save_temps: bool = False, defines=(), out: str | None = None) -> str:
+    """Compile every source and link libgha.so (or `out`); returns its path.
+    `defines` are extra -D tuning knobs."""
     extra = ["-save-temps=obj"] if save_temps else []
+    extra += [f"-D{d}" for d in defines]
+    target = out or LIB
+    objdir = OBJDIR if out is None else os.path.join(OBJDIR, os.path.basename(out) + ".objs")
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, objdir), SOURCES))
+    tmp = target + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, target)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {target}")
+    return target
 
 
 def clean() -> None:

@@ -141,7 +141,7 @@ gha_status gqa_prefill(const gha_tensor* q, const gha_tensor* k, const gha_tenso
   const int G = a.group;
   a.heads_per_wg = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
   a.n_subgroups = G / a.heads_per_wg;
-  const int pos_per_wg = (4 / a.heads_per_wg) * gha::prefill_rows_per_wave();
+  const int pos_per_wg = (4 / a.heads_per_wg) * gha::prefill_rows_per_wave(false);
   a.n_qblocks = (S_q + pos_per_wg - 1) / pos_per_wg;
   const int64_t nb = (int64_t)B * h_kv * a.n_subgroups * a.n_qblocks;
   if (nb > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
@@ -233,7 +233,7 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
   a.lse = lse; a.lse_heads = n_grp;
   a.S_q = S; a.S_k = S; a.h_kv = n_grp; a.group = per;
   a.heads_per_wg = 1; a.n_subgroups = 1;
-  const int pos_per_wg = 4 * gha::prefill_rows_per_wave();
+  const int pos_per_wg = 4 * gha::prefill_rows_per_wave(true);
   a.n_qblocks = (S + pos_per_wg - 1) / pos_per_wg;
   a.n_blocks = B * n_grp * a.n_qblocks;
   a.dv_head = d_v;

@@ -63,7 +63,7 @@ struct LatentArgs {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int dqk, int dv, bool out_f32, bool gta,
                                hipStream_t st);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
-int prefill_rows_per_wave();
+int prefill_rows_per_wave(bool gta);
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, int d, bool out_f32, hipStream_t st);
 hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st);

@@ -28,7 +28,8 @@ constexpr int TKEYS = 32;                          // tokens per tile
 constexpr int LP = DL + 8;                         // LDS row pitch (elements), 16 B pad
 constexpr int CHUNKS = TKEYS * DL / 8;             // 16-byte chunks per tile
 constexpr int LOADS = CHUNKS / 256;                // per thread
-static_assert(CHUNKS % 256 == 0, "tile staging");
+static_assert(CHUNKS % 256 == 0 && TKEYS * 8 == 256 && LOADS == 9 && RKV == 64 * (LOADS - 1) && DR == 64,
+              "tile staging: 8 threads per token row, 8 latent chunks + 1 RoPE chunk each");
 
 __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   constexpr int DS = DL / 32;  // 18 score MFMA steps
@@ -70,25 +71,24 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   const __bf16* rbase = (const __bf16*)a.kr + (int64_t)b * a.kr_sb;
   const float c2 = a.scale * kLog2e;
 
+  // Staging: thread t owns token row t/8 of the tile and its 16-byte chunks
+  // (t%8) + 8m, m = 0..8 (72 chunks per 576-wide row): one row pointer per
+  // tile, the chunks at constant offsets.  Rows past `end` are clamped to the
+  // last token (masked to -inf below).
+  const int s_row = tid >> 3, s_chunk = tid & 7;
   u32x4 stg[LOADS];
   auto load_tile = [&](int k0) {
+    const int kk = min(k0 + s_row, end - 1);
+    const __bf16* cp = cbase + (int64_t)kk * a.c_ss + 8 * s_chunk;
+    const __bf16* rp = rbase + (int64_t)kk * a.kr_ss + 8 * s_chunk;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (DL / 8), col = (c % (DL / 8)) * 8;
-      // clamped, not branched: tokens at or past `end` are masked to -inf
-      const int kk = min(k0 + key, end - 1);
-      stg[i] = (col < RKV) ? ld16(cbase + (int64_t)kk * a.c_ss + col)
-                           : ld16(rbase + (int64_t)kk * a.kr_ss + (col - RKV));
-    }
+    for (int m = 0; m < LOADS - 1; ++m) stg[m] = ld16(cp + 64 * m);
+    stg[LOADS - 1] = ld16(rp);
   };
   auto store_tile = [&](int buf) {
+    __bf16* dst = &smem[buf][s_row * LP + 8 * s_chunk];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (DL / 8), col = (c % (DL / 8)) * 8;
-      st16(&smem[buf][key * LP + col], stg[i]);
-    }
+    for (int m = 0; m < LOADS; ++m) st16(dst + 64 * m, stg[m]);
   };
 
   f32x4 oacc[4][8];

@@ -31,6 +31,19 @@ namespace {
 
 constexpr int KB = 64;  // keys per iteration
 
+// Tuning knobs (compile-time): 16-row query tiles per wave for the GQA
+// kernels, minimum resident work-groups per CU, and whether waves raise
+// their issue priority while in the score-MFMA phase.
+#ifndef GHA_PF_QT
+#define GHA_PF_QT 2
+#endif
+#ifndef GHA_PF_MIN_WG
+#define GHA_PF_MIN_WG 2
+#endif
+#ifndef GHA_PF_SETPRIO
+#define GHA_PF_SETPRIO 1
+#endif
+
 // Position of key u (0..63) of a tile inside a V^T row.  The S^T accumulator
 // of lane group g holds keys 16*kt + 4*g + r; the PV contraction step ks takes
 // tiles 2ks and 2ks+1, so group g's eight slots are keys
@@ -41,7 +54,7 @@ __device__ __forceinline__ int vt_pos(int u) {
 }
 
 template <int DQK, int DV, int QT, bool OUT_F32, bool GTA>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int KP = DQK + 8;   // K row pitch in LDS (elements): 16 B pad
   constexpr int VP = KB + 8;    // V^T row pitch in LDS (elements): 16 B pad
   constexpr int K_ELEMS = KB * KP;
@@ -219,6 +232,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (GHA_PF_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
         u32x4 kf[4];
@@ -230,6 +244,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
           for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma_bf16(kf[kt], qf[qt][s], sacc[kt][qt]);
       }
 
+      if (GHA_PF_SETPRIO) __builtin_amdgcn_s_setprio(0);
       // mask + online softmax (per query column = per lane)
       const bool need_mask = (key0 + KB > a.S_k) ||
                              (a.causal && key0 + KB - 1 > pos0 + off);
@@ -339,8 +354,8 @@ hipError_t launch_dims(const PrefillArgs& a, int dqk, int dv, bool out_f32, hipS
     return out_f32 ? launch_one<DQ, DVV, QTT, true, GTA>(a, st)                       \
                    : launch_one<DQ, DVV, QTT, false, GTA>(a, st);
   if constexpr (!GTA) {
-    GHA_CASE(128, 128, 2)
-    GHA_CASE(64, 64, 2)
+    GHA_CASE(128, 128, GHA_PF_QT)
+    GHA_CASE(64, 64, GHA_PF_QT)
   } else {
     GHA_CASE(64, 256, 2)
     GHA_CASE(64, 128, 2)
@@ -355,7 +370,7 @@ hipError_t launch_dims(const PrefillArgs& a, int dqk, int dv, bool out_f32, hipS
 
 }  // namespace
 
-int prefill_rows_per_wave() { return 2 * 16; }
+int prefill_rows_per_wave(bool gta) { return (gta ? 2 : GHA_PF_QT) * 16; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int dqk, int dv, bool out_f32, bool gta,
                                hipStream_t st) {
