@@ -141,13 +141,12 @@ gha_status gqa_prefill(const gha_tensor* q, const gha_tensor* k, const gha_tenso
   const int G = a.group;
   a.heads_per_wg = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
   a.n_subgroups = G / a.heads_per_wg;
-  const int pos_per_wg = (4 / a.heads_per_wg) * gha::prefill_rows_per_wave(false);
+  const int pos_per_wg = (4 / a.heads_per_wg) * gha::prefill_rows_per_wave();
   a.n_qblocks = (S_q + pos_per_wg - 1) / pos_per_wg;
   const int64_t nb = (int64_t)B * h_kv * a.n_subgroups * a.n_qblocks;
   if (nb > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
   a.n_blocks = (int)nb;
-  a.dv_head = d;
-  return launched(gha::launch_prefill_bf16(a, d, d, out_dtype == GHA_F32, false, st), "gqa_prefill");
+  return launched(gha::launch_prefill_bf16(a, d, out_dtype == GHA_F32, st), "gqa_prefill");
 }
 
 size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint, int d) {
@@ -233,15 +232,15 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
   a.lse = lse; a.lse_heads = n_grp;
   a.S_q = S; a.S_k = S; a.h_kv = n_grp; a.group = per;
   a.heads_per_wg = 1; a.n_subgroups = 1;
-  const int pos_per_wg = 4 * gha::prefill_rows_per_wave(true);
+  const int pos_per_wg = gha::gta_positions_per_wg();
   a.n_qblocks = (S + pos_per_wg - 1) / pos_per_wg;
-  a.n_blocks = B * n_grp * a.n_qblocks;
-  a.dv_head = d_v;
+  const int64_t nb = (int64_t)B * n_grp * a.n_qblocks;
+  if (nb > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  a.n_blocks = (int)nb;
   a.causal = causal ? 1 : 0;
   a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d_qk);
   a.B = B;
-  return launched(gha::launch_prefill_bf16(a, d_qk, DV, out_dtype == GHA_F32, true,
-                                           reinterpret_cast<hipStream_t>(stream)),
+  return launched(gha::launch_gta(a, d_qk, per, out_dtype == GHA_F32, reinterpret_cast<hipStream_t>(stream)),
                   "gta_shared_score_prefill");
 }
 

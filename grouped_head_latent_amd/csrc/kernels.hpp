@@ -20,7 +20,6 @@ struct PrefillArgs {
   int n_subgroups;    // group / heads_per_wg
   int n_qblocks;      // position blocks per (batch, head set)
   int n_blocks;       // work-groups with work
-  int dv_head;        // GTA: value width of one head
   int causal;
   int B;
   float scale;
@@ -60,10 +59,11 @@ struct LatentArgs {
   float scale;
 };
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int dqk, int dv, bool out_f32, bool gta,
-                               hipStream_t st);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, bool out_f32, hipStream_t st);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
-int prefill_rows_per_wave(bool gta);
+int prefill_rows_per_wave();
+hipError_t launch_gta(const PrefillArgs& a, int d_qk, int heads_per_group, bool out_f32, hipStream_t st);
+int gta_positions_per_wg();
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, int d, bool out_f32, hipStream_t st);
 hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st);

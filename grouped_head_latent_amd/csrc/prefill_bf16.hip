@@ -1,16 +1,8 @@
-// Causal grouped-head attention prefill, bf16 inputs, fp32 accumulation, on
-// gfx950 MFMA.  One kernel serves two of the library's operations:
-//
-//  * GQA ("Grouped Query Attention (GQA)", Ultralytics glossary, "How GQA
-//    works"): a group of query heads shares one key/value head.  A work-group
-//    takes up to four query heads of one group and one block of positions, so
-//    every K/V tile staged in LDS is used by all of those heads.
-//  * GTA shared-score attention ("GTA: Grouped-head latenT Attention" news
-//    article, grouped shared attention matrix): a group has one query and one
-//    key, so one score matrix, applied to the value of every head in the
-//    group.  Here the group's head values are treated as one wide value
-//    (heads_per_group * d_v columns), so P is computed once per group and
-//    multiplied into all of the group's heads in the same pass.
+// Causal grouped-query attention prefill, bf16 inputs, fp32 accumulation, on
+// gfx950 MFMA ("Grouped Query Attention (GQA)", Ultralytics glossary, "How
+// GQA works": a group of query heads shares one key/value head).  A
+// work-group takes up to four query heads of one group and one block of
+// positions, so every K/V tile staged in LDS is used by all of those heads.
 //
 // Per wave: QT tiles of 16 query rows.  Per iteration: 64 keys.
 //   S^T (keys x queries) = K Q^T on MFMA, K from LDS, Q^T resident in VGPRs.
@@ -53,7 +45,7 @@ __device__ __forceinline__ int vt_pos(int u) {
   return 32 * ks + 8 * g + 4 * half + r;
 }
 
-template <int DQK, int DV, int QT, bool OUT_F32, bool GTA>
+template <int DQK, int DV, int QT, bool OUT_F32>
 __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int KP = DQK + 8;   // K row pitch in LDS (elements): 16 B pad
   constexpr int VP = KB + 8;    // V^T row pitch in LDS (elements): 16 B pad
@@ -84,12 +76,12 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_bf16_kernel(Prefil
   const int qb = n_qb - 1 - (int)(lid % n_qb);  // heavy (late) blocks first
   int rest = (int)(lid / n_qb);
   const int sg = rest % a.n_subgroups;  rest /= a.n_subgroups;
-  const int kvh = rest % a.h_kv;        // GQA: KV head; GTA: group
+  const int kvh = rest % a.h_kv;        // KV head
   const int b = rest / a.h_kv;
 
   const int wph = 4 / a.heads_per_wg;   // waves per head
   const int pos_per_wg = wph * QT * 16;
-  const int qhead = GTA ? kvh : kvh * a.group + sg * a.heads_per_wg + wave / wph;
+  const int qhead = kvh * a.group + sg * a.heads_per_wg + wave / wph;
   const int pos0 = qb * pos_per_wg + (wave % wph) * QT * 16;  // this wave's first row
   const int off = a.S_k - a.S_q;  // bottom-right causal offset
 
@@ -105,8 +97,7 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_bf16_kernel(Prefil
 
   const __bf16* qbase = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)qhead * a.q_sh;
   const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
-  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb +
-                        (int64_t)(GTA ? kvh * a.group : kvh) * a.v_sh;
+  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
 
   // ---- resident Q^T fragments (B operand of the score MFMA) ---------------
   u32x4 qf[QT][DS];
@@ -133,8 +124,7 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_bf16_kernel(Prefil
     v_dchunk[i] = u % VCH;
     v_kgrp[i] = u / VCH;
     const int d = v_dchunk[i] * 8;
-    const __bf16* vp = GTA ? vbase + (int64_t)(d / a.dv_head) * a.v_sh + (d % a.dv_head) : vbase + d;
-    vthr[i] = vp + (int64_t)(4 * v_kgrp[i]) * a.v_ss;
+    vthr[i] = vbase + d + (int64_t)(4 * v_kgrp[i]) * a.v_ss;
   }
 
   u32x4 kreg[K_LOADS];
@@ -323,13 +313,7 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_bf16_kernel(Prefil
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int d = 16 * dt + 4 * lg;
-      int64_t obase;
-      if constexpr (GTA) {
-        obase = (int64_t)b * a.o_sb + (int64_t)(kvh * a.group + d / a.dv_head) * a.o_sh +
-                (int64_t)qpos * a.o_ss + (d % a.dv_head);
-      } else {
-        obase = (int64_t)b * a.o_sb + (int64_t)qhead * a.o_sh + (int64_t)qpos * a.o_ss + d;
-      }
+      const int64_t obase = (int64_t)b * a.o_sb + (int64_t)qhead * a.o_sh + (int64_t)qpos * a.o_ss + d;
       const f32x4 v = oacc[dt][qt] * inv;
       if constexpr (OUT_F32) {
         *reinterpret_cast<f32x4*>((float*)a.o + obase) = v;
@@ -340,41 +324,21 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_bf16_kernel(Prefil
   }
 }
 
-template <int DQK, int DV, int QT, bool OUT_F32, bool GTA>
+template <int D, int QT, bool OUT_F32>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t st) {
   const uint32_t padded = (uint32_t)((a.n_blocks + 7) / 8 * 8);
-  hipLaunchKernelGGL((prefill_bf16_kernel<DQK, DV, QT, OUT_F32, GTA>), dim3(padded), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, D, QT, OUT_F32>), dim3(padded), dim3(256), 0, st, a);
   return hipGetLastError();
-}
-
-template <bool GTA>
-hipError_t launch_dims(const PrefillArgs& a, int dqk, int dv, bool out_f32, hipStream_t st) {
-#define GHA_CASE(DQ, DVV, QTT)                                                        \
-  if (dqk == DQ && dv == DVV)                                                         \
-    return out_f32 ? launch_one<DQ, DVV, QTT, true, GTA>(a, st)                       \
-                   : launch_one<DQ, DVV, QTT, false, GTA>(a, st);
-  if constexpr (!GTA) {
-    GHA_CASE(128, 128, GHA_PF_QT)
-    GHA_CASE(64, 64, GHA_PF_QT)
-  } else {
-    GHA_CASE(64, 256, 2)
-    GHA_CASE(64, 128, 2)
-    GHA_CASE(64, 64, 2)
-    GHA_CASE(128, 256, 2)
-    GHA_CASE(128, 128, 2)
-    GHA_CASE(128, 64, 2)
-  }
-#undef GHA_CASE
-  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int prefill_rows_per_wave(bool gta) { return (gta ? 2 : GHA_PF_QT) * 16; }
+int prefill_rows_per_wave() { return GHA_PF_QT * 16; }
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int dqk, int dv, bool out_f32, bool gta,
-                               hipStream_t st) {
-  return gta ? launch_dims<true>(a, dqk, dv, out_f32, st) : launch_dims<false>(a, dqk, dv, out_f32, st);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, bool out_f32, hipStream_t st) {
+  if (d == 128) return out_f32 ? launch_one<128, GHA_PF_QT, true>(a, st) : launch_one<128, GHA_PF_QT, false>(a, st);
+  if (d == 64) return out_f32 ? launch_one<64, GHA_PF_QT, true>(a, st) : launch_one<64, GHA_PF_QT, false>(a, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gha
