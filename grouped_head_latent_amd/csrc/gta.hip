@@ -198,13 +198,18 @@ __global__ __launch_bounds__(256, 2) void gta_kernel(PrefillArgs a) {
   };
   // value phase of tile t: this wave's head over its position tiles
   auto value_rescale = [&](int t) __attribute__((always_inline)) {
+    float al[QTV];
+    bool any = false;
 #pragma unroll
-    for (int q = 0; q < QTV; ++q) {
-      const float al = alpha_s[t & 1][16 * (vq0 + q) + li];
-      if (wave_any(al != 1.f)) {
+    for (int q = 0; q < QTV; ++q) {  // all reads first: one LDS round trip
+      al[q] = alpha_s[t & 1][16 * (vq0 + q) + li];
+      any |= al[q] != 1.f;
+    }
+    if (wave_any(any)) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) oacc[w][q] *= al;
-      }
+      for (int q = 0; q < QTV; ++q)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) oacc[w][q] *= al[q];
     }
   };
   auto value_mfma = [&](int t, u32x2 (&vr)[2][8]) __attribute__((always_inline)) {
