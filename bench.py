@@ -40,6 +40,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel_substr: str):
+    """HBM bytes per dispatch of a kernel, from the counter runs recorded in
+    profiles/traffic.json (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of
+    known size).  None if there is no record or the kernel's source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel_substr)
+    if rec is None:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_dispatch"]
+
+
 def to_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
 
@@ -230,7 +248,8 @@ def main():
                    "global_batch": PREFILL["B"], "seq_len": PREFILL["S"], "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(head["tflops"], 2), "peak": acc.PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(head["tflops"] / acc.PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic("prefill_bf16_kernel<128, 128"),
+                     "algorithmic_bytes": head["bytes"]},
     }
     if not args.no_cpu:
         log("cpu baseline ...")
