@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgha.so")
 OBJDIR = os.path.join(ROOT, "_build", "gha")
-SOURCES = ["abi.cpp", "prefill_bf16.hip", "prefill_f32.hip", "gta.hip", "decode.hip", "latent.hip"]
+SOURCES = ["abi.cpp", "prefill_bf16.hip", "prefill_d128.hip", "prefill_f32.hip", "gta.hip", "decode.hip", "latent.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -60,6 +60,8 @@ struct LatentArgs {
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, bool out_f32, hipStream_t st);
+bool prefill_d128_supported(const PrefillArgs& a);
+hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t st);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
 int prefill_rows_per_wave();
 hipError_t launch_gta(const PrefillArgs& a, int d_qk, int heads_per_group, bool out_f32, hipStream_t st);

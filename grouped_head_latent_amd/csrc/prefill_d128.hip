@@ -1,0 +1,392 @@
+// Causal grouped-query attention prefill for head dim 128, bf16 in, fp32
+// accumulation ("Grouped Query Attention (GQA)", Ultralytics glossary, "How
+// GQA works": a group of query heads shares one key/value head).  Same work
+// split and math as the generic bf16 kernel; what differs is how K/V tiles
+// reach the MFMAs:
+//
+//  * Tiles go from global memory straight into LDS (buffer_load_dwordx4 ...
+//    lds: lane l of a wave writes 16 bytes at LDS base + 16 l).  No VGPR staging,
+//    no LDS stores, no transposition work on the VALU.  Each lane picks the
+//    16-byte unit of global memory that belongs at its LDS slot, so the LDS
+//    layout can be swizzled freely: rows are 256 bytes (16 units); K row r
+//    keeps unit u at slot u ^ (r & 15), V row r keeps unit u at slot
+//    u ^ 2(r & 7).
+//  * S^T = K Q^T reads K fragments with ds_read_b128 (16 lanes, 16 rows, one
+//    logical unit: 16 distinct slots, no bank conflict).
+//  * O^T += V^T P^T reads V^T fragments from the row-major V tile with
+//    ds_read_b64_tr_b16.  Within each 16-lane group that instruction hands
+//    destination lane d, element j, the element d % 4 of source lane
+//    4 j + d / 4.  Source lane s of group g points at key row
+//    K0 + s / 4 (K0 = 32 k2 + 16 h + 4 g), columns 16 dt + 4 (s % 4) .. + 3,
+//    so lane d receives V[K0 + j][16 dt + d], j = 0..3: the four keys that
+//    the score accumulator of lane group g holds in rows 4 g .. 4 g + 3.  Two
+//    such reads (h = 0, 1) give the eight contraction slots of the group.
+//    The 32 bytes a row contributes sit in slots 2(dt ^ (r & 7)) + {0, 1}, so
+//    the eight rows read by one half-wave cover all 16 slots.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+#include <type_traits>
+
+namespace gha {
+
+namespace {
+
+constexpr int KB = 64;     // keys per tile
+constexpr int ROWB = 256;  // bytes per K or V row in LDS (128 bf16)
+constexpr int TILEB = KB * ROWB;
+
+#ifndef GHA_PF_QT
+#define GHA_PF_QT 2
+#endif
+#ifndef GHA_PF_MIN_WG
+#define GHA_PF_MIN_WG 2
+#endif
+#ifndef GHA_PF_SETPRIO
+#define GHA_PF_SETPRIO 1
+#endif
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Buffer resource word 3 for raw (unswizzled, untyped) dword access.
+constexpr int kBufferFlags = 0x00020000;
+
+// 16 bytes per lane from buffer `rs` at voff + soff into LDS at lds + 16 lane
+// (buffer_load_dwordx4 ... lds; rows past the buffer's range come back as
+// zeros).  Written as inline asm so that the compiler does not see an LDS
+// write it cannot disambiguate: with the builtin it waits for every
+// outstanding tile load before each LDS read, which serialises the prefetch.
+// The kernel orders these loads itself (s_waitcnt vmcnt + barrier).  The
+// instruction has no destination register; M0 needs one wait state after
+// it is written.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ u32x2 ld_tr(const unsigned char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
+
+template <int QT, bool OUT_F32>
+__global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(PrefillArgs a) {
+  constexpr int D = 128;
+  constexpr int DS = D / 32;  // contraction steps of the score MFMA
+  constexpr int DT = D / 16;  // 16-wide output column tiles
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+
+  // ---- which work this work-group does (as in the generic kernel) ---------
+  const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  if (lid >= (uint32_t)a.n_blocks) return;
+  const int n_qb = a.n_qblocks;
+  const int qb = n_qb - 1 - (int)(lid % n_qb);  // heavy (late) blocks first
+  int rest = (int)(lid / n_qb);
+  const int sg = rest % a.n_subgroups;  rest /= a.n_subgroups;
+  const int kvh = rest % a.h_kv;
+  const int b = rest / a.h_kv;
+
+  const int wph = 4 / a.heads_per_wg;
+  const int pos_per_wg = wph * QT * 16;
+  const int qhead = kvh * a.group + sg * a.heads_per_wg + wave / wph;
+  const int pos0 = qb * pos_per_wg + (wave % wph) * QT * 16;
+  const int off = a.S_k - a.S_q;  // bottom-right causal offset
+
+  int k_end = a.S_k;
+  int wave_kmax = a.S_k - 1;
+  if (a.causal) {
+    const int last_pos = min(qb * pos_per_wg + pos_per_wg - 1, a.S_q - 1);
+    k_end = min(a.S_k, last_pos + off + 1);
+    wave_kmax = min(a.S_k - 1, min(pos0 + QT * 16 - 1, a.S_q - 1) + off);
+  }
+  const int n_kb = (k_end + KB - 1) / KB;
+
+  const __bf16* qbase = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)qhead * a.q_sh;
+  const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
+  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
+
+  // ---- resident Q^T fragments ---------------------------------------------
+  u32x4 qf[QT][DS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int pos = min(pos0 + qt * 16 + li, a.S_q - 1);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qf[qt][s] = ld16(qbase + (int64_t)pos * a.q_ss + 32 * s + 8 * lg);
+  }
+
+  // ---- tile loads: wave w fills rows 16 w .. 16 w + 15 of both tiles -------
+  // Load i of a wave covers rows 16 w + 4 i + lane / 16, LDS slot lane % 16.
+  // Buffer loads with the range set to the last key's row: rows past the
+  // sequence end come back as zeros (their scores are masked anyway), so the
+  // tail tile needs no address clamping.
+  const int lrow = lane >> 4, lslot = lane & 15;
+  uint32_t kofs[4], vofs[4];  // byte offsets from the tile's first key
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = 4 * i + lrow;  // row within the wave's 16 (= r & 15)
+    const int r = 16 * wave + rr;
+    kofs[i] = (uint32_t)(r * a.k_ss + 8 * (lslot ^ rr)) * 2u;
+    vofs[i] = (uint32_t)(r * a.v_ss + 8 * (lslot ^ (2 * (rr & 7)))) * 2u;
+  }
+  const uint32_t k_step = (uint32_t)a.k_ss * (2u * KB), v_step = (uint32_t)a.v_ss * (2u * KB);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)kbase, 0, (int)((uint32_t)(a.S_k - 1) * (uint32_t)a.k_ss * 2u + 2u * D), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)vbase, 0, (int)((uint32_t)(a.S_k - 1) * (uint32_t)a.v_ss * 2u + 2u * D), kBufferFlags);
+  // LDS: K tiles in buffers 0/1 at 0 and 16 KiB, V tiles in buffers 0/1 at
+  // 32 and 48 KiB; tile t goes to buffer t % 2.
+  auto issue_k = [&](int t) {
+    const uint32_t dst = lds_offset(smem) + (t & 1) * TILEB + wave * 16 * ROWB;
+    const uint32_t so = (uint32_t)t * k_step;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(krs, dst + 1024 * i, kofs[i], so);
+  };
+  auto issue_v = [&](int t) {
+    const uint32_t dst = lds_offset(smem) + 2 * TILEB + (t & 1) * TILEB + wave * 16 * ROWB;
+    const uint32_t so = (uint32_t)t * v_step;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(vrs, dst + 1024 * i, vofs[i], so);
+  };
+
+  // ---- fragment addresses inside a stage (bytes) ----------------------------
+  // K: row 16 kt + li, logical unit 4 s + lg -> slot (4 s + lg) ^ li.  Since
+  // 4 s and lg occupy different bits, the byte address is
+  // (li * 256 + 16 (lg ^ li)) ^ 64 s, plus 4096 kt.
+  const uint32_t kfrag = li * ROWB + 16 * (lg ^ li);
+  // V: source lane li of group lg reads row vr = 4 lg + li / 4 (+ 32 k2 + 16 h),
+  // columns 16 dt + 4 (li % 4): logical unit 2 dt + (li / 2) % 2, byte 8 (li % 2)
+  // of it, at slot 2 (dt ^ (vr & 7)) + (li / 2) % 2.  Bits 5..7 of the
+  // remaining terms are zero, so the address is vfrag ^ 32 dt.
+  uint32_t vfrag;
+  {
+    const int vr = 4 * lg + (li >> 2);
+    vfrag = (2 * TILEB + vr * ROWB + 16 * ((li >> 1) & 1) + 8 * (li & 1)) ^ (32 * (vr & 7));
+  }
+  // buffer 1 of either tile sits 16 KiB above buffer 0, and no fragment
+  // offset reaches bit 14
+  static_assert(TILEB == 16384, "buffer bit");
+
+  // ---- running state -------------------------------------------------------
+  f32x4 oacc[DT][QT], lacc[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m2[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) m2[qt] = kNegInf;
+  const float c2 = a.scale * kLog2e;
+  const u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+
+  // The MFMA phase of iteration t runs in eight steps, each issuing the LDS
+  // reads of the next step before its own MFMAs (register double buffer):
+  //   steps 0..3: O^T += V^T P^T for k2 = step / 2, column tiles 4 (step % 2) ..
+  //               + 3 (V from buffer t % 2; step 0 also adds 1^T P^T to the
+  //               normaliser, step 2 likewise for k2 = 1)
+  //   steps 4..7: S^T += K Q^T for contraction step s = step - 4 (K of tile
+  //               t + 1 from buffer (t + 1) % 2)
+  f32x4 sacc[4][QT];
+  u32x4 fr[2][4];
+  auto load_step = [&](int j, int t, u32x4 (&f)[4]) __attribute__((always_inline)) {
+    if (j < 4) {
+      const uint32_t vst = vfrag ^ ((t & 1) << 14);
+      const int k2 = j >> 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t va = vst ^ ((4 * (j & 1) + i) << 5);
+        const u32x2 h0 = ld_tr(smem + va + k2 * 32 * ROWB);
+        const u32x2 h1 = ld_tr(smem + va + k2 * 32 * ROWB + 16 * ROWB);
+        f[i] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+      }
+    } else {
+      const uint32_t kst = kfrag ^ (((t + 1) & 1) << 14);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) f[kt] = ld16(smem + (kst ^ ((j - 4) << 6)) + kt * 16 * ROWB);
+    }
+  };
+  auto mfma_step = [&](int j, const u32x4 (&f)[4], const u32x4 (&pf)[QT][2]) __attribute__((always_inline)) {
+    if (j < 4) {
+      const int k2 = j >> 1;
+      if ((j & 1) == 0) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) lacc[qt] = mfma_bf16(ones, pf[qt][k2], lacc[qt]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const int dt = 4 * (j & 1) + i;
+          oacc[dt][qt] = mfma_bf16(f[i], pf[qt][k2], oacc[dt][qt]);
+        }
+    } else {
+      const int st = j - 4;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          sacc[kt][qt] = mfma_bf16(f[kt], qf[qt][st], st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kt][qt]);
+    }
+  };
+  // scores of tile 0 (prologue): steps 4..7 of a phantom iteration -1
+  auto score0 = [&]() __attribute__((always_inline)) {
+    const u32x4 nopf[QT][2] = {};
+    load_step(4, -1, fr[0]);
+#pragma unroll
+    for (int j = 4; j < 8; ++j) {
+      if (j + 1 < 8) load_step(j + 1, -1, fr[(j + 1) & 1]);
+      mfma_step(j, fr[j & 1], nopf);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Software pipeline: iteration t runs the softmax of tile t (VALU), then
+  // P(t) V(t) and the scores of tile t + 1 back to back (MFMA), so each wave
+  // alternates one VALU phase and one MFMA phase per tile and the two waves
+  // sharing a SIMD can overlap them.  K runs one tile ahead of V.
+  if (n_kb > 0) issue_k(0);
+  if (n_kb > 0) issue_v(0);
+  if (n_kb > 1) issue_k(1);
+  wait_vmem_all();
+  __syncthreads();
+  if (n_kb > 0 && wave_kmax >= 0) score0();
+  __syncthreads();  // every wave is done with K buffer 0 before tile 2 lands there
+
+  // Tiles before t_mask are fully visible to every wave of the work-group
+  // (no key past the sequence end or past any row's diagonal); from t_mask
+  // on, the softmax applies the mask.  Two copies of the loop keep the mask
+  // test out of the main one.
+  int t_mask = a.S_k / KB;
+  if (a.causal) t_mask = min(t_mask, max(0, (qb * pos_per_wg + off + 1) / KB));
+  t_mask = min(t_mask, n_kb);
+
+  auto iteration = [&](int t, auto masked) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
+    // V(t+1) replaces V(t-1) and K(t+2) replaces K(t): both were last read
+    // before the previous barrier
+    if (t + 1 < n_kb) issue_v(t + 1);
+    if (t + 2 < n_kb) issue_k(t + 2);
+
+    const int key0 = t * KB;
+    if (!kMasked || key0 <= wave_kmax) {  // wave-uniform: skip tiles wholly above the diagonal
+      load_step(0, t, fr[0]);  // in flight during the softmax
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 pf[QT][2];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        if (kMasked) {
+          const int qpos = pos0 + qt * 16 + li;
+          const int kmax = a.causal ? min(qpos + off, a.S_k - 1) : a.S_k - 1;
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (key0 + 16 * kt + 4 * lg + r > kmax) sacc[kt][qt][r] = kNegInf;
+        }
+        float mx = fmaxf(fmaxf(sacc[0][qt][0], sacc[0][qt][1]), sacc[0][qt][2]);
+        mx = fmaxf(fmaxf(mx, sacc[0][qt][3]), sacc[1][qt][0]);
+        mx = fmaxf(fmaxf(mx, sacc[1][qt][1]), sacc[1][qt][2]);
+        mx = fmaxf(fmaxf(mx, sacc[1][qt][3]), sacc[2][qt][0]);
+        mx = fmaxf(fmaxf(mx, sacc[2][qt][1]), sacc[2][qt][2]);
+        mx = fmaxf(fmaxf(mx, sacc[2][qt][3]), sacc[3][qt][0]);
+        mx = fmaxf(fmaxf(mx, sacc[3][qt][1]), sacc[3][qt][2]);
+        mx = fmaxf(mx, sacc[3][qt][3]);
+        const float mx2 = group4_max(mx) * c2;
+        if (wave_any(mx2 > m2[qt] + kRescaleSlack)) {
+          const float mnew = fmaxf(m2[qt], mx2);
+          const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2[qt] - mnew);
+          m2[qt] = mnew;
+          lacc[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+        }
+        const float msub = (m2[qt] == kNegInf) ? 0.f : m2[qt];
+        float p[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[kt][r] = fast_exp2(__builtin_fmaf(sacc[kt][qt][r], c2, -msub));
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          pf[qt][k2] = u32x4{pack_bf16(p[2 * k2][0], p[2 * k2][1]), pack_bf16(p[2 * k2][2], p[2 * k2][3]),
+                             pack_bf16(p[2 * k2 + 1][0], p[2 * k2 + 1][1]),
+                             pack_bf16(p[2 * k2 + 1][2], p[2 * k2 + 1][3])};
+        }
+      }
+
+      if (GHA_PF_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      // P(t) V(t), then the scores of tile t + 1; past this wave's last tile
+      // (or the last tile) those read a stale buffer and are never used
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j + 1 < 8) load_step(j + 1, t, fr[(j + 1) & 1]);
+        mfma_step(j, fr[j & 1], pf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (GHA_PF_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    }
+
+
+    wait_vmem_all();
+    __syncthreads();
+  };
+  for (int t = 0; t < t_mask; ++t) iteration(t, std::false_type{});
+  for (int t = t_mask; t < n_kb; ++t) iteration(t, std::true_type{});
+
+  // ---- epilogue --------------------------------------------------------------
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qpos = pos0 + qt * 16 + li;
+    const float l = lacc[qt][0];
+    if (qpos >= a.S_q) continue;
+    const float inv = 1.f / l;
+    if (a.lse != nullptr && lg == 0) {
+      a.lse[((int64_t)b * a.lse_heads + qhead) * a.S_q + qpos] = (m2[qt] + fast_log2(l)) * kLn2;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 16 * dt + 4 * lg;
+      const int64_t obase = (int64_t)b * a.o_sb + (int64_t)qhead * a.o_sh + (int64_t)qpos * a.o_ss + d;
+      const f32x4 v = oacc[dt][qt] * inv;
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<f32x4*>((float*)a.o + obase) = v;
+      } else {
+        *reinterpret_cast<u32x2*>((__bf16*)a.o + obase) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool prefill_d128_supported(const PrefillArgs& a) {
+  // one (batch, head) sequence of K or V must span less than 2^31 bytes
+  // (buffer offsets and range are 32-bit), and rows must not overlap, so
+  // that the range check cuts exactly at the last key
+  const int64_t ss = a.k_ss > a.v_ss ? a.k_ss : a.v_ss;
+  const int64_t span = ((int64_t)a.S_k + KB) * ss * 2;
+  return a.k_ss >= 128 && a.v_ss >= 128 && span < ((int64_t)1 << 31);
+}
+
+hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t st) {
+  const uint32_t padded = (uint32_t)((a.n_blocks + 7) / 8 * 8);
+  if (out_f32)
+    hipLaunchKernelGGL((prefill_d128_kernel<GHA_PF_QT, true>), dim3(padded), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_d128_kernel<GHA_PF_QT, false>), dim3(padded), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace gha
