@@ -62,9 +62,23 @@ def to_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
 
 
+SPINUP_S = 1.0  # set from --spinup-s
+
+
 def time_steps(fn, steps, warmup, torch):
-    """Warm up, then time exactly `steps` calls between two synchronisations
-    with HIP events recorded on the stream the kernels are launched on."""
+    """Spin the GPU clocks up, warm up, then time exactly `steps` calls
+    between two synchronisations with HIP events recorded on the stream the
+    kernels are launched on.
+
+    The MI355X ramps its clocks over tens of milliseconds of sustained load;
+    a few warmup steps of a sub-millisecond kernel leave it below its steady
+    clock.  So the same call first runs untimed for SPINUP_S seconds (not
+    counted in `warmup` or `steps`)."""
+    t_end = time.perf_counter() + SPINUP_S
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -185,7 +199,11 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="prefill|decode|gta|latent: time one workload")
+    ap.add_argument("--spinup-s", type=float, default=1.0,
+                    help="untimed seconds of the same workload before the warmup steps (clock ramp)")
     args = ap.parse_args()
+    global SPINUP_S
+    SPINUP_S = args.spinup_s
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
@@ -237,6 +255,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spinup_s": args.spinup_s,
         "ms_per_step": round(head["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -248,7 +267,7 @@ def main():
                    "global_batch": PREFILL["B"], "seq_len": PREFILL["S"], "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(head["tflops"], 2), "peak": acc.PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(head["tflops"] / acc.PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_bf16_kernel<128, 128"),
+                     "traffic": measured_traffic("prefill_d128_kernel<2, false>"),
                      "algorithmic_bytes": head["bytes"]},
     }
     if not args.no_cpu:

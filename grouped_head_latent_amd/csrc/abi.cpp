@@ -141,7 +141,7 @@ gha_status gqa_prefill(const gha_tensor* q, const gha_tensor* k, const gha_tenso
   const int G = a.group;
   a.heads_per_wg = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
   a.n_subgroups = G / a.heads_per_wg;
-  const int pos_per_wg = (4 / a.heads_per_wg) * gha::prefill_rows_per_wave();
+  const int pos_per_wg = (gha::prefill_bf16_waves(a, d) / a.heads_per_wg) * gha::prefill_rows_per_wave();
   a.n_qblocks = (S_q + pos_per_wg - 1) / pos_per_wg;
   const int64_t nb = (int64_t)B * h_kv * a.n_subgroups * a.n_qblocks;
   if (nb > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");

@@ -339,8 +339,12 @@ int prefill_rows_per_wave() { return GHA_PF_QT * 16; }
 #define GHA_PF_DIRECT 1
 #endif
 
+static bool use_d128(const PrefillArgs& a, int d) { return d == 128 && GHA_PF_DIRECT && prefill_d128_supported(a); }
+
+int prefill_bf16_waves(const PrefillArgs& a, int d) { return use_d128(a, d) ? prefill_d128_waves() : 4; }
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, bool out_f32, hipStream_t st) {
-  if (d == 128 && GHA_PF_DIRECT && prefill_d128_supported(a)) return launch_prefill_d128(a, out_f32, st);
+  if (use_d128(a, d)) return launch_prefill_d128(a, out_f32, st);
   if (d == 128) return out_f32 ? launch_one<128, GHA_PF_QT, true>(a, st) : launch_one<128, GHA_PF_QT, false>(a, st);
   if (d == 64) return out_f32 ? launch_one<64, GHA_PF_QT, true>(a, st) : launch_one<64, GHA_PF_QT, false>(a, st);
   return hipErrorInvalidValue;
