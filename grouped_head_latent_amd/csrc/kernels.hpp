@@ -61,7 +61,6 @@ struct LatentArgs {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, bool out_f32, hipStream_t st);
 bool prefill_d128_supported(const PrefillArgs& a);
-int prefill_d128_waves();  // waves per work-group of the d = 128 kernel
 hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t st);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
 int prefill_rows_per_wave();

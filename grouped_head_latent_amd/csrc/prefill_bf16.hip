@@ -341,7 +341,7 @@ int prefill_rows_per_wave() { return GHA_PF_QT * 16; }
 
 static bool use_d128(const PrefillArgs& a, int d) { return d == 128 && GHA_PF_DIRECT && prefill_d128_supported(a); }
 
-int prefill_bf16_waves(const PrefillArgs& a, int d) { return use_d128(a, d) ? prefill_d128_waves() : 4; }
+int prefill_bf16_waves(const PrefillArgs&, int) { return 4; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, bool out_f32, hipStream_t st) {
   if (use_d128(a, d)) return launch_prefill_d128(a, out_f32, st);

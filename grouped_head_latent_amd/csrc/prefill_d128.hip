@@ -27,7 +27,6 @@
 #include "kernels.hpp"
 
 #include <type_traits>
-#include <utility>
 
 namespace gha {
 
@@ -46,11 +45,11 @@ constexpr int TILEB = KB * ROWB;
 #ifndef GHA_PF_SETPRIO
 #define GHA_PF_SETPRIO 1
 #endif
-#ifndef GHA_PF_ILV
-#define GHA_PF_ILV 1
-#endif
 #ifndef GHA_PF_PFD
 #define GHA_PF_PFD 1
+#endif
+#ifndef GHA_PF_ORDER
+#define GHA_PF_ORDER 1
 #endif
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -207,6 +206,10 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
   //               t + 1 from buffer (t + 1) % 2)
   f32x4 sacc[4][QT];
   constexpr int NFR = GHA_PF_PFD + 1;  // fragment buffers (LDS reads run PFD steps ahead)
+  // Order of the steps in the MFMA phase: PV and score steps alternate, so
+  // that the transposing V reads (slow per wave) of one step overlap the
+  // MFMAs of a score step, whose own K reads are few.
+  auto step_at = [](int j) { return GHA_PF_ORDER ? ((j & 1) ? 4 + (j >> 1) : (j >> 1)) : j; };
   u32x4 fr[NFR][4];
   auto load_step = [&](int j, int t, u32x4 (&f)[4]) __attribute__((always_inline)) {
     if (j < 4) {
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
     const int key0 = t * KB;
     if (!kMasked || key0 <= wave_kmax) {  // wave-uniform: skip tiles wholly above the diagonal
 #pragma unroll
-      for (int j = 0; j < GHA_PF_PFD; ++j) load_step(j, t, fr[j]);  // in flight during the softmax
+      for (int j = 0; j < GHA_PF_PFD; ++j) load_step(step_at(j), t, fr[j]);  // in flight during the softmax
       __builtin_amdgcn_sched_barrier(0);
       u32x4 pf[QT][2];
 #pragma unroll
@@ -341,8 +344,8 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
       // (or the last tile) those read a stale buffer and are never used
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (j + GHA_PF_PFD < 8) load_step(j + GHA_PF_PFD, t, fr[(j + GHA_PF_PFD) % NFR]);
-        mfma_step(j, fr[j % NFR], pf);
+        if (j + GHA_PF_PFD < 8) load_step(step_at(j + GHA_PF_PFD), t, fr[(j + GHA_PF_PFD) % NFR]);
+        mfma_step(step_at(j), fr[j % NFR], pf);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (GHA_PF_SETPRIO) __builtin_amdgcn_s_setprio(0);
@@ -378,334 +381,6 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
   }
 }
 
-// ---------------------------------------------------------------------------
-// Eight-wave variant: two groups of four waves on the same K/V tiles, the
-// two waves on each SIMD (w and w + 4) phase-locked by barriers so that one
-// runs its MFMA phase while the other runs its softmax:
-//
-//   phase 2t:    group 0: softmax(t)             group 1: PV(t-1), S(t)
-//   phase 2t+1:  group 0: PV(t), S(t+1)          group 1: softmax(t)
-//
-// Both groups run the same instruction stream; group 1 is one barrier
-// behind.  K(t) is read in phases 2t-1 and 2t, V(t) in 2t+1 and 2t+2.
-// Three LDS slots per tile kind: each wave loads its rows of K(t+3) and
-// V(t+2) when its MFMA phase of tile t starts, into the slots of K(t) and
-// V(t-1), which no wave reads any more.
-__device__ __forceinline__ void wait_vm4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void phase_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Ask the scheduler to alternate LDS reads and MFMAs in the current region:
-// pairs of (one DS read, M MFMAs).  A wave issues in order and a transposing
-// LDS read keeps the wave's LDS path busy for tens of cycles, so a burst of
-// reads ahead of the MFMAs that follow it stalls them.
-template <int M, int... I>
-__device__ __forceinline__ void ds_mfma_pairs(std::integer_sequence<int, I...>) {
-  ((__builtin_amdgcn_sched_group_barrier(0x100, 1, 0), __builtin_amdgcn_sched_group_barrier(0x008, M, 0), (void)I), ...);
-}
-
-template <bool OUT_F32>
-__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
-  constexpr int D = 128, QT = 2;
-  constexpr int DS = D / 32;
-  constexpr int DT = D / 16;
-  constexpr int NSLOT = 3;
-  constexpr uint32_t VBASE = NSLOT * TILEB;  // V slots after the K slots
-
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NSLOT * TILEB];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int li = lane & 15;
-  const int lg = lane >> 4;
-
-  const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  if (lid >= (uint32_t)a.n_blocks) return;
-  const int n_qb = a.n_qblocks;
-  const int qb = n_qb - 1 - (int)(lid % n_qb);
-  int rest = (int)(lid / n_qb);
-  const int sg = rest % a.n_subgroups;  rest /= a.n_subgroups;
-  const int kvh = rest % a.h_kv;
-  const int b = rest / a.h_kv;
-
-  const int wph = 8 / a.heads_per_wg;  // waves per head
-  const int pos_per_wg = wph * QT * 16;
-  const int qhead = kvh * a.group + sg * a.heads_per_wg + wave / wph;
-  const int pos0 = qb * pos_per_wg + (wave % wph) * QT * 16;
-  const int off = a.S_k - a.S_q;
-
-  int k_end = a.S_k;
-  int wave_kmax = a.S_k - 1;
-  if (a.causal) {
-    const int last_pos = min(qb * pos_per_wg + pos_per_wg - 1, a.S_q - 1);
-    k_end = min(a.S_k, last_pos + off + 1);
-    wave_kmax = min(a.S_k - 1, min(pos0 + QT * 16 - 1, a.S_q - 1) + off);
-  }
-  const int n_kb = (k_end + KB - 1) / KB;
-
-  const __bf16* qbase = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)qhead * a.q_sh;
-  const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
-  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
-
-  u32x4 qf[QT][DS];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int pos = min(pos0 + qt * 16 + li, a.S_q - 1);
-#pragma unroll
-    for (int s = 0; s < DS; ++s) qf[qt][s] = ld16(qbase + (int64_t)pos * a.q_ss + 32 * s + 8 * lg);
-  }
-  wait_vmem_all();
-
-  // ---- tile loads: group 0 loads K tiles, group 1 V tiles; wave w of a group
-  // fills rows 16 (w % 4) .. + 15 (load i: rows + 4 i + lane / 16) -----------
-  const int lrow = lane >> 4, lslot = lane & 15;
-  const int wg4 = wave & 3;
-  uint32_t tofs[4];  // byte offsets from the tile's first key
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = 4 * i + lrow;
-    const int r = 16 * wg4 + rr;
-    tofs[i] = grp == 0 ? (uint32_t)(r * a.k_ss + 8 * (lslot ^ rr)) * 2u
-                       : (uint32_t)(r * a.v_ss + 8 * (lslot ^ (2 * (rr & 7)))) * 2u;
-  }
-  const uint32_t t_step = grp == 0 ? (uint32_t)a.k_ss * (2u * KB) : (uint32_t)a.v_ss * (2u * KB);
-  const __amdgpu_buffer_rsrc_t trs = grp == 0
-      ? __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, (int)((uint32_t)(a.S_k - 1) * (uint32_t)a.k_ss * 2u + 2u * D), kBufferFlags)
-      : __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, (int)((uint32_t)(a.S_k - 1) * (uint32_t)a.v_ss * 2u + 2u * D), kBufferFlags);
-  const uint32_t lds0 = lds_offset(smem) + (grp == 0 ? 0u : VBASE) + wg4 * 16 * ROWB;
-  // this wave's rows of tile t (K for group 0, V for group 1) into slot t % 3;
-  // always four loads per call (tiles past the end read as zeros), so that
-  // vmcnt counts stay exact
-  auto issue = [&](int t) {
-    const uint32_t so = (uint32_t)t * t_step;
-    const uint32_t dst = lds0 + (t % NSLOT) * TILEB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(trs, dst + 1024 * i, tofs[i], so);
-  };
-
-  // fragment addresses (bytes) without the slot offset; see the 4-wave kernel
-  const uint32_t kfrag = li * ROWB + 16 * (lg ^ li);
-  uint32_t vfrag;
-  {
-    const int vr = 4 * lg + (li >> 2);
-    vfrag = (vr * ROWB + 16 * ((li >> 1) & 1) + 8 * (li & 1)) ^ (32 * (vr & 7));
-  }
-
-  f32x4 oacc[DT][QT], lacc[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  float m2[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) m2[qt] = kNegInf;
-  const float c2 = a.scale * kLog2e;
-  const u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
-
-  f32x4 sacc[4][QT];
-  u32x4 pf[QT][2];
-  u32x4 fr[3][4];
-
-  // MFMA-phase steps as in the 4-wave kernel: 0..3 PV of tile t (V slot
-  // vslot), 4..7 scores of tile t + 1 (K slot kslot)
-  auto load_step = [&](int j, uint32_t vb, uint32_t kbv, u32x4 (&f)[4]) __attribute__((always_inline)) {
-    if (j < 4) {
-      const int k2 = j >> 1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t va = vb ^ ((4 * (j & 1) + i) << 5);
-        const u32x2 h0 = ld_tr(smem + va + k2 * 32 * ROWB);
-        const u32x2 h1 = ld_tr(smem + va + k2 * 32 * ROWB + 16 * ROWB);
-        f[i] = u32x4{h0[0], h0[1], h1[0], h1[1]};
-      }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) f[kt] = ld16(smem + (kbv ^ ((j - 4) << 6)) + kt * 16 * ROWB);
-    }
-  };
-  auto mfma_step = [&](int j, const u32x4 (&f)[4]) __attribute__((always_inline)) {
-    if (j < 4) {
-      const int k2 = j >> 1;
-      if ((j & 1) == 0) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) lacc[qt] = mfma_bf16(ones, pf[qt][k2], lacc[qt]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const int dt = 4 * (j & 1) + i;
-          oacc[dt][qt] = mfma_bf16(f[i], pf[qt][k2], oacc[dt][qt]);
-        }
-    } else {
-      const int st = j - 4;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          sacc[kt][qt] = mfma_bf16(f[kt], qf[qt][st], st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kt][qt]);
-    }
-  };
-  // MFMA phase: steps [J0, J1) with V slot vs and K slot ks.  LDS reads run
-  // two steps ahead (three fragment buffers); the reads of the first two
-  // steps may already have been issued (prefetch_m).
-  auto prefetch_m = [&](int vs, int ks, auto j0) __attribute__((always_inline)) {
-    constexpr int J0 = decltype(j0)::value;
-    const uint32_t vb = vfrag + VBASE + vs * TILEB;
-    const uint32_t kbv = kfrag + ks * TILEB;
-    load_step(J0, vb, kbv, fr[J0 % 3]);
-    load_step(J0 + 1, vb, kbv, fr[(J0 + 1) % 3]);
-  };
-  auto m_work = [&](int vs, int ks, auto j0, auto j1) __attribute__((always_inline)) {
-    constexpr int J0 = decltype(j0)::value, J1 = decltype(j1)::value;
-    const uint32_t vb = vfrag + VBASE + vs * TILEB;
-    const uint32_t kbv = kfrag + ks * TILEB;
-    if (GHA_PF_SETPRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int j = J0; j < J1; ++j) {
-      if (j + 2 < J1) {
-        load_step(j + 2, vb, kbv, fr[(j + 2) % 3]);
-        mfma_step(j, fr[j % 3]);
-        // steps 0..3 read 8 V^T halves, steps 4..7 read 4 K fragments;
-        // steps 0 and 2 run 10 MFMAs, the others 8
-        if (GHA_PF_ILV) {
-          if (j + 2 < 4) ds_mfma_pairs<1>(std::make_integer_sequence<int, 8>{});
-          else ds_mfma_pairs<2>(std::make_integer_sequence<int, 4>{});
-        }
-      } else {
-        mfma_step(j, fr[j % 3]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (GHA_PF_SETPRIO) __builtin_amdgcn_s_setprio(0);
-  };
-  // softmax of tile t (scores in sacc) into pf
-  auto v_work = [&](int t, auto masked) __attribute__((always_inline)) {
-    constexpr bool kMasked = decltype(masked)::value;
-    const int key0 = t * KB;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      if (kMasked) {
-        const int qpos = pos0 + qt * 16 + li;
-        const int kmax = a.causal ? min(qpos + off, a.S_k - 1) : a.S_k - 1;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (key0 + 16 * kt + 4 * lg + r > kmax) sacc[kt][qt][r] = kNegInf;
-      }
-      float mx = fmaxf(fmaxf(sacc[0][qt][0], sacc[0][qt][1]), sacc[0][qt][2]);
-      mx = fmaxf(fmaxf(mx, sacc[0][qt][3]), sacc[1][qt][0]);
-      mx = fmaxf(fmaxf(mx, sacc[1][qt][1]), sacc[1][qt][2]);
-      mx = fmaxf(fmaxf(mx, sacc[1][qt][3]), sacc[2][qt][0]);
-      mx = fmaxf(fmaxf(mx, sacc[2][qt][1]), sacc[2][qt][2]);
-      mx = fmaxf(fmaxf(mx, sacc[2][qt][3]), sacc[3][qt][0]);
-      mx = fmaxf(fmaxf(mx, sacc[3][qt][1]), sacc[3][qt][2]);
-      mx = fmaxf(mx, sacc[3][qt][3]);
-      const float mx2 = group4_max(mx) * c2;
-      if (wave_any(mx2 > m2[qt] + kRescaleSlack)) {
-        const float mnew = fmaxf(m2[qt], mx2);
-        const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2[qt] - mnew);
-        m2[qt] = mnew;
-        lacc[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
-      }
-      const float msub = (m2[qt] == kNegInf) ? 0.f : m2[qt];
-      float p[4][4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[kt][r] = fast_exp2(__builtin_fmaf(sacc[kt][qt][r], c2, -msub));
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        pf[qt][k2] = u32x4{pack_bf16(p[2 * k2][0], p[2 * k2][1]), pack_bf16(p[2 * k2][2], p[2 * k2][3]),
-                           pack_bf16(p[2 * k2 + 1][0], p[2 * k2 + 1][1]),
-                           pack_bf16(p[2 * k2 + 1][2], p[2 * k2 + 1][3])};
-      }
-    }
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I4 = std::integral_constant<int, 4>;
-  using I8 = std::integral_constant<int, 8>;
-
-  int t_mask = a.S_k / KB;
-  if (a.causal) t_mask = min(t_mask, max(0, (qb * pos_per_wg + off + 1) / KB));
-  t_mask = min(t_mask, n_kb);
-
-  // prologue: tiles 0 and 1 of K (group 0) and V (group 1); every wave
-  // scores tile 0
-  issue(0);
-  issue(1);
-  wait_vm0();
-  phase_barrier();
-  if (n_kb > 0) {
-    prefetch_m(0, 0, I4{});
-    m_work(0, 0, I4{}, I8{});
-  }
-  // group 1 runs one phase behind group 0
-  if (grp == 1) phase_barrier();
-
-  // Every wave runs: load its rows of tile t + 2, softmax(t) | PV(t), S(t+1) |,
-  // one barrier per phase.  Tile t lives in slot t % 3 (K and V alike).
-  // Group 0 loads K(t+2) in phase 2t, replacing K(t-1), last read in phase
-  // 2t-2; group 1 loads V(t+2) in phase 2t+1, replacing V(t-1), last read in
-  // phase 2t.  A wave's loads are waited for at the end of its next softmax
-  // phase (vmcnt 4: only the newer batch may be in flight), three phases
-  // before they are read.  The tile loads thus stay out of the MFMA phases.
-  auto tile = [&](int t, auto masked) __attribute__((always_inline)) {
-    constexpr bool kMasked = decltype(masked)::value;
-    const int s0 = t % NSLOT;                     // slot of K(t), V(t)
-    const int s1 = s0 == NSLOT - 1 ? 0 : s0 + 1;  // slot of K(t+1)
-    const bool mine = !kMasked || t * KB <= wave_kmax;
-    issue(t + 2);
-    if (mine) {
-      prefetch_m(s0, s1, I0{});  // in flight during the softmax
-      __builtin_amdgcn_sched_barrier(0);
-      v_work(t, masked);
-    }
-    wait_vm4();
-    phase_barrier();
-    if (mine) m_work(s0, s1, I0{}, I8{});
-    phase_barrier();
-  };
-  int t = 0;
-  for (; t < t_mask; ++t) tile(t, std::false_type{});
-  for (; t < n_kb; ++t) tile(t, std::true_type{});
-  if (grp == 0) phase_barrier();  // matches group 1's extra barrier
-  wait_vm0();  // no tile load outlives the work-group
-
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int qpos = pos0 + qt * 16 + li;
-    const float l = lacc[qt][0];
-    if (qpos >= a.S_q) continue;
-    const float inv = 1.f / l;
-    if (a.lse != nullptr && lg == 0) {
-      a.lse[((int64_t)b * a.lse_heads + qhead) * a.S_q + qpos] = (m2[qt] + fast_log2(l)) * kLn2;
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 16 * dt + 4 * lg;
-      const int64_t obase = (int64_t)b * a.o_sb + (int64_t)qhead * a.o_sh + (int64_t)qpos * a.o_ss + d;
-      const f32x4 v = oacc[dt][qt] * inv;
-      if constexpr (OUT_F32) {
-        *reinterpret_cast<f32x4*>((float*)a.o + obase) = v;
-      } else {
-        *reinterpret_cast<u32x2*>((__bf16*)a.o + obase) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-      }
-    }
-  }
-}
-
 }  // namespace
 
 bool prefill_d128_supported(const PrefillArgs& a) {
@@ -717,21 +392,8 @@ bool prefill_d128_supported(const PrefillArgs& a) {
   return a.k_ss >= 128 && a.v_ss >= 128 && span < ((int64_t)1 << 31);
 }
 
-#ifndef GHA_PF_PINGPONG
-#define GHA_PF_PINGPONG 0
-#endif
-
-int prefill_d128_waves() { return GHA_PF_PINGPONG ? 8 : 4; }
-
 hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t st) {
   const uint32_t padded = (uint32_t)((a.n_blocks + 7) / 8 * 8);
-  if (GHA_PF_PINGPONG) {
-    if (out_f32)
-      hipLaunchKernelGGL((prefill_pp_kernel<true>), dim3(padded), dim3(512), 0, st, a);
-    else
-      hipLaunchKernelGGL((prefill_pp_kernel<false>), dim3(padded), dim3(512), 0, st, a);
-    return hipGetLastError();
-  }
   if (out_f32)
     hipLaunchKernelGGL((prefill_d128_kernel<GHA_PF_QT, true>), dim3(padded), dim3(256), 0, st, a);
   else
