@@ -3,6 +3,7 @@
 // launched; see include/gha.h for the contract of each entry point.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -77,7 +78,10 @@ void latent_plan(int B, int n_rb, int L_max, int* split_len, int* n_splits) {
 }
 
 int gqa_row_blocks(int h_q, int h_kv, int s_q) { return ((h_q / h_kv) * s_q + 15) / 16; }
-int latent_row_blocks(int h_q, int s_q) { return (h_q * s_q + 63) / 64; }
+int latent_row_blocks(int h_q, int s_q) {
+  const int r = gha::latent_rows_per_wg();
+  return (h_q * s_q + r - 1) / r;
+}
 
 }  // namespace
 
@@ -249,7 +253,7 @@ size_t latent_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_h
   const int n_rb = latent_row_blocks(h_q, s_q);
   int sl, ns;
   latent_plan(B, n_rb, L_max_hint, &sl, &ns);
-  const size_t rows = (size_t)B * n_rb * ns * 64;
+  const size_t rows = (size_t)B * n_rb * ns * gha::latent_rows_per_wg();
   return rows * (size_t)r_kv * 4 + rows * 4;
 }
 
@@ -274,6 +278,13 @@ gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rop
   if ((s = check_view("c_kv", c_kv, in_dtype, B > 1, false, true)) != GHA_OK) return s;
   if ((s = check_view("k_rope", k_rope, in_dtype, B > 1, false, true)) != GHA_OK) return s;
   if ((s = check_view("o_lat", o_lat, out_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  // cache rows are read with 32-bit buffer offsets and a range that ends at
+  // each sequence's last token: rows must not overlap, and one sequence must
+  // span less than 2^31 bytes
+  if (c_kv->ss < r_kv || k_rope->ss < d_r)
+    return fail(GHA_ERR_STRIDE, "cache rows overlap (c_kv ss=%lld, k_rope ss=%lld)", (long long)c_kv->ss, (long long)k_rope->ss);
+  if ((int64_t)(L_cap + gha::latent_tile_tokens()) * std::max(c_kv->ss, k_rope->ss) * 2 >= (1LL << 31))
+    return fail(GHA_ERR_SHAPE, "one sequence of the cache spans 2 GiB or more (L_cap=%d)", L_cap);
   const size_t need = latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_max_hint, r_kv);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
@@ -292,7 +303,7 @@ gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rop
   a.B = B; a.h_q = h_q; a.s_q = s_q;
   a.n_rb = latent_row_blocks(h_q, s_q);
   latent_plan(B, a.n_rb, L_max_hint, &a.split_len, &a.n_splits);
-  const size_t n_part = (size_t)B * a.n_rb * a.n_splits * 64;
+  const size_t n_part = (size_t)B * a.n_rb * a.n_splits * gha::latent_rows_per_wg();
   a.ws_o = reinterpret_cast<float*>(workspace);
   a.ws_lse = a.ws_o + n_part * r_kv;
   a.scale = scale;

@@ -50,10 +50,10 @@ struct LatentArgs {
   const int32_t* seqlens;
   void* o;       int64_t o_sb, o_sh, o_ss;     // o_lat (B, s_q, h_q, r_kv)
   float* lse;         // dense (B, s_q, h_q) or null
-  float* ws_o;        // (B, n_rb, n_splits, 64, r_kv)
-  float* ws_lse;      // (B, n_rb, n_splits, 64)
+  float* ws_o;        // (B, n_rb, n_splits, rows per work-group, r_kv)
+  float* ws_lse;      // (B, n_rb, n_splits, rows per work-group)
   int B, h_q, s_q;
-  int n_rb;           // 64-row blocks over s_q * h_q rows
+  int n_rb;           // row blocks (of latent_rows_per_wg()) over s_q * h_q rows
   int split_len;
   int n_splits;
   float scale;
@@ -70,5 +70,7 @@ int gta_positions_per_wg();
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, int d, bool out_f32, hipStream_t st);
 hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st);
+int latent_rows_per_wg();    // query rows per work-group of the split kernel
+int latent_tile_tokens();    // tokens per tile (split lengths are multiples of it)
 
 }  // namespace gha

@@ -302,6 +302,35 @@ def test_latent_absorb_decode(gha_lib, B, h_q, s_q, L_cap, seqlens):
     check("latent lse", lse.cpu().numpy(), ref_lse)
 
 
+def test_latent_growing_scores_restart(gha_lib):
+    """Scores that jump far above the first tiles' maximum, twice (latent
+    rows of three magnitudes): the kernel's fixed per-row reference must be
+    replaced and the split recomputed, and the result is still the softmax."""
+    say("latent growing scores (reference restart)")
+    B, h_q, s_q, L = 1, 128, 1, 300
+    rng_bits = gen((B, L, 576), 21, synth.STREAM["latent"])
+    cache = rng_bits.copy()
+    one = np.float32(1.0).view(np.uint32) >> 16
+    two = np.float32(2.0).view(np.uint32) >> 16
+    four = np.float32(4.0).view(np.uint32) >> 16
+    cache[:, 100:200, :512] = two
+    cache[:, 200:, :512] = four
+    cache[:, 100:, 512:] = 0
+    q_lat = np.full((B, s_q, h_q, 512), one, dtype=np.uint16)
+    q_r = np.zeros((B, s_q, h_q, 64), dtype=np.uint16)
+    seqlens = np.array([L], dtype=np.int32)
+    scale = 1 / math.sqrt(128 + 64)
+    dcache = bf16_to_torch(cache)
+    o = gha_lib.latent_absorb_decode(bf16_to_torch(q_lat), bf16_to_torch(q_r), dcache[..., :512],
+                                     dcache[..., 512:], torch.from_numpy(seqlens).cuda(), scale=scale,
+                                     out_dtype=torch.float32)
+    c = widen(cache)
+    ref, _ = oracle.latent_absorb_decode(widen(q_lat), widen(q_r), c[..., :512], c[..., 512:],
+                                         seqlens, scale=scale)
+    check("latent restart", o.cpu().numpy(), ref)
+    assert np.allclose(ref, 4.0)
+
+
 @pytest.mark.parametrize("s_q", [1, 2])
 def test_latent_full_size_sampled_and_expanded_path(gha_lib, s_q):
     """h_q 128, r_kv 512, RoPE 64, batch 64, lengths uniform in [8192, 65536],
