@@ -9,21 +9,26 @@
 // 576-long dot product) and the value is c_u (the first 512 features).
 //
 // One work-group takes 128 query rows (all heads of one token at s_q = 1),
-// one wave per SIMD and 32 rows per wave, and walks a split of the cache in
-// tiles of 64 tokens.  Every tile goes from HBM straight into LDS (buffer
-// DMA, no VGPR staging) once and serves all 128 rows:
-//   S^T (tokens x rows) = C Q^T over 576 features: K-side fragments are 16 B
-//   LDS reads, Q^T (32 rows x 576) stays in VGPRs;
-//   O^T (512 x rows) += C^T P^T: C^T fragments come from transposing LDS
-//   reads (ds_read_b64_tr_b16) and the score accumulator is P^T.
-// The O^T accumulator (512 x 32 fp32 per wave) lives in AGPRs.
+// one wave per SIMD, and walks a split of the cache in tiles of 32 tokens.
+// Every tile goes from HBM straight into LDS (buffer DMA, no VGPR staging)
+// once and serves all 128 rows:
+//   S^T (tokens x rows) = C Q^T over 576 features: wave w scores rows
+//   32 w .. 32 w + 31; K-side fragments are 16 B LDS reads, Q^T stays in
+//   VGPRs.  The wave runs the softmax of its rows and publishes P^T in LDS.
+//   O^T (512 x rows) += C^T P^T: wave w owns output columns
+//   128 w .. 128 w + 127 for all 128 rows; C^T fragments come from
+//   transposing LDS reads (ds_read_b64_tr_b16) and P^T of all rows from LDS.
+// The O^T accumulator (128 x 128 fp32 per wave) lives in AGPRs.  The scores
+// of tile t and the values of tile t - 1 are contracted in one interleaved
+// MFMA stream, so LDS latency hides behind the other half's matrix work.
 //
-// LDS tile layout, unit-major: the 72 units (8 features, 16 B) of the 64
-// tokens; unit u of token k sits at byte 1024 u + 16 (k ^ 8 (u & 1)).  One
-// DMA instruction fills one unit of all 64 tokens (lane = slot).  The XOR of
-// odd units makes the transposing reads, which touch units 2 dt and 2 dt + 1
-// of 8 tokens per half-wave, land in distinct banks; score reads touch 16
-// consecutive tokens of one unit.
+// LDS tile layout, token-major: token k's latent row (64 chunks of 16 B) at
+// 1024 k with chunk c at position c ^ sw(k), sw a 4-bit permutation of
+// k mod 16; its RoPE row (8 chunks) at 128 k in a separate ring with chunk c
+// at position c ^ ((k / 2) mod 8).  One DMA instruction moves one token's
+// 1 KiB latent row (or the RoPE rows of 8 tokens) from contiguous HBM.
+// Score reads (16 tokens, one chunk) and transposing reads (4 tokens x 32 B
+// per 16 lanes, 8 tokens per half-wave) land in distinct banks.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -34,18 +39,28 @@ namespace {
 
 constexpr int RKV = 512, DR = 64, DL = RKV + DR;  // 576
 constexpr int T = 32;                             // tokens per tile
-constexpr int NU = DL / 8;                        // 72 units per token
-constexpr int NUC = RKV / 8;                      // 64 latent units; the rest are RoPE units
-constexpr int UNITB = T * 16;                     // 512 bytes: one unit of every token
-constexpr int TILEB = NU * UNITB;                 // 36 KiB
+constexpr int LROW = RKV * 2;                     // 1 KiB latent row of a token in LDS
+constexpr int RROW = DR * 2;                      // 128 B RoPE row
+constexpr int LTILE = T * LROW;                   // 32 KiB
+constexpr int RTILE = T * RROW;                   // 4 KiB
+constexpr int NLS = 4, NRS = 3;                   // latent and RoPE ring slots
 constexpr int ROWS = 128;                         // query rows per work-group
 constexpr int DS = DL / 32;                       // 18 score contraction steps
-constexpr int DT = RKV / 16;                      // 32 output column tiles
+constexpr int PQT = 1024;                         // P^T fragments of one q-tile (64 lanes x 16 B)
+constexpr int PBUF = 8 * PQT;                     // P^T of the work-group's 8 q-tiles
+constexpr int RBASE = NLS * LTILE;
+constexpr int PBASE = RBASE + NRS * RTILE;
+constexpr int LDS_BYTES = PBASE + 2 * PBUF;       // 156 KiB
 constexpr int kBufferFlags = 0x00020000;          // raw dword buffer access
 constexpr float kLatentSlack = 96.f;              // see the running state below
+constexpr uint32_t kOutOfRange = 0x80000000u;     // buffer offset past any range: loads read zeros
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// chunk swizzles of the LDS rows (see the layout above)
+__host__ __device__ constexpr int lat_sw(int k) { return ((k & 7) << 1) | ((k >> 3) & 1); }
+__host__ __device__ constexpr int rope_sw(int k) { return (k >> 1) & 7; }
 
 // 16 bytes per lane from buffer `rs` at voff + soff into LDS at lds + 16 lane;
 // bytes past the buffer's range come back as zeros.  Inline asm so that the
@@ -60,14 +75,14 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 // The MFMAs are written as inline asm to pin register classes: the O^T
-// accumulator (512 x 32 fp32 per wave) in AGPRs, the scores, the normaliser
-// and every operand in VGPRs.  Left to itself the compiler puts every MFMA
-// result, scores included, in AGPRs and spills.  The asm is volatile so that
-// the MFMAs keep their program order.  The compiler does not see these as
-// MFMAs, so the kernel pads the two hazards it would otherwise cover: VALU
-// writes of an operand need two wait states before an MFMA reads it, and an
-// MFMA result needs more than eight before a VALU reads it.  MFMA to MFMA
-// accumulator chains need none.
+// accumulator in AGPRs, the scores, the normaliser and every operand in
+// VGPRs.  Left to itself the compiler puts every MFMA result, scores
+// included, in AGPRs and spills.  The asm is volatile so that the MFMAs keep
+// their program order.  The compiler does not see these as MFMAs, so the
+// kernel pads the two hazards it would otherwise cover: VALU writes of an
+// operand need two wait states before an MFMA reads it, and an MFMA result
+// needs more than eight before a VALU reads it.  MFMA to MFMA accumulator
+// chains need none.
 __device__ __forceinline__ void mfma_acc(f32x4& acc, const u32x4& a, const u32x4& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
@@ -80,9 +95,12 @@ __device__ __forceinline__ void mfma_v0(f32x4& acc, const u32x4& a, const u32x4&
 __device__ __forceinline__ u32x2 ld_tr(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
 }
+// wait until at most one tile's DMAs (9 per wave) are in flight
+__device__ __forceinline__ void wait_vmem_but_one_tile() { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); }
 
 __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+  __shared__ int restart_flag[2][4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -100,7 +118,9 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   if (start >= L) return;
   const int end = min(L, start + a.split_len);
 
-  // ---- this lane's two query rows (q-tiles): R = t * h_q + head ------------
+  // ---- rows: wave w scores rows 32 w .. 32 w + 31 (two q-tiles) and owns
+  // their softmax; it accumulates output columns 128 w .. 128 w + 127 for all
+  // 128 rows of the work-group.  Row R = t * h_q + head. --------------------
   const int n_rows = a.s_q * a.h_q;
   int kvis[2];
   bool row_ok[2];
@@ -124,51 +144,59 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   const float c2 = a.scale * kLog2e;
 
   // ---- tile loads ------------------------------------------------------------
-  // One DMA instruction (64 lanes x 16 B) fills two units of 32 tokens:
-  // lane l writes slot l % 32 of unit u0 + l / 32 (u0 even), i.e. token
-  // (l % 32) ^ 8 (l / 32).  Wave w fills latent units 16 w .. 16 w + 15 and
-  // RoPE units 64 + 2 w, 65 + 2 w.  Rows at or past the sequence end read as
-  // zeros (range check).
+  // Tile t: latent rows in ring slot t % 4, RoPE rows in slot t % 3.  Wave w
+  // moves tokens 8 w .. 8 w + 7: one instruction per latent row (lane l
+  // brings chunk l ^ sw(k) to position l) and one for their RoPE rows (lane l:
+  // token 8 w + l / 8, position l % 8).  Rows at or past the sequence end,
+  // and tiles past the split, read as zeros (range check).
   const uint32_t c_row = (uint32_t)a.c_ss * 2u, r_row = (uint32_t)a.kr_ss * 2u;
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const __bf16*)a.c + (int64_t)b * a.c_sb), 0, (int)((uint32_t)(L - 1) * c_row + 2u * RKV), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const __bf16*)a.kr + (int64_t)b * a.kr_sb), 0, (int)((uint32_t)(L - 1) * r_row + 2u * DR), kBufferFlags);
-  static_assert(T == 32 && UNITB == 512, "a DMA instruction covers two units");
-  const int dma_tok = (lane & 31) ^ (8 * (lane >> 5)), dma_u = lane >> 5;
-  const uint32_t c_off = (uint32_t)dma_tok * c_row + 16u * dma_u;
-  const uint32_t r_off = (uint32_t)dma_tok * r_row + 16u * dma_u;
+  // lat_sw(8 w + j) = 2 j + (w & 1): the chunk of lane l for row j is l ^ (2 j + (w & 1))
+  const uint32_t dma_v = (16u * lane) ^ (16u * (wave & 1));
+  const int rtok = 8 * wave + (lane >> 3);
+  const uint32_t r_off = (uint32_t)(lane >> 3) * r_row + 16u * ((lane & 7) ^ rope_sw(rtok));
   const uint32_t lds0 = lds_offset(smem);
-  auto issue_tile = [&](int k0, int buf) __attribute__((always_inline)) {
-    const uint32_t dst = lds0 + buf * TILEB;
-    const uint32_t cs = (uint32_t)k0 * c_row + 16u * (16 * wave), rsft = (uint32_t)k0 * r_row + 16u * (2 * wave);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lds_dma16(crs, dst + (16 * wave + 2 * j) * UNITB, c_off, cs + 32u * j);
-    lds_dma16(rrs, dst + (NUC + 2 * wave) * UNITB, r_off, rsft);
+  const int n_t = (end - start + T - 1) / T;
+  // the DMAs of tile t, spread over the first score steps of an iteration
+  auto dma = [&](int t, int j) __attribute__((always_inline)) {
+    const bool ok = t < n_t;
+    const uint32_t tok = (uint32_t)(start + t * T + 8 * wave);
+    if (j < 8) {
+      const uint32_t so = ok ? (tok + j) * c_row : kOutOfRange;
+      lds_dma16(crs, lds0 + (t & 3) * LTILE + (8 * wave + j) * LROW, dma_v ^ (32u * j), so);
+    } else {
+      const uint32_t so = ok ? tok * r_row : kOutOfRange;
+      lds_dma16(rrs, lds0 + RBASE + (t % NRS) * RTILE + wave * 1024, r_off, so);
+    }
   };
 
-  // ---- fragment addresses (bytes within a tile) -----------------------------
-  // score A operand: token 16 kt + li, unit 4 s + lg (parity lg & 1)
-  const uint32_t sfrag = lg * UNITB + ((li ^ (8 * (lg & 1))) * 16);
+  // ---- fragment addresses (byte offsets in smem) ----------------------------
+  // score A operand: chunk 4 s + lg of token 16 kt + li, i.e. byte
+  // 1024 (16 kt + li) + 16 ((4 s + lg) ^ sw(li)) = (sfrag ^ 64 s) + 16384 kt
+  const uint32_t sfrag = li * LROW + 16 * (lg ^ lat_sw(li));
+  // RoPE steps s = 16, 17: chunk 4 (s - 16) + lg: (rfrag ^ 64 (s - 16)) + 2048 kt
+  const uint32_t rfrag = li * RROW + 16 * (lg ^ rope_sw(li));
   // value A operand (transposing read), source lane li of group lg: token
-  // 32 k2 + 16 h + 4 lg + li / 4, unit 2 dt + b with b = (li / 2) % 2, byte
-  // 8 (li % 2) of it
-  const int vb = (li >> 1) & 1;
-  const uint32_t vfrag = vb * UNITB + (((4 * lg + (li >> 2)) ^ (8 * vb)) * 16) + 8 * (li & 1);
+  // 4 lg + li / 4 (+ 16 for the second half), chunk 16 w + 2 dt + (li / 2) % 2,
+  // byte 8 (li % 2) of it: (vfrag ^ 32 dt) + 16384 half
+  const int vtok = 4 * lg + (li >> 2);
+  const uint32_t vfrag = vtok * LROW + 256 * wave + 16 * (((li >> 1) & 1) ^ lat_sw(vtok)) + 8 * (li & 1);
 
   // ---- running state -----------------------------------------------------------
   // Scores are taken against a per-row reference m2 (log2 units) fixed by
   // the first visible tile: probabilities 2^(s - m2) up to 2^kLatentSlack stay
   // far inside bf16 and fp32 range, so the accumulators never need
-  // rescaling (they live in AGPRs, where rescaling would be costly).  A tile
-  // whose maximum exceeds m2 + kLatentSlack restarts the split with the new
-  // maximum as reference; the result is the same softmax either way.
-  f32x4 oacc[DT][2], lacc[2];
+  // rescaling, and the other waves can use a row's probabilities without its
+  // statistics.  A tile whose maximum exceeds m2 + kLatentSlack restarts the
+  // split with the new maximum as reference; the result is the same softmax
+  // either way.
+  f32x4 oacc[8][8], lacc[2];  // oacc[column tile][q-tile of the work-group] (AGPRs)
   float m2[2] = {kNegInf, kNegInf};
-  __shared__ int restart_flag[2][4];
+  u32x4 pall[8];              // P^T of all 8 q-tiles of the previous tile
   const u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
-
-  const int n_t = (end - start + T - 1) / T;
 
   // Tiles wholly before `end` and before every row's causal limit need no
   // mask; only the last one or two may.
@@ -178,33 +206,66 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
     t_mask = min(t_mask, max(0, (lim + 1 - start) / T));
   }
 
-  auto tile = [&](int it, auto masked) __attribute__((always_inline)) -> bool {
-    constexpr bool kMasked = decltype(masked)::value;
-    const int buf = it & 1;
-    const int k0 = start + it * T;
-    if (it + 1 < n_t) issue_tile(k0 + T, buf ^ 1);
-    const unsigned char* ts = smem + buf * TILEB;
+  // O^T += C^T P^T for this wave's 8 column tiles of the tile in slot `slot`,
+  // one column tile (8 MFMAs) per step, C^T fragments read one step ahead
+  u32x4 vf[2];
+  auto load_v = [&](uint32_t vb, int dt, u32x4& v) __attribute__((always_inline)) {
+    const unsigned char* vp = smem + (vb ^ (32u * dt));
+    const u32x2 h0 = ld_tr(vp);
+    const u32x2 h1 = ld_tr(vp + 16384);
+    v = u32x4{h0[0], h0[1], h1[0], h1[1]};
+  };
+  auto pv_step = [&](uint32_t vb, int dt) __attribute__((always_inline)) {
+    if (dt + 1 < 8) load_v(vb, dt + 1, vf[(dt + 1) & 1]);
+#pragma unroll
+    for (int qt = 0; qt < 8; ++qt) mfma_acc(oacc[dt][qt], vf[dt & 1], pall[qt]);
+  };
 
-    // S^T tiles: token tile kt (16 tokens) x q-tile qt, one contraction step
-    // (32 features) per scheduling region, K fragments read one step ahead
+  // Iteration t: DMAs of tile t + 2 (into the slots of tiles t - 2), then one
+  // MFMA stream that interleaves the scores of tile t with the values of
+  // tile t - 1, the softmax of this wave's rows, P^T to LDS, and one barrier
+  // (tile t + 1 has landed, every row's P^T is visible).
+  auto iter = [&](int it, auto masked, auto has_pv) __attribute__((always_inline)) -> bool {
+    constexpr bool kMasked = decltype(masked)::value;
+    constexpr bool kPV = decltype(has_pv)::value;
+    const int k0 = start + it * T;
+    const uint32_t sb = (uint32_t)(it & 3) * LTILE + sfrag;
+    const uint32_t rb_ = RBASE + (uint32_t)(it % NRS) * RTILE + rfrag;
+    const uint32_t vb = (uint32_t)((it + 3) & 3) * LTILE + vfrag;
+
     f32x4 sacc[2][2];
-    u32x4 kf[2][2];
+    u32x4 kf[3][2];
     auto load_k = [&](int s, u32x4 (&f)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) f[kt] = ld16(ts + sfrag + (4 * s) * UNITB + 256 * kt);
+      for (int kt = 0; kt < 2; ++kt) {
+        if (s < 16) f[kt] = ld16(smem + (sb ^ (64u * s)) + 16384 * kt);
+        else f[kt] = ld16(smem + (rb_ ^ (64u * (s - 16))) + 2048 * kt);
+      }
     };
-    load_k(0, kf[0]);
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      if (s + 1 < DS) load_k(s + 1, kf[(s + 1) & 1]);
+    auto s_step = [&](int s) __attribute__((always_inline)) {
+      if (s + 2 < DS) load_k(s + 2, kf[(s + 2) % 3]);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-          if (s == 0) mfma_v0(sacc[kt][qt], kf[s & 1][kt], qf[qt][s]);
-          else mfma_v(sacc[kt][qt], kf[s & 1][kt], qf[qt][s]);
+          if (s == 0) mfma_v0(sacc[kt][qt], kf[s % 3][kt], qf[qt][s]);
+          else mfma_v(sacc[kt][qt], kf[s % 3][kt], qf[qt][s]);
         }
+    };
+    load_k(0, kf[0]);
+    load_k(1, kf[1]);
+    if (kPV) load_v(vb, 0, vf[0]);
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      dma(it + 2, j);
+      s_step(2 * j);
       __builtin_amdgcn_sched_barrier(0);
+      s_step(2 * j + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kPV && j < 8) {
+        pv_step(vb, j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // scores retire before the softmax reads them
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(sacc[0][0]), "+v"(sacc[0][1]), "+v"(sacc[1][0]), "+v"(sacc[1][1]));
@@ -243,78 +304,87 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
       pf[qt] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
                      pack_bf16(p[1][2], p[1][3])};
     }
-
-    // O^T += C^T P^T (accumulators in AGPRs) and the normaliser += 1^T P^T,
-    // four column tiles per scheduling region, C^T fragments read one region
-    // ahead.  Two wait states between the VALU writes of P^T (and of any
-    // rescaled accumulator) and the first MFMA that reads them.
+    // the normaliser of this wave's rows (two wait states after the VALU
+    // writes of P^T before an MFMA reads them)
     asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]));
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) mfma_v(lacc[qt], ones, pf[qt]);
-    u32x4 vf[2][4];
-    auto load_v = [&](int j, u32x4 (&f)[4]) __attribute__((always_inline)) {
+    unsigned char* pb = smem + PBASE + (it & 1) * PBUF;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const unsigned char* vp = ts + vfrag + (2 * (4 * j + i)) * UNITB;
-        const u32x2 h0 = ld_tr(vp);
-        const u32x2 h1 = ld_tr(vp + 256);
-        f[i] = u32x4{h0[0], h0[1], h1[0], h1[1]};
-      }
-    };
-    load_v(0, vf[0]);
-#pragma unroll
-    for (int j = 0; j < DT / 4; ++j) {
-      if (j + 1 < DT / 4) load_v(j + 1, vf[(j + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) mfma_acc(oacc[4 * j + i][qt], vf[j & 1][i], pf[qt]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
+    for (int qt = 0; qt < 2; ++qt) st16(pb + (2 * wave + qt) * PQT + 16 * lane, pf[qt]);
     // a wave whose rows outgrew their reference asks the whole work-group
     // to start the split again (every wave must run the same tiles and
     // barriers)
     if (lane == 0) restart_flag[it & 1][wave] = wave_any(restart_row) ? 1 : 0;
-    wait_vmem_all();
+    wait_vmem_but_one_tile();
     __syncthreads();
     const int* f = restart_flag[it & 1];
-    return (f[0] | f[1] | f[2] | f[3]) != 0;
+    if ((f[0] | f[1] | f[2] | f[3]) != 0) return true;
+#pragma unroll
+    for (int qt = 0; qt < 8; ++qt) pall[qt] = ld16(pb + qt * PQT + 16 * lane);
+    return false;
   };
+
+  int it = 0;
   for (;;) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < 2; ++qt) lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    issue_tile(start, 0);
-    wait_vmem_all();
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < 8; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 9; ++j) dma(0, j);
+#pragma unroll
+    for (int j = 0; j < 9; ++j) dma(1, j);
+    wait_vmem_but_one_tile();
     __syncthreads();
-    bool restart = false;
-    int it = 0;
-    for (; it < t_mask && !restart; ++it) restart = tile(it, std::false_type{});
-    for (; it < n_t && !restart; ++it) restart = tile(it, std::true_type{});
+    bool restart = iter(0, std::true_type{}, std::false_type{});
+    for (it = 1; it < t_mask && !restart; ++it) restart = iter(it, std::false_type{}, std::true_type{});
+    for (; it < n_t && !restart; ++it) restart = iter(it, std::true_type{}, std::true_type{});
+    wait_vmem_all();  // no DMA may still target a slot that is about to be reused
     if (!restart) break;
+  }
+  // values of the last tile
+  {
+    const uint32_t vb = (uint32_t)((n_t - 1) & 3) * LTILE + vfrag;
+    load_v(vb, 0, vf[0]);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      pv_step(vb, dt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // ---- partial of this split: normalised output and log2-sum-exp ---------
   // the last accumulator MFMAs must retire before the VALU reads them
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(oacc[DT - 1][0]), "+a"(oacc[DT - 1][1]), "+v"(lacc[0]), "+v"(lacc[1]));
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(oacc[7][7]), "+a"(oacc[7][6]), "+v"(lacc[0]), "+v"(lacc[1]));
+  // 1 / l of all 128 rows, in the RoPE ring (idle now)
+  float* stats = reinterpret_cast<float*>(smem + RBASE);
+  const int64_t pbase = (((int64_t)b * a.n_rb + rb) * a.n_splits + split) * ROWS;
+  __syncthreads();
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const float l = lacc[qt][0];
-    if (!row_ok[qt]) continue;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t pidx = (((int64_t)b * a.n_rb + rb) * a.n_splits + split) * ROWS + 32 * wave + 16 * qt + li;
-    float* wo = a.ws_o + pidx * RKV;
-    // oacc[dt][qt][r] is feature 16 dt + 4 lg + r
+    const int row = 32 * wave + 16 * qt + li;
+    if (lg == 0) {
+      stats[row] = l > 0.f ? 1.f / l : 0.f;
+      if (row_ok[qt]) a.ws_lse[pbase + row] = l > 0.f ? m2[qt] + fast_log2(l) : kNegInf;
+    }
+  }
+  __syncthreads();
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      *reinterpret_cast<f32x4*>(wo + 16 * dt + 4 * lg) = oacc[dt][qt] * inv;
+  for (int qt = 0; qt < 8; ++qt) {
+    const int row = 16 * qt + li;
+    if (rb * ROWS + row >= n_rows) continue;
+    const float inv = stats[row];
+    float* wo = a.ws_o + (pbase + row) * RKV + 128 * wave + 4 * lg;
+    // oacc[dt][qt][r] is feature 128 w + 16 dt + 4 lg + r
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      *reinterpret_cast<f32x4*>(wo + 16 * dt) = oacc[dt][qt] * inv;
       if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    if (lg == 0) a.ws_lse[pidx] = l > 0.f ? m2[qt] + fast_log2(l) : kNegInf;
   }
 }
 
