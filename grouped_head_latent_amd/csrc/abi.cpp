@@ -65,18 +65,6 @@ void gqa_decode_plan(int B, int h_kv, int n_rb, int L_max, int* split_len, int* 
   *n_splits = (int)((L_max + sl - 1) / sl);
 }
 
-// Split plan of the latent decode: about 1024 work-groups; each split's
-// partial (64 rows x 512 fp32) should stay small next to the tokens it reads.
-void latent_plan(int B, int n_rb, int L_max, int* split_len, int* n_splits) {
-  const int64_t units = (int64_t)B * n_rb;
-  const int64_t want = units >= 1024 ? 1 : (1024 + units - 1) / units;
-  int64_t sl = (L_max + want - 1) / want;
-  sl = (sl + 255) / 256 * 256;
-  if (sl < 256) sl = 256;
-  *split_len = (int)sl;
-  *n_splits = (int)((L_max + sl - 1) / sl);
-}
-
 int gqa_row_blocks(int h_q, int h_kv, int s_q) { return ((h_q / h_kv) * s_q + 15) / 16; }
 int latent_row_blocks(int h_q, int s_q) {
   const int r = gha::latent_rows_per_wg();
@@ -251,10 +239,10 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
 size_t latent_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_hint, int r_kv) {
   if (B < 1 || h_q < 1 || s_q < 1 || L_max_hint < 1 || r_kv < 1) return 0;
   const int n_rb = latent_row_blocks(h_q, s_q);
-  int sl, ns;
-  latent_plan(B, n_rb, L_max_hint, &sl, &ns);
-  const size_t rows = (size_t)B * n_rb * ns * gha::latent_rows_per_wg();
-  return rows * (size_t)r_kv * 4 + rows * 4;
+  const int T = gha::latent_tile_tokens();
+  const int n_wg = gha::latent_plan_wgs(n_rb, (int64_t)B * ((L_max_hint + T - 1) / T));
+  const size_t rows = (size_t)n_rb * (n_wg + B) * gha::latent_rows_per_wg();
+  return rows * (size_t)r_kv * 4 + rows * 4 + (size_t)(B + 1) * 4;
 }
 
 gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rope,
@@ -301,13 +289,17 @@ gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rop
   a.o = o_lat->ptr; a.o_sb = o_lat->sb; a.o_sh = o_lat->sh; a.o_ss = o_lat->ss;
   a.lse = lse;
   a.B = B; a.h_q = h_q; a.s_q = s_q;
+  a.L_cap = L_cap;
   a.n_rb = latent_row_blocks(h_q, s_q);
-  latent_plan(B, a.n_rb, L_max_hint, &a.split_len, &a.n_splits);
-  const size_t n_part = (size_t)B * a.n_rb * a.n_splits * gha::latent_rows_per_wg();
+  const int T = gha::latent_tile_tokens();
+  a.n_wg = gha::latent_plan_wgs(a.n_rb, (int64_t)B * ((L_max_hint + T - 1) / T));
+  const size_t n_part = (size_t)a.n_rb * (a.n_wg + B) * gha::latent_rows_per_wg();
   a.ws_o = reinterpret_cast<float*>(workspace);
   a.ws_lse = a.ws_o + n_part * r_kv;
+  a.ws_tiles = reinterpret_cast<int32_t*>(a.ws_lse + n_part);
   a.scale = scale;
-  if ((int64_t)B * a.n_rb * a.n_splits > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  if ((int64_t)B * a.n_rb * (gha::latent_rows_per_wg() / 4) > (1LL << 30) || (int64_t)B * ((L_cap + T - 1) / T) >= (1LL << 31))
+    return fail(GHA_ERR_SHAPE, "problem too large for one launch");
   return launched(gha::launch_latent_decode(a, out_dtype == GHA_F32, reinterpret_cast<hipStream_t>(stream)),
                   "latent_absorb_decode");
 }

@@ -50,12 +50,12 @@ struct LatentArgs {
   const int32_t* seqlens;
   void* o;       int64_t o_sb, o_sh, o_ss;     // o_lat (B, s_q, h_q, r_kv)
   float* lse;         // dense (B, s_q, h_q) or null
-  float* ws_o;        // (B, n_rb, n_splits, rows per work-group, r_kv)
-  float* ws_lse;      // (B, n_rb, n_splits, rows per work-group)
-  int B, h_q, s_q;
+  float* ws_o;        // (n_rb, n_wg + B, rows per work-group, r_kv) partials
+  float* ws_lse;      // (n_rb, n_wg + B, rows per work-group)
+  int32_t* ws_tiles;  // (B + 1) prefix sums of the tiles per sequence
+  int B, h_q, s_q, L_cap;
   int n_rb;           // row blocks (of latent_rows_per_wg()) over s_q * h_q rows
-  int split_len;
-  int n_splits;
+  int n_wg;           // work-groups per row block, each takes 1/n_wg of all tiles
   float scale;
 };
 
@@ -71,6 +71,8 @@ int gta_positions_per_wg();
 hipError_t launch_gqa_decode(const DecodeArgs& a, int d, bool out_f32, hipStream_t st);
 hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st);
 int latent_rows_per_wg();    // query rows per work-group of the split kernel
-int latent_tile_tokens();    // tokens per tile (split lengths are multiples of it)
+int latent_tile_tokens();    // tokens per tile
+// work-groups per row block for n_rb row blocks and at most max_tiles tiles
+int latent_plan_wgs(int n_rb, int64_t max_tiles);
 
 }  // namespace gha

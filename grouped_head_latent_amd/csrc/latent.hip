@@ -32,6 +32,7 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace gha {
@@ -56,6 +57,15 @@ constexpr float kLatentSlack = 96.f;              // see the running state below
 constexpr uint32_t kOutOfRange = 0x80000000u;     // buffer offset past any range: loads read zeros
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// f(integral_constant<int, I>) for I = B .. E - 1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // chunk swizzles of the LDS rows (see the layout above)
@@ -95,28 +105,79 @@ __device__ __forceinline__ void mfma_v0(f32x4& acc, const u32x4& a, const u32x4&
 __device__ __forceinline__ u32x2 ld_tr(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
 }
+// tiles of sequence b (0 past the batch); lengths are clamped to [0, L_cap]
+__device__ __forceinline__ int latent_tiles(const LatentArgs& a, int b) {
+  return b < a.B ? (min(max(a.seqlens[b], 0), a.L_cap) + T - 1) / T : 0;
+}
+// inclusive prefix sum over the lanes of a wave
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
 // wait until at most one tile's DMAs (9 per wave) are in flight
 __device__ __forceinline__ void wait_vmem_but_one_tile() { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); }
 
 __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
-  __shared__ int restart_flag[2][4];
+  __shared__ __attribute__((aligned(4))) unsigned char restart_flag[2][4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
 
   const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int n_units = a.B * a.n_splits * a.n_rb;
-  if (lid >= (uint32_t)n_units) return;
-  // work-group-uniform indices, kept in scalar registers
+  if (lid >= (uint32_t)(a.n_wg * a.n_rb)) return;
+  // work-group-uniform indices, kept in scalar registers; the two row
+  // blocks of one tile range are neighbours (same XCD, shared L2)
   const int rb = __builtin_amdgcn_readfirstlane(lid % a.n_rb);
-  const int split = __builtin_amdgcn_readfirstlane((lid / a.n_rb) % a.n_splits);
-  const int b = __builtin_amdgcn_readfirstlane(lid / (a.n_rb * a.n_splits));
-  const int L = __builtin_amdgcn_readfirstlane(a.seqlens[b]);
-  const int start = split * a.split_len;
-  if (start >= L) return;
-  const int end = min(L, start + a.split_len);
+  const int w = __builtin_amdgcn_readfirstlane(lid / a.n_rb);
+
+  // ---- this work-group's share of the tiles of all sequences ----------------
+  // The tiles of sequences 0 .. B - 1 are numbered one after another (NT in
+  // all) and work-group w takes tiles [w NT / n_wg, (w + 1) NT / n_wg): equal
+  // shares whatever the length mix.  Each sequence it touches is a segment
+  // with its own partial, in slot w + b (unique: along the segments either w
+  // or b grows).
+  int NT = 0;
+  for (int c0 = 0; c0 < a.B; c0 += 64)
+    NT += __builtin_amdgcn_readlane(wave_incl_scan(latent_tiles(a, c0 + lane)), 63);
+  const int lo = (int)((int64_t)w * NT / a.n_wg), hi = (int)((int64_t)(w + 1) * NT / a.n_wg);
+  // one work-group publishes the prefix sums for the merge
+  if (lid == 0 && wave == 0) {
+    int run = 0;
+    for (int c0 = 0; c0 < a.B; c0 += 64) {
+      const int t = latent_tiles(a, c0 + lane);
+      const int incl = wave_incl_scan(t) + run;
+      if (c0 + lane < a.B) a.ws_tiles[c0 + lane] = incl - t;
+      run = __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) a.ws_tiles[a.B] = run;
+  }
+
+  if (lo >= hi) return;
+  // first sequence with tiles at or after lo, and the tiles before it
+  int b0 = 0, P = 0;
+  for (int c0 = 0;; c0 += 64) {
+    const int t = latent_tiles(a, c0 + lane);
+    const int incl = wave_incl_scan(t) + P;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(incl > lo);
+    if (m != 0) {
+      const int j = __builtin_ctzll(m);
+      b0 = c0 + j;
+      P = __builtin_amdgcn_readlane(incl - t, j);
+      break;
+    }
+    P = __builtin_amdgcn_readlane(incl, 63);
+  }
+  b0 = __builtin_amdgcn_readfirstlane(b0);
+  P = __builtin_amdgcn_readfirstlane(P);
+  // ---- one segment: sequence b, tokens [start, end), partial slot ----------
+  auto segment = [&](int b, int L, int start, int end, int slot) __attribute__((always_inline)) {
 
   // ---- rows: wave w scores rows 32 w .. 32 w + 31 (two q-tiles) and owns
   // their softmax; it accumulates output columns 128 w .. 128 w + 127 for all
@@ -160,17 +221,18 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   const uint32_t r_off = (uint32_t)(lane >> 3) * r_row + 16u * ((lane & 7) ^ rope_sw(rtok));
   const uint32_t lds0 = lds_offset(smem);
   const int n_t = (end - start + T - 1) / T;
-  // the DMAs of tile t, spread over the first score steps of an iteration
-  auto dma = [&](int t, int j) __attribute__((always_inline)) {
+  // the DMAs of tile t (offsets of a tile past the split land out of range),
+  // spread over the first score steps of an iteration
+  struct DmaTile { uint32_t cso, rso, ldl, ldr; };
+  auto dma_tile = [&](int t) __attribute__((always_inline)) -> DmaTile {
     const bool ok = t < n_t;
     const uint32_t tok = (uint32_t)(start + t * T + 8 * wave);
-    if (j < 8) {
-      const uint32_t so = ok ? (tok + j) * c_row : kOutOfRange;
-      lds_dma16(crs, lds0 + (t & 3) * LTILE + (8 * wave + j) * LROW, dma_v ^ (32u * j), so);
-    } else {
-      const uint32_t so = ok ? tok * r_row : kOutOfRange;
-      lds_dma16(rrs, lds0 + RBASE + (t % NRS) * RTILE + wave * 1024, r_off, so);
-    }
+    return DmaTile{ok ? tok * c_row : kOutOfRange, ok ? tok * r_row : kOutOfRange,
+                   lds0 + (t & 3) * LTILE + (8 * wave) * LROW, lds0 + RBASE + (t % NRS) * RTILE + wave * 1024};
+  };
+  auto dma = [&](const DmaTile& d, int j) __attribute__((always_inline)) {
+    if (j < 8) lds_dma16(crs, d.ldl + j * LROW, dma_v ^ (32u * j), d.cso + j * c_row);
+    else lds_dma16(rrs, d.ldr, r_off, d.rso);
   };
 
   // ---- fragment addresses (byte offsets in smem) ----------------------------
@@ -196,7 +258,6 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   f32x4 oacc[8][8], lacc[2];  // oacc[column tile][q-tile of the work-group] (AGPRs)
   float m2[2] = {kNegInf, kNegInf};
   u32x4 pall[8];              // P^T of all 8 q-tiles of the previous tile
-  const u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
 
   // Tiles wholly before `end` and before every row's causal limit need no
   // mask; only the last one or two may.
@@ -215,16 +276,26 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
     const u32x2 h1 = ld_tr(vp + 16384);
     v = u32x4{h0[0], h0[1], h1[0], h1[1]};
   };
+  // P^T of all rows for tile t (double-buffered by tile parity)
+  auto load_p = [&](int t) __attribute__((always_inline)) {
+    const unsigned char* pb = smem + PBASE + (t & 1) * PBUF + 16 * lane;
+#pragma unroll
+    for (int qt = 0; qt < 8; ++qt) pall[qt] = ld16(pb + qt * PQT);
+  };
   auto pv_step = [&](uint32_t vb, int dt) __attribute__((always_inline)) {
     if (dt + 1 < 8) load_v(vb, dt + 1, vf[(dt + 1) & 1]);
 #pragma unroll
     for (int qt = 0; qt < 8; ++qt) mfma_acc(oacc[dt][qt], vf[dt & 1], pall[qt]);
   };
 
-  // Iteration t: DMAs of tile t + 2 (into the slots of tiles t - 2), then one
-  // MFMA stream that interleaves the scores of tile t with the values of
-  // tile t - 1, the softmax of this wave's rows, P^T to LDS, and one barrier
-  // (tile t + 1 has landed, every row's P^T is visible).
+  // Iteration t: phase A, the scores of tile t (with the DMAs of tile t + 2
+  // into the slots of tile t - 2, and the P^T reads of tile t - 1), then
+  // phase B, the values of tile t - 1 with the softmax of tile t spread
+  // between their MFMAs (VALU and matrix core run side by side).  P^T goes
+  // to LDS and one barrier follows (tile t + 1 has landed, every row's P^T
+  // is visible).  Restart requests raised at a barrier are acted on before
+  // the next one: nothing computed in between is kept.
+  uint32_t flags = 0;  // restart requests (one byte per wave) read after the last barrier
   auto iter = [&](int it, auto masked, auto has_pv) __attribute__((always_inline)) -> bool {
     constexpr bool kMasked = decltype(masked)::value;
     constexpr bool kPV = decltype(has_pv)::value;
@@ -252,61 +323,91 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
           else mfma_v(sacc[kt][qt], kf[s % 3][kt], qf[qt][s]);
         }
     };
+
+    // ---- phase A ----
+    const DmaTile dt2 = dma_tile(it + 2);
     load_k(0, kf[0]);
     load_k(1, kf[1]);
-    if (kPV) load_v(vb, 0, vf[0]);
-#pragma unroll
-    for (int j = 0; j < 9; ++j) {
-      dma(it + 2, j);
-      s_step(2 * j);
+    static_for<0, DS>([&](auto S_) __attribute__((always_inline)) {
+      constexpr int s = decltype(S_)::value;
+      if (s < 9) dma(dt2, s);
+      if (kPV && s == DS - 2) load_p(it - 1);
+      if (kPV && s == DS - 1) load_v(vb, 0, vf[0]);
+      s_step(s);
       __builtin_amdgcn_sched_barrier(0);
-      s_step(2 * j + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kPV && j < 8) {
-        pv_step(vb, j);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // scores retire before the softmax reads them
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(sacc[0][0]), "+v"(sacc[0][1]), "+v"(sacc[1][0]), "+v"(sacc[1][1]));
+    });
 
-    // softmax per row (= per lane and q-tile) against a fixed reference;
-    // sacc[kt][qt][r] is token k0 + 16 kt + 4 lg + r
+    // ---- phase B: softmax per row (= per lane and q-tile) against a fixed
+    // reference, in 32 small stages; sacc[kt][qt][r] is token
+    // k0 + 16 kt + 4 lg + r and becomes its probability in place ----
+    float mx[2], msub[2];
     u32x4 pf[2];
     bool restart_row = false;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      if (kMasked) {
-        const int kmax = min(end - 1, kvis[qt]);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+    auto stage = [&](auto K_) __attribute__((always_inline)) {
+      constexpr int k = decltype(K_)::value;
+      constexpr int qt = k / 16, st = k % 16;
+      if constexpr (st <= 1) {
+        if constexpr (kMasked) {
+          const int kmax = min(end - 1, kvis[qt]);
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (k0 + 16 * kt + 4 * lg + r > kmax) sacc[kt][qt][r] = kNegInf;
-      }
-      float mx = fmaxf(fmaxf(sacc[0][qt][0], sacc[0][qt][1]), sacc[0][qt][2]);
-      mx = fmaxf(fmaxf(mx, sacc[0][qt][3]), sacc[1][qt][0]);
-      mx = fmaxf(fmaxf(mx, sacc[1][qt][1]), sacc[1][qt][2]);
-      mx = fmaxf(mx, sacc[1][qt][3]);
-      const float mx2 = group4_max(mx) * c2;
-      if (m2[qt] == kNegInf) {
-        m2[qt] = mx2;  // first visible scores of this row: nothing accumulated yet
-      } else if (mx2 > m2[qt] + kLatentSlack) {
-        m2[qt] = mx2;
-        restart_row = true;
-      }
-      const float msub = (m2[qt] == kNegInf) ? 0.f : m2[qt];
-      float p[2][4];
+            if (k0 + 16 * st + 4 * lg + r > kmax) sacc[st][qt][r] = kNegInf;
+        }
+      } else if constexpr (st == 2) {
+        mx[qt] = fmaxf(fmaxf(sacc[0][qt][0], sacc[0][qt][1]), fmaxf(sacc[0][qt][2], sacc[0][qt][3]));
+      } else if constexpr (st == 3) {
+        mx[qt] = fmaxf(mx[qt], fmaxf(fmaxf(sacc[1][qt][0], sacc[1][qt][1]), fmaxf(sacc[1][qt][2], sacc[1][qt][3])));
+      } else if constexpr (st == 4) {
+        mx[qt] = xor16_max(mx[qt]);
+      } else if constexpr (st == 5) {
+        mx[qt] = xor32_max(mx[qt]) * c2;
+      } else if constexpr (st == 6) {
+        // the first visible scores of a row fix its reference; a tile that
+        // outgrows it by more than the slack asks for a restart
+        const bool first = m2[qt] == kNegInf;
+        const bool grow = !first && mx[qt] > m2[qt] + kLatentSlack;
+        restart_row = restart_row || grow;
+        m2[qt] = (first || grow) ? mx[qt] : m2[qt];
+        msub[qt] = (m2[qt] == kNegInf) ? 0.f : m2[qt];
+      } else if constexpr (st == 7 || st == 10) {
+        constexpr int kt = st == 7 ? 0 : 1;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[kt][r] = fast_exp2(__builtin_fmaf(sacc[kt][qt][r], c2, -msub));
-      pf[qt] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
-                     pack_bf16(p[1][2], p[1][3])};
+        for (int r = 0; r < 4; ++r) sacc[kt][qt][r] = __builtin_fmaf(sacc[kt][qt][r], c2, -msub[qt]);
+      } else if constexpr (st == 8 || st == 9 || st == 11 || st == 12) {
+        constexpr int kt = st < 10 ? 0 : 1, r0 = (st == 8 || st == 11) ? 0 : 2;
+        sacc[kt][qt][r0] = fast_exp2(sacc[kt][qt][r0]);
+        sacc[kt][qt][r0 + 1] = fast_exp2(sacc[kt][qt][r0 + 1]);
+      } else if constexpr (st == 13) {
+        pf[qt] = u32x4{pack_bf16(sacc[0][qt][0], sacc[0][qt][1]), pack_bf16(sacc[0][qt][2], sacc[0][qt][3]),
+                       pack_bf16(sacc[1][qt][0], sacc[1][qt][1]), pack_bf16(sacc[1][qt][2], sacc[1][qt][3])};
+      }
+    };
+    constexpr int NST = 32;
+    // the scores must retire before the softmax reads them
+    auto scores_retire = [&]() __attribute__((always_inline)) {
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(sacc[0][0]), "+v"(sacc[0][1]), "+v"(sacc[1][0]), "+v"(sacc[1][1]));
+    };
+    if constexpr (kPV) {
+      constexpr int NB = 64;
+      static_for<0, NB>([&](auto M_) __attribute__((always_inline)) {
+        constexpr int m = decltype(M_)::value;
+        constexpr int dt = m / 8, qt = m % 8;
+        if (qt == 0 && dt + 1 < 8) load_v(vb, dt + 1, vf[(dt + 1) & 1]);
+        mfma_acc(oacc[dt][qt], vf[dt & 1], pall[qt]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m == 0) scores_retire();
+        static_for<m * NST / NB, (m + 1) * NST / NB>(stage);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
+      scores_retire();
+      static_for<0, NST>(stage);
     }
+
     // the normaliser of this wave's rows (two wait states after the VALU
-    // writes of P^T before an MFMA reads them)
-    asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]));
+    // writes of its operands, accumulator included, before an MFMA reads them)
+    u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+    asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]), "+v"(ones), "+v"(lacc[0]), "+v"(lacc[1]));
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) mfma_v(lacc[qt], ones, pf[qt]);
     unsigned char* pb = smem + PBASE + (it & 1) * PBUF;
@@ -316,12 +417,10 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
     // to start the split again (every wave must run the same tiles and
     // barriers)
     if (lane == 0) restart_flag[it & 1][wave] = wave_any(restart_row) ? 1 : 0;
+    if (__builtin_amdgcn_readfirstlane(flags) != 0) return true;
     wait_vmem_but_one_tile();
     __syncthreads();
-    const int* f = restart_flag[it & 1];
-    if ((f[0] | f[1] | f[2] | f[3]) != 0) return true;
-#pragma unroll
-    for (int qt = 0; qt < 8; ++qt) pall[qt] = ld16(pb + qt * PQT + 16 * lane);
+    flags = *reinterpret_cast<const uint32_t*>(restart_flag[it & 1]);
     return false;
   };
 
@@ -333,21 +432,30 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int qt = 0; qt < 8; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    flags = 0;
+    {
+      const DmaTile d0 = dma_tile(0), d1 = dma_tile(1);
 #pragma unroll
-    for (int j = 0; j < 9; ++j) dma(0, j);
+      for (int j = 0; j < 9; ++j) dma(d0, j);
 #pragma unroll
-    for (int j = 0; j < 9; ++j) dma(1, j);
+      for (int j = 0; j < 9; ++j) dma(d1, j);
+    }
     wait_vmem_but_one_tile();
     __syncthreads();
     bool restart = iter(0, std::true_type{}, std::false_type{});
     for (it = 1; it < t_mask && !restart; ++it) restart = iter(it, std::false_type{}, std::true_type{});
     for (; it < n_t && !restart; ++it) restart = iter(it, std::true_type{}, std::true_type{});
-    wait_vmem_all();  // no DMA may still target a slot that is about to be reused
+    if (!restart) restart = __builtin_amdgcn_readfirstlane(flags) != 0;
+    // no DMA may still target a slot that is about to be reused, and no wave
+    // may still read one
+    wait_vmem_all();
     if (!restart) break;
+    __syncthreads();
   }
   // values of the last tile
   {
     const uint32_t vb = (uint32_t)((n_t - 1) & 3) * LTILE + vfrag;
+    load_p(n_t - 1);
     load_v(vb, 0, vf[0]);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -361,7 +469,7 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(oacc[7][7]), "+a"(oacc[7][6]), "+v"(lacc[0]), "+v"(lacc[1]));
   // 1 / l of all 128 rows, in the RoPE ring (idle now)
   float* stats = reinterpret_cast<float*>(smem + RBASE);
-  const int64_t pbase = (((int64_t)b * a.n_rb + rb) * a.n_splits + split) * ROWS;
+  const int64_t pbase = ((int64_t)rb * (a.n_wg + a.B) + slot) * ROWS;
   __syncthreads();
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -386,11 +494,23 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
       if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // the next segment's first DMAs overwrite the statistics
+  __syncthreads();
+  };
+
+  for (int b = b0; b < a.B && P < hi; ++b) {
+    const int L = __builtin_amdgcn_readfirstlane(min(max(a.seqlens[b], 0), a.L_cap));
+    const int nt = (L + T - 1) / T;
+    const int t0 = max(lo, P) - P, t1 = min(hi, P + nt) - P;
+    if (t0 < t1) segment(b, L, t0 * T, min(L, t1 * T), w + b);
+    P += nt;
+  }
 }
 
-// Merge the splits of 4 query rows per work-group (64 threads per row, 8
-// features per thread): each split s holds its normalised output O_s and its
-// log2-sum-exp l_s; the result is sum_s 2^(l_s - M) O_s / sum_s 2^(l_s - M).
+// Merge the segments of a sequence, 4 query rows per work-group (64 threads
+// per row, 8 features per thread): each segment s holds its normalised output
+// O_s and its log2-sum-exp l_s; the result is
+// sum_s 2^(l_s - M) O_s / sum_s 2^(l_s - M).
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
   const int unit = blockIdx.x / (ROWS / 4);  // b * n_rb + rb
@@ -400,24 +520,35 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
   const int f = (tid & 63) * 8;
   const int R = rb * ROWS + row;
   if (R >= a.s_q * a.h_q) return;
-  const int L = a.seqlens[b];
-  // lengths above the plan's bound are a precondition violation; never read
-  // partials the plan did not allot
-  const int ns = min((L + a.split_len - 1) / a.split_len, a.n_splits);
-  const int64_t base = (int64_t)unit * a.n_splits * ROWS + row;
+  // the work-groups whose tile range meets this sequence's tiles [p0, p1)
+  const int p0 = a.ws_tiles[b], p1 = a.ws_tiles[b + 1], NT = a.ws_tiles[a.B];
+  const int64_t n = a.n_wg;
+  int w_first = 0, w_last = -1;
+  if (p0 < p1) {
+    w_first = (int)(((int64_t)(p0 + 1) * n - 1) / NT);  // last w with w NT / n <= p0
+    w_last = (int)(((int64_t)p1 * n - 1) / NT);         // last w with w NT / n < p1
+  }
+  auto meets = [&](int w) {
+    const int lo = (int)(w * (int64_t)NT / n), hi = (int)((w + 1) * (int64_t)NT / n);
+    return max(lo, p0) < min(hi, p1);
+  };
+  const int64_t base = (int64_t)rb * (a.n_wg + a.B) * ROWS + row;
   float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_lse[base + (int64_t)s * ROWS]);
+  for (int w = w_first; w <= w_last; ++w)
+    if (meets(w)) M = fmaxf(M, a.ws_lse[base + (int64_t)(w + b) * ROWS]);
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float ls = a.ws_lse[base + (int64_t)s * ROWS];
-    const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
-    den += w;
-    const float* src = a.ws_o + (base + (int64_t)s * ROWS) * RKV + f;
-    acc0 += w * *reinterpret_cast<const f32x4*>(src);
-    acc1 += w * *reinterpret_cast<const f32x4*>(src + 4);
+  for (int w = w_first; w <= w_last; ++w) {
+    if (!meets(w)) continue;
+    const float ls = a.ws_lse[base + (int64_t)(w + b) * ROWS];
+    const float wt = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
+    den += wt;
+    const float* src = a.ws_o + (base + (int64_t)(w + b) * ROWS) * RKV + f;
+    acc0 += wt * *reinterpret_cast<const f32x4*>(src);
+    acc1 += wt * *reinterpret_cast<const f32x4*>(src + 4);
   }
-  const float inv = 1.f / den;
+  // a row with no visible token gets zeros (and lse = -inf)
+  const float inv = den > 0.f ? 1.f / den : 0.f;
   acc0 *= inv;
   acc1 *= inv;
   const int tq = R / a.h_q, head = R % a.h_q;
@@ -431,7 +562,7 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
               pack_bf16(acc1[2], acc1[3])};
   }
   if (a.lse != nullptr && (tid & 63) == 0)
-    a.lse[((int64_t)b * a.s_q + tq) * a.h_q + head] = (M + fast_log2(den)) * kLn2;
+    a.lse[((int64_t)b * a.s_q + tq) * a.h_q + head] = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
 }
 
 }  // namespace
@@ -439,8 +570,15 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
 int latent_rows_per_wg() { return ROWS; }
 int latent_tile_tokens() { return T; }
 
+int latent_plan_wgs(int n_rb, int64_t max_tiles) {
+  // one work-group per CU in a single round: equal tile shares then finish
+  // together
+  int64_t n = std::max<int64_t>(1, 256 / n_rb);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(n, max_tiles));
+}
+
 hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st) {
-  const int n_units = a.B * a.n_splits * a.n_rb;
+  const int n_units = a.n_wg * a.n_rb;
   const int padded = (n_units + 7) / 8 * 8;
   hipLaunchKernelGGL(latent_split_kernel, dim3(padded), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();

@@ -98,8 +98,13 @@ def test_decode_rejects_bad_arguments(lib, kw, status):
 def test_workspace_sizes_cover_the_split_plan(lib):
     assert lib.gqa_decode_workspace_bytes(64, 32, 8, 1, 32768, 128) > 0
     assert lib.gqa_decode_workspace_bytes(64, 32, 7, 1, 32768, 128) == 0
+    # latent: 2 row blocks of 128 rows, 128 work-groups per row block, one
+    # partial (512 outputs + lse, fp32) per work-group and per sequence it
+    # touches (at most n_wg + B slots), plus B + 1 tile prefix sums
     n = lib.latent_absorb_decode_workspace_bytes(64, 128, 2, 65536, 512)
-    assert n > 0 and n % (4 * 513) == 0
+    assert n == 2 * (128 + 64) * 128 * 513 * 4 + 65 * 4
+    # a tiny problem has no more work-groups than tiles
+    assert lib.latent_absorb_decode_workspace_bytes(1, 128, 1, 40, 512) == 1 * (2 + 1) * 128 * 513 * 4 + 2 * 4
 
 
 def latent(lib, **kw):
