@@ -55,6 +55,10 @@ constexpr int LDS_BYTES = PBASE + 2 * PBUF;       // 156 KiB
 constexpr int kBufferFlags = 0x00020000;          // raw dword buffer access
 constexpr float kLatentSlack = 96.f;              // see the running state below
 constexpr uint32_t kOutOfRange = 0x80000000u;     // buffer offset past any range: loads read zeros
+#ifndef GHA_LAT_SOFT_SLOTS
+#define GHA_LAT_SOFT_SLOTS 48
+#endif
+constexpr int kSoftSlots = GHA_LAT_SOFT_SLOTS;     // value MFMAs that carry the softmax (< 64)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -288,13 +292,15 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
     for (int qt = 0; qt < 8; ++qt) mfma_acc(oacc[dt][qt], vf[dt & 1], pall[qt]);
   };
 
-  // Iteration t: phase A, the scores of tile t (with the DMAs of tile t + 2
-  // into the slots of tile t - 2, and the P^T reads of tile t - 1), then
+  // Iteration t: phase A, the scores of tile t (with the P^T reads of tile
+  // t - 1), then
   // phase B, the values of tile t - 1 with the softmax of tile t spread
   // between their MFMAs (VALU and matrix core run side by side).  P^T goes
   // to LDS and one barrier follows (tile t + 1 has landed, every row's P^T
-  // is visible).  Restart requests raised at a barrier are acted on before
-  // the next one: nothing computed in between is kept.
+  // is visible).  The DMAs of tile t + 2 (into the slots of tile t - 2) are
+  // spread over both phases: the CU moves about 1 KiB per 64 cycles into LDS,
+  // and bursts stall the issuing wave.  Restart requests raised at a barrier
+  // are acted on before the next one: nothing computed in between is kept.
   uint32_t flags = 0;  // restart requests (one byte per wave) read after the last barrier
   auto iter = [&](int it, auto masked, auto has_pv) __attribute__((always_inline)) -> bool {
     constexpr bool kMasked = decltype(masked)::value;
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
     load_k(1, kf[1]);
     static_for<0, DS>([&](auto S_) __attribute__((always_inline)) {
       constexpr int s = decltype(S_)::value;
-      if (s < 9) dma(dt2, s);
+      if (s % 4 == 0) dma(dt2, s / 4);
       if (kPV && s == DS - 2) load_p(it - 1);
       if (kPV && s == DS - 1) load_v(vb, 0, vf[0]);
       s_step(s);
@@ -387,36 +393,46 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
     auto scores_retire = [&]() __attribute__((always_inline)) {
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(sacc[0][0]), "+v"(sacc[0][1]), "+v"(sacc[1][0]), "+v"(sacc[1][1]));
     };
+    // P^T of this wave's rows to LDS, with their normaliser (two wait states
+    // after the VALU writes of the MFMA operands, accumulator included), and
+    // the restart request; issued well before the barrier so that the LDS
+    // writes drain behind matrix work
+    unsigned char* pb = smem + PBASE + (it & 1) * PBUF;
+    auto publish = [&]() __attribute__((always_inline)) {
+      u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+      asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]), "+v"(ones), "+v"(lacc[0]), "+v"(lacc[1]));
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) mfma_v(lacc[qt], ones, pf[qt]);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) st16(pb + (2 * wave + qt) * PQT + 16 * lane, pf[qt]);
+      // a wave whose rows outgrew their reference asks the whole work-group
+      // to start the split again (every wave must run the same tiles and
+      // barriers)
+      if (lane == 0) restart_flag[it & 1][wave] = wave_any(restart_row) ? 1 : 0;
+    };
     if constexpr (kPV) {
-      constexpr int NB = 64;
+      constexpr int NB = 64;         // value MFMAs
+      constexpr int NBS = kSoftSlots;  // the softmax stages share the first NBS of them
       static_for<0, NB>([&](auto M_) __attribute__((always_inline)) {
         constexpr int m = decltype(M_)::value;
         constexpr int dt = m / 8, qt = m % 8;
         if (qt == 0 && dt + 1 < 8) load_v(vb, dt + 1, vf[(dt + 1) & 1]);
+        if (m % 16 == 8) dma(dt2, 5 + m / 16);
         mfma_acc(oacc[dt][qt], vf[dt & 1], pall[qt]);
         __builtin_amdgcn_sched_barrier(0);
         if (m == 0) scores_retire();
-        static_for<m * NST / NB, (m + 1) * NST / NB>(stage);
+        if (m < NBS) static_for<m * NST / NBS, (m + 1) * NST / NBS>(stage);
+        if (m == NBS) publish();
         __builtin_amdgcn_sched_barrier(0);
       });
     } else {
       scores_retire();
       static_for<0, NST>(stage);
+#pragma unroll
+      for (int j = 5; j < 9; ++j) dma(dt2, j);
+      publish();
     }
 
-    // the normaliser of this wave's rows (two wait states after the VALU
-    // writes of its operands, accumulator included, before an MFMA reads them)
-    u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
-    asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]), "+v"(ones), "+v"(lacc[0]), "+v"(lacc[1]));
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) mfma_v(lacc[qt], ones, pf[qt]);
-    unsigned char* pb = smem + PBASE + (it & 1) * PBUF;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) st16(pb + (2 * wave + qt) * PQT + 16 * lane, pf[qt]);
-    // a wave whose rows outgrew their reference asks the whole work-group
-    // to start the split again (every wave must run the same tiles and
-    // barriers)
-    if (lane == 0) restart_flag[it & 1][wave] = wave_any(restart_row) ? 1 : 0;
     if (__builtin_amdgcn_readfirstlane(flags) != 0) return true;
     wait_vmem_but_one_tile();
     __syncthreads();
