@@ -27,10 +27,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
 
 
-# Per-source flags.  The d = 128 prefill kernels never see NaN scores (rows
-# past the sequence end read as zeros and masked scores are -inf), so fmaxf
-# there needs no NaN canonicalisation of its operands.
-SOURCE_FLAGS = {"prefill_d128.hip": ["-fno-honor-nans"]}
+# Per-source flags.  The d = 128 prefill and GTA kernels never see NaN scores
+# (rows past the sequence end read as zeros and masked scores are -inf), so
+# fmaxf there needs no NaN canonicalisation of its operands.
+SOURCE_FLAGS = {"prefill_d128.hip": ["-fno-honor-nans"], "gta.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, extra=(), objdir=None) -> str:

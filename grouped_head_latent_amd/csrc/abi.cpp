@@ -232,6 +232,9 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
   a.causal = causal ? 1 : 0;
   a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d_qk);
   a.B = B;
+  if (!gha::gta_layout_supported(a, d_qk, d_v))
+    return fail(GHA_ERR_STRIDE, "k/v rows overlap or one sequence spans 2 GiB or more (k ss=%lld, v ss=%lld, S=%d)",
+                (long long)k->ss, (long long)v->ss, S);
   return launched(gha::launch_gta(a, d_qk, per, out_dtype == GHA_F32, reinterpret_cast<hipStream_t>(stream)),
                   "gta_shared_score_prefill");
 }

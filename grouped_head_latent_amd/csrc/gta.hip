@@ -1,315 +1,458 @@
-// GTA shared-score attention prefill, bf16, fp32 accumulation, on gfx950 MFMA.
+// GTA shared-score attention prefill, bf16 in, fp32 accumulation, gfx950.
 //
 // "GTA: Grouped-head latenT Attention" news article, grouped shared attention
 // matrix mechanism: the heads of a group share one attention matrix, computed
-// once and handed to every head of the group.  The kernel mirrors that
-// structure.  A work-group owns 64 positions of one group:
-//   * Score phase: wave w computes S for positions 16w..16w+15 against the
-//     group's key tile (S^T = K Q^T, K staged in LDS), runs the online softmax
-//     for those rows, and publishes the bf16 probabilities P and a per-row
-//     rescale factor in LDS.
-//   * Value phase: wave w acts as head w of the group (with fewer than four
-//     heads, waves split a head's positions): it applies the shared P of all
-//     64 positions to its own head's values.  V never passes through LDS:
-//     each lane loads 8 keys x 4 features of its head's V tile with 8-byte
-//     loads and transposes them in registers into MFMA operands, and the key
-//     order of the score tiles makes P^T line up with those keys.
-// The two phases are software-pipelined across key tiles: iteration t runs
-// the score phase of tile t+1 and the value phase of tile t, which are
-// independent, in one basic block (so one wave's softmax VALU work can fill
-// the gaps between its own value MFMAs), with one barrier per tile; K and P
-// are double-buffered in LDS and V in registers.
-#include <type_traits>
-
+// once and applied to the values of every head in the group.  Per group there
+// is one query and one key (d_qk wide) and one 64-wide value per head.
+//
+// One work-group (eight waves, two per SIMD) owns 128 positions of one group
+// and walks the keys in tiles of 64:
+//   score: wave w computes S^T = K Q^T for positions 16 w .. 16 w + 15 (K
+//          from LDS, Q^T resident in VGPRs), runs their softmax and publishes
+//          the bf16 probabilities as P^T operand fragments in LDS;
+//   value: the waves split the group's heads and positions (with four heads,
+//          wave w takes head w / 2 for positions 64 (w % 2) .. + 63) and
+//          accumulate O^T += V^T P^T: V^T fragments come from transposing LDS
+//          reads of the head's V tile, P^T fragments from LDS.
+// So the score matrix is computed once per group and every K or V tile is
+// fetched once per work-group.  Two waves per SIMD let one wave's softmax and
+// LDS traffic overlap the other's matrix work.
+//
+// Tiles reach LDS by buffer DMA (buffer_load ... lds, no VGPR staging) into
+// rings of NS slots: the DMAs of an iteration fetch the K tile NS - 1 ahead of
+// the one being scored and the V tile NS - 2 ahead of the one being applied.
+// Rows past the sequence end read as zeros (buffer range check).
+//
+// Softmax against a fixed reference: each position's reference m (log2 units)
+// is the maximum of its first tile (key 0 is always visible), so the
+// accumulators never need rescaling and the value waves can use any
+// position's probabilities without its statistics.  A tile whose maximum
+// exceeds m by more than kSlack (2^96 stays far inside bf16 and fp32 range)
+// makes the work-group start again with the larger reference; the result is
+// the same softmax either way.
+//
+// Iteration it: phase A, the score MFMAs of tile it; phase B, the value MFMAs
+// of tile it - 1 with the softmax of tile it spread between them (VALU and
+// matrix core run side by side), then P^T(it) to LDS and one barrier.
+//
+// LDS rows, 16-byte units swizzled so that every fragment read touches
+// distinct banks:
+//   K row r (d_qk = 64: 8 units) keeps unit u at u ^ ((r / 2) % 8); score
+//     reads (16 rows, one unit) then cover all 16 positions of a 256 B window;
+//     (d_qk = 128: 16 units) unit u at u ^ (r % 16).
+//   V row r (8 units) keeps unit u at u ^ 2 ((r / 2) % 4); a transposing read
+//     of one half-wave takes 32 B from each of 8 consecutive rows, which then
+//     land on 8 distinct 32 B bank groups.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "lds_pipe.hpp"
 
 namespace gha {
 namespace {
 
-constexpr int KB = 64;   // keys per iteration
-constexpr int PR = 64;   // positions per work-group
-constexpr int PP = KB + 8;  // P row pitch in LDS (elements), 16 B pad
-static_assert(PR == KB, "every wave sees every tile it visits: tile t <= the diagonal tile");
+constexpr int KB = 64;                  // keys per tile
+constexpr int ROWS = 128;               // positions per work-group
+constexpr int VROW = 128;               // bytes per V row (64 bf16)
+constexpr int VHEAD = KB * VROW;        // one head's V tile: 8 KiB
+constexpr int PFRAG = 1024;             // one P^T operand fragment: 64 lanes x 16 B
+constexpr int PBUF = 16 * PFRAG;        // P^T of 8 row tiles x 2 contraction steps
+constexpr float kSlack = 96.f;
+constexpr int NW = 8;                   // waves per work-group
+constexpr int QT = ROWS / (16 * NW);    // 16-position score tiles per wave
+
+template <int DQK, int H>
+struct GtaLayout {
+  static constexpr int KROW = 2 * DQK;          // bytes per K row
+  static constexpr int KTILE = KB * KROW;
+  static constexpr int VTILE = H * VHEAD;
+  // ring slots: three when they fit (two tiles in flight), else two
+  static constexpr int NS = (3 * (KTILE + VTILE) + 2 * PBUF <= 152 * 1024) ? 3 : 2;
+  static constexpr int KBASE = 0;
+  static constexpr int VBASE = NS * KTILE;
+  static constexpr int PBASE = VBASE + NS * VTILE;
+  static constexpr int STATS = PBASE + 2 * PBUF;  // 128 floats, then 2 x 8 restart flags
+  static constexpr int FLAGS = STATS + 4 * ROWS;
+  static constexpr int BYTES = FLAGS + 16;
+  static constexpr int KDMA = KTILE / 1024 / NW;  // DMA instructions per wave per K tile
+  static constexpr int VDMA = VTILE / 1024 / NW;  // ... per V tile
+  static constexpr int NDMA = KDMA + VDMA;
+  static constexpr int RPD = 1024 / KROW;         // K rows per DMA instruction
+};
+
+__host__ __device__ constexpr int k_swz(int dqk, int r) { return dqk == 64 ? ((r >> 1) & 7) : (r & 15); }
 
 template <int DQK, int H, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void gta_kernel(PrefillArgs a) {
-  constexpr int KP = DQK + 8;
-  constexpr int DS = DQK / 32;
-  constexpr int KCH = DQK / 8;              // 16-byte chunks per K row
-  constexpr int K_LOADS = KB * KCH / 256;   // per thread
-  constexpr int K_ROWSTEP = 256 / KCH;
-  constexpr int QTV = H;                    // position tiles per wave in the value phase
+__global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
+  using Ly = GtaLayout<DQK, H>;
+  constexpr int DS = DQK / 32;      // score contraction steps
+  constexpr int HW = NW / H;        // waves per head in the value phase
+  constexpr int RT = 8 / HW;        // row tiles per wave in the value phase
+  constexpr int NB = 8 * RT;        // value MFMAs per tile: 2 steps x 4 column tiles x RT
+  constexpr int NBS = 3 * NB / 4;   // the softmax shares the first NBS of them
+  constexpr int U = Ly::KROW / 16;  // 16-byte units per K row
+  constexpr int NS = Ly::NS;
   static_assert(H == 1 || H == 2 || H == 4, "heads per group");
+  static_assert(QT == 1, "one score tile per wave");
+  static_assert(RT == 1 || RT == 2 || RT == 4, "row tiles per wave");
+  static_assert(Ly::KDMA >= 1 && Ly::KDMA <= DS && Ly::VDMA >= 1 && NB % Ly::VDMA == 0, "DMA slots");
+  static_assert(Ly::BYTES <= 160 * 1024, "LDS");
 
-  __shared__ __attribute__((aligned(16))) __bf16 k_s[2][KB * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 p_s[2][PR * PP];
-  __shared__ float alpha_s[2][PR];
-  __shared__ float l_s[PR];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Ly::BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
 
+  // ---- which positions of which group -----------------------------------------
   const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
   if (lid >= (uint32_t)a.n_blocks) return;
   const int n_qb = a.n_qblocks;
-  const int qb = n_qb - 1 - (int)(lid % n_qb);  // heavy (late) blocks first
-  const int grp = (int)(lid / n_qb) % a.h_kv;
-  const int b = (int)(lid / n_qb) / a.h_kv;
-  const int pos_wg = qb * PR;
+  const int qb = __builtin_amdgcn_readfirstlane(n_qb - 1 - (int)(lid % n_qb));  // heavy (late) blocks first
+  const int grp = __builtin_amdgcn_readfirstlane((int)(lid / n_qb) % a.h_kv);
+  const int b = __builtin_amdgcn_readfirstlane((int)(lid / n_qb) / a.h_kv);
   const int S = a.S_q;
+  const int pos_wg = qb * ROWS;
+  const int hv = wave / HW;          // value phase: head hv of the group
+  const int rt0 = (wave % HW) * RT;  //   and its first row tile
 
-  const int spos0 = pos_wg + 16 * wave;        // score phase: this wave's 16 positions
-  const int vhead = wave / (4 / H);            // value phase: this wave's head
-  const int vq0 = (wave % (4 / H)) * QTV;      //   and its position tiles
-
-  const int k_end = a.causal ? min(S, pos_wg + PR) : S;
-  const int n_kb = (k_end + KB - 1) / KB;
+  // tiles to visit; tiles from t_mask on need the mask (diagonal or ragged)
+  int n_kb, t_mask;
+  if (a.causal) {
+    n_kb = (min(S, pos_wg + ROWS) + KB - 1) / KB;
+    t_mask = min((pos_wg + 1) / KB, S / KB);
+  } else {
+    n_kb = (S + KB - 1) / KB;
+    t_mask = S / KB;
+  }
+  n_kb = __builtin_amdgcn_readfirstlane(n_kb);
+  t_mask = __builtin_amdgcn_readfirstlane(min(t_mask, n_kb));
 
   const __bf16* qbase = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)grp * a.q_sh;
   const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)grp * a.k_sh;
-  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)(grp * a.group + vhead) * a.v_sh;
+  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)(grp * H + hv) * a.v_sh;
 
-  u32x4 qf[DS];
-  {
-    const int pos = min(spos0 + li, S - 1);
+  // ---- Q^T fragments of this wave's score rows ----------------------------------
+  u32x4 qf[QT][DS];
+  int kmax[QT];  // last key each lane's row sees
 #pragma unroll
-    for (int s = 0; s < DS; ++s) qf[s] = ld16(qbase + (int64_t)pos * a.q_ss + 32 * s + 8 * lg);
+  for (int qt = 0; qt < QT; ++qt) {
+    const int pos = pos_wg + 16 * (QT * wave + qt) + li;
+    const int pc = min(pos, S - 1);
+    kmax[qt] = a.causal ? pc : S - 1;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qf[qt][s] = ld16(qbase + (int64_t)pc * a.q_ss + 32 * s + 8 * lg);
   }
-
-  // ---- K: global -> registers -> LDS (double buffer) -----------------------
-  // Whole tiles use strided addresses; the tail tile clamps rows to the last
-  // position (their scores are masked).
-  const int k_row = tid / KCH, k_col = (tid % KCH) * 8;
-  const __bf16* kthr = kbase + (int64_t)k_row * a.k_ss + k_col;
-  const int64_t k_rowstep = (int64_t)K_ROWSTEP * a.k_ss;
-  u32x4 kreg[K_LOADS];
-  auto load_k = [&](int kb) __attribute__((always_inline)) {
-    const int key0 = kb * KB;
-    if (key0 + KB <= S) {
-      const __bf16* p = kthr + (int64_t)key0 * a.k_ss;
-#pragma unroll
-      for (int i = 0; i < K_LOADS; ++i) kreg[i] = ld16(p + i * k_rowstep);
-    } else {
-#pragma unroll
-      for (int i = 0; i < K_LOADS; ++i) {
-        const int kk = min(key0 + k_row + K_ROWSTEP * i, S - 1);
-        kreg[i] = ld16(kbase + (int64_t)kk * a.k_ss + k_col);
-      }
-    }
-  };
-  auto store_k = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) st16(&k_s[buf][(k_row + K_ROWSTEP * i) * KP + k_col], kreg[i]);
-  };
-
-  // ---- V: global -> registers (double buffer) ------------------------------
-  // lane (li, lg) loads keys 32*hk + 8*lg + tt, features
-  // 8*(li & 7) + 4*(li >> 3) .. +3 (8 bytes); lanes 0..15 of one load cover a
-  // whole 128-byte row.
-  const int v_col = 8 * (li & 7) + 4 * (li >> 3);
-  const __bf16* vthr = vbase + (int64_t)(8 * lg) * a.v_ss + v_col;
-  u32x2 vbuf0[2][8], vbuf1[2][8];
-  auto load_v = [&](int kb, u32x2 (&vr)[2][8]) __attribute__((always_inline)) {
-    const int key0 = kb * KB;
-    if (key0 + KB <= S) {
-      const __bf16* p = vthr + (int64_t)key0 * a.v_ss;
-#pragma unroll
-      for (int hk = 0; hk < 2; ++hk)
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-          vr[hk][tt] = *reinterpret_cast<const u32x2*>(p + (int64_t)(32 * hk + tt) * a.v_ss);
-    } else {
-#pragma unroll
-      for (int hk = 0; hk < 2; ++hk)
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          const int kk = min(key0 + 32 * hk + 8 * lg + tt, S - 1);
-          vr[hk][tt] = *reinterpret_cast<const u32x2*>(vbase + (int64_t)kk * a.v_ss + v_col);
-        }
-    }
-  };
-
-  // ---- state ----------------------------------------------------------------
-  f32x4 oacc[4][QTV];
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-#pragma unroll
-    for (int q = 0; q < QTV; ++q) oacc[w][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
-  float m2 = kNegInf;
-  const float c2 = a.scale * kLog2e;
-  const u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
-  const int kmax = a.causal ? min(spos0 + li, S - 1) : S - 1;  // last key this lane's row sees
-
-  // score MFMAs of tile t: S^T tile j, row i  <->  key 32*(j/2) + 8*(i/4) + 4*(j%2) + i%4
-  auto score_mfma = [&](int t, f32x4 (&sacc)[4]) __attribute__((always_inline)) {
-    const __bf16* kb_s = k_s[t & 1];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const __bf16* kr = kb_s + (32 * (j >> 1) + 8 * (li >> 2) + 4 * (j & 1) + (li & 3)) * KP + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < DS; ++s) sacc[j] = mfma_bf16(ld16(kr + 32 * s), qf[s], sacc[j]);
-    }
-  };
-  // softmax of tile t (lane group lg, tile j, element r <-> key 32*(j/2) + 8*lg
-  // + 4*(j%2) + r), publishing P and the rescale factor of this wave's rows.
-  // The running maximum moves per row (the four lanes of a row agree), so the
-  // phase is branch-free.
-  auto score_softmax = [&](int t, f32x4 (&sacc)[4], auto masked) __attribute__((always_inline)) {
-    const int key0 = t * KB;
-    if constexpr (decltype(masked)::value) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (key0 + 32 * (j >> 1) + 8 * lg + 4 * (j & 1) + r > kmax) sacc[j][r] = kNegInf;
-    }
-    float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
-    mx = fmaxf(fmaxf(mx, sacc[0][3]), sacc[1][0]);
-    mx = fmaxf(fmaxf(mx, sacc[1][1]), sacc[1][2]);
-    mx = fmaxf(fmaxf(mx, sacc[1][3]), sacc[2][0]);
-    mx = fmaxf(fmaxf(mx, sacc[2][1]), sacc[2][2]);
-    mx = fmaxf(fmaxf(mx, sacc[2][3]), sacc[3][0]);
-    mx = fmaxf(fmaxf(mx, sacc[3][1]), sacc[3][2]);
-    mx = fmaxf(mx, sacc[3][3]);
-    const float mx2 = group4_max(mx) * c2;
-    const float mnew = (mx2 > m2 + kRescaleSlack) ? fmaxf(m2, mx2) : m2;
-    const float alpha = (m2 == mnew) ? 1.f : fast_exp2(m2 - mnew);
-    m2 = mnew;
-    lacc *= alpha;
-    const float msub = (m2 == kNegInf) ? 0.f : m2;
-    float p[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[j][r] = fast_exp2(__builtin_fmaf(sacc[j][r], c2, -msub));
-    __bf16* pb = p_s[t & 1];
-#pragma unroll
-    for (int hk = 0; hk < 2; ++hk) {
-      const u32x4 pf = {pack_bf16(p[2 * hk][0], p[2 * hk][1]), pack_bf16(p[2 * hk][2], p[2 * hk][3]),
-                        pack_bf16(p[2 * hk + 1][0], p[2 * hk + 1][1]),
-                        pack_bf16(p[2 * hk + 1][2], p[2 * hk + 1][3])};
-      lacc = mfma_bf16(ones, pf, lacc);
-      st16(pb + (16 * wave + li) * PP + 32 * hk + 8 * lg, pf);  // row 16*wave + li, keys 32hk + 8lg ..
-    }
-    alpha_s[t & 1][16 * wave + li] = alpha;  // the four lane groups write the same value
-  };
-  // value phase of tile t: this wave's head over its position tiles
-  auto value_rescale = [&](int t) __attribute__((always_inline)) {
-    float al[QTV];
-    bool any = false;
-#pragma unroll
-    for (int q = 0; q < QTV; ++q) {  // all reads first: one LDS round trip
-      al[q] = alpha_s[t & 1][16 * (vq0 + q) + li];
-      any |= al[q] != 1.f;
-    }
-    if (wave_any(any)) {
-#pragma unroll
-      for (int q = 0; q < QTV; ++q)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) oacc[w][q] *= al[q];
-    }
-  };
-  auto value_mfma = [&](int t, u32x2 (&vr)[2][8]) __attribute__((always_inline)) {
-    const __bf16* pb = p_s[t & 1];
-#pragma unroll
-    for (int hk = 0; hk < 2; ++hk) {
-      u32x4 pt[QTV];
-#pragma unroll
-      for (int q = 0; q < QTV; ++q) pt[q] = ld16(pb + (16 * (vq0 + q) + li) * PP + 32 * hk + 8 * lg);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // features 8*(li&7) + 4*(li>>3) + w: dword w/2 of each key's 4 features
-        const int dw = w >> 1;
-        const u32x4 av = (w & 1) ? u32x4{hi_pair(vr[hk][0][dw], vr[hk][1][dw]), hi_pair(vr[hk][2][dw], vr[hk][3][dw]),
-                                         hi_pair(vr[hk][4][dw], vr[hk][5][dw]), hi_pair(vr[hk][6][dw], vr[hk][7][dw])}
-                                 : u32x4{lo_pair(vr[hk][0][dw], vr[hk][1][dw]), lo_pair(vr[hk][2][dw], vr[hk][3][dw]),
-                                         lo_pair(vr[hk][4][dw], vr[hk][5][dw]), lo_pair(vr[hk][6][dw], vr[hk][7][dw])};
-#pragma unroll
-        for (int q = 0; q < QTV; ++q) oacc[w][q] = mfma_bf16(av, pt[q], oacc[w][q]);
-      }
-    }
-  };
-
-  // ---- prologue: K(0), K(1) staged, score(0) published, V(0) in flight ------
-  load_k(0);
-  store_k(0);
   wait_vmem_all();
-  __syncthreads();
-  load_v(0, vbuf0);
-  load_k(min(1, n_kb - 1));
+  const float c2 = a.scale * kLog2e;
+
+  // ---- tile DMAs -----------------------------------------------------------------
+  // K: wave w moves rows RPD (w KDMA + j) .. + RPD - 1 with its j-th
+  // instruction (lane l: row l / U, unit position l % U).  V: wave w moves
+  // rows 8 n .. 8 n + 7 of its value head with instruction j, n = (w VDMA + j)
+  // mod 8 (lane l: row l / 8, position l % 8).  Offsets of tiles past the
+  // last read as zeros.
+  const uint32_t krow = (uint32_t)a.k_ss * 2u, vrow = (uint32_t)a.v_ss * 2u;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)kbase, 0, (int)((uint32_t)(S - 1) * krow + (uint32_t)Ly::KROW), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)vbase, 0, (int)((uint32_t)(S - 1) * vrow + (uint32_t)VROW), kBufferFlags);
+  uint32_t kofs[Ly::KDMA];
+#pragma unroll
+  for (int j = 0; j < Ly::KDMA; ++j) {
+    const int r = (wave * Ly::KDMA + j) * Ly::RPD + lane / U;
+    kofs[j] = (uint32_t)(lane / U) * krow + 16u * ((lane % U) ^ k_swz(DQK, r));
+  }
+  const uint32_t vofs = (uint32_t)(lane >> 3) * vrow + 16u * ((lane & 7) ^ (2 * ((lane >> 4) & 3)));
+  const uint32_t lds0 = lds_offset(smem);
+  auto issue_k = [&](int t, int j) __attribute__((always_inline)) {
+    const int n = wave * Ly::KDMA + j;
+    const uint32_t so = t < n_kb ? (uint32_t)(t * KB + n * Ly::RPD) * krow : kOutOfRange;
+    lds_dma16(krs, lds0 + Ly::KBASE + (t % NS) * Ly::KTILE + n * 1024, kofs[j], so);
+  };
+  auto issue_v = [&](int t, int j) __attribute__((always_inline)) {
+    const int n = (wave * Ly::VDMA + j) & 7;
+    const uint32_t so = t < n_kb ? (uint32_t)(t * KB + 8 * n) * vrow : kOutOfRange;
+    lds_dma16(vrs, lds0 + Ly::VBASE + (t % NS) * Ly::VTILE + hv * VHEAD + n * 1024, vofs, so);
+  };
+
+  // ---- fragment addresses (bytes in smem) -------------------------------------------
+  // score A operand: K row 16 kt + li, unit 4 s + lg:
+  //   (kfrag ^ 64 s) + 16 KROW kt
+  const uint32_t kfrag = DQK == 64 ? li * 128 + 16 * (lg ^ ((li >> 1) & 7)) : li * 256 + 16 * (lg ^ li);
+  // value A operand (transposing read), source lane li of group lg: V row
+  // 32 ks + 16 h + 4 lg + li / 4, columns 16 ct + 4 (li % 4) .. + 3, i.e. unit
+  // 2 ct + (li / 2) % 2, byte 8 (li % 2) of it: (vfrag ^ 32 ct) + 4096 ks + 2048 h
+  uint32_t vfrag;
   {
-    f32x4 sacc[4];
-    score_mfma(0, sacc);
-    score_softmax(0, sacc, std::true_type{});
+    const int vr = 4 * lg + (li >> 2);
+    vfrag = vr * VROW + 32 * ((vr >> 1) & 3) + 16 * ((li >> 1) & 1) + 8 * (li & 1);
   }
-  store_k(1);
-  __syncthreads();
+  const uint32_t plane = 16 * lane;  // P^T fragments are lane-linear
+  uint32_t vfr[4];                   // transposing-read lane offsets of the 4 column tiles
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) vfr[ct] = vfrag ^ (32u * ct);
 
-  // ---- steady state: iteration t = value(t) + score(t+1) ---------------------
-  // loads: V(t+1) into the other register set, K(t+2) into k_s[t & 1], which
-  // held K(t), last read by score(t) one iteration earlier.
-  auto step = [&](int t, u32x2 (&vr)[2][8], u32x2 (&vn)[2][8], auto with_score, auto masked) __attribute__((always_inline)) {
-    load_v(min(t + 1, n_kb - 1), vn);
-    load_k(min(t + 2, n_kb - 1));
-    value_rescale(t);
-    if constexpr (decltype(with_score)::value) {
-      f32x4 sacc[4];
-      score_mfma(t + 1, sacc);
-      value_mfma(t, vr);
-      score_softmax(t + 1, sacc, masked);
+  // ---- running state ----------------------------------------------------------------
+  f32x4 oacc[4][RT];  // O^T: [column tile][row tile] (AGPRs)
+  f32x4 lacc[QT];     // normaliser of this wave's score rows
+  float m2[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) m2[qt] = kNegInf;
+  // P^T fragments [contraction step][row tile]; with d_qk = 128 (more score
+  // registers) one set is reloaded between the steps instead
+  constexpr int NPB = DS == 4 ? 1 : 2;
+  u32x4 pall[NPB][RT];
+  u32x4 vf[2];        // V^T fragment, double-buffered across value steps
+  uint64_t flags = 0; // restart requests (one byte per wave) read after the last barrier
+  unsigned char* const flag_s = smem + Ly::FLAGS;
+
+  // The accumulators are written by inline-asm MFMAs, which the compiler's
+  // hazard checks do not see: before any other instruction may touch the
+  // last value steps' accumulators (the compiler may insert copies at the end
+  // of an iteration), those MFMAs must retire.  The nops are tied to them.
+  auto value_retire = [&]() __attribute__((always_inline)) {
+#define GHA_RETIRE "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+    if constexpr (RT == 1) asm volatile(GHA_RETIRE : "+a"(oacc[3][0]), "+a"(oacc[2][0]), "+a"(oacc[1][0]));
+    if constexpr (RT == 2)
+      asm volatile(GHA_RETIRE : "+a"(oacc[3][0]), "+a"(oacc[3][RT - 1]), "+a"(oacc[2][0]), "+a"(oacc[2][RT - 1]));
+    if constexpr (RT == 4)
+      asm volatile(GHA_RETIRE : "+a"(oacc[3][0]), "+a"(oacc[3][1]), "+a"(oacc[3][2]), "+a"(oacc[3][RT - 1]));
+#undef GHA_RETIRE
+  };
+
+  auto iter = [&](int it, auto masked, auto has_score, auto has_pv) __attribute__((always_inline)) -> bool {
+    constexpr bool kMasked = decltype(masked)::value;
+    constexpr bool kS = decltype(has_score)::value;
+    constexpr bool kP = decltype(has_pv)::value;
+    const int k0 = it * KB;
+    // slot bases of this iteration, kept opaque so that each fragment address
+    // is one add of a scalar to a loop-invariant lane offset
+    uint32_t kb_ = Ly::KBASE + (uint32_t)(it % NS) * Ly::KTILE;
+    uint32_t vb_ = Ly::VBASE + (uint32_t)((it + NS - 1) % NS) * Ly::VTILE + hv * VHEAD;
+    uint32_t pr_ = Ly::PBASE + (uint32_t)((it + 1) & 1) * PBUF;  // P^T of tile it - 1
+    asm volatile("" : "+s"(kb_), "+s"(vb_), "+s"(pr_));
+    const int dk = it + NS - 1, dv = it + NS - 2;  // tiles whose DMAs this iteration issues
+
+    auto load_v = [&](int step, u32x4& v) __attribute__((always_inline)) {
+      const unsigned char* p = smem + vb_ + vfr[step & 3] + 4096 * (step >> 2);
+      const u32x2 h0 = ld_tr(p);
+      const u32x2 h1 = ld_tr(p + 2048);
+      v = u32x4{h0[0], h0[1], h1[0], h1[1]};
+    };
+    auto load_p = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) pall[ks % NPB][rt] = ld16(smem + pr_ + plane + (2 * (rt0 + rt) + ks) * PFRAG);
+    };
+
+    // ---- phase A: S^T of tile it for this wave's rows ----
+    f32x4 sacc[4][QT];
+    if constexpr (kS) {
+      u32x4 kf[2][4];
+      auto load_k = [&](int s, u32x4 (&f)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) f[kt] = ld16(smem + kb_ + kt * 16 * Ly::KROW + (kfrag ^ (64u * s)));
+      };
+      load_k(0, kf[0]);
+      static_for<0, DS>([&](auto S_) __attribute__((always_inline)) {
+        constexpr int s = decltype(S_)::value;
+        if (s + 1 < DS) load_k(s + 1, kf[(s + 1) & 1]);
+        if (s < Ly::KDMA) issue_k(dk, s);
+        if (kP && s == DS - 1) {
+          load_p(0);
+          load_v(0, vf[0]);
+        }
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            if (s == 0) mfma_v0(sacc[kt][qt], kf[s & 1][kt], qf[qt][s]);
+            else mfma_v(sacc[kt][qt], kf[s & 1][kt], qf[qt][s]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     } else {
-      value_mfma(t, vr);
+#pragma unroll
+      for (int j = 0; j < Ly::KDMA; ++j) issue_k(dk, j);
+      load_p(0);
+      load_v(0, vf[0]);
     }
-    store_k(t & 1);
-    __syncthreads();
-  };
-  auto rotate_v = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int hk = 0; hk < 2; ++hk)
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) vbuf0[hk][tt] = vbuf1[hk][tt];
-  };
-  // steady state: the next tile is neither the diagonal nor the ragged tail
-  int t = 0;
-  for (; t + 1 < n_kb - 1; ++t) {
-    step(t, vbuf0, vbuf1, std::true_type{}, std::false_type{});
-    rotate_v();
-  }
-  // the last two tiles, peeled: the next tile is masked, then value only
-  if (t + 1 == n_kb - 1) {
-    step(t, vbuf0, vbuf1, std::true_type{}, std::true_type{});
-    rotate_v();
-    ++t;
-  }
-  step(t, vbuf0, vbuf1, std::false_type{}, std::false_type{});
 
-  // ---- epilogue ------------------------------------------------------------
-  if (lg == 0) l_s[16 * wave + li] = lacc[0];
-  if (lg == 0 && a.lse != nullptr && spos0 + li < S)
-    a.lse[((int64_t)b * a.lse_heads + grp) * S + spos0 + li] = (m2 + fast_log2(lacc[0])) * kLn2;
-  __syncthreads();
-  // oacc[w][q][r] of lane (li, lg) is feature 8*((4*lg + r) & 7) + 4*((4*lg + r) >> 3) + w
-  // of position tile vq0 + q, row li: four consecutive features per (q, r).
-  const int head = grp * a.group + vhead;
+    // ---- phase B: softmax of tile it in 23 small stages per score row (=
+    // lane and q-tile); sacc[kt][qt][r] is key k0 + 16 kt + 4 lg + r and
+    // becomes its probability in place ----
+    float mx[QT], msub[QT];
+    u32x4 pf[QT][2];
+    bool restart_row = false;
+    constexpr int NSQ = 23, NST = QT * NSQ;
+    auto stage = [&](auto K_) __attribute__((always_inline)) {
+      constexpr int k = decltype(K_)::value;
+      constexpr int qt = k / NSQ, st = k % NSQ;
+      if constexpr (st < 4) {
+        if constexpr (kMasked) {
 #pragma unroll
-  for (int q = 0; q < QTV; ++q) {
-    const int row = 16 * (vq0 + q) + li;
+          for (int r = 0; r < 4; ++r)
+            if (k0 + 16 * st + 4 * lg + r > kmax[qt]) sacc[st][qt][r] = kNegInf;
+        }
+      } else if constexpr (st == 4 || st == 5) {
+        constexpr int kt = 2 * (st - 4);
+        float x = fmaxf(fmaxf(sacc[kt][qt][0], sacc[kt][qt][1]), fmaxf(sacc[kt][qt][2], sacc[kt][qt][3]));
+        x = fmaxf(x, fmaxf(fmaxf(sacc[kt + 1][qt][0], sacc[kt + 1][qt][1]), fmaxf(sacc[kt + 1][qt][2], sacc[kt + 1][qt][3])));
+        mx[qt] = st == 4 ? x : fmaxf(mx[qt], x);
+      } else if constexpr (st == 6) {
+        mx[qt] = xor16_max(mx[qt]);
+      } else if constexpr (st == 7) {
+        mx[qt] = xor32_max(mx[qt]) * c2;
+      } else if constexpr (st == 8) {
+        // the first tile fixes a row's reference; a tile that outgrows it by
+        // more than the slack asks for a restart
+        const bool first = m2[qt] == kNegInf;
+        const bool grow = !first && mx[qt] > m2[qt] + kSlack;
+        restart_row = restart_row || grow;
+        m2[qt] = (first || grow) ? mx[qt] : m2[qt];
+        msub[qt] = (m2[qt] == kNegInf) ? 0.f : m2[qt];
+      } else if constexpr (st >= 9 && st <= 12) {
+        constexpr int kt = st - 9;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[kt][qt][r] = __builtin_fmaf(sacc[kt][qt][r], c2, -msub[qt]);
+      } else if constexpr (st >= 13 && st <= 20) {
+        constexpr int kt = (st - 13) / 2, r0 = 2 * ((st - 13) % 2);
+        sacc[kt][qt][r0] = fast_exp2(sacc[kt][qt][r0]);
+        sacc[kt][qt][r0 + 1] = fast_exp2(sacc[kt][qt][r0 + 1]);
+      } else {
+        constexpr int ks = st - 21;
+        pf[qt][ks] = u32x4{pack_bf16(sacc[2 * ks][qt][0], sacc[2 * ks][qt][1]),
+                           pack_bf16(sacc[2 * ks][qt][2], sacc[2 * ks][qt][3]),
+                           pack_bf16(sacc[2 * ks + 1][qt][0], sacc[2 * ks + 1][qt][1]),
+                           pack_bf16(sacc[2 * ks + 1][qt][2], sacc[2 * ks + 1][qt][3])};
+      }
+    };
+    // the score MFMAs must retire before the softmax reads their results
+    // (the nops are tied to every score register so that no read moves above them)
+    auto scores_retire = [&]() __attribute__((always_inline)) {
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                   : "+v"(sacc[0][0]), "+v"(sacc[1][0]), "+v"(sacc[2][0]), "+v"(sacc[3][0]));
+    };
+    // P^T of this wave's rows to LDS with their normaliser (two wait states
+    // after the VALU writes of the MFMA operands, accumulator included), and
+    // the restart request
+    auto publish = [&]() __attribute__((always_inline)) {
+      u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+      asm volatile("s_nop 1" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(lacc[0]), "+v"(ones));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) mfma_v(lacc[qt], ones, pf[qt][ks]);
+      unsigned char* pw = smem + Ly::PBASE + (it & 1) * PBUF + 16 * lane;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) st16(pw + (2 * (QT * wave + qt) + ks) * PFRAG, pf[qt][ks]);
+      // a wave whose rows outgrew their reference asks the whole work-group to
+      // start again (every wave must run the same tiles and barriers)
+      const bool any_restart = wave_any(restart_row);  // all lanes vote, outside the lane-0 branch
+      if (lane == 0) flag_s[NW * (it & 1) + wave] = any_restart ? 1 : 0;
+    };
+
+    if constexpr (kP) {
+      // O^T += V^T P^T of tile it - 1: step = 4 ks + ct, RT MFMAs per step
+      static_for<0, NB>([&](auto M_) __attribute__((always_inline)) {
+        constexpr int m = decltype(M_)::value;
+        constexpr int step = m / RT, rt = m % RT, ks = step / 4, ct = step % 4;
+        if (rt == 0 && step + 1 < 8) load_v(step + 1, vf[(step + 1) & 1]);
+        if (NPB == 2 && m == 1) load_p(1);
+        if (m % (NB / Ly::VDMA) == NB / Ly::VDMA / 2) issue_v(dv, m / (NB / Ly::VDMA));
+        mfma_acc(oacc[ct][rt], vf[step & 1], pall[ks % NPB][rt]);
+        // a single set of P^T fragments is refilled once its last reader has issued
+        if (NPB == 1 && m == 4 * RT - 1) load_p(1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kS) {
+          if (m == 0) scores_retire();
+          if constexpr (m < NBS) static_for<m * NST / NBS, (m + 1) * NST / NBS>(stage);
+          if (m == NBS) publish();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      value_retire();
+    } else {
+      scores_retire();
+      static_for<0, NST>(stage);
+#pragma unroll
+      for (int j = 0; j < Ly::VDMA; ++j) issue_v(dv, j);
+      publish();
+    }
+
+    // a restart raised at the previous barrier: nothing since is kept
+    if (__builtin_amdgcn_readfirstlane((uint32_t)(flags | (flags >> 32))) != 0) return true;
+    // the tiles of the next iteration have landed (this one's DMAs may fly on)
+    wait_vmem_at_most<Ly::NDMA * (NS - 2)>();
+    __syncthreads();
+    if constexpr (kS) flags = *reinterpret_cast<const uint64_t*>(flag_s + NW * (it & 1));
+    return false;
+  };
+
+  for (;;) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) oacc[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    flags = 0;
+    // K of tiles 0 .. NS - 2 and V of tiles 0 .. NS - 3, in that order
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+#pragma unroll
+      for (int j = 0; j < Ly::KDMA; ++j) issue_k(t, j);
+#pragma unroll
+    for (int t = 0; t < NS - 2; ++t)
+#pragma unroll
+      for (int j = 0; j < Ly::VDMA; ++j) issue_v(t, j);
+    wait_vmem_at_most<Ly::NDMA * (NS - 2)>();
+    __syncthreads();
+    bool restart = t_mask > 0 ? iter(0, std::false_type{}, std::true_type{}, std::false_type{})
+                              : iter(0, std::true_type{}, std::true_type{}, std::false_type{});
+    int it = 1;
+    for (; it < t_mask && !restart; ++it)
+      restart = iter(it, std::false_type{}, std::true_type{}, std::true_type{});
+    for (; it < n_kb && !restart; ++it)
+      restart = iter(it, std::true_type{}, std::true_type{}, std::true_type{});
+    if (!restart) restart = iter(n_kb, std::false_type{}, std::false_type{}, std::true_type{});
+    // no DMA may still target a slot that is about to be reused
+    wait_vmem_all();
+    if (!restart) break;
+    __syncthreads();
+  }
+
+  // ---- epilogue: 1 / l of every row through LDS, then O = O^T / l ------------------
+  float* stats = reinterpret_cast<float*>(smem + Ly::STATS);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l = lacc[qt][0];
+    const int row = 16 * (QT * wave + qt) + li;
+    const int pos = pos_wg + row;
+    if (lg == 0) {
+      stats[row] = 1.f / l;
+      if (a.lse != nullptr && pos < S)
+        a.lse[((int64_t)b * a.lse_heads + grp) * S + pos] = (m2[qt] + fast_log2(l)) * kLn2;
+    }
+  }
+  __syncthreads();
+  const int head = grp * H + hv;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = 16 * (rt0 + rt) + li;
     const int pos = pos_wg + row;
     if (pos >= S) continue;
-    const float inv = 1.f / l_s[row];
-    const int64_t obase = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh + (int64_t)pos * a.o_ss;
+    const float inv = stats[row];
+    const int64_t obase = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh + (int64_t)pos * a.o_ss + 4 * lg;
+    // oacc[ct][rt][r] is feature 16 ct + 4 lg + r of this row
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * lg + r;
-      const int f = 8 * (i & 7) + 4 * (i >> 3);
-      const f32x4 v = f32x4{oacc[0][q][r], oacc[1][q][r], oacc[2][q][r], oacc[3][q][r]} * inv;
+    for (int ct = 0; ct < 4; ++ct) {
+      const f32x4 v = oacc[ct][rt] * inv;
       if constexpr (OUT_F32)
-        *reinterpret_cast<f32x4*>((float*)a.o + obase + f) = v;
+        *reinterpret_cast<f32x4*>((float*)a.o + obase + 16 * ct) = v;
       else
-        *reinterpret_cast<u32x2*>((__bf16*)a.o + obase + f) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        *reinterpret_cast<u32x2*>((__bf16*)a.o + obase + 16 * ct) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
     }
   }
 }
@@ -318,15 +461,24 @@ template <int DQK, int H>
 hipError_t launch_h(const PrefillArgs& a, bool out_f32, hipStream_t st) {
   const uint32_t padded = (uint32_t)((a.n_blocks + 7) / 8 * 8);
   if (out_f32)
-    hipLaunchKernelGGL((gta_kernel<DQK, H, true>), dim3(padded), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gta_kernel<DQK, H, true>), dim3(padded), dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((gta_kernel<DQK, H, false>), dim3(padded), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gta_kernel<DQK, H, false>), dim3(padded), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gta_positions_per_wg() { return PR; }
+int gta_positions_per_wg() { return ROWS; }
+
+bool gta_layout_supported(const PrefillArgs& a, int d_qk, int d_v) {
+  // one (batch, group) K or (batch, head) V sequence must span less than 2^31
+  // bytes (32-bit buffer offsets and range) and rows must not overlap, so that
+  // the range check cuts exactly at the last position
+  const int64_t span_k = ((int64_t)a.S_q + 2 * KB) * a.k_ss * 2;
+  const int64_t span_v = ((int64_t)a.S_q + 2 * KB) * a.v_ss * 2;
+  return a.k_ss >= d_qk && a.v_ss >= d_v && span_k < ((int64_t)1 << 31) && span_v < ((int64_t)1 << 31);
+}
 
 hipError_t launch_gta(const PrefillArgs& a, int d_qk, int heads_per_group, bool out_f32, hipStream_t st) {
 #define GHA_GTA_CASE(DQ, HH) \

@@ -67,6 +67,8 @@ int prefill_rows_per_wave();
 int prefill_bf16_waves(const PrefillArgs& a, int d);  // waves per work-group of the kernel chosen for a
 hipError_t launch_gta(const PrefillArgs& a, int d_qk, int heads_per_group, bool out_f32, hipStream_t st);
 int gta_positions_per_wg();
+// K/V spans and row pitches the GTA kernel's 32-bit buffer addressing covers
+bool gta_layout_supported(const PrefillArgs& a, int d_qk, int d_v);
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, int d, bool out_f32, hipStream_t st);
 hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st);

@@ -31,6 +31,7 @@
 // per 16 lanes, 8 tokens per half-wave) land in distinct banks.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "lds_pipe.hpp"
 
 #include <algorithm>
 #include <type_traits>
@@ -52,63 +53,16 @@ constexpr int PBUF = 8 * PQT;                     // P^T of the work-group's 8 q
 constexpr int RBASE = NLS * LTILE;
 constexpr int PBASE = RBASE + NRS * RTILE;
 constexpr int LDS_BYTES = PBASE + 2 * PBUF;       // 156 KiB
-constexpr int kBufferFlags = 0x00020000;          // raw dword buffer access
 constexpr float kLatentSlack = 96.f;              // see the running state below
-constexpr uint32_t kOutOfRange = 0x80000000u;     // buffer offset past any range: loads read zeros
 #ifndef GHA_LAT_SOFT_SLOTS
 #define GHA_LAT_SOFT_SLOTS 48
 #endif
 constexpr int kSoftSlots = GHA_LAT_SOFT_SLOTS;     // value MFMAs that carry the softmax (< 64)
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// f(integral_constant<int, I>) for I = B .. E - 1, unrolled at compile time
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
 // chunk swizzles of the LDS rows (see the layout above)
 __host__ __device__ constexpr int lat_sw(int k) { return ((k & 7) << 1) | ((k >> 3) & 1); }
 __host__ __device__ constexpr int rope_sw(int k) { return (k >> 1) & 7; }
 
-// 16 bytes per lane from buffer `rs` at voff + soff into LDS at lds + 16 lane;
-// bytes past the buffer's range come back as zeros.  Inline asm so that the
-// compiler sees no LDS write it would have to order every LDS read after;
-// the kernel orders these loads itself (vmcnt wait + barrier).  M0 needs one
-// wait state after it is written.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// The MFMAs are written as inline asm to pin register classes: the O^T
-// accumulator in AGPRs, the scores, the normaliser and every operand in
-// VGPRs.  Left to itself the compiler puts every MFMA result, scores
-// included, in AGPRs and spills.  The asm is volatile so that the MFMAs keep
-// their program order.  The compiler does not see these as MFMAs, so the
-// kernel pads the two hazards it would otherwise cover: VALU writes of an
-// operand need two wait states before an MFMA reads it, and an MFMA result
-// needs more than eight before a VALU reads it.  MFMA to MFMA accumulator
-// chains need none.
-__device__ __forceinline__ void mfma_acc(f32x4& acc, const u32x4& a, const u32x4& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v(f32x4& acc, const u32x4& a, const u32x4& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v0(f32x4& acc, const u32x4& a, const u32x4& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ u32x2 ld_tr(const unsigned char* p) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
-}
 // tiles of sequence b (0 past the batch); lengths are clamped to [0, L_cap]
 __device__ __forceinline__ int latent_tiles(const LatentArgs& a, int b) {
   return b < a.B ? (min(max(a.seqlens[b], 0), a.L_cap) + T - 1) / T : 0;
@@ -408,7 +362,8 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
       // a wave whose rows outgrew their reference asks the whole work-group
       // to start the split again (every wave must run the same tiles and
       // barriers)
-      if (lane == 0) restart_flag[it & 1][wave] = wave_any(restart_row) ? 1 : 0;
+      const bool any_restart = wave_any(restart_row);  // all lanes vote, outside the lane-0 branch
+      if (lane == 0) restart_flag[it & 1][wave] = any_restart ? 1 : 0;
     };
     if constexpr (kPV) {
       constexpr int NB = 64;         // value MFMAs
@@ -421,7 +376,7 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
         mfma_acc(oacc[dt][qt], vf[dt & 1], pall[qt]);
         __builtin_amdgcn_sched_barrier(0);
         if (m == 0) scores_retire();
-        if (m < NBS) static_for<m * NST / NBS, (m + 1) * NST / NBS>(stage);
+        if constexpr (m < NBS) static_for<m * NST / NBS, (m + 1) * NST / NBS>(stage);
         if (m == NBS) publish();
         __builtin_amdgcn_sched_barrier(0);
       });

@@ -25,6 +25,7 @@
 //    the eight rows read by one half-wave cover all 16 slots.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "lds_pipe.hpp"
 
 #include <type_traits>
 
@@ -51,33 +52,6 @@ constexpr int TILEB = KB * ROWB;
 #ifndef GHA_PF_ORDER
 #define GHA_PF_ORDER 1
 #endif
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// Buffer resource word 3 for raw (unswizzled, untyped) dword access.
-constexpr int kBufferFlags = 0x00020000;
-
-// 16 bytes per lane from buffer `rs` at voff + soff into LDS at lds + 16 lane
-// (buffer_load_dwordx4 ... lds; rows past the buffer's range come back as
-// zeros).  Written as inline asm so that the compiler does not see an LDS
-// write it cannot disambiguate: with the builtin it waits for every
-// outstanding tile load before each LDS read, which serialises the prefetch.
-// The kernel orders these loads itself (s_waitcnt vmcnt + barrier).  The
-// instruction has no destination register; M0 needs one wait state after
-// it is written.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ u32x2 ld_tr(const unsigned char* p) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
-}
 
 template <int QT, bool OUT_F32>
 __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(PrefillArgs a) {

@@ -245,6 +245,39 @@ def test_gta_shared_score(gha_lib, B, h, n_grp, S, d_qk, d_v):
     check("gta lse", lse.cpu().numpy(), ref_lse)
 
 
+def test_gta_not_causal(gha_lib):
+    """Every position sees all S keys; S ragged against the 64-key tiles."""
+    B, h, n_grp, S, d = 1, 8, 2, 200, 64
+    say(f"GTA non-causal B={B} h={h} groups={n_grp} S={S}")
+    qb, kb, vb = gen((B, n_grp, S, d), 15, 1), gen((B, n_grp, S, d), 15, 2), gen((B, h, S, d), 15, 3)
+    o = gha_lib.gta_shared_score_prefill(*(bf16_to_torch(x) for x in (qb, kb, vb)), causal=False,
+                                         out_dtype=torch.float32)
+    ref, _ = oracle.gta_prefill(widen(qb), widen(kb), widen(vb), causal=False)
+    check("gta non-causal", o.cpu().numpy(), ref)
+
+
+def test_gta_growing_scores_restart(gha_lib):
+    """Keys whose scores jump far above the first tile's maximum, twice, for a
+    few positions held by lanes other than the first of their wave (the other
+    positions see flat scores): the kernel's fixed per-row reference must be
+    replaced and the work-group recomputed, and the result is still the
+    softmax."""
+    B, h, n_grp, S, d = 1, 8, 2, 300, 64
+    say("GTA growing scores (reference restart)")
+    one, k_mid, k_hi = (np.float32(x).view(np.uint32) >> 16 for x in (1.0, 16.0, 32.0))
+    qb = np.zeros((B, n_grp, S, d), dtype=np.uint16)
+    rows = [150, 170, 250, 299]
+    qb[:, 0, rows] = one
+    qb[:, 1] = gen((B, 1, S, d), 16, 1)[:, 0]
+    kb = gen((B, n_grp, S, d), 16, 2)
+    kb[:, 0, 100:200] = k_mid
+    kb[:, 0, 200:] = k_hi
+    vb = gen((B, h, S, d), 16, 3)
+    o = gha_lib.gta_shared_score_prefill(*(bf16_to_torch(x) for x in (qb, kb, vb)), out_dtype=torch.float32)
+    ref, _ = oracle.gta_prefill(widen(qb), widen(kb), widen(vb))
+    check("gta restart", o.cpu().numpy(), ref)
+
+
 def test_gta_full_size_sampled(gha_lib):
     """Batch 8, 16 heads in 4 groups of 4, 2048 tokens, dims 64."""
     B, h, n_grp, S, d = 8, 16, 4, 2048, 64
@@ -302,11 +335,14 @@ def test_latent_absorb_decode(gha_lib, B, h_q, s_q, L_cap, seqlens):
     check("latent lse", lse.cpu().numpy(), ref_lse)
 
 
-def test_latent_growing_scores_restart(gha_lib):
+@pytest.mark.parametrize("heads", [None, (5, 77, 126)])
+def test_latent_growing_scores_restart(gha_lib, heads):
     """Scores that jump far above the first tiles' maximum, twice (latent
     rows of three magnitudes): the kernel's fixed per-row reference must be
-    replaced and the split recomputed, and the result is still the softmax."""
-    say("latent growing scores (reference restart)")
+    replaced and the split recomputed, and the result is still the softmax.
+    With `heads`, only those heads (none held by the first lane of a wave)
+    see the jump; every other head has a zero query and flat scores."""
+    say(f"latent growing scores (reference restart), heads={heads}")
     B, h_q, s_q, L = 1, 128, 1, 300
     rng_bits = gen((B, L, 576), 21, synth.STREAM["latent"])
     cache = rng_bits.copy()
@@ -317,6 +353,9 @@ def test_latent_growing_scores_restart(gha_lib):
     cache[:, 200:, :512] = four
     cache[:, 100:, 512:] = 0
     q_lat = np.full((B, s_q, h_q, 512), one, dtype=np.uint16)
+    if heads is not None:
+        q_lat[:] = 0
+        q_lat[:, :, list(heads)] = one
     q_r = np.zeros((B, s_q, h_q, 64), dtype=np.uint16)
     seqlens = np.array([L], dtype=np.int32)
     scale = 1 / math.sqrt(128 + 64)
@@ -328,7 +367,8 @@ def test_latent_growing_scores_restart(gha_lib):
     ref, _ = oracle.latent_absorb_decode(widen(q_lat), widen(q_r), c[..., :512], c[..., 512:],
                                          seqlens, scale=scale)
     check("latent restart", o.cpu().numpy(), ref)
-    assert np.allclose(ref, 4.0)
+    jumped = list(heads) if heads is not None else slice(None)
+    assert np.allclose(ref[:, :, jumped], 4.0)
 
 
 @pytest.mark.parametrize("s_q", [1, 2])
