@@ -52,8 +52,8 @@ import numpy as np
 
 __all__ = [
     "widen_bf16", "softmax_attention", "gqa_prefill", "gqa_decode",
-    "gta_prefill", "latent_absorb_decode", "absorb_query", "absorb_output",
-    "expand_latent",
+    "gta_prefill", "gta_decode", "latent_absorb_decode", "gqla_gqa_decode",
+    "absorb_query", "absorb_output", "expand_latent",
 ]
 
 
@@ -184,6 +184,70 @@ def gta_prefill(q, k, v, *, causal: bool = True, scale: float | None = None,
     for b, i in pairs:
         j = _group_of(i, h, n_grp)
         o[b, i], lse[b, j] = softmax_attention(q[b, j], k[b, j], v[b, i], nvis, scale)
+    return o, lse
+
+
+def gta_decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
+               heads=None):
+    """Decode step of GTA shared-score attention (GTA article, grouped shared
+    attention matrix) over a contiguous cache: each group has one query and
+    one cached key per token, so one score vector per new token, and every
+    head of the group applies it to its own cached values.
+
+    q: (B, n_grp, s_q, d_qk); k_cache: (B, n_grp, L_cap, d_qk);
+    v_cache: (B, h, L_cap, d_v); seqlens: (B,) with s_q <= L_b <= L_cap,
+    counting the new tokens, aligned bottom-right as in gqa_decode.
+    Returns o (B, h, s_q, d_v) and lse (B, n_grp, s_q).
+    """
+    B, n_grp, s_q, d_qk = q.shape
+    h = v_cache.shape[1]
+    if h % n_grp:
+        raise ValueError("h must be a multiple of n_grp")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_qk)
+    o = np.full((B, h, s_q, v_cache.shape[3]), np.nan)
+    lse = np.full((B, n_grp, s_q), np.nan)
+    pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h)]
+    for b, i in pairs:
+        L = int(seqlens[b])
+        if not (s_q <= L <= k_cache.shape[2]):
+            raise ValueError("need s_q <= L_b <= L_cap")
+        j = _group_of(i, h, n_grp)
+        nvis = np.arange(s_q) + (L - s_q) + 1
+        o[b, i], lse[b, j] = softmax_attention(q[b, j], k_cache[b, j, :L], v_cache[b, i, :L],
+                                               nvis, scale)
+    return o, lse
+
+
+def gqla_gqa_decode(q_c, q_r, k_c, k_r, v_cache, seqlens, *, scale: float,
+                    heads=None):
+    """GQLA's GQA-path decode (section 1 and section 3.1, Eq. (1)): g groups,
+    each with its own cached key k^C and value, plus one decoupled RoPE key
+    k^R per token shared by every group.  Head i of group j = g(i) scores
+        scale * (q^C_i . k^C_{j,u} + q^R_i . k^R_u),
+    the dot product of [q^C_i; q^R_i] with the group's key [k^C_j; k^R], and
+    takes the group's value v_{j,u}.
+
+    q_c: (B, h_q, s_q, d_h); q_r: (B, h_q, s_q, d_r); k_c: (B, g, L_cap, d_h);
+    k_r: (B, L_cap, d_r); v_cache: (B, g, L_cap, d_v); seqlens as gqa_decode.
+    Returns o (B, h_q, s_q, d_v) and lse (B, h_q, s_q).
+    """
+    B, h_q, s_q, _ = q_c.shape
+    g = k_c.shape[1]
+    if h_q % g:
+        raise ValueError("h_q must be a multiple of g")
+    o = np.full((B, h_q, s_q, v_cache.shape[3]), np.nan)
+    lse = np.full((B, h_q, s_q), np.nan)
+    pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h_q)]
+    for b, i in pairs:
+        L = int(seqlens[b])
+        if not (s_q <= L <= k_c.shape[2]):
+            raise ValueError("need s_q <= L_b <= L_cap")
+        j = _group_of(i, h_q, g)
+        qi = np.concatenate([q_c[b, i], q_r[b, i]], axis=1)
+        kj = np.concatenate([k_c[b, j, :L], k_r[b, :L]], axis=1)
+        nvis = np.arange(s_q) + (L - s_q) + 1
+        o[b, i], lse[b, i] = softmax_attention(qi, kj, v_cache[b, j, :L], nvis, scale)
     return o, lse
 
 

@@ -124,6 +124,52 @@ def test_gta_matches_brute_force():
         np.testing.assert_allclose(lse[0, j], bl, atol=1e-13, rtol=0)
 
 
+def test_gta_decode_matches_brute_force():
+    B, n_grp, h, s_q, dqk, dv, L_cap = 2, 2, 4, 2, 3, 2, 5
+    q = rnd((B, n_grp, s_q, dqk), 17, 1)
+    kc = rnd((B, n_grp, L_cap, dqk), 17, 2)
+    vc = rnd((B, h, L_cap, dv), 17, 3)
+    seqlens = np.array([2, 5])
+    o, lse = oracle.gta_decode(q, kc, vc, seqlens)
+    for b in range(B):
+        L = int(seqlens[b])
+        for i in range(h):
+            j = i // 2
+            bo, bl = brute_attention(q[b, j].tolist(), kc[b, j, :L].tolist(), vc[b, i, :L].tolist(),
+                                     1 / math.sqrt(dqk), causal_offset=L - s_q)
+            np.testing.assert_allclose(o[b, i], bo, atol=1e-13, rtol=0)
+            np.testing.assert_allclose(lse[b, j], bl, atol=1e-13, rtol=0)
+
+
+def test_gqla_gqa_decode_matches_brute_force():
+    """Scores written out term by term: the group's key part plus the RoPE
+    part that every group shares."""
+    B, h_q, g, s_q, d_h, d_r, dv, L_cap = 1, 4, 2, 2, 3, 2, 3, 5
+    qc = rnd((B, h_q, s_q, d_h), 18, 1)
+    qr = rnd((B, h_q, s_q, d_r), 18, 2)
+    kc = rnd((B, g, L_cap, d_h), 18, 3)
+    kr = rnd((B, L_cap, d_r), 18, 4)
+    vc = rnd((B, g, L_cap, dv), 18, 5)
+    seqlens = np.array([4])
+    scale = 0.37
+    o, lse = oracle.gqla_gqa_decode(qc, qr, kc, kr, vc, seqlens, scale=scale)
+    L = 4
+    for i in range(h_q):
+        j = i // 2
+        for t in range(s_q):
+            scores = []
+            for u in range(L - s_q + t + 1):
+                sc = sum(qc[0, i, t, x] * kc[0, j, u, x] for x in range(d_h))
+                sc += sum(qr[0, i, t, x] * kr[0, u, x] for x in range(d_r))
+                scores.append(scale * sc)
+            mx = max(scores)
+            w = [math.exp(x - mx) for x in scores]
+            z = sum(w)
+            row = [sum(w[u] / z * vc[0, j, u, x] for u in range(len(w))) for x in range(dv)]
+            np.testing.assert_allclose(o[0, i, t], row, atol=1e-13, rtol=0)
+            assert abs(lse[0, i, t] - (mx + math.log(z))) < 1e-13
+
+
 # ------------------------------------------------ library routine: torch SDPA
 
 def sdpa(q, k, v, mask, scale, enable_gqa=False):
@@ -310,6 +356,35 @@ def test_absorbed_latent_equals_expanded_gqa_path():
     O_exp, lse_exp = oracle.gqa_decode(q_full, K, V, seqlens, scale=scale)
     np.testing.assert_allclose(O_abs, O_exp.transpose(0, 2, 1, 3), rtol=1e-10, atol=1e-13)
     np.testing.assert_allclose(lse_lat, lse_exp.transpose(0, 2, 1), rtol=0, atol=1e-12)
+
+
+def test_gqla_gqa_path_equals_absorbed_latent_path():
+    """GQLA Figure 2: the GQA path over the per-group expanded cache with the
+    shared RoPE key (k^C_j = W^UK_j c, v_j = W^UV_j c) gives the same outputs as
+    the absorbed latent path."""
+    g, d_h, d_r = 4, 8, 4
+    q_c, q_r, c, kr, w_uk, w_uv = latent_case(g=g, d_h=d_h, d_r=d_r)
+    seqlens = np.array([5, 24])
+    scale = 1 / math.sqrt(d_h + d_r)
+    o_lat, lse_lat = oracle.latent_absorb_decode(oracle.absorb_query(q_c, w_uk, g), q_r, c, kr, seqlens,
+                                                 scale=scale)
+    O_abs = oracle.absorb_output(o_lat, w_uv, g, d_h)
+    K, V = oracle.expand_latent(c, kr, w_uk, w_uv, g)
+    O_gqa, lse_gqa = oracle.gqla_gqa_decode(q_c.transpose(0, 2, 1, 3), q_r.transpose(0, 2, 1, 3),
+                                            K[..., :d_h], kr, V, seqlens, scale=scale)
+    np.testing.assert_allclose(O_gqa.transpose(0, 2, 1, 3), O_abs, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(lse_gqa.transpose(0, 2, 1), lse_lat, rtol=0, atol=1e-12)
+
+
+def test_gta_decode_is_last_rows_of_gta_prefill():
+    """Bottom-right alignment: decoding the last s_q tokens of a sequence gives
+    the last s_q rows of the causal shared-score prefill."""
+    B, n_grp, h, L, d, s_q = 1, 2, 4, 12, 8, 3
+    q, k, v = rnd((B, n_grp, L, d), 44, 1), rnd((B, n_grp, L, d), 44, 2), rnd((B, h, L, d), 44, 3)
+    o_pre, lse_pre = oracle.gta_prefill(q, k, v)
+    o_dec, lse_dec = oracle.gta_decode(q[:, :, L - s_q:], k, v, np.array([L]))
+    np.testing.assert_allclose(o_dec, o_pre[:, :, L - s_q:], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse_dec, lse_pre[:, :, L - s_q:], rtol=0, atol=1e-14)
 
 
 def test_absorb_query_uses_group_blocks():
