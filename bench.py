@@ -8,8 +8,9 @@ resident in HBM.  The headline workload is causal GQA prefill at batch 4,
 32 query heads over 8 KV heads, 4096 tokens, head dim 128, bf16 inputs with
 fp32 accumulation; `value` is its algorithmic attention TFLOP/s (the causal
 pair count times 4*d FLOP, whatever the kernel actually executes).  The other
-workloads (GQA decode, GTA shared-score prefill, latent-absorbed decode) are
-timed the same way and reported under "extras".
+workloads (GQA decode, GTA shared-score prefill and decode, latent-absorbed
+decode, GQLA's per-group GQA-path decode) are timed the same way and reported
+under "extras".
 
 Rank 0 prints one JSON line.  Only one GPU is used: --gpus above 1 exits.
 """
@@ -34,6 +35,10 @@ PREFILL = dict(B=4, h_q=32, h_kv=8, S=4096, d=128, seed=2)
 DECODE = dict(B=64, h_q=32, h_kv=8, d=128, L_lo=1024, L_hi=32768, seed=3)
 GTA = dict(B=8, h=16, n_grp=4, S=2048, d=64, seed=4)
 LATENT = dict(B=64, h_q=128, r_kv=512, d_r=64, L_lo=8192, L_hi=65536, seed=5, d_h=128)
+# decode forms built on the same shapes: GTA's groups at the GQA decode lengths,
+# and GQLA's per-group expanded cache (g = 8) at the latent decode lengths
+GTA_DECODE = dict(B=64, h=16, n_grp=4, d=64, L_lo=1024, L_hi=32768, seed=6)
+GQLA_DECODE = dict(B=64, h_q=128, g=8, d_h=128, d_r=64, L_lo=8192, L_hi=65536, seed=7, kv_std=0.45)
 
 
 def log(*a):
@@ -140,6 +145,51 @@ def bench_gta(gha, torch, steps, warmup):
     return dict(ms=ms, tflops=fl / ms / 1e9, flops=fl)
 
 
+def bench_gta_decode(gha, torch, steps, warmup, s_q):
+    c = GTA_DECODE
+    B, h, g, d = c["B"], c["h"], c["n_grp"], c["d"]
+    L_cap = c["L_hi"]
+    seqlens = synth.uniform_i32(B, c["L_lo"], c["L_hi"], c["seed"], synth.STREAM["seqlens"])
+    kc = to_dev(synth.cache_bf16(B, g, L_cap, d, seqlens, c["seed"], 2), torch)
+    vc = to_dev(synth.cache_bf16(B, h, L_cap, d, seqlens, c["seed"], 3), torch)
+    q = to_dev(synth.normal_bf16((B, g, s_q, d), c["seed"], 1), torch)
+    sl = torch.from_numpy(seqlens).cuda()
+    o = torch.empty((B, h, s_q, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gha.gta_shared_score_decode_workspace_bytes(B, h, g, s_q, L_cap, d), dtype=torch.uint8,
+                     device="cuda")
+    ms, wall = time_steps(lambda: gha.gta_shared_score_decode(q, kc, vc, sl, out=o, workspace=ws), steps, warmup,
+                          torch)
+    by = acc.gta_decode_bytes(seqlens, h, g, s_q, d, d)
+    fl = acc.gta_decode_flops(seqlens, h, g, s_q, d, d)
+    del kc, vc
+    return dict(ms=ms, gbps=by / ms / 1e6, tflops=fl / ms / 1e9, bytes=by, flops=fl,
+                sum_L=int(seqlens.sum()))
+
+
+def bench_gqla_decode(gha, torch, steps, warmup, s_q):
+    c = GQLA_DECODE
+    B, h_q, g, d_h, d_r = c["B"], c["h_q"], c["g"], c["d_h"], c["d_r"]
+    L_cap = c["L_hi"]
+    seqlens = synth.uniform_i32(B, c["L_lo"], c["L_hi"], c["seed"], synth.STREAM["seqlens"])
+    kc = to_dev(synth.cache_bf16(B, g, L_cap, d_h, seqlens, c["seed"], synth.STREAM["k"], c["kv_std"]), torch)
+    vc = to_dev(synth.cache_bf16(B, g, L_cap, d_h, seqlens, c["seed"], synth.STREAM["v"], c["kv_std"]), torch)
+    kr = to_dev(synth.cache_bf16(B, 1, L_cap, d_r, seqlens, c["seed"], synth.STREAM["k_rope"])[:, 0], torch)
+    qc = to_dev(synth.normal_bf16((B, h_q, s_q, d_h), c["seed"], synth.STREAM["q_c"]), torch)
+    qr = to_dev(synth.normal_bf16((B, h_q, s_q, d_r), c["seed"], synth.STREAM["q_rope"]), torch)
+    sl = torch.from_numpy(seqlens).cuda()
+    o = torch.empty((B, h_q, s_q, d_h), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gha.gqla_gqa_decode_workspace_bytes(B, h_q, g, s_q, L_cap, d_h), dtype=torch.uint8,
+                     device="cuda")
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    ms, wall = time_steps(lambda: gha.gqla_gqa_decode(qc, qr, kc, kr, vc, sl, scale=scale, out=o, workspace=ws),
+                          steps, warmup, torch)
+    by = acc.gqla_decode_bytes(seqlens, h_q, g, s_q, d_h, d_r)
+    fl = acc.gqla_decode_flops(seqlens, h_q, s_q, d_h, d_r)
+    del kc, vc, kr
+    return dict(ms=ms, gbps=by / ms / 1e6, tflops=fl / ms / 1e9, bytes=by, flops=fl,
+                sum_L=int(seqlens.sum()))
+
+
 def bench_latent(gha, torch, steps, warmup, s_q):
     c = LATENT
     B, h_q, r, dr = c["B"], c["h_q"], c["r_kv"], c["d_r"]
@@ -198,7 +248,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default=None, help="prefill|decode|gta|latent: time one workload")
+    ap.add_argument("--only", default=None,
+                    help="prefill|decode|gta|latent|gta_decode|gqla_decode: time one workload")
     ap.add_argument("--spinup-s", type=float, default=1.0,
                     help="untimed seconds of the same workload before the warmup steps (clock ramp)")
     args = ap.parse_args()
@@ -239,6 +290,18 @@ def main():
                 log(f"latent s_q={s_q} ...")
                 extras[f"latent_decode_sq{s_q}"] = bench_latent(gha, torch, args.steps, args.warmup, s_q)
                 log(extras[f"latent_decode_sq{s_q}"])
+                torch.cuda.empty_cache()
+        if only in (None, "gta_decode"):
+            for s_q in (1, 2):
+                log(f"gta decode s_q={s_q} ...")
+                extras[f"gta_decode_sq{s_q}"] = bench_gta_decode(gha, torch, args.steps, args.warmup, s_q)
+                log(extras[f"gta_decode_sq{s_q}"])
+                torch.cuda.empty_cache()
+        if only in (None, "gqla_decode"):
+            for s_q in (1, 2):
+                log(f"gqla decode s_q={s_q} ...")
+                extras[f"gqla_decode_sq{s_q}"] = bench_gqla_decode(gha, torch, args.steps, args.warmup, s_q)
+                log(extras[f"gqla_decode_sq{s_q}"])
                 torch.cuda.empty_cache()
     for k_, e in extras.items():
         if "gbps" in e:

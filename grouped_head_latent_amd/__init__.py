@@ -9,8 +9,9 @@ the library's HIP kernels; there is no fallback of any kind.  If the library
 is missing or cannot be loaded, every call raises.
 
 Entry points (same names as the C ABI):
-  gqa_prefill, gqa_decode, gta_shared_score_prefill, latent_absorb_decode,
-  gqa_decode_workspace_bytes, latent_absorb_decode_workspace_bytes.
+  gqa_prefill, gqa_decode, gta_shared_score_prefill, gta_shared_score_decode,
+  gqla_gqa_decode, latent_absorb_decode, and the *_workspace_bytes queries of
+  the decode calls.
 """
 from __future__ import annotations
 
@@ -19,8 +20,10 @@ import math
 import os
 
 __all__ = [
-    "gqa_prefill", "gqa_decode", "gta_shared_score_prefill", "latent_absorb_decode",
-    "gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
+    "gqa_prefill", "gqa_decode", "gta_shared_score_prefill", "gta_shared_score_decode",
+    "gqla_gqa_decode", "latent_absorb_decode",
+    "gqa_decode_workspace_bytes", "gta_shared_score_decode_workspace_bytes",
+    "gqla_gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
     "GhaError", "library_path", "load_library", "GHA_F32", "GHA_BF16",
 ]
 
@@ -70,6 +73,14 @@ def load_library():
     lib.gqa_decode_workspace_bytes.restype = S
     lib.gta_shared_score_prefill.argtypes = [P, P, P, P, V, I, I, I, I, I, I, I, I, F, I, V]
     lib.gta_shared_score_prefill.restype = I
+    lib.gta_shared_score_decode.argtypes = [P, P, P, V, P, V, I, I, I, I, I, I, I, I, I, I, F, V, S, V]
+    lib.gta_shared_score_decode.restype = I
+    lib.gta_shared_score_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.gta_shared_score_decode_workspace_bytes.restype = S
+    lib.gqla_gqa_decode.argtypes = [P, P, P, P, P, V, P, V, I, I, I, I, I, I, I, I, I, I, F, V, S, V]
+    lib.gqla_gqa_decode.restype = I
+    lib.gqla_gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.gqla_gqa_decode_workspace_bytes.restype = S
     lib.latent_absorb_decode.argtypes = [P, P, P, P, V, P, V, I, I, I, I, I, I, I, I, I, F, V, S, V]
     lib.latent_absorb_decode.restype = I
     lib.latent_absorb_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -187,6 +198,64 @@ def gta_shared_score_prefill(q, k, v, *, causal: bool = True, scale: float | Non
     _check(lib.gta_shared_score_prefill(_desc(q), _desc(k), _desc(v), _desc(o), _ptr(lse), B, h,
                                         n_grp, S, d_qk, d_v, _dtype_code(q), _out_code(o.dtype),
                                         float(scale or 0.0), int(bool(causal)), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def gta_shared_score_decode_workspace_bytes(B, h, n_grp, s_q, L_max, d_v) -> int:
+    return int(load_library().gta_shared_score_decode_workspace_bytes(B, h, n_grp, s_q, L_max, d_v))
+
+
+def gta_shared_score_decode(q, k_cache, v_cache, seqlens, *, L_max: int | None = None,
+                            scale: float | None = None, out=None, out_dtype=None, workspace=None,
+                            return_lse: bool = False, stream=None):
+    """q (B, n_grp, s_q, d_qk); k_cache (B, n_grp, L_cap, d_qk); v_cache
+    (B, h, L_cap, d_v); seqlens int32 device (B,).  Returns o (B, h, s_q, d_v)
+    [and lse (B, n_grp, s_q)]."""
+    import torch
+    lib = load_library()
+    B, n_grp, s_q, d_qk = q.shape
+    h, L_cap, d_v = v_cache.shape[1], v_cache.shape[2], v_cache.shape[3]
+    L_max = L_cap if L_max is None else int(L_max)
+    out_dtype = out_dtype or torch.bfloat16
+    o = out if out is not None else torch.empty((B, h, s_q, d_v), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, n_grp, s_q), dtype=torch.float32, device=q.device) if return_lse else None
+    need = gta_shared_score_decode_workspace_bytes(B, h, n_grp, s_q, L_max, d_v)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    _check(lib.gta_shared_score_decode(_desc(q), _desc(k_cache), _desc(v_cache), _ptr(seqlens), _desc(o),
+                                       _ptr(lse), B, h, n_grp, s_q, L_cap, L_max, d_qk, d_v, _dtype_code(q),
+                                       _out_code(o.dtype), float(scale or 0.0), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def gqla_gqa_decode_workspace_bytes(B, h_q, g, s_q, L_max, d_h) -> int:
+    return int(load_library().gqla_gqa_decode_workspace_bytes(B, h_q, g, s_q, L_max, d_h))
+
+
+def gqla_gqa_decode(q_c, q_r, k_c, k_r, v_cache, seqlens, *, scale: float, L_max: int | None = None,
+                    out=None, out_dtype=None, workspace=None, return_lse: bool = False, stream=None):
+    """q_c (B, h_q, s_q, d_h), q_r (B, h_q, s_q, d_r); k_c, v_cache (B, g, L_cap, d_h);
+    k_r (B, L_cap, d_r), shared by the groups; seqlens int32 device (B,).
+    Returns o (B, h_q, s_q, d_h) [and lse (B, h_q, s_q)]."""
+    import torch
+    lib = load_library()
+    B, h_q, s_q, d_h = q_c.shape
+    d_r = q_r.shape[3]
+    g, L_cap = k_c.shape[1], k_c.shape[2]
+    L_max = L_cap if L_max is None else int(L_max)
+    out_dtype = out_dtype or torch.bfloat16
+    o = out if out is not None else torch.empty((B, h_q, s_q, d_h), dtype=out_dtype, device=q_c.device)
+    lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=q_c.device) if return_lse else None
+    need = gqla_gqa_decode_workspace_bytes(B, h_q, g, s_q, L_max, d_h)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q_c.device)
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    _check(lib.gqla_gqa_decode(_desc(q_c), _desc(q_r), _desc(k_c), _desc(k_r, (0, None, 1)), _desc(v_cache),
+                               _ptr(seqlens), _desc(o), _ptr(lse), B, h_q, g, s_q, L_cap, L_max, d_h, d_r,
+                               _dtype_code(q_c), _out_code(o.dtype), float(scale), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)))
     return (o, lse) if return_lse else o
 
 

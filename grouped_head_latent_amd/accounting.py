@@ -119,3 +119,32 @@ def latent_decode_bytes(seqlens, h_q, s_q, r_kv, d_r, in_bytes=BF16_BYTES,
 
 def latent_decode_flops(seqlens, h_q, s_q, r_kv, d_r) -> float:
     return 2.0 * h_q * decode_pairs(seqlens, s_q) * ((r_kv + d_r) + r_kv)
+
+
+def gta_decode_bytes(seqlens, h, n_grp, s_q, d_qk, d_v, in_bytes=BF16_BYTES,
+                     out_bytes=BF16_BYTES) -> float:
+    """Per token one key per group and one value per head, read once; plus
+    the queries (one per group) and the outputs (one per head)."""
+    L = int(np.sum(np.asarray(seqlens, dtype=np.int64)))
+    B = len(seqlens)
+    return float(L * (n_grp * d_qk + h * d_v) * in_bytes
+                 + B * s_q * (n_grp * d_qk * in_bytes + h * d_v * out_bytes))
+
+
+def gta_decode_flops(seqlens, h, n_grp, s_q, d_qk, d_v) -> float:
+    """One score per group and visible pair, one value update per head."""
+    return 2.0 * decode_pairs(seqlens, s_q) * (n_grp * d_qk + h * d_v)
+
+
+def gqla_decode_bytes(seqlens, h_q, g, s_q, d_h, d_r, in_bytes=BF16_BYTES,
+                      out_bytes=BF16_BYTES) -> float:
+    """The per-group expanded cache, 2 g d_h + d^R elements per token, read
+    once; plus queries [q^C; q^R] and outputs."""
+    L = int(np.sum(np.asarray(seqlens, dtype=np.int64)))
+    B = len(seqlens)
+    return float(L * gqla_gqa_path_elems_per_token(g, d_h, d_r) * in_bytes
+                 + B * s_q * h_q * ((d_h + d_r) * in_bytes + d_h * out_bytes))
+
+
+def gqla_decode_flops(seqlens, h_q, s_q, d_h, d_r) -> float:
+    return 2.0 * h_q * decode_pairs(seqlens, s_q) * ((d_h + d_r) + d_h)

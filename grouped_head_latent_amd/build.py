@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgha.so")
 OBJDIR = os.path.join(ROOT, "_build", "gha")
-SOURCES = ["abi.cpp", "prefill_bf16.hip", "prefill_d128.hip", "prefill_f32.hip", "gta.hip", "decode.hip", "latent.hip"]
+SOURCES = ["abi.cpp", "prefill_bf16.hip", "prefill_d128.hip", "prefill_f32.hip", "gta.hip", "decode.hip",
+           "stream_decode.hip", "latent.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -27,10 +28,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
 
 
-# Per-source flags.  The d = 128 prefill and GTA kernels never see NaN scores
-# (rows past the sequence end read as zeros and masked scores are -inf), so
-# fmaxf there needs no NaN canonicalisation of its operands.
-SOURCE_FLAGS = {"prefill_d128.hip": ["-fno-honor-nans"], "gta.hip": ["-fno-honor-nans"]}
+# Per-source flags.  The d = 128 prefill, GTA and streaming decode kernels
+# never see NaN scores (rows past the sequence end read as zeros and masked
+# scores are -inf), so fmaxf there needs no NaN canonicalisation of its
+# operands.
+SOURCE_FLAGS = {"prefill_d128.hip": ["-fno-honor-nans"], "gta.hip": ["-fno-honor-nans"],
+                "stream_decode.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, extra=(), objdir=None) -> str:

@@ -66,6 +66,28 @@ void gqa_decode_plan(int B, int h_kv, int n_rb, int L_max, int* split_len, int* 
 }
 
 int gqa_row_blocks(int h_q, int h_kv, int s_q) { return ((h_q / h_kv) * s_q + 15) / 16; }
+
+// Split plan of the streaming decode: about 8192 work-groups over all
+// (sequence, group) units; splits are whole multiples of the kernel's tile
+// stride.  Padded rows per unit: 16 or 32.
+void stream_decode_plan(int B, int G, int L_max, int* split_len, int* n_splits) {
+  const int64_t units = (int64_t)B * G;
+  const int64_t m = gha::stream_decode_split_multiple();
+  const int64_t want = units >= 8192 ? 1 : (8192 + units - 1) / units;
+  int64_t sl = (L_max + want - 1) / want;
+  sl = std::max<int64_t>(m, (sl + m - 1) / m * m);
+  *split_len = (int)sl;
+  *n_splits = (int)((L_max + sl - 1) / sl);
+}
+size_t stream_decode_ws(int B, int G, int rows, int L_max, int dv) {
+  int sl, ns;
+  stream_decode_plan(B, G, L_max, &sl, &ns);
+  const size_t rp = rows <= 16 ? 16 : 32;
+  const size_t n = (size_t)B * G * ns * rp;
+  return n * (size_t)dv * 4 + n * 4;
+}
+// one (batch, head) sequence of a cache read through 32-bit buffer offsets
+bool span_ok(int L_cap, int64_t ss) { return ((int64_t)L_cap + 64) * ss * 2 < ((int64_t)1 << 31); }
 int latent_row_blocks(int h_q, int s_q) {
   const int r = gha::latent_rows_per_wg();
   return (h_q * s_q + r - 1) / r;
@@ -237,6 +259,123 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
                 (long long)k->ss, (long long)v->ss, S);
   return launched(gha::launch_gta(a, d_qk, per, out_dtype == GHA_F32, reinterpret_cast<hipStream_t>(stream)),
                   "gta_shared_score_prefill");
+}
+
+size_t gta_shared_score_decode_workspace_bytes(int B, int h, int n_grp, int s_q, int L_max_hint, int d_v) {
+  if (B < 1 || h < 1 || n_grp < 1 || s_q < 1 || s_q > 32 || L_max_hint < 1 || d_v < 1 || h % n_grp) return 0;
+  return stream_decode_ws(B, n_grp, s_q, L_max_hint, (h / n_grp) * d_v);
+}
+
+gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
+                                   const int32_t* seqlens_k, const gha_tensor* o, float* lse, int B, int h,
+                                   int n_grp, int s_q, int L_cap, int L_max_hint, int d_qk, int d_v,
+                                   gha_dtype in_dtype, gha_dtype out_dtype, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (B < 1 || h < 1 || n_grp < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
+    return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (h % n_grp) return fail(GHA_ERR_GROUPING, "h=%d is not a multiple of n_grp=%d", h, n_grp);
+  const int per = h / n_grp;
+  if (L_max_hint > L_cap || s_q > L_max_hint)
+    return fail(GHA_ERR_SHAPE, "need s_q <= L_max_hint <= L_cap (s_q=%d L_max_hint=%d L_cap=%d)", s_q, L_max_hint, L_cap);
+  if (s_q > 32) return fail(GHA_ERR_SHAPE, "s_q=%d above 32 new tokens per step", s_q);
+  if ((d_qk != 64 && d_qk != 128) || d_v != 64 || (per != 1 && per != 2 && per != 4))
+    return fail(GHA_ERR_HEAD_DIM, "need d_qk in {64,128}, d_v == 64 and h/n_grp in {1,2,4} (d_qk=%d d_v=%d per=%d)", d_qk, d_v, per);
+  if (in_dtype != GHA_BF16 || (out_dtype != GHA_BF16 && out_dtype != GHA_F32))
+    return fail(GHA_ERR_DTYPE, "GTA decode takes bf16 inputs and bf16 or f32 outputs");
+  if (seqlens_k == nullptr) return fail(GHA_ERR_NULL, "seqlens_k is null");
+  gha_status s;
+  if ((s = check_view("q", q, in_dtype, B > 1, n_grp > 1, s_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("k_cache", k_cache, in_dtype, B > 1, n_grp > 1, true)) != GHA_OK) return s;
+  if ((s = check_view("v_cache", v_cache, in_dtype, B > 1, h > 1, true)) != GHA_OK) return s;
+  if ((s = check_view("o", o, out_dtype, B > 1, h > 1, s_q > 1)) != GHA_OK) return s;
+  if (k_cache->ss < d_qk || v_cache->ss < d_v)
+    return fail(GHA_ERR_STRIDE, "cache rows overlap (k ss=%lld, v ss=%lld)", (long long)k_cache->ss, (long long)v_cache->ss);
+  if (!span_ok(L_cap, k_cache->ss) || !span_ok(L_cap, v_cache->ss))
+    return fail(GHA_ERR_SHAPE, "one sequence of a cache spans 2 GiB or more (L_cap=%d)", L_cap);
+  const size_t need = gta_shared_score_decode_workspace_bytes(B, h, n_grp, s_q, L_max_hint, d_v);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
+  if ((s = check_device()) != GHA_OK) return s;
+
+  gha::StreamDecodeArgs a{};
+  a.q = q->ptr; a.q_sb = q->sb; a.q_sh = q->sh; a.q_ss = q->ss;
+  a.k = k_cache->ptr; a.k_sb = k_cache->sb; a.k_sh = k_cache->sh; a.k_ss = k_cache->ss;
+  a.v = v_cache->ptr; a.v_sb = v_cache->sb; a.v_sh = v_cache->sh; a.v_ss = v_cache->ss;
+  a.seqlens = seqlens_k;
+  a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
+  a.lse = lse;
+  a.B = B; a.n_groups = n_grp; a.qpg = 1; a.s_q = s_q; a.rows = s_q; a.L_cap = L_cap;
+  stream_decode_plan(B, n_grp, L_max_hint, &a.split_len, &a.n_splits);
+  const size_t n_part = (size_t)B * n_grp * a.n_splits * (s_q <= 16 ? 16 : 32);
+  a.ws_o = reinterpret_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + n_part * (size_t)(per * d_v);
+  a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d_qk);
+  if ((int64_t)B * n_grp * a.n_splits > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  return launched(gha::launch_stream_decode(a, d_qk, 0, d_v, per, out_dtype == GHA_F32,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                  "gta_shared_score_decode");
+}
+
+size_t gqla_gqa_decode_workspace_bytes(int B, int h_q, int g, int s_q, int L_max_hint, int d_h) {
+  if (B < 1 || h_q < 1 || g < 1 || s_q < 1 || L_max_hint < 1 || d_h < 1 || h_q % g || (h_q / g) * s_q > 32) return 0;
+  return stream_decode_ws(B, g, (h_q / g) * s_q, L_max_hint, d_h);
+}
+
+gha_status gqla_gqa_decode(const gha_tensor* q_c, const gha_tensor* q_r, const gha_tensor* k_c,
+                           const gha_tensor* k_r, const gha_tensor* v_cache, const int32_t* seqlens_k,
+                           const gha_tensor* o, float* lse, int B, int h_q, int g, int s_q, int L_cap,
+                           int L_max_hint, int d_h, int d_r, gha_dtype in_dtype, gha_dtype out_dtype,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || h_q < 1 || g < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
+    return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (h_q % g) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of g=%d", h_q, g);
+  if (L_max_hint > L_cap || s_q > L_max_hint)
+    return fail(GHA_ERR_SHAPE, "need s_q <= L_max_hint <= L_cap (s_q=%d L_max_hint=%d L_cap=%d)", s_q, L_max_hint, L_cap);
+  const int rows = (h_q / g) * s_q;
+  if (rows > 32) return fail(GHA_ERR_SHAPE, "(h_q/g)*s_q=%d above 32 query rows per group", rows);
+  if (d_h != 128 || d_r != 64) return fail(GHA_ERR_HEAD_DIM, "need d_h == 128 and d_r == 64 (got %d, %d)", d_h, d_r);
+  if (!(scale > 0.f)) return fail(GHA_ERR_SHAPE, "scale must be given (> 0): 1/sqrt(d_h + d_r) for the expanded key");
+  if (in_dtype != GHA_BF16 || (out_dtype != GHA_BF16 && out_dtype != GHA_F32))
+    return fail(GHA_ERR_DTYPE, "GQLA decode takes bf16 inputs and bf16 or f32 outputs");
+  if (seqlens_k == nullptr) return fail(GHA_ERR_NULL, "seqlens_k is null");
+  gha_status s;
+  if ((s = check_view("q_c", q_c, in_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("q_r", q_r, in_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("k_c", k_c, in_dtype, B > 1, g > 1, true)) != GHA_OK) return s;
+  if ((s = check_view("k_r", k_r, in_dtype, B > 1, false, true)) != GHA_OK) return s;
+  if ((s = check_view("v_cache", v_cache, in_dtype, B > 1, g > 1, true)) != GHA_OK) return s;
+  if ((s = check_view("o", o, out_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  if (k_c->ss < d_h || k_r->ss < d_r || v_cache->ss < d_h)
+    return fail(GHA_ERR_STRIDE, "cache rows overlap (k_c ss=%lld, k_r ss=%lld, v ss=%lld)", (long long)k_c->ss,
+                (long long)k_r->ss, (long long)v_cache->ss);
+  if (!span_ok(L_cap, k_c->ss) || !span_ok(L_cap, k_r->ss) || !span_ok(L_cap, v_cache->ss))
+    return fail(GHA_ERR_SHAPE, "one sequence of a cache spans 2 GiB or more (L_cap=%d)", L_cap);
+  const size_t need = gqla_gqa_decode_workspace_bytes(B, h_q, g, s_q, L_max_hint, d_h);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
+  if ((s = check_device()) != GHA_OK) return s;
+
+  gha::StreamDecodeArgs a{};
+  a.q = q_c->ptr; a.q_sb = q_c->sb; a.q_sh = q_c->sh; a.q_ss = q_c->ss;
+  a.q2 = q_r->ptr; a.q2_sb = q_r->sb; a.q2_sh = q_r->sh; a.q2_ss = q_r->ss;
+  a.k = k_c->ptr; a.k_sb = k_c->sb; a.k_sh = k_c->sh; a.k_ss = k_c->ss;
+  a.k2 = k_r->ptr; a.k2_sb = k_r->sb; a.k2_ss = k_r->ss;
+  a.v = v_cache->ptr; a.v_sb = v_cache->sb; a.v_sh = v_cache->sh; a.v_ss = v_cache->ss;
+  a.seqlens = seqlens_k;
+  a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
+  a.lse = lse;
+  a.B = B; a.n_groups = g; a.qpg = h_q / g; a.s_q = s_q; a.rows = rows; a.L_cap = L_cap;
+  stream_decode_plan(B, g, L_max_hint, &a.split_len, &a.n_splits);
+  const size_t n_part = (size_t)B * g * a.n_splits * (rows <= 16 ? 16 : 32);
+  a.ws_o = reinterpret_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + n_part * (size_t)d_h;
+  a.scale = scale;
+  if ((int64_t)B * g * a.n_splits > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  return launched(gha::launch_stream_decode(a, d_h, d_r, d_h, 1, out_dtype == GHA_F32,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                  "gqla_gqa_decode");
 }
 
 size_t latent_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_hint, int r_kv) {

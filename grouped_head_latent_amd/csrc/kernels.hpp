@@ -59,6 +59,25 @@ struct LatentArgs {
   float scale;
 };
 
+// Streaming split-KV decode where a group's key is a per-group part (width
+// dk1) optionally followed by a part shared by all groups (width dk2), and
+// its value is the concatenation of nvs value heads (width dvw each).
+struct StreamDecodeArgs {
+  const void* q;  int64_t q_sb, q_sh, q_ss;    // query part 1: (B, G * qpg, s_q, dk1)
+  const void* q2; int64_t q2_sb, q2_sh, q2_ss; // query part 2: (B, G * qpg, s_q, dk2), if dk2 > 0
+  const void* k;  int64_t k_sb, k_sh, k_ss;    // per-group key cache (B, G, L_cap, dk1)
+  const void* k2; int64_t k2_sb, k2_ss;        // shared key cache (B, L_cap, dk2), if dk2 > 0
+  const void* v;  int64_t v_sb, v_sh, v_ss;    // value heads (B, G * nvs, L_cap, dvw)
+  const int32_t* seqlens;
+  void* o;        int64_t o_sb, o_sh, o_ss;    // (B, G * qpg * nvs, s_q, dvw)
+  float* lse;         // dense (B, G * qpg, s_q) or null
+  float* ws_o;        // (B * G, n_splits, rows padded to 16 or 32, nvs * dvw) partials
+  float* ws_lse;      // (B * G, n_splits, padded rows)
+  int B, n_groups, qpg, s_q, rows;  // rows = qpg * s_q query rows per group (<= 32)
+  int L_cap, split_len, n_splits;
+  float scale;
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, bool out_f32, hipStream_t st);
 bool prefill_d128_supported(const PrefillArgs& a);
 hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t st);
@@ -71,6 +90,9 @@ int gta_positions_per_wg();
 bool gta_layout_supported(const PrefillArgs& a, int d_qk, int d_v);
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, int d, bool out_f32, hipStream_t st);
+hipError_t launch_stream_decode(const StreamDecodeArgs& a, int dk1, int dk2, int dvw, int nvs, bool out_f32,
+                                hipStream_t st);
+int stream_decode_split_multiple();  // split lengths are multiples of this many keys
 hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st);
 int latent_rows_per_wg();    // query rows per work-group of the split kernel
 int latent_tile_tokens();    // tokens per tile

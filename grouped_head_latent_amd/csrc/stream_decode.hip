@@ -1,0 +1,431 @@
+// Streaming decode over contiguous caches, bf16, split-KV with a
+// log-sum-exp merge, for the decode forms that differ only in where a
+// group's key and value come from:
+//   * GTA shared-score decode ("GTA: Grouped-head latenT Attention" news
+//     article, grouped shared attention matrix): per group one query and one
+//     cached key (d_qk wide) per token, so one score vector per new token, and
+//     the cached values of the group's H heads (H x 64 wide) that all use it;
+//   * GQLA's GQA-path decode ("GQLA: Group-Query Latent Attention ...",
+//     section 1 and section 3.1, Eq. (1)): per group a cached key k^C and a
+//     cached value, plus one decoupled RoPE key k^R per token that every group
+//     shares (2 g d_h + d^R cached elements per token); each head's key is
+//     [k^C_j; k^R];
+//   * plain grouped-query decode, with no shared key part.
+//
+// Decode reads the whole cache once per step, so the kernel streams: a
+// work-group (four waves, one per SIMD) owns one (sequence, group, key split)
+// and every wave walks its own 32-key tiles of the split (tiles w, w + 4, ...).
+// A wave moves its tiles from HBM into a private LDS ring by buffer DMA
+// (buffer_load ... lds; no VGPR staging), keeps NSLOT - 1 tiles in flight
+// while it computes on the oldest, and never waits for another wave until the
+// end.  Per tile, with all query rows of the group (the query heads times the
+// s_q new tokens, padded to 16 or 32) in one wave:
+//   S^T = K Q^T from 16-byte LDS reads of the key rows (group part, then shared
+//   part), online softmax with a lazily moved running maximum, and
+//   O^T += V^T P^T with V^T fragments from transposing LDS reads; the score
+//   accumulator is the P^T operand, no data movement.
+// The waves combine through LDS at the end and write one normalised partial
+// plus its log2-sum-exp per split; a second kernel merges the splits.
+//
+// LDS rows keep their 16-byte units swizzled so that fragment reads touch
+// distinct banks: key rows of 128 B keep unit u at u ^ ((r / 2) % 8) and of
+// 256 B at u ^ (r % 16) (16 rows of one unit per read); value rows of 128 B
+// keep u at u ^ 2 ((r / 2) % 4) and of 256 B at u ^ 2 (r % 8) (a transposing
+// read takes 32 B from each of 8 consecutive rows per half-wave).
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "lds_pipe.hpp"
+
+namespace gha {
+namespace {
+
+constexpr int T = 32;      // keys per tile: one contraction step of the value MFMA
+
+template <int DK1, int DK2, int DVW, int NVS>
+struct SdLayout {
+  static constexpr int K1ROW = 2 * DK1, K2ROW = 2 * DK2, VROW = 2 * DVW;
+  static constexpr int K1B = T * K1ROW, K2B = T * K2ROW, VB = T * VROW;
+  static constexpr int SLOT = K1B + K2B + NVS * VB;            // one tile
+  // four waves per work-group when each can keep two tiles, else two
+  static constexpr int NW = 8 * SLOT <= 160 * 1024 ? 4 : 2;
+  static constexpr int NSLOT_FIT = (160 * 1024) / (NW * SLOT);
+  static constexpr int NSLOT = NSLOT_FIT > 4 ? 4 : NSLOT_FIT;  // ring slots per wave
+  static constexpr int WAVE = NSLOT * SLOT;
+  static constexpr int BYTES = NW * WAVE;
+  static constexpr int NK1 = K1B / 1024, NK2 = K2B / 1024, NV = VB / 1024;
+  static constexpr int NDMA = NK1 + NK2 + NVS * NV;            // DMA instructions per tile
+  static constexpr int DV = NVS * DVW;                         // output width of a row
+};
+
+// unit swizzles (see above)
+__device__ __forceinline__ int key_swz(int row_bytes, int r) { return row_bytes == 128 ? ((r >> 1) & 7) : (r & 15); }
+__device__ __forceinline__ int val_swz(int row_bytes, int r) { return row_bytes == 128 ? 2 * ((r >> 1) & 3) : 2 * (r & 7); }
+
+template <int DK1, int DK2, int DVW, int NVS, int QT>
+__global__ __launch_bounds__((64 * SdLayout<DK1, DK2, DVW, NVS>::NW), 1)
+void stream_decode_split_kernel(StreamDecodeArgs a) {
+  using Ly = SdLayout<DK1, DK2, DVW, NVS>;
+  constexpr int NWAVE = Ly::NW;
+  constexpr int DS1 = DK1 / 32, DS = (DK1 + DK2) / 32;  // score contraction steps
+  constexpr int NCT = DVW / 16;                         // 16-wide column tiles per value source
+  constexpr int NSLOT = Ly::NSLOT;
+  static_assert(NSLOT >= 2, "LDS ring");
+  static_assert(DK1 == 64 || DK1 == 128, "group key width");
+  static_assert(DK2 == 0 || DK2 == 64, "shared key width");
+  static_assert(DVW == 64 || DVW == 128, "value width");
+  static_assert(Ly::NDMA * (NSLOT - 1) < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Ly::BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+
+  // ---- (sequence, group, split); groups of one split are neighbours (they
+  // share the RoPE-key rows in L2) ------------------------------------------
+  const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  if (lid >= (uint32_t)(a.B * a.n_groups * a.n_splits)) return;
+  const int j = __builtin_amdgcn_readfirstlane((int)(lid % a.n_groups));
+  const int split = __builtin_amdgcn_readfirstlane((int)((lid / a.n_groups) % a.n_splits));
+  const int b = __builtin_amdgcn_readfirstlane((int)(lid / ((uint32_t)a.n_groups * a.n_splits)));
+  const int L = __builtin_amdgcn_readfirstlane(min(max(a.seqlens[b], 0), a.L_cap));
+  const int start = split * a.split_len;
+  if (start >= L) return;  // the merge reads only the splits a sequence has
+  const int end = min(L, start + a.split_len);
+  const int n_tiles = (end - start + T - 1) / T;
+  const int n_my = (n_tiles - wave + NWAVE - 1) / NWAVE;  // tiles w, w + 4, ... of the split
+
+  // ---- query rows: R = hh * s_q + t, head j * qpg + hh -----------------------
+  u32x4 qf[QT][DS];
+  int kvis[QT];  // last key each lane's row sees (bottom-right causal)
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int R = 16 * qt + li;
+    const bool ok = R < a.rows;
+    const int hh = ok ? R / a.s_q : 0, tq = ok ? R % a.s_q : 0;
+    kvis[qt] = L - a.s_q + tq;
+    const int head = j * a.qpg + hh;
+    const __bf16* qp = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)head * a.q_sh + (int64_t)tq * a.q_ss;
+#pragma unroll
+    for (int s = 0; s < DS1; ++s) qf[qt][s] = ok ? ld16(qp + 32 * s + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (DK2 > 0) {
+      const __bf16* qp2 = (const __bf16*)a.q2 + (int64_t)b * a.q2_sb + (int64_t)head * a.q2_sh + (int64_t)tq * a.q2_ss;
+#pragma unroll
+      for (int s = DS1; s < DS; ++s) qf[qt][s] = ok ? ld16(qp2 + 32 * (s - DS1) + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  wait_vmem_all();
+  const float c2 = a.scale * kLog2e;
+
+  // ---- tile DMAs into this wave's ring -------------------------------------------
+  // Each source is a buffer whose range ends at this sequence's last token:
+  // rows past it read as zeros.  One instruction moves 1 KiB: 1024 / row_bytes
+  // rows, lane l taking row l / (row_bytes / 16), unit position
+  // l % (row_bytes / 16) and fetching the global unit that belongs there.
+  const uint32_t k1row = (uint32_t)a.k_ss * 2u, k2row = (uint32_t)a.k2_ss * 2u, vrow = (uint32_t)a.v_ss * 2u;
+  const uint32_t lastk = (uint32_t)(L - 1);
+  const __amdgpu_buffer_rsrc_t k1rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)j * a.k_sh), 0,
+      (int)(lastk * k1row + (uint32_t)Ly::K1ROW), kBufferFlags);
+  __amdgpu_buffer_rsrc_t k2rs = k1rs;
+  if constexpr (DK2 > 0)
+    k2rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const __bf16*)a.k2 + (int64_t)b * a.k2_sb), 0,
+                                             (int)(lastk * k2row + (uint32_t)Ly::K2ROW), kBufferFlags);
+  __amdgpu_buffer_rsrc_t vrs[NVS];
+#pragma unroll
+  for (int vs = 0; vs < NVS; ++vs)
+    vrs[vs] = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)(j * NVS + vs) * a.v_sh), 0,
+        (int)(lastk * vrow + (uint32_t)Ly::VROW), kBufferFlags);
+  // per-lane offsets of the instructions of one tile (they repeat every tile)
+  auto lane_ofs = [&](int row_bytes, uint32_t gl_row, int n, bool is_key) -> uint32_t {
+    const int upr = row_bytes / 16, rpi = 1024 / row_bytes;
+    const int r = n * rpi + lane / upr;  // row in the tile
+    const int sw = is_key ? key_swz(row_bytes, r) : val_swz(row_bytes, r);
+    return (uint32_t)r * gl_row + 16u * (uint32_t)((lane % upr) ^ sw);
+  };
+  uint32_t k1o[Ly::NK1], k2o[Ly::NK2 > 0 ? Ly::NK2 : 1], vo[Ly::NV];
+#pragma unroll
+  for (int n = 0; n < Ly::NK1; ++n) k1o[n] = lane_ofs(Ly::K1ROW, k1row, n, true);
+#pragma unroll
+  for (int n = 0; n < Ly::NK2; ++n) k2o[n] = lane_ofs(Ly::K2ROW, k2row, n, true);
+#pragma unroll
+  for (int n = 0; n < Ly::NV; ++n) vo[n] = lane_ofs(Ly::VROW, vrow, n, false);
+  const uint32_t ring = lds_offset(smem) + wave * Ly::WAVE;
+  // tile i of this wave (global tile i * 4 + w of the split) into slot i % NSLOT;
+  // tiles past the split read out of range (zeros), keeping DMA counts uniform
+  auto issue_tile = [&](int i) __attribute__((always_inline)) {
+    const bool ok = i < n_my;
+    const uint32_t key0 = (uint32_t)(start + (i * NWAVE + wave) * T);
+    const uint32_t dst = ring + (uint32_t)(i % NSLOT) * Ly::SLOT;
+#pragma unroll
+    for (int n = 0; n < Ly::NK1; ++n)
+      lds_dma16(k1rs, dst + 1024 * n, k1o[n], ok ? key0 * k1row : kOutOfRange);
+#pragma unroll
+    for (int n = 0; n < Ly::NK2; ++n)
+      lds_dma16(k2rs, dst + Ly::K1B + 1024 * n, k2o[n], ok ? key0 * k2row : kOutOfRange);
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+      for (int n = 0; n < Ly::NV; ++n)
+        lds_dma16(vrs[vs], dst + Ly::K1B + Ly::K2B + vs * Ly::VB + 1024 * n, vo[n], ok ? key0 * vrow : kOutOfRange);
+  };
+
+  // ---- fragment addresses ----------------------------------------------------------
+  // score A operand, key row 16 kt + li, unit 4 s + lg of a part with
+  // row_bytes: (frag ^ 64 s) + 16 row_bytes kt
+  auto key_frag = [&](int row_bytes) -> uint32_t {
+    return row_bytes == 128 ? li * 128 + 16 * (lg ^ ((li >> 1) & 7)) : li * 256 + 16 * (lg ^ li);
+  };
+  const uint32_t kf1 = key_frag(Ly::K1ROW);
+  const uint32_t kf2 = DK2 > 0 ? key_frag(Ly::K2ROW) : 0u;
+  // value A operand (transposing read), source lane li of group lg: row
+  // 16 h + 4 lg + li / 4, columns 16 ct + 4 (li % 4) .. + 3:
+  // (vfrag ^ 32 ct) + 16 row_bytes h
+  uint32_t vfrag;
+  {
+    const int vr = 4 * lg + (li >> 2);
+    const uint32_t in_row = 16 * ((li >> 1) & 1) + 8 * (li & 1);
+    vfrag = Ly::VROW == 128 ? vr * 128 + 32 * ((vr >> 1) & 3) + in_row
+                            : (vr * 256 + in_row) ^ (32 * (vr & 7));
+  }
+
+  // ---- running state (per lane: one row per q-tile) ------------------------------
+  f32x4 oacc[NVS][NCT][QT], lacc[QT];
+  float m2[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m2[qt] = kNegInf;
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) oacc[vs][ct][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+
+#pragma unroll
+  for (int i = 0; i < NSLOT - 1; ++i) issue_tile(i);
+  for (int i = 0; i < n_my; ++i) {
+    issue_tile(i + NSLOT - 1);                       // into the slot of tile i - 1
+    wait_vmem_at_most<Ly::NDMA * (NSLOT - 1)>();     // tile i has landed
+    const unsigned char* sl = smem + wave * Ly::WAVE + (i % NSLOT) * Ly::SLOT;
+    const int key0 = start + (i * NWAVE + wave) * T;
+
+    // S^T = K Q^T: keys key0 + 16 kt + 4 lg + r in sacc[kt][qt][r]
+    f32x4 sacc[2][QT];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      u32x4 kf[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        if (s < DS1) kf[kt] = ld16(sl + kt * 16 * Ly::K1ROW + (kf1 ^ (64u * s)));
+        else kf[kt] = ld16(sl + Ly::K1B + kt * 16 * Ly::K2ROW + (kf2 ^ (64u * (s - DS1))));
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          sacc[kt][qt] = mfma_bf16(kf[kt], qf[qt][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kt][qt]);
+    }
+
+    // online softmax per row, running maximum moved lazily (log2 units)
+    u32x4 pf[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + 16 * kt + 4 * lg + r;
+          if (key >= end || key > kvis[qt]) sacc[kt][qt][r] = kNegInf;
+          mx = fmaxf(mx, sacc[kt][qt][r]);
+        }
+      const float mx2 = group4_max(mx) * c2;
+      if (wave_any(mx2 > m2[qt] + kRescaleSlack)) {
+        const float mnew = fmaxf(m2[qt], mx2);
+        const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2[qt] - mnew);
+        m2[qt] = mnew;
+        lacc[qt] *= alpha;
+#pragma unroll
+        for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) oacc[vs][ct][qt] *= alpha;
+      }
+      const float msub = (m2[qt] == kNegInf) ? 0.f : m2[qt];
+      float p[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[kt][r] = fast_exp2(__builtin_fmaf(sacc[kt][qt][r], c2, -msub));
+      pf[qt] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
+                     pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
+      lacc[qt] = mfma_bf16(ones, pf[qt], lacc[qt]);
+    }
+
+    // O^T += V^T P^T for every value source and column tile
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const unsigned char* vp = sl + Ly::K1B + Ly::K2B + vs * Ly::VB + (vfrag ^ (32u * ct));
+        const u32x2 h0 = ld_tr(vp);
+        const u32x2 h1 = ld_tr(vp + 16 * Ly::VROW);
+        const u32x4 vt = {h0[0], h0[1], h1[0], h1[1]};
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) oacc[vs][ct][qt] = mfma_bf16(vt, pf[qt], oacc[vs][ct][qt]);
+      }
+  }
+  // no DMA of this wave may still land in the ring, which now holds the
+  // combination buffers
+  wait_vmem_all();
+  __syncthreads();
+
+  // ---- combine the four waves: per row M = max m_w, weights 2^(m_w - M) ----------
+  constexpr int RP = 16 * QT;               // padded rows
+  constexpr int DV = Ly::DV;
+  constexpr int OP = DV + 4;                // row pitch in floats (spreads banks)
+  float* s_o = reinterpret_cast<float*>(smem);                 // [4][RP][OP]
+  float* s_m = s_o + NWAVE * RP * OP;                          // [4][RP]
+  float* s_l = s_m + NWAVE * RP;                               // [4][RP]
+  static_assert((NWAVE * RP * OP + 2 * NWAVE * RP) * 4 <= Ly::BYTES, "combine buffers");
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int row = 16 * qt + li;
+    if (lg == 0) {
+      s_m[wave * RP + row] = m2[qt];
+      s_l[wave * RP + row] = lacc[qt][0];
+    }
+    // oacc[vs][ct][qt][r] is feature vs * DVW + 16 ct + 4 lg + r of the row
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        *reinterpret_cast<f32x4*>(&s_o[(wave * RP + row) * OP + vs * DVW + 16 * ct + 4 * lg]) = oacc[vs][ct][qt];
+  }
+  __syncthreads();
+  constexpr int TPR = 64 * NWAVE / RP, FPT = DV / TPR;  // threads per row, features per thread
+  static_assert(FPT % 4 == 0, "features per thread");
+  const int row = tid / TPR, f0 = (tid % TPR) * FPT;
+  if (row >= a.rows) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[w * RP + row]);
+  float wt[NWAVE], Lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    const float mw = s_m[w * RP + row];
+    wt[w] = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+    Lsum += wt[w] * s_l[w * RP + row];
+  }
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  const int64_t unit = (int64_t)b * a.n_groups + j;
+  const int64_t pidx = (unit * a.n_splits + split) * RP + row;
+  float* wo = a.ws_o + pidx * DV + f0;
+#pragma unroll
+  for (int f = 0; f < FPT; f += 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) acc += wt[w] * *reinterpret_cast<const f32x4*>(&s_o[(w * RP + row) * OP + f0 + f]);
+    *reinterpret_cast<f32x4*>(wo + f) = acc * inv;
+  }
+  if (tid % TPR == 0) a.ws_lse[pidx] = Lsum > 0.f ? M + fast_log2(Lsum) : kNegInf;
+}
+
+// Merge the splits of one (sequence, group): split s holds its normalised
+// output O_s and log2-sum-exp l_s; the result is
+// sum_s 2^(l_s - M) O_s / sum_s 2^(l_s - M), M = max_s l_s.
+template <int DV, int DVW, int QT, bool OUT_F32>
+__global__ __launch_bounds__(256) void stream_decode_merge_kernel(StreamDecodeArgs a) {
+  constexpr int RP = 16 * QT, TPR = 256 / RP, FPT = DV / TPR;
+  const int unit = blockIdx.x;
+  const int j = unit % a.n_groups, b = unit / a.n_groups;
+  const int tid = threadIdx.x;
+  const int row = tid / TPR, f0 = (tid % TPR) * FPT;
+  if (row >= a.rows) return;
+  const int L = min(max(a.seqlens[b], 0), a.L_cap);
+  // lengths above the plan's bound are a precondition violation; never read
+  // partials the plan did not allot
+  const int ns = min((L + a.split_len - 1) / a.split_len, a.n_splits);
+  const int64_t base = (int64_t)unit * a.n_splits * RP + row;
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_lse[base + (int64_t)s * RP]);
+  float acc[FPT];
+#pragma unroll
+  for (int f = 0; f < FPT; ++f) acc[f] = 0.f;
+  float den = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float ls = a.ws_lse[base + (int64_t)s * RP];
+    const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
+    den += w;
+    const float* src = a.ws_o + (base + (int64_t)s * RP) * DV + f0;
+#pragma unroll
+    for (int f = 0; f < FPT; f += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + f);
+      acc[f] += w * x[0]; acc[f + 1] += w * x[1]; acc[f + 2] += w * x[2]; acc[f + 3] += w * x[3];
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const int hh = row / a.s_q, tq = row % a.s_q;
+  const int qhead = j * a.qpg + hh;
+#pragma unroll
+  for (int f = 0; f < FPT; f += 4) {
+    // features f0 + f .. + 3 lie in one value source (DVW is a multiple of FPT)
+    const int fe = f0 + f;
+    const int head = qhead * (DV / DVW) + fe / DVW;
+    const int64_t o = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh + (int64_t)tq * a.o_ss + fe % DVW;
+    if constexpr (OUT_F32)
+      *reinterpret_cast<f32x4*>((float*)a.o + o) = f32x4{acc[f] * inv, acc[f + 1] * inv, acc[f + 2] * inv, acc[f + 3] * inv};
+    else
+      *reinterpret_cast<u32x2*>((__bf16*)a.o + o) =
+          u32x2{pack_bf16(acc[f] * inv, acc[f + 1] * inv), pack_bf16(acc[f + 2] * inv, acc[f + 3] * inv)};
+  }
+  if (a.lse != nullptr && tid % TPR == 0)
+    a.lse[((int64_t)b * a.n_groups * a.qpg + qhead) * a.s_q + tq] = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
+}
+
+template <int DK1, int DK2, int DVW, int NVS, int QT>
+hipError_t launch_cfg(const StreamDecodeArgs& a, bool out_f32, hipStream_t st) {
+  constexpr int DV = NVS * DVW;
+  const uint32_t n = (uint32_t)a.B * a.n_groups * a.n_splits;
+  const uint32_t padded = (n + 7) / 8 * 8;
+  hipLaunchKernelGGL((stream_decode_split_kernel<DK1, DK2, DVW, NVS, QT>), dim3(padded),
+                     dim3(64 * SdLayout<DK1, DK2, DVW, NVS>::NW), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (out_f32)
+    hipLaunchKernelGGL((stream_decode_merge_kernel<DV, DVW, QT, true>), dim3(a.B * a.n_groups), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((stream_decode_merge_kernel<DV, DVW, QT, false>), dim3(a.B * a.n_groups), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DK1, int DK2, int DVW, int NVS>
+hipError_t launch_qt(const StreamDecodeArgs& a, bool out_f32, hipStream_t st) {
+  if (a.rows <= 16) return launch_cfg<DK1, DK2, DVW, NVS, 1>(a, out_f32, st);
+  if (a.rows <= 32) return launch_cfg<DK1, DK2, DVW, NVS, 2>(a, out_f32, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int stream_decode_split_multiple() { return 4 * T; }
+
+hipError_t launch_stream_decode(const StreamDecodeArgs& a, int dk1, int dk2, int dvw, int nvs, bool out_f32,
+                                hipStream_t st) {
+#define GHA_SD_CASE(K1, K2, VW, NV) \
+  if (dk1 == K1 && dk2 == K2 && dvw == VW && nvs == NV) return launch_qt<K1, K2, VW, NV>(a, out_f32, st);
+  GHA_SD_CASE(64, 0, 64, 1)
+  GHA_SD_CASE(64, 0, 64, 2)
+  GHA_SD_CASE(64, 0, 64, 4)
+  GHA_SD_CASE(128, 0, 64, 1)
+  GHA_SD_CASE(128, 0, 64, 2)
+  GHA_SD_CASE(128, 0, 64, 4)
+  GHA_SD_CASE(128, 64, 128, 1)
+  GHA_SD_CASE(128, 0, 128, 1)
+#undef GHA_SD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gha

@@ -1,7 +1,7 @@
 /* gha.h - C ABI of the grouped-head attention library for AMD Instinct MI355X
  * (gfx950).
  *
- * Four operations, all exact causal scaled dot-product attention
+ * Six operations, all exact causal scaled dot-product attention
  * o = softmax(scale * q k^T) v with fp32 accumulation, differing in which heads
  * share what:
  *
@@ -20,6 +20,14 @@
  *                             to the value of every head in the group.  ("GTA:
  *                             Grouped-head latenT Attention" news article,
  *                             grouped shared attention matrix mechanism.)
+ *   gta_shared_score_decode   the same shared score for s_q new tokens per
+ *                             sequence against a contiguous cache of one key
+ *                             per group and one value per head.
+ *   gqla_gqa_decode           the GQA path of GQLA: per group a cached key k^C
+ *                             and value, plus one RoPE key k^R per token shared
+ *                             by every group; head i of group j uses the key
+ *                             [k^C_j; k^R].  ("GQLA: Group-Query Latent
+ *                             Attention ...", section 1, section 3.1 Eq. (1).)
  *   latent_absorb_decode      the absorbed (MQA-like) path of MLA/GQLA: every
  *                             query head attends straight over the cached
  *                             latent c^KV (width r_kv) plus the shared RoPE key
@@ -136,6 +144,56 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k,
                                     int B, int h, int n_grp, int S, int d_qk, int d_v,
                                     gha_dtype in_dtype, gha_dtype out_dtype,
                                     float scale, int causal, void* stream);
+
+/* One decode step of GTA shared-score attention against a contiguous cache
+ * (GTA news article, grouped shared attention matrix; decode as in the GQLA
+ * page's section 1: each new token reads the whole cached history).
+ *   q (B, n_grp, s_q, d_qk): one query per group and new token;
+ *   k_cache (B, n_grp, L_cap, d_qk): one key per group and token;
+ *   v_cache (B, h, L_cap, d_v): one value per head; head i is in group
+ *   i / (h / n_grp) and applies its group's score vector to its own values;
+ *   seqlens_k: device int32 (B,), s_q <= seqlens_k[b] <= L_cap, counting the
+ *   new tokens (bottom-right alignment as in gqa_decode);
+ *   o (B, h, s_q, d_v); lse NULL or dense fp32 (B, n_grp, s_q), one per group.
+ * d_qk in {64, 128}, d_v == 64, h / n_grp in {1, 2, 4}, s_q <= 32; in BF16,
+ * out BF16 or F32; scale <= 0 means 1/sqrt(d_qk).  Rows of a cache must not
+ * overlap (ss >= width) and one (batch, group or head) sequence must span less
+ * than 2 GiB.  workspace: at least gta_shared_score_decode_workspace_bytes(...)
+ * bytes of device memory; its contents on entry do not matter. */
+gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cache,
+                                   const gha_tensor* v_cache, const int32_t* seqlens_k,
+                                   const gha_tensor* o, float* lse,
+                                   int B, int h, int n_grp, int s_q, int L_cap, int L_max_hint,
+                                   int d_qk, int d_v, gha_dtype in_dtype, gha_dtype out_dtype,
+                                   float scale, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+size_t gta_shared_score_decode_workspace_bytes(int B, int h, int n_grp, int s_q, int L_max_hint,
+                                               int d_v);
+
+/* One decode step of GQLA's GQA path (GQLA section 1: the per-group expanded
+ * cache of 2 g d_h + d^R elements per token; section 3.1, Eq. (1): the group
+ * key is the up-projected latent k^C concatenated with the decoupled RoPE key
+ * k^R, which all groups share).  The score of head i (group j = i / (h_q/g))
+ * with token u is scale * (q_c_i . k_c_{j,u} + q_r_i . k_r_u); its value is
+ * v_{j,u}.
+ *   q_c (B, h_q, s_q, d_h), q_r (B, h_q, s_q, d_r): the head's query parts;
+ *   k_c (B, g, L_cap, d_h), v_cache (B, g, L_cap, d_h): per group;
+ *   k_r (B, L_cap, d_r): shared (its head stride is ignored);
+ *   seqlens_k as in gqa_decode; o (B, h_q, s_q, d_h);
+ *   lse NULL or dense fp32 (B, h_q, s_q).
+ * d_h == 128, d_r == 64, (h_q / g) * s_q <= 32; in BF16, out BF16 or F32.
+ * scale must be given (> 0): 1/sqrt(d_h + d_r) is the scale of the expanded
+ * key.  Rows must not overlap and one sequence must span less than 2 GiB.
+ * workspace: at least gqla_gqa_decode_workspace_bytes(...) bytes. */
+gha_status gqla_gqa_decode(const gha_tensor* q_c, const gha_tensor* q_r, const gha_tensor* k_c,
+                           const gha_tensor* k_r, const gha_tensor* v_cache,
+                           const int32_t* seqlens_k, const gha_tensor* o, float* lse,
+                           int B, int h_q, int g, int s_q, int L_cap, int L_max_hint,
+                           int d_h, int d_r, gha_dtype in_dtype, gha_dtype out_dtype,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t gqla_gqa_decode_workspace_bytes(int B, int h_q, int g, int s_q, int L_max_hint, int d_h);
 
 /* Absorbed latent decode (GQLA section 1 and Figure 2, right: with W^UK folded
  * into the query and W^UV into the output, all h_q heads attend directly over

@@ -116,16 +116,17 @@ def normal_bf16_rows(shape, seed: int, stream: int, index, stddev: float = 1.0) 
     return normal_bf16(shape[n_lead:], seed, stream, stddev, offset=flat * inner)
 
 
-def cache_bf16(B: int, H: int, L_cap: int, d: int, seqlens, seed: int, stream: int) -> np.ndarray:
-    """A contiguous (B, H, L_cap, d) bf16 KV cache: slots [0, L_b) of sequence b
-    hold the stream's values for the full-shape tensor (so any slice can be
-    regenerated alone); every slot at or beyond L_b is NaN, so a kernel that
-    reads past a sequence's length poisons its output."""
+def cache_bf16(B: int, H: int, L_cap: int, d: int, seqlens, seed: int, stream: int,
+               stddev: float = 1.0) -> np.ndarray:
+    """A contiguous (B, H, L_cap, d) bf16 KV cache of stddev*N(0,1): slots
+    [0, L_b) of sequence b hold the stream's values for the full-shape tensor
+    (so any slice can be regenerated alone); every slot at or beyond L_b is
+    NaN, so a kernel that reads past a sequence's length poisons its output."""
     out = np.full((B, H, L_cap, d), BF16_NAN, dtype=np.uint16)
     for b in range(B):
         L = int(seqlens[b])
         for h in range(H):
-            out[b, h, :L] = normal_bf16((L, d), seed, stream, offset=((b * H + h) * L_cap) * d)
+            out[b, h, :L] = normal_bf16((L, d), seed, stream, stddev, offset=((b * H + h) * L_cap) * d)
     return out
 
 

@@ -31,6 +31,8 @@ def declared_functions():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"gqa_prefill", "gqa_decode", "gta_shared_score_prefill", "latent_absorb_decode",
+            "gta_shared_score_decode", "gqla_gqa_decode", "gta_shared_score_decode_workspace_bytes",
+            "gqla_gqa_decode_workspace_bytes",
             "gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
             "gha_status_string", "gha_last_error", "gha_version"} <= set(names)
     for n in names:
@@ -141,6 +143,56 @@ def gta(lib, **kw):
 ])
 def test_gta_rejects_bad_arguments(lib, kw, status):
     assert gta(lib, **kw) == status
+
+
+def gta_dec(lib, **kw):
+    a = dict(h=16, n_grp=4, s_q=1, L_cap=4096, L_max=4096, d_qk=64, d_v=64, seq=FAKE, ws=FAKE, ws_bytes=1 << 40,
+             k=T(), v=T())
+    a.update(kw)
+    return lib.gta_shared_score_decode(ctypes.byref(T()), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                                       ctypes.c_void_p(a["seq"]) if a["seq"] else None, ctypes.byref(T()), None,
+                                       2, a["h"], a["n_grp"], a["s_q"], a["L_cap"], a["L_max"], a["d_qk"],
+                                       a["d_v"], gha.GHA_BF16, gha.GHA_BF16, 0.0,
+                                       ctypes.c_void_p(a["ws"]) if a["ws"] else None, a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_grp=3), 3), (dict(d_v=128), 7), (dict(h=32, n_grp=4), 7), (dict(d_qk=96), 7),
+    (dict(s_q=33, L_max=64), 2), (dict(L_max=8192), 2), (dict(seq=0), 1), (dict(ws_bytes=16), 8),
+    (dict(k=T(ss=32)), 4),                  # key rows of 64 elements would overlap
+    (dict(v=T(ss=1 << 20)), 2),             # a sequence spanning 8 GiB
+])
+def test_gta_decode_rejects_bad_arguments(lib, kw, status):
+    assert gta_dec(lib, **kw) == status
+
+
+def gqla(lib, **kw):
+    a = dict(h_q=128, g=8, s_q=2, L_cap=4096, L_max=4096, d_h=128, d_r=64, scale=0.07, ws=FAKE, ws_bytes=1 << 40,
+             k_r=T(ss=64))
+    a.update(kw)
+    return lib.gqla_gqa_decode(ctypes.byref(T()), ctypes.byref(T()), ctypes.byref(T()), ctypes.byref(a["k_r"]),
+                               ctypes.byref(T()), ctypes.c_void_p(FAKE), ctypes.byref(T()), None, 2, a["h_q"],
+                               a["g"], a["s_q"], a["L_cap"], a["L_max"], a["d_h"], a["d_r"], gha.GHA_BF16,
+                               gha.GHA_BF16, a["scale"], ctypes.c_void_p(a["ws"]) if a["ws"] else None,
+                               a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=3), 3), (dict(d_h=64), 7), (dict(d_r=32), 7), (dict(scale=0.0), 2),
+    (dict(s_q=3), 2),                       # 16 heads x 3 tokens: more than 32 rows per group
+    (dict(ws=0), 8), (dict(k_r=T(ss=32)), 4),
+])
+def test_gqla_decode_rejects_bad_arguments(lib, kw, status):
+    assert gqla(lib, **kw) == status
+
+
+def test_stream_decode_workspace_sizes(lib):
+    # GTA: 64 x 4 units, 32 splits of 1024 keys, 16 padded rows of 4 x 64
+    # outputs + lse each
+    assert lib.gta_shared_score_decode_workspace_bytes(64, 16, 4, 1, 32768, 64) == 64 * 4 * 32 * 16 * 257 * 4
+    # GQLA at s_q = 2: 32 rows per group, 16 splits of 4096 keys
+    assert lib.gqla_gqa_decode_workspace_bytes(64, 128, 8, 2, 65536, 128) == 64 * 8 * 16 * 32 * 129 * 4
+    assert lib.gqla_gqa_decode_workspace_bytes(64, 128, 8, 3, 65536, 128) == 0
 
 
 def test_valid_call_without_device_reports_hip_error(lib):

@@ -221,6 +221,153 @@ def test_gqa_decode_full_size_sampled(gha_lib, s_q):
         check(f"full decode b={b} L={L}", o[b:b + 1], ref)
 
 
+# -------------------------------------------------------------- GTA decode
+
+GTA_DECODE_CASES = [
+    # B, h, n_grp, s_q, L_cap, seqlens, d_qk
+    (3, 16, 4, 1, 1100, [1, 700, 1100], 64),
+    (3, 16, 4, 2, 1100, [2, 333, 1099], 64),
+    (2, 8, 4, 1, 600, [64, 599], 64),        # two heads per group
+    (2, 4, 4, 2, 300, [5, 300], 64),         # one head per group
+    (2, 8, 2, 1, 500, [3, 480], 128),        # d_qk 128: two waves per work-group
+    (1, 16, 4, 16, 400, [390], 64),          # 16 new tokens
+    (1, 4, 4, 20, 400, [390], 64),           # 20 rows: two row tiles
+]
+
+
+@pytest.mark.parametrize("B,h,n_grp,s_q,L_cap,seqlens,d_qk", GTA_DECODE_CASES)
+def test_gta_shared_score_decode(gha_lib, B, h, n_grp, s_q, L_cap, seqlens, d_qk):
+    say(f"GTA decode B={B} h={h} groups={n_grp} s_q={s_q} L_cap={L_cap} L={seqlens} d_qk={d_qk}")
+    seqlens = np.array(seqlens, dtype=np.int32)
+    qb = gen((B, n_grp, s_q, d_qk), 22, 1)
+    kb = cache_bits(B, n_grp, L_cap, d_qk, seqlens, 22, 2)
+    vb = cache_bits(B, h, L_cap, 64, seqlens, 22, 3)
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    sl = torch.from_numpy(seqlens).cuda()
+    o32, lse = gha_lib.gta_shared_score_decode(q, k, v, sl, out_dtype=torch.float32, return_lse=True)
+    o16 = gha_lib.gta_shared_score_decode(q, k, v, sl)
+    ref, ref_lse = oracle.gta_decode(widen(qb), widen(kb), widen(vb), seqlens)
+    check("gta decode fp32", o32.cpu().numpy(), ref)
+    check("gta decode bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("gta decode lse", lse.cpu().numpy(), ref_lse)
+
+
+def test_gta_decode_single_key_returns_value(gha_lib):
+    say("GTA decode L=1")
+    B, h, n_grp = 2, 16, 4
+    qb = gen((B, n_grp, 1, 64), 23, 1)
+    kb = cache_bits(B, n_grp, 64, 64, np.array([1, 1]), 23, 2)
+    vb = cache_bits(B, h, 64, 64, np.array([1, 1]), 23, 3)
+    o = gha_lib.gta_shared_score_decode(*(bf16_to_torch(x) for x in (qb, kb, vb)),
+                                        torch.ones(B, dtype=torch.int32, device="cuda"), out_dtype=torch.float32)
+    assert np.abs(o.cpu().numpy() - widen(vb)[:, :, :1]).max() <= 1e-6
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_gta_decode_full_size_sampled(gha_lib, s_q):
+    """Batch 64, 16 heads in 4 groups, dims 64, lengths uniform in
+    [1024, 32768], capacity 32768 with NaN beyond each length."""
+    B, h, n_grp, d, L_cap = 64, 16, 4, 64, 32768
+    say(f"full-size GTA decode s_q={s_q}")
+    seqlens = synth.uniform_i32(B, 1024, 32768, 6, synth.STREAM["seqlens"])
+    qb = gen((B, n_grp, s_q, d), 6, 1)
+    kb = cache_bits(B, n_grp, L_cap, d, seqlens, 6, 2)
+    vb = cache_bits(B, h, L_cap, d, seqlens, 6, 3)
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    o = gha_lib.gta_shared_score_decode(q, k, v, torch.from_numpy(seqlens).cuda(),
+                                        out_dtype=torch.float32).cpu().numpy()
+    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 21]:
+        L = int(seqlens[b])
+        ref, _ = oracle.gta_decode(widen(qb[b:b + 1]), widen(kb[b:b + 1, :, :L]), widen(vb[b:b + 1, :, :L]),
+                                   np.array([L]))
+        check(f"full GTA decode b={b} L={L}", o[b:b + 1], ref)
+
+
+# ------------------------------------------------------ GQLA GQA-path decode
+
+GQLA_CASES = [
+    # B, h_q, g, s_q, L_cap, seqlens
+    (2, 128, 8, 1, 700, [1, 700]),
+    (2, 128, 8, 2, 600, [2, 555]),
+    (2, 32, 2, 1, 300, [17, 300]),
+    (1, 16, 1, 2, 400, [399]),
+]
+
+
+def gqla_case(B, h_q, g, s_q, L_cap, seqlens, seed, kv_std=1.0):
+    qc = gen((B, h_q, s_q, 128), seed, synth.STREAM["q_c"])
+    qr = gen((B, h_q, s_q, 64), seed, synth.STREAM["q_rope"])
+    kc = synth.cache_bf16(B, g, L_cap, 128, seqlens, seed, synth.STREAM["k"], kv_std)
+    kr = synth.cache_bf16(B, 1, L_cap, 64, seqlens, seed, synth.STREAM["k_rope"])[:, 0]
+    v = synth.cache_bf16(B, g, L_cap, 128, seqlens, seed, synth.STREAM["v"], kv_std)
+    return qc, qr, kc, kr, v
+
+
+@pytest.mark.parametrize("B,h_q,g,s_q,L_cap,seqlens", GQLA_CASES)
+def test_gqla_gqa_decode(gha_lib, B, h_q, g, s_q, L_cap, seqlens):
+    say(f"GQLA GQA-path decode B={B} h_q={h_q} g={g} s_q={s_q} L_cap={L_cap} L={seqlens}")
+    seqlens = np.array(seqlens, dtype=np.int32)
+    qc, qr, kc, kr, v = gqla_case(B, h_q, g, s_q, L_cap, seqlens, 24)
+    scale = 1 / math.sqrt(128 + 64)
+    args = [bf16_to_torch(x) for x in (qc, qr, kc, kr, v)] + [torch.from_numpy(seqlens).cuda()]
+    o32, lse = gha_lib.gqla_gqa_decode(*args, scale=scale, out_dtype=torch.float32, return_lse=True)
+    o16 = gha_lib.gqla_gqa_decode(*args, scale=scale)
+    ref, ref_lse = oracle.gqla_gqa_decode(*(widen(x) for x in (qc, qr, kc, kr, v)), seqlens, scale=scale)
+    check("gqla fp32", o32.cpu().numpy(), ref)
+    check("gqla bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("gqla lse", lse.cpu().numpy(), ref_lse)
+
+
+def test_gqla_gqa_path_matches_absorbed_path_on_gpu(gha_lib):
+    """GQLA Figure 2 end to end: the GQA path over the per-group expanded
+    cache (k^C = W^UK c, v = W^UV c, rounded to bf16) and the absorbed latent
+    path (q~ = W^UK^T q^C rounded to bf16, then W^UV o_lat on the host) agree
+    within the bf16-input tolerance."""
+    B, h_q, g, d_h, s_q, L_cap = 2, 128, 8, 128, 2, 300
+    seqlens = np.array([40, 300], dtype=np.int32)
+    say("GQLA GQA path vs absorbed path")
+    q_c, q_r, cache, w_uk, w_uv, q_lat = latent_inputs(B, s_q, h_q, L_cap, seqlens, 25, g=g)
+    c = widen(cache)
+    c = np.where(np.isnan(c), 0.0, c)
+    K, V = oracle.expand_latent(c[..., :512], c[..., 512:], w_uk, w_uv, g)
+    kc = synth.round_bf16(K[..., :d_h].astype(np.float32))
+    vb = synth.round_bf16(V.astype(np.float32))
+    kr = cache[..., 512:]
+    scale = 1 / math.sqrt(d_h + 64)
+    sl = torch.from_numpy(seqlens).cuda()
+    o_gqa = gha_lib.gqla_gqa_decode(bf16_to_torch(np.ascontiguousarray(q_c.transpose(0, 2, 1, 3))),
+                                    bf16_to_torch(np.ascontiguousarray(q_r.transpose(0, 2, 1, 3))),
+                                    bf16_to_torch(kc), bf16_to_torch(np.ascontiguousarray(kr)),
+                                    bf16_to_torch(vb), sl, scale=scale, out_dtype=torch.float32).cpu().numpy()
+    dcache = bf16_to_torch(cache)
+    o_lat = gha_lib.latent_absorb_decode(bf16_to_torch(q_lat), bf16_to_torch(q_r), dcache[..., :512],
+                                         dcache[..., 512:], sl, scale=scale, out_dtype=torch.float32)
+    O_abs = oracle.absorb_output(o_lat.cpu().numpy().astype(np.float64), w_uv, g, d_h)  # (B, s_q, h_q, d_h)
+    check("GQA path vs absorbed path", o_gqa.transpose(0, 2, 1, 3), O_abs)
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_gqla_decode_full_size_sampled(gha_lib, s_q):
+    """h_q 128 in g = 8 groups, d_h 128, RoPE 64, batch 64, lengths uniform in
+    [8192, 65536]: the per-group expanded cache of the latent workload (key
+    and value spread 0.45, that of W^UK c with W ~ N(0, 0.02))."""
+    B, h_q, g, L_cap = 64, 128, 8, 65536
+    say(f"full-size GQLA decode s_q={s_q}")
+    seqlens = synth.uniform_i32(B, 8192, 65536, 7, synth.STREAM["seqlens"])
+    qc, qr, kc, kr, v = gqla_case(B, h_q, g, s_q, L_cap, seqlens, 7, kv_std=0.45)
+    args = [bf16_to_torch(x) for x in (qc, qr, kc, kr, v)]
+    scale = 1 / math.sqrt(128 + 64)
+    o = gha_lib.gqla_gqa_decode(*args, torch.from_numpy(seqlens).cuda(), scale=scale,
+                                out_dtype=torch.float32).cpu().numpy()
+    del args
+    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 9]:
+        L = int(seqlens[b])
+        ref, _ = oracle.gqla_gqa_decode(widen(qc[b:b + 1]), widen(qr[b:b + 1]), widen(kc[b:b + 1, :, :L]),
+                                        widen(kr[b:b + 1, :L]), widen(v[b:b + 1, :, :L]), np.array([L]),
+                                        scale=scale)
+        check(f"full GQLA decode b={b} L={L}", o[b:b + 1], ref)
+
+
 # ---------------------------------------------------------------------- GTA
 
 GTA_CASES = [
