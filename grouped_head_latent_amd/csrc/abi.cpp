@@ -67,24 +67,31 @@ void gqa_decode_plan(int B, int h_kv, int n_rb, int L_max, int* split_len, int* 
 
 int gqa_row_blocks(int h_q, int h_kv, int s_q) { return ((h_q / h_kv) * s_q + 15) / 16; }
 
-// Split plan of the streaming decode: about 8192 work-groups over all
-// (sequence, group) units; splits are whole multiples of the kernel's tile
-// stride.  Padded rows per unit: 16 or 32.
-void stream_decode_plan(int B, int G, int L_max, int* split_len, int* n_splits) {
-  const int64_t units = (int64_t)B * G;
-  const int64_t m = gha::stream_decode_split_multiple();
-  const int64_t want = units >= 8192 ? 1 : (8192 + units - 1) / units;
-  int64_t sl = (L_max + want - 1) / want;
-  sl = std::max<int64_t>(m, (sl + m - 1) / m * m);
-  *split_len = (int)sl;
-  *n_splits = (int)((L_max + sl - 1) / sl);
+// Plan of the streaming decode: teams of Z work-groups, about GHA_SD_WGS
+// work-groups in all (one per CU, a single round), share all 128-key chunks
+// of all units equally; fewer teams when there are fewer chunks than that.
+// Z = 1 (units are (sequence, group)) unless the groups share a key part,
+// then Z = G (units are sequences, member j serves group j).  Partials: one
+// slot per team and per unit for each member, 16 or 32 padded rows each.
+#ifndef GHA_SD_WGS
+#define GHA_SD_WGS 256
+#endif
+int stream_decode_wgs(int B, int G, int Z, int L_max) {
+  const int64_t chunks = (int64_t)B * (G / Z) * ((L_max + gha::stream_decode_chunk() - 1) / gha::stream_decode_chunk());
+  const int64_t teams = std::max<int64_t>(1, std::min<int64_t>(GHA_SD_WGS / Z, chunks));
+  return (int)(teams * Z);
 }
-size_t stream_decode_ws(int B, int G, int rows, int L_max, int dv) {
-  int sl, ns;
-  stream_decode_plan(B, G, L_max, &sl, &ns);
+size_t stream_decode_ws(int B, int G, int Z, int rows, int L_max, int dv) {
   const size_t rp = rows <= 16 ? 16 : 32;
-  const size_t n = (size_t)B * G * ns * rp;
-  return n * (size_t)dv * 4 + n * 4;
+  const size_t n = ((size_t)stream_decode_wgs(B, G, Z, L_max) + (size_t)B * G) * rp;
+  return n * (size_t)dv * 4 + n * 4 + (size_t)(B + 1) * 4;
+}
+// workspace carve-up: partial outputs, their log2-sum-exp, the chunk prefix sums
+void stream_decode_carve(gha::StreamDecodeArgs& a, void* workspace, int dv) {
+  const size_t n = ((size_t)a.n_wg + (size_t)a.B * a.n_groups) * (a.rows <= 16 ? 16 : 32);
+  a.ws_o = reinterpret_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + n * (size_t)dv;
+  a.ws_pref = reinterpret_cast<int32_t*>(a.ws_lse + n);
 }
 // one (batch, head) sequence of a cache read through 32-bit buffer offsets
 bool span_ok(int L_cap, int64_t ss) { return ((int64_t)L_cap + 64) * ss * 2 < ((int64_t)1 << 31); }
@@ -169,7 +176,10 @@ size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_h
   int sl, ns;
   gqa_decode_plan(B, h_kv, n_rb, L_max_hint, &sl, &ns);
   const size_t rows = (size_t)B * h_kv * n_rb * ns * 16;
-  return rows * (size_t)d * 4 + rows * 4;
+  size_t need = rows * (size_t)d * 4 + rows * 4;
+  // the streaming kernel takes up to 32 query rows per group
+  if ((h_q / h_kv) * s_q <= 32) need = std::max(need, stream_decode_ws(B, h_kv, 1, (h_q / h_kv) * s_q, L_max_hint, d));
+  return need;
 }
 
 gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
@@ -197,6 +207,32 @@ gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
     return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
   if ((s = check_device()) != GHA_OK) return s;
+
+  // Up to 32 query rows per group (heads per group times new tokens) and
+  // caches the 32-bit buffer addressing covers: the streaming kernel (one
+  // pass over each group's cache with every row of the group); otherwise the
+  // register-fed kernel with 16-row blocks.
+  const int rows = (h_q / h_kv) * s_q;
+  if (rows <= 32 && k_cache->ss >= d && v_cache->ss >= d && span_ok(L_cap, k_cache->ss) &&
+      span_ok(L_cap, v_cache->ss)) {
+    gha::StreamDecodeArgs sa{};
+    sa.q = q->ptr; sa.q_sb = q->sb; sa.q_sh = q->sh; sa.q_ss = q->ss;
+    sa.k = k_cache->ptr; sa.k_sb = k_cache->sb; sa.k_sh = k_cache->sh; sa.k_ss = k_cache->ss;
+    sa.v = v_cache->ptr; sa.v_sb = v_cache->sb; sa.v_sh = v_cache->sh; sa.v_ss = v_cache->ss;
+    sa.seqlens = seqlens_k;
+    sa.o = o->ptr; sa.o_sb = o->sb; sa.o_sh = o->sh; sa.o_ss = o->ss;
+    sa.lse = lse;
+    sa.B = B; sa.n_groups = h_kv; sa.qpg = h_q / h_kv; sa.s_q = s_q; sa.rows = rows; sa.L_cap = L_cap;
+    sa.team = 1;
+    sa.n_wg = stream_decode_wgs(B, h_kv, 1, L_max_hint);
+    stream_decode_carve(sa, workspace, d);
+    sa.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+    if ((int64_t)B * ((L_cap + 127) / 128) >= (1LL << 31) || (int64_t)h_kv * 2 > (1LL << 30))
+      return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+    return launched(gha::launch_stream_decode(sa, d, 0, d, 1, out_dtype == GHA_F32,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                    "gqa_decode");
+  }
 
   gha::DecodeArgs a{};
   a.q = q->ptr; a.q_sb = q->sb; a.q_sh = q->sh; a.q_ss = q->ss;
@@ -263,7 +299,7 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
 
 size_t gta_shared_score_decode_workspace_bytes(int B, int h, int n_grp, int s_q, int L_max_hint, int d_v) {
   if (B < 1 || h < 1 || n_grp < 1 || s_q < 1 || s_q > 32 || L_max_hint < 1 || d_v < 1 || h % n_grp) return 0;
-  return stream_decode_ws(B, n_grp, s_q, L_max_hint, (h / n_grp) * d_v);
+  return stream_decode_ws(B, n_grp, 1, s_q, L_max_hint, (h / n_grp) * d_v);
 }
 
 gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
@@ -306,12 +342,11 @@ gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cach
   a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
   a.lse = lse;
   a.B = B; a.n_groups = n_grp; a.qpg = 1; a.s_q = s_q; a.rows = s_q; a.L_cap = L_cap;
-  stream_decode_plan(B, n_grp, L_max_hint, &a.split_len, &a.n_splits);
-  const size_t n_part = (size_t)B * n_grp * a.n_splits * (s_q <= 16 ? 16 : 32);
-  a.ws_o = reinterpret_cast<float*>(workspace);
-  a.ws_lse = a.ws_o + n_part * (size_t)(per * d_v);
+  a.team = 1;
+  a.n_wg = stream_decode_wgs(B, n_grp, 1, L_max_hint);
+  stream_decode_carve(a, workspace, per * d_v);
   a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d_qk);
-  if ((int64_t)B * n_grp * a.n_splits > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  if ((int64_t)B * ((L_cap + 127) / 128) >= (1LL << 31)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
   return launched(gha::launch_stream_decode(a, d_qk, 0, d_v, per, out_dtype == GHA_F32,
                                             reinterpret_cast<hipStream_t>(stream)),
                   "gta_shared_score_decode");
@@ -319,7 +354,7 @@ gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cach
 
 size_t gqla_gqa_decode_workspace_bytes(int B, int h_q, int g, int s_q, int L_max_hint, int d_h) {
   if (B < 1 || h_q < 1 || g < 1 || s_q < 1 || L_max_hint < 1 || d_h < 1 || h_q % g || (h_q / g) * s_q > 32) return 0;
-  return stream_decode_ws(B, g, (h_q / g) * s_q, L_max_hint, d_h);
+  return stream_decode_ws(B, g, g, (h_q / g) * s_q, L_max_hint, d_h);
 }
 
 gha_status gqla_gqa_decode(const gha_tensor* q_c, const gha_tensor* q_r, const gha_tensor* k_c,
@@ -367,12 +402,11 @@ gha_status gqla_gqa_decode(const gha_tensor* q_c, const gha_tensor* q_r, const g
   a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
   a.lse = lse;
   a.B = B; a.n_groups = g; a.qpg = h_q / g; a.s_q = s_q; a.rows = rows; a.L_cap = L_cap;
-  stream_decode_plan(B, g, L_max_hint, &a.split_len, &a.n_splits);
-  const size_t n_part = (size_t)B * g * a.n_splits * (rows <= 16 ? 16 : 32);
-  a.ws_o = reinterpret_cast<float*>(workspace);
-  a.ws_lse = a.ws_o + n_part * (size_t)d_h;
+  a.team = g;  // every group reads the shared RoPE key
+  a.n_wg = stream_decode_wgs(B, g, g, L_max_hint);
+  stream_decode_carve(a, workspace, d_h);
   a.scale = scale;
-  if ((int64_t)B * g * a.n_splits > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  if ((int64_t)B * ((L_cap + 127) / 128) >= (1LL << 31)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
   return launched(gha::launch_stream_decode(a, d_h, d_r, d_h, 1, out_dtype == GHA_F32,
                                             reinterpret_cast<hipStream_t>(stream)),
                   "gqla_gqa_decode");

@@ -107,6 +107,17 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
 // on vmcnt(0) every iteration, i.e. on the prefetch of the next tile too.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 // True in every lane if any lane's predicate holds (wave-uniform branch).
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 

@@ -71,10 +71,12 @@ struct StreamDecodeArgs {
   const int32_t* seqlens;
   void* o;        int64_t o_sb, o_sh, o_ss;    // (B, G * qpg * nvs, s_q, dvw)
   float* lse;         // dense (B, G * qpg, s_q) or null
-  float* ws_o;        // (B * G, n_splits, rows padded to 16 or 32, nvs * dvw) partials
-  float* ws_lse;      // (B * G, n_splits, padded rows)
+  float* ws_o;        // (n_wg + B * G slots, rows padded to 16 or 32, nvs * dvw) partials
+  float* ws_lse;      // (n_wg + B * G slots, padded rows)
+  int32_t* ws_pref;   // (B + 1) prefix sums over sequences of (G / team) * (128-key chunks)
   int B, n_groups, qpg, s_q, rows;  // rows = qpg * s_q query rows per group (<= 32)
-  int L_cap, split_len, n_splits;
+  int L_cap, n_wg;    // n_wg work-groups (teams of `team`) share all chunks equally
+  int team;           // 1, or n_groups when the groups share a key part
   float scale;
 };
 
@@ -92,7 +94,7 @@ bool gta_layout_supported(const PrefillArgs& a, int d_qk, int d_v);
 hipError_t launch_gqa_decode(const DecodeArgs& a, int d, bool out_f32, hipStream_t st);
 hipError_t launch_stream_decode(const StreamDecodeArgs& a, int dk1, int dk2, int dvw, int nvs, bool out_f32,
                                 hipStream_t st);
-int stream_decode_split_multiple();  // split lengths are multiples of this many keys
+int stream_decode_chunk();  // keys per scheduling chunk of the streaming decode
 hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st);
 int latent_rows_per_wg();    // query rows per work-group of the split kernel
 int latent_tile_tokens();    // tokens per tile

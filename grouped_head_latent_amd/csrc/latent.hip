@@ -67,16 +67,6 @@ __host__ __device__ constexpr int rope_sw(int k) { return (k >> 1) & 7; }
 __device__ __forceinline__ int latent_tiles(const LatentArgs& a, int b) {
   return b < a.B ? (min(max(a.seqlens[b], 0), a.L_cap) + T - 1) / T : 0;
 }
-// inclusive prefix sum over the lanes of a wave
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d *= 2) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
 // wait until at most one tile's DMAs (9 per wave) are in flight
 __device__ __forceinline__ void wait_vmem_but_one_tile() { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); }
 

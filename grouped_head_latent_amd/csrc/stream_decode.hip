@@ -12,9 +12,16 @@
 //     [k^C_j; k^R];
 //   * plain grouped-query decode, with no shared key part.
 //
-// Decode reads the whole cache once per step, so the kernel streams: a
-// work-group (four waves, one per SIMD) owns one (sequence, group, key split)
-// and every wave walks its own 32-key tiles of the split (tiles w, w + 4, ...).
+// Decode reads the whole cache once per step, so the kernel streams, with one
+// work-group (four waves, one per SIMD) per CU in a single round: the keys of
+// every unit are cut into 128-key chunks, all units' chunks are numbered one
+// after another, and teams of Z work-groups take equal shares of them whatever
+// the length mix.  Without a shared key part Z = 1 and a unit is one
+// (sequence, group); with one, Z = G, a unit is a sequence, and member j of a
+// team serves group j, so a team's members walk the same keys together on one
+// XCD and the shared key rows meet in its L2.  Each unit a share touches is a
+// segment with its own partial; inside a segment every wave walks its own
+// tiles (tiles w, w + 4, ...).
 // A wave moves its tiles from HBM into a private LDS ring by buffer DMA
 // (buffer_load ... lds; no VGPR staging), keeps NSLOT - 1 tiles in flight
 // while it computes on the oldest, and never waits for another wave until the
@@ -25,7 +32,8 @@
 //   O^T += V^T P^T with V^T fragments from transposing LDS reads; the score
 //   accumulator is the P^T operand, no data movement.
 // The waves combine through LDS at the end and write one normalised partial
-// plus its log2-sum-exp per split; a second kernel merges the splits.
+// plus its log2-sum-exp per segment; a second kernel merges the segments of
+// each unit.
 //
 // LDS rows keep their 16-byte units swizzled so that fragment reads touch
 // distinct banks: key rows of 128 B keep unit u at u ^ ((r / 2) % 8) and of
@@ -39,9 +47,9 @@
 namespace gha {
 namespace {
 
-constexpr int T = 32;      // keys per tile: one contraction step of the value MFMA
-
-template <int DK1, int DK2, int DVW, int NVS>
+// T keys per tile: 32 (one 16x16x32 value MFMA step) or 16 (one 16x16x16
+// step), whichever lets a wave keep more tiles in flight
+template <int DK1, int DK2, int DVW, int NVS, int T>
 struct SdLayout {
   static constexpr int K1ROW = 2 * DK1, K2ROW = 2 * DK2, VROW = 2 * DVW;
   static constexpr int K1B = T * K1ROW, K2B = T * K2ROW, VB = T * VROW;
@@ -49,7 +57,7 @@ struct SdLayout {
   // four waves per work-group when each can keep two tiles, else two
   static constexpr int NW = 8 * SLOT <= 160 * 1024 ? 4 : 2;
   static constexpr int NSLOT_FIT = (160 * 1024) / (NW * SLOT);
-  static constexpr int NSLOT = NSLOT_FIT > 4 ? 4 : NSLOT_FIT;  // ring slots per wave
+  static constexpr int NSLOT = NSLOT_FIT > 6 ? 6 : NSLOT_FIT;  // ring slots per wave
   static constexpr int WAVE = NSLOT * SLOT;
   static constexpr int BYTES = NW * WAVE;
   static constexpr int NK1 = K1B / 1024, NK2 = K2B / 1024, NV = VB / 1024;
@@ -57,15 +65,34 @@ struct SdLayout {
   static constexpr int DV = NVS * DVW;                         // output width of a row
 };
 
+constexpr int CH = 128;  // keys per scheduling chunk
+
+// chunks of sequence b (0 past the batch); lengths are clamped to [0, L_cap]
+__device__ __forceinline__ int sd_chunks(const StreamDecodeArgs& a, int b) {
+  return b < a.B ? (min(max(a.seqlens[b], 0), a.L_cap) + CH - 1) / CH : 0;
+}
+
+template <int DK1, int DK2, int DVW, int NVS>
+constexpr int sd_tile_keys() { return SdLayout<DK1, DK2, DVW, NVS, 32>::NSLOT >= 3 ? 32 : 16; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// v_mfma_f32_16x16x16_bf16: lane (i, g) supplies A[i][4g .. 4g + 3] and
+// B[4g .. 4g + 3][i], and receives D[4g + r][i] as the 16x16x32 form does
+__device__ __forceinline__ f32x4 mfma_k16(const u32x2& a, const u32x2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
 // unit swizzles (see above)
 __device__ __forceinline__ int key_swz(int row_bytes, int r) { return row_bytes == 128 ? ((r >> 1) & 7) : (r & 15); }
 __device__ __forceinline__ int val_swz(int row_bytes, int r) { return row_bytes == 128 ? 2 * ((r >> 1) & 3) : 2 * (r & 7); }
 
-template <int DK1, int DK2, int DVW, int NVS, int QT>
-__global__ __launch_bounds__((64 * SdLayout<DK1, DK2, DVW, NVS>::NW), 1)
+template <int DK1, int DK2, int DVW, int NVS, int T, int QT>
+__global__ __launch_bounds__((64 * SdLayout<DK1, DK2, DVW, NVS, T>::NW), 1)
 void stream_decode_split_kernel(StreamDecodeArgs a) {
-  using Ly = SdLayout<DK1, DK2, DVW, NVS>;
+  using Ly = SdLayout<DK1, DK2, DVW, NVS, T>;
   constexpr int NWAVE = Ly::NW;
+  constexpr int KT = T / 16;  // 16-key score tiles per tile
+  static_assert(T == 16 || T == 32, "tile keys");
   constexpr int DS1 = DK1 / 32, DS = (DK1 + DK2) / 32;  // score contraction steps
   constexpr int NCT = DVW / 16;                         // 16-wide column tiles per value source
   constexpr int NSLOT = Ly::NSLOT;
@@ -81,19 +108,53 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
 
-  // ---- (sequence, group, split); groups of one split are neighbours (they
-  // share the RoPE-key rows in L2) ------------------------------------------
-  const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  if (lid >= (uint32_t)(a.B * a.n_groups * a.n_splits)) return;
-  const int j = __builtin_amdgcn_readfirstlane((int)(lid % a.n_groups));
-  const int split = __builtin_amdgcn_readfirstlane((int)((lid / a.n_groups) % a.n_splits));
-  const int b = __builtin_amdgcn_readfirstlane((int)(lid / ((uint32_t)a.n_groups * a.n_splits)));
-  const int L = __builtin_amdgcn_readfirstlane(min(max(a.seqlens[b], 0), a.L_cap));
-  const int start = split * a.split_len;
-  if (start >= L) return;  // the merge reads only the splits a sequence has
-  const int end = min(L, start + a.split_len);
+  // ---- this team's equal share of all chunks -----------------------------------
+  // Unit (b, jb), jb < G / Z, has ceil(L_b / 128) chunks; team t (work-groups
+  // t Z .. t Z + Z - 1; member m serves group jb Z + m) takes chunks
+  // [t NT / n_teams, (t + 1) NT / n_teams) of the NT in all.
+  const int G = a.n_groups, Z = a.team, GZ = G / Z;
+  const int wid = (int)xcd_logical_id(blockIdx.x, gridDim.x);
+  if (wid >= a.n_wg) return;
+  const int n_teams = a.n_wg / Z;
+  const int team = wid / Z, m = wid % Z;
+  int NT = 0;
+  for (int c0 = 0; c0 < a.B; c0 += 64)
+    NT += __builtin_amdgcn_readlane(wave_incl_scan(sd_chunks(a, c0 + lane) * GZ), 63);
+  NT = __builtin_amdgcn_readfirstlane(NT);
+  const int lo = (int)((int64_t)team * NT / n_teams), hi = (int)((int64_t)(team + 1) * NT / n_teams);
+  // one work-group publishes the per-sequence prefix sums for the merge
+  if (wid == 0 && wave == 0) {
+    int run = 0;
+    for (int c0 = 0; c0 < a.B; c0 += 64) {
+      const int t = sd_chunks(a, c0 + lane) * GZ;
+      const int incl = wave_incl_scan(t) + run;
+      if (c0 + lane < a.B) a.ws_pref[c0 + lane] = incl - t;
+      run = __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) a.ws_pref[a.B] = run;
+  }
+  if (lo >= hi) return;
+  // first sequence whose chunks reach past lo, and the chunks before it
+  int b0 = 0, P0 = 0;
+  for (int c0 = 0;; c0 += 64) {
+    const int t = sd_chunks(a, c0 + lane) * GZ;
+    const int incl = wave_incl_scan(t) + P0;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(incl > lo);
+    if (m != 0) {
+      const int f = __builtin_ctzll(m);
+      b0 = c0 + f;
+      P0 = __builtin_amdgcn_readlane(incl - t, f);
+      break;
+    }
+    P0 = __builtin_amdgcn_readlane(incl, 63);
+  }
+  b0 = __builtin_amdgcn_readfirstlane(b0);
+  P0 = __builtin_amdgcn_readfirstlane(P0);
+
+  // ---- one segment: unit (b, j), keys [start, end), partial slot ----------------
+  auto segment = [&](int b, int j, int L, int start, int end, int slot) __attribute__((always_inline)) {
   const int n_tiles = (end - start + T - 1) / T;
-  const int n_my = (n_tiles - wave + NWAVE - 1) / NWAVE;  // tiles w, w + 4, ... of the split
+  const int n_my = (n_tiles - wave + NWAVE - 1) / NWAVE;  // tiles w, w + 4, ... of the segment
 
   // ---- query rows: R = hh * s_q + t, head j * qpg + hh -----------------------
   u32x4 qf[QT][DS];
@@ -213,29 +274,30 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
     const int key0 = start + (i * NWAVE + wave) * T;
 
     // S^T = K Q^T: keys key0 + 16 kt + 4 lg + r in sacc[kt][qt][r]
-    f32x4 sacc[2][QT];
+    f32x4 sacc[KT][QT];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      u32x4 kf[2];
+      u32x4 kf[KT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
         if (s < DS1) kf[kt] = ld16(sl + kt * 16 * Ly::K1ROW + (kf1 ^ (64u * s)));
         else kf[kt] = ld16(sl + Ly::K1B + kt * 16 * Ly::K2ROW + (kf2 ^ (64u * (s - DS1))));
       }
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
           sacc[kt][qt] = mfma_bf16(kf[kt], qf[qt][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kt][qt]);
     }
 
-    // online softmax per row, running maximum moved lazily (log2 units)
-    u32x4 pf[QT];
+    // online softmax per row, running maximum moved lazily (log2 units); the
+    // bf16 probabilities of a row are the value MFMA's P^T operand as they lie
+    std::conditional_t<T == 32, u32x4, u32x2> pf[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       float mx = kNegInf;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = key0 + 16 * kt + 4 * lg + r;
@@ -254,14 +316,19 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
           for (int ct = 0; ct < NCT; ++ct) oacc[vs][ct][qt] *= alpha;
       }
       const float msub = (m2[qt] == kNegInf) ? 0.f : m2[qt];
-      float p[2][4];
+      float p[KT][4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[kt][r] = fast_exp2(__builtin_fmaf(sacc[kt][qt][r], c2, -msub));
-      pf[qt] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
-                     pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
-      lacc[qt] = mfma_bf16(ones, pf[qt], lacc[qt]);
+      if constexpr (T == 32) {
+        pf[qt] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
+                       pack_bf16(p[KT - 1][0], p[KT - 1][1]), pack_bf16(p[KT - 1][2], p[KT - 1][3])};
+        lacc[qt] = mfma_bf16(ones, pf[qt], lacc[qt]);
+      } else {
+        pf[qt] = u32x2{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3])};
+        lacc[qt] = mfma_k16(u32x2{kBf16OnePair, kBf16OnePair}, pf[qt], lacc[qt]);
+      }
     }
 
     // O^T += V^T P^T for every value source and column tile
@@ -271,10 +338,15 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
       for (int ct = 0; ct < NCT; ++ct) {
         const unsigned char* vp = sl + Ly::K1B + Ly::K2B + vs * Ly::VB + (vfrag ^ (32u * ct));
         const u32x2 h0 = ld_tr(vp);
-        const u32x2 h1 = ld_tr(vp + 16 * Ly::VROW);
-        const u32x4 vt = {h0[0], h0[1], h1[0], h1[1]};
+        if constexpr (T == 32) {
+          const u32x2 h1 = ld_tr(vp + 16 * Ly::VROW);
+          const u32x4 vt = {h0[0], h0[1], h1[0], h1[1]};
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) oacc[vs][ct][qt] = mfma_bf16(vt, pf[qt], oacc[vs][ct][qt]);
+          for (int qt = 0; qt < QT; ++qt) oacc[vs][ct][qt] = mfma_bf16(vt, pf[qt], oacc[vs][ct][qt]);
+        } else {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) oacc[vs][ct][qt] = mfma_k16(h0, pf[qt], oacc[vs][ct][qt]);
+        }
       }
   }
   // no DMA of this wave may still land in the ring, which now holds the
@@ -308,33 +380,52 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
   constexpr int TPR = 64 * NWAVE / RP, FPT = DV / TPR;  // threads per row, features per thread
   static_assert(FPT % 4 == 0, "features per thread");
   const int row = tid / TPR, f0 = (tid % TPR) * FPT;
-  if (row >= a.rows) return;
-  float M = kNegInf;
+  if (row < a.rows) {
+    float M = kNegInf;
 #pragma unroll
-  for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[w * RP + row]);
-  float wt[NWAVE], Lsum = 0.f;
+    for (int v = 0; v < NWAVE; ++v) M = fmaxf(M, s_m[v * RP + row]);
+    float wt[NWAVE], Lsum = 0.f;
 #pragma unroll
-  for (int w = 0; w < NWAVE; ++w) {
-    const float mw = s_m[w * RP + row];
-    wt[w] = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
-    Lsum += wt[w] * s_l[w * RP + row];
+    for (int v = 0; v < NWAVE; ++v) {
+      const float mw = s_m[v * RP + row];
+      wt[v] = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+      Lsum += wt[v] * s_l[v * RP + row];
+    }
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    const int64_t pidx = (int64_t)slot * RP + row;
+    float* wo = a.ws_o + pidx * DV + f0;
+#pragma unroll
+    for (int f = 0; f < FPT; f += 4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < NWAVE; ++v) acc += wt[v] * *reinterpret_cast<const f32x4*>(&s_o[(v * RP + row) * OP + f0 + f]);
+      *reinterpret_cast<f32x4*>(wo + f) = acc * inv;
+    }
+    if (tid % TPR == 0) a.ws_lse[pidx] = Lsum > 0.f ? M + fast_log2(Lsum) : kNegInf;
   }
-  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  const int64_t unit = (int64_t)b * a.n_groups + j;
-  const int64_t pidx = (unit * a.n_splits + split) * RP + row;
-  float* wo = a.ws_o + pidx * DV + f0;
-#pragma unroll
-  for (int f = 0; f < FPT; f += 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) acc += wt[w] * *reinterpret_cast<const f32x4*>(&s_o[(w * RP + row) * OP + f0 + f]);
-    *reinterpret_cast<f32x4*>(wo + f) = acc * inv;
+  // the next segment's DMAs overwrite the combination buffers
+  __syncthreads();
+  };
+
+  // partial slot (t + b GZ + jb) Z + m: unique, since along a team's segments
+  // the unit index b GZ + jb grows and across teams t grows with it never
+  // falling
+  for (int b = b0, P = P0; b < a.B && P < hi; ++b) {
+    const int L = __builtin_amdgcn_readfirstlane(min(max(a.seqlens[b], 0), a.L_cap));
+    const int c = (L + CH - 1) / CH;
+    for (int jb = 0; jb < GZ; ++jb) {
+      const int U0 = P + jb * c;
+      const int s0 = max(lo, U0), s1 = min(hi, U0 + c);
+      if (s0 < s1)
+        segment(b, jb * Z + m, L, (s0 - U0) * CH, min(L, (s1 - U0) * CH), (team + b * GZ + jb) * Z + m);
+    }
+    P += c * GZ;
   }
-  if (tid % TPR == 0) a.ws_lse[pidx] = Lsum > 0.f ? M + fast_log2(Lsum) : kNegInf;
 }
 
-// Merge the splits of one (sequence, group): split s holds its normalised
-// output O_s and log2-sum-exp l_s; the result is
+// Merge the segments of one (sequence, group): the teams whose chunk share
+// meets the unit's chunks each left a normalised output O_s and log2-sum-exp
+// l_s in slot (t + u) Z + m; the result is
 // sum_s 2^(l_s - M) O_s / sum_s 2^(l_s - M), M = max_s l_s.
 template <int DV, int DVW, int QT, bool OUT_F32>
 __global__ __launch_bounds__(256) void stream_decode_merge_kernel(StreamDecodeArgs a) {
@@ -344,22 +435,34 @@ __global__ __launch_bounds__(256) void stream_decode_merge_kernel(StreamDecodeAr
   const int tid = threadIdx.x;
   const int row = tid / TPR, f0 = (tid % TPR) * FPT;
   if (row >= a.rows) return;
-  const int L = min(max(a.seqlens[b], 0), a.L_cap);
-  // lengths above the plan's bound are a precondition violation; never read
-  // partials the plan did not allot
-  const int ns = min((L + a.split_len - 1) / a.split_len, a.n_splits);
-  const int64_t base = (int64_t)unit * a.n_splits * RP + row;
+  const int Z = a.team, GZ = a.n_groups / Z, jb = j / Z, m = j % Z;
+  const int c = sd_chunks(a, b);
+  const int p0 = a.ws_pref[b] + jb * c, p1 = p0 + c, NT = a.ws_pref[a.B];
+  const int64_t u = (int64_t)b * GZ + jb;
+  const int64_t n = a.n_wg / Z;
+  int w_first = 0, w_last = -1;
+  if (p0 < p1) {
+    w_first = (int)(((int64_t)(p0 + 1) * n - 1) / NT);  // last w with w NT / n <= p0
+    w_last = (int)(((int64_t)p1 * n - 1) / NT);         // last w with w NT / n < p1
+  }
+  auto meets = [&](int w) {
+    const int lo = (int)(w * (int64_t)NT / n), hi = (int)((w + 1) * (int64_t)NT / n);
+    return max(lo, p0) < min(hi, p1);
+  };
   float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_lse[base + (int64_t)s * RP]);
+  for (int t = w_first; t <= w_last; ++t)
+    if (meets(t)) M = fmaxf(M, a.ws_lse[((t + u) * Z + m) * RP + row]);
   float acc[FPT];
 #pragma unroll
   for (int f = 0; f < FPT; ++f) acc[f] = 0.f;
   float den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float ls = a.ws_lse[base + (int64_t)s * RP];
+  for (int s = w_first; s <= w_last; ++s) {
+    if (!meets(s)) continue;
+    const int64_t base = ((s + u) * Z + m) * RP + row;
+    const float ls = a.ws_lse[base];
     const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
     den += w;
-    const float* src = a.ws_o + (base + (int64_t)s * RP) * DV + f0;
+    const float* src = a.ws_o + base * DV + f0;
 #pragma unroll
     for (int f = 0; f < FPT; f += 4) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(src + f);
@@ -388,10 +491,10 @@ __global__ __launch_bounds__(256) void stream_decode_merge_kernel(StreamDecodeAr
 template <int DK1, int DK2, int DVW, int NVS, int QT>
 hipError_t launch_cfg(const StreamDecodeArgs& a, bool out_f32, hipStream_t st) {
   constexpr int DV = NVS * DVW;
-  const uint32_t n = (uint32_t)a.B * a.n_groups * a.n_splits;
-  const uint32_t padded = (n + 7) / 8 * 8;
-  hipLaunchKernelGGL((stream_decode_split_kernel<DK1, DK2, DVW, NVS, QT>), dim3(padded),
-                     dim3(64 * SdLayout<DK1, DK2, DVW, NVS>::NW), 0, st, a);
+  constexpr int T = sd_tile_keys<DK1, DK2, DVW, NVS>();
+  const uint32_t padded = (uint32_t)(a.n_wg + 7) / 8 * 8;
+  hipLaunchKernelGGL((stream_decode_split_kernel<DK1, DK2, DVW, NVS, T, QT>), dim3(padded),
+                     dim3(64 * SdLayout<DK1, DK2, DVW, NVS, T>::NW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (out_f32)
@@ -410,7 +513,7 @@ hipError_t launch_qt(const StreamDecodeArgs& a, bool out_f32, hipStream_t st) {
 
 }  // namespace
 
-int stream_decode_split_multiple() { return 4 * T; }
+int stream_decode_chunk() { return CH; }
 
 hipError_t launch_stream_decode(const StreamDecodeArgs& a, int dk1, int dk2, int dvw, int nvs, bool out_f32,
                                 hipStream_t st) {

@@ -187,12 +187,16 @@ def test_gqla_decode_rejects_bad_arguments(lib, kw, status):
 
 
 def test_stream_decode_workspace_sizes(lib):
-    # GTA: 64 x 4 units, 32 splits of 1024 keys, 16 padded rows of 4 x 64
-    # outputs + lse each
-    assert lib.gta_shared_score_decode_workspace_bytes(64, 16, 4, 1, 32768, 64) == 64 * 4 * 32 * 16 * 257 * 4
-    # GQLA at s_q = 2: 32 rows per group, 16 splits of 4096 keys
-    assert lib.gqla_gqa_decode_workspace_bytes(64, 128, 8, 2, 65536, 128) == 64 * 8 * 16 * 32 * 129 * 4
+    # one partial slot per work-group (256 of them, one per CU) and per
+    # (sequence, group), padded rows of (outputs + lse), then B + 1 chunk
+    # prefix sums
+    # GTA: 64 x 4 (sequence, group) units, 16 padded rows of 4 x 64 outputs
+    assert lib.gta_shared_score_decode_workspace_bytes(64, 16, 4, 1, 32768, 64) == (256 + 256) * 16 * 257 * 4 + 65 * 4
+    # GQLA at s_q = 2: 32 teams of 8, 64 x 8 (sequence, group), 32 rows each
+    assert lib.gqla_gqa_decode_workspace_bytes(64, 128, 8, 2, 65536, 128) == (256 + 512) * 32 * 129 * 4 + 65 * 4
     assert lib.gqla_gqa_decode_workspace_bytes(64, 128, 8, 3, 65536, 128) == 0
+    # a tiny problem has no more work-groups than chunks
+    assert lib.gta_shared_score_decode_workspace_bytes(1, 4, 1, 1, 100, 64) == (1 + 1) * 16 * 257 * 4 + 2 * 4
 
 
 def test_valid_call_without_device_reports_hip_error(lib):

@@ -169,6 +169,8 @@ DECODE_CASES = [
     (2, 32, 1, 1, 300, [257, 299], 128),    # 32 rows: two row blocks
     (2, 4, 4, 1, 260, [256, 260], 128),     # MHA
     (2, 8, 2, 2, 500, [3, 480], 64),        # head dim 64
+    (2, 32, 1, 2, 300, [4, 299], 128),      # 64 rows per group: the 16-row-block kernel
+    (1, 4, 1, 8, 200, [150], 64),           # 32 rows, head dim 64
 ]
 
 
