@@ -256,7 +256,7 @@ def main():
     global SPINUP_S
     SPINUP_S = args.spinup_s
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 

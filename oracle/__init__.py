@@ -11,7 +11,7 @@ softmax and no reordering: each output row is a two-pass softmax over its
 visible keys followed by one weighted sum, evaluated with numpy matrix
 products as the only library primitive.
 
-Sources (the web pages this build works from):
+Sources (the web pages the method is taken from):
   * "Grouped Query Attention (GQA)", Ultralytics glossary, section "How GQA
     works": a group of query heads shares one key head and one value head;
     inside each head the computation is unchanged scaled dot-product attention;
@@ -30,7 +30,7 @@ Sources (the web pages this build works from):
     all h_q heads attend straight over the cached latent, and both paths give
     the same outputs.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * decode / chunked causal alignment is bottom-right: with L keys and s_q new
     queries, query t sees keys 0 .. L - s_q + t;
   * head i belongs to group floor(i / (heads per group)) (consecutive heads,
