@@ -68,26 +68,51 @@ def to_dev(bits, torch):
 
 
 SPINUP_S = 1.0  # set from --spinup-s
+# written before every timed prefill call: larger than the L2s and the MALL
+# together, so each call starts with its inputs in HBM only
+FLUSH_BYTES = 512 << 20
 
 
-def time_steps(fn, steps, warmup, torch):
+def time_steps(fn, steps, warmup, torch, flush=None):
     """Spin the GPU clocks up, warm up, then time exactly `steps` calls
     between two synchronisations with HIP events recorded on the stream the
     kernels are launched on.
+
+    With `flush` (a large device buffer) every timed call is preceded by a
+    fill of that buffer, which evicts the inputs from L2 and the MALL, and is
+    bracketed by its own pair of events; the result is the mean of those
+    per-call times (for workloads whose inputs would otherwise stay cached).
 
     The MI355X ramps its clocks over tens of milliseconds of sustained load;
     a few warmup steps of a sub-millisecond kernel leave it below its steady
     clock.  So the same call first runs untimed for SPINUP_S seconds (not
     counted in `warmup` or `steps`)."""
+    # untimed calls follow the same pattern as the timed ones (flush or not),
+    # so the clocks settle for that mix of work
+    def call(i):
+        if flush is not None:
+            flush.fill_(i & 127)
+        fn()
     t_end = time.perf_counter() + SPINUP_S
     while time.perf_counter() < t_end:
-        for _ in range(10):
-            fn()
+        for i in range(10):
+            call(i)
         torch.cuda.synchronize()
-    for _ in range(warmup):
-        fn()
+    for i in range(warmup):
+        call(i)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
+    if flush is not None:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            flush.fill_(i & 127)
+            evs[i][0].record(st)
+            fn()
+            evs[i][1].record(st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return sum(a.elapsed_time(b) for a, b in evs) / steps, wall
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(st)
@@ -108,7 +133,9 @@ def bench_prefill(gha, torch, steps, warmup):
     k = to_dev(synth.normal_bf16((B, h_kv, S, d), c["seed"], 2), torch)
     v = to_dev(synth.normal_bf16((B, h_kv, S, d), c["seed"], 3), torch)
     o = torch.empty((B, h_q, S, d), dtype=torch.bfloat16, device="cuda")
-    ms, wall = time_steps(lambda: gha.gqa_prefill(q, k, v, causal=True, out=o), steps, warmup, torch)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    ms, wall = time_steps(lambda: gha.gqa_prefill(q, k, v, causal=True, out=o), steps, warmup, torch, flush)
+    del flush
     flops = acc.gqa_prefill_flops(B, h_q, S, S, d)
     return dict(ms=ms, wall=wall, flops=flops, tflops=flops / ms / 1e9,
                 bytes=acc.gqa_prefill_bytes(B, h_q, h_kv, S, S, d))
@@ -140,7 +167,9 @@ def bench_gta(gha, torch, steps, warmup):
     k = to_dev(synth.normal_bf16((B, g, S, d), c["seed"], 2), torch)
     v = to_dev(synth.normal_bf16((B, h, S, d), c["seed"], 3), torch)
     o = torch.empty((B, h, S, d), dtype=torch.bfloat16, device="cuda")
-    ms, wall = time_steps(lambda: gha.gta_shared_score_prefill(q, k, v, out=o), steps, warmup, torch)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    ms, wall = time_steps(lambda: gha.gta_shared_score_prefill(q, k, v, out=o), steps, warmup, torch, flush)
+    del flush
     fl = acc.gta_prefill_flops(B, h, g, S, d, d)
     return dict(ms=ms, tflops=fl / ms / 1e9, flops=fl)
 
