@@ -65,14 +65,15 @@ def widen_bf16(bits: np.ndarray) -> np.ndarray:
 
 
 def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
-                      n_visible: np.ndarray, scale: float):
+                      n_visible: np.ndarray, scale: float, first_visible=None):
     """The definition of scaled dot-product attention for a set of query rows
     that share one key/value head ("How GQA works": unchanged scaled
     dot-product attention inside each head).
 
     q: (n, dk) query rows; k: (m, dk); v: (m, dv); n_visible: (n,) integers,
-    row r attends to keys 0 .. n_visible[r]-1 (the causal mask; n_visible = m
-    means no mask).  Returns o (n, dv) and lse (n,) = log sum_u exp(s_u) in
+    row r attends to keys first_visible[r] .. n_visible[r]-1 (the causal mask;
+    n_visible = m means no mask; first_visible defaults to 0, a sliding window
+    raises it).  Returns o (n, dv) and lse (n,) = log sum_u exp(s_u) in
     natural-log units of the scaled scores.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -80,14 +81,17 @@ def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     v = np.asarray(v, dtype=np.float64)
     n_visible = np.asarray(n_visible, dtype=np.int64)
     n, m = q.shape[0], k.shape[0]
+    first = np.zeros(n, dtype=np.int64) if first_visible is None else np.asarray(first_visible, dtype=np.int64)
     if n == 0:
         return np.zeros((0, v.shape[1])), np.zeros((0,))
-    if np.any(n_visible < 1) or np.any(n_visible > m):
+    if np.any(n_visible < 1) or np.any(n_visible > m) or np.any(first < 0) or np.any(first >= n_visible):
         raise ValueError("every query row must see between 1 and m keys")
     # step 1: scores s_u = scale * q . k_u
     s = scale * (q @ k.T)
-    # causal mask: keys at or beyond n_visible[r] take no weight
-    visible = np.arange(m)[None, :] < n_visible[:, None]
+    # causal mask: keys at or beyond n_visible[r] take no weight, nor (with a
+    # sliding window) keys before first_visible[r]
+    u = np.arange(m)[None, :]
+    visible = (u < n_visible[:, None]) & (u >= first[:, None])
     s = np.where(visible, s, -np.inf)
     # step 2: softmax, two passes (max, then exponentials and their sum)
     mx = np.max(s, axis=1, keepdims=True)
@@ -136,13 +140,18 @@ def gqa_prefill(q, k, v, *, causal: bool = True, scale: float | None = None,
 
 
 def gqa_decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
-               heads=None):
+               heads=None, window: int = 0):
     """Decode step of grouped-query attention over a contiguous KV cache.
 
     q: (B, h_q, s_q, d); k_cache, v_cache: (B, h_kv, L_cap, d); seqlens: (B,)
     with s_q <= L_b <= L_cap.  The cache of sequence b holds L_b tokens, the
     last s_q of which are the new queries' own keys, so query t sees keys
     0 .. L_b - s_q + t.  Slots at or beyond L_b are never read.
+
+    window > 0 is a sliding window ("GQA vs related techniques" names it as a
+    complement to GQA; its extent is a reading): query t then sees only the
+    last `window` of those keys, L_b - s_q + t - window + 1 .. L_b - s_q + t
+    (its own key included).
     """
     B, h_q, s_q, d = q.shape
     h_kv = k_cache.shape[1]
@@ -157,8 +166,9 @@ def gqa_decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
             raise ValueError("need s_q <= L_b <= L_cap")
         j = _group_of(i, h_q, h_kv)
         nvis = np.arange(s_q) + (L - s_q) + 1
+        first = np.maximum(nvis - window, 0) if window > 0 else None
         o[b, i], lse[b, i] = softmax_attention(q[b, i], k_cache[b, j, :L],
-                                               v_cache[b, j, :L], nvis, scale)
+                                               v_cache[b, j, :L], nvis, scale, first)
     return o, lse
 
 

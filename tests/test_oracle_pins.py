@@ -26,12 +26,15 @@ def rnd(shape, seed, stream, std=1.0):
 
 # ---------------------------------------------------------------- brute force
 
-def brute_attention(q, k, v, scale, causal_offset=None):
+def brute_attention(q, k, v, scale, causal_offset=None, window=0):
     """Pure-Python loops: q (n, d), k (m, d), v (m, dv) nested lists.  Row t
-    sees keys u <= t + causal_offset (None: all keys)."""
+    sees keys u <= t + causal_offset (None: all keys), and with window > 0
+    only the last `window` of them."""
     out, lses = [], []
     for t, qt in enumerate(q):
         keys = range(len(k)) if causal_offset is None else range(min(len(k), t + causal_offset + 1))
+        if window > 0:
+            keys = keys[max(0, len(keys) - window):]
         scores = []
         for u in keys:
             acc = 0.0
@@ -82,6 +85,51 @@ def test_decode_matches_brute_force():
                                      1 / math.sqrt(d), causal_offset=L - s_q)
             np.testing.assert_allclose(o[b, i], bo, atol=1e-13, rtol=0)
             np.testing.assert_allclose(lse[b, i], bl, atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("window", [1, 2, 3])
+def test_windowed_decode_matches_brute_force(window):
+    B, h_q, h_kv, s_q, d, L_cap = 2, 4, 2, 2, 3, 6
+    q = rnd((B, h_q, s_q, d), 14, 1)
+    kc = rnd((B, h_kv, L_cap, d), 14, 2)
+    vc = rnd((B, h_kv, L_cap, d), 14, 3)
+    seqlens = np.array([2, 6])
+    o, lse = oracle.gqa_decode(q, kc, vc, seqlens, window=window)
+    for b in range(B):
+        L = seqlens[b]
+        for i in range(h_q):
+            j = i // 2
+            bo, bl = brute_attention(q[b, i].tolist(), kc[b, j, :L].tolist(), vc[b, j, :L].tolist(),
+                                     1 / math.sqrt(d), causal_offset=L - s_q, window=window)
+            np.testing.assert_allclose(o[b, i], bo, atol=1e-13, rtol=0)
+            np.testing.assert_allclose(lse[b, i], bl, atol=1e-13, rtol=0)
+
+
+def test_windowed_decode_equals_decode_of_the_window():
+    """A one-query decode with window W sees exactly the last W cached keys:
+    it equals a plain decode over the cache cut to those keys; a window at
+    least as long as the sequence changes nothing; window 1 returns the
+    query's own value."""
+    B, h_q, h_kv, d, L_cap, W = 3, 4, 2, 8, 40, 13
+    q = rnd((B, h_q, 1, d), 15, 1)
+    kc, vc = rnd((B, h_kv, L_cap, d), 15, 2), rnd((B, h_kv, L_cap, d), 15, 3)
+    seqlens = np.array([40, 13, 5])
+    o_w, l_w = oracle.gqa_decode(q, kc, vc, seqlens, window=W)
+    for b in range(B):
+        L = int(seqlens[b])
+        lo = max(0, L - W)
+        o_c, l_c = oracle.gqa_decode(q[b:b + 1], kc[b:b + 1, :, lo:L], vc[b:b + 1, :, lo:L], np.array([L - lo]))
+        np.testing.assert_allclose(o_w[b], o_c[0], atol=1e-14)
+        np.testing.assert_allclose(l_w[b], l_c[0], atol=1e-14)
+    o_all, l_all = oracle.gqa_decode(q, kc, vc, seqlens)
+    o_big, l_big = oracle.gqa_decode(q, kc, vc, seqlens, window=L_cap)
+    np.testing.assert_array_equal(o_all, o_big)
+    np.testing.assert_array_equal(l_all, l_big)
+    o_1, _ = oracle.gqa_decode(q, kc, vc, seqlens, window=1)
+    for b in range(B):
+        L = int(seqlens[b])
+        for i in range(h_q):
+            np.testing.assert_array_equal(o_1[b, i, 0], vc[b, i // 2, L - 1])
 
 
 def test_latent_matches_brute_force():
