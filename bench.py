@@ -37,6 +37,9 @@ GTA = dict(B=8, h=16, n_grp=4, S=2048, d=64, seed=4)
 LATENT = dict(B=64, h_q=128, r_kv=512, d_r=64, L_lo=8192, L_hi=65536, seed=5, d_h=128)
 # decode forms built on the same shapes: GTA's groups at the GQA decode lengths,
 # and GQLA's per-group expanded cache (g = 8) at the latent decode lengths
+# the decode workload's cache scattered over a shuffled pool of 128-token pages,
+# and the same with a 4096-key sliding window
+PAGED = dict(page=128, window=4096, seed=8)
 GTA_DECODE = dict(B=64, h=16, n_grp=4, d=64, L_lo=1024, L_hi=32768, seed=6)
 GQLA_DECODE = dict(B=64, h_q=128, g=8, d_h=128, d_r=64, L_lo=8192, L_hi=65536, seed=7, kv_std=0.45)
 
@@ -160,6 +163,40 @@ def bench_decode(gha, torch, steps, warmup, s_q):
                 sum_L=int(seqlens.sum()))
 
 
+def bench_decode_paged(gha, torch, steps, warmup, s_q, window):
+    c, pc = DECODE, PAGED
+    B, h_q, h_kv, d = c["B"], c["h_q"], c["h_kv"], c["d"]
+    L_cap, page = c["L_hi"], pc["page"]
+    seqlens = synth.uniform_i32(B, c["L_lo"], c["L_hi"], c["seed"], synth.STREAM["seqlens"])
+    n_pps = L_cap // page
+    perm = torch.from_numpy(np.random.default_rng(pc["seed"]).permutation(B * n_pps)).cuda()
+    table = torch.empty(B * n_pps, dtype=torch.int32, device="cuda")
+    table[perm] = torch.arange(B * n_pps, dtype=torch.int32, device="cuda")
+    pools = []
+    for stream in (2, 3):
+        # page i of sequence b goes to pool page table[b * n_pps + i]
+        x = to_dev(synth.cache_bf16(B, h_kv, L_cap, d, seqlens, c["seed"], stream), torch)
+        src = x.view(B, h_kv, n_pps, page, d).permute(0, 2, 1, 3, 4).reshape(B * n_pps, h_kv, page, d)
+        del x
+        pool = torch.empty_like(src)
+        pool[table.long()] = src
+        del src
+        pools.append(pool)
+    table = table.view(B, n_pps)
+    q = to_dev(synth.normal_bf16((B, h_q, s_q, d), c["seed"], 1), torch)
+    sl = torch.from_numpy(seqlens).cuda()
+    o = torch.empty((B, h_q, s_q, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gha.gqa_decode_paged_workspace_bytes(B, h_q, h_kv, s_q, L_cap, window, d),
+                     dtype=torch.uint8, device="cuda")
+    ms, wall = time_steps(lambda: gha.gqa_decode_paged(q, pools[0], pools[1], sl, block_table=table, page_size=page,
+                                                       window=window, out=o, workspace=ws), steps, warmup, torch)
+    by = acc.gqa_decode_bytes(seqlens, h_q, h_kv, s_q, d, window=window)
+    fl = acc.gqa_decode_flops(seqlens, h_q, s_q, d, window=window)
+    del pools
+    return dict(ms=ms, gbps=by / ms / 1e6, tflops=fl / ms / 1e9, bytes=by, flops=fl,
+                keys=acc.windowed_keys(seqlens, s_q, window), page=page, window=window)
+
+
 def bench_gta(gha, torch, steps, warmup):
     c = GTA
     B, h, g, S, d = c["B"], c["h"], c["n_grp"], c["S"], c["d"]
@@ -278,7 +315,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None,
-                    help="prefill|decode|gta|latent|gta_decode|gqla_decode: time one workload")
+                    help="prefill|decode|paged|gta|latent|gta_decode|gqla_decode: time one workload")
     ap.add_argument("--spinup-s", type=float, default=1.0,
                     help="untimed seconds of the same workload before the warmup steps (clock ramp)")
     args = ap.parse_args()
@@ -313,6 +350,13 @@ def main():
                 log(f"decode s_q={s_q} ...")
                 extras[f"gqa_decode_sq{s_q}"] = bench_decode(gha, torch, args.steps, args.warmup, s_q)
                 log(extras[f"gqa_decode_sq{s_q}"])
+                torch.cuda.empty_cache()
+        if only in (None, "paged"):
+            for s_q, window in ((1, 0), (2, 0), (1, PAGED["window"])):
+                name = f"gqa_decode_paged{PAGED['page']}" + (f"_window{window}" if window else "") + f"_sq{s_q}"
+                log(f"{name} ...")
+                extras[name] = bench_decode_paged(gha, torch, args.steps, args.warmup, s_q, window)
+                log(extras[name])
                 torch.cuda.empty_cache()
         if only in (None, "latent"):
             for s_q in (1, 2):

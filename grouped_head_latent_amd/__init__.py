@@ -20,9 +20,9 @@ import math
 import os
 
 __all__ = [
-    "gqa_prefill", "gqa_decode", "gta_shared_score_prefill", "gta_shared_score_decode",
+    "gqa_prefill", "gqa_decode", "gqa_decode_paged", "gta_shared_score_prefill", "gta_shared_score_decode",
     "gqla_gqa_decode", "latent_absorb_decode",
-    "gqa_decode_workspace_bytes", "gta_shared_score_decode_workspace_bytes",
+    "gqa_decode_workspace_bytes", "gqa_decode_paged_workspace_bytes", "gta_shared_score_decode_workspace_bytes",
     "gqla_gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
     "GhaError", "library_path", "load_library", "GHA_F32", "GHA_BF16",
 ]
@@ -71,6 +71,10 @@ def load_library():
     lib.gqa_decode.restype = I
     lib.gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.gqa_decode_workspace_bytes.restype = S
+    lib.gqa_decode_paged.argtypes = [P, P, P, V, I, I, V, P, V, I, I, I, I, I, I, I, I, I, I, F, V, S, V]
+    lib.gqa_decode_paged.restype = I
+    lib.gqa_decode_paged_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.gqa_decode_paged_workspace_bytes.restype = S
     lib.gta_shared_score_prefill.argtypes = [P, P, P, P, V, I, I, I, I, I, I, I, I, F, I, V]
     lib.gta_shared_score_prefill.restype = I
     lib.gta_shared_score_decode.argtypes = [P, P, P, V, P, V, I, I, I, I, I, I, I, I, I, I, F, V, S, V]
@@ -181,6 +185,50 @@ def gqa_decode(q, k_cache, v_cache, seqlens, *, L_max: int | None = None,
                           _ptr(lse), B, h_q, h_kv, s_q, L_cap, L_max, d, _dtype_code(q),
                           _out_code(o.dtype), float(scale or 0.0), _ptr(ws), ws.numel() * ws.element_size(),
                           _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def gqa_decode_paged_workspace_bytes(B, h_q, h_kv, s_q, L_max, window, d) -> int:
+    return int(load_library().gqa_decode_paged_workspace_bytes(B, h_q, h_kv, s_q, L_max, window, d))
+
+
+def gqa_decode_paged(q, k_cache, v_cache, seqlens, *, block_table=None, page_size: int = 0,
+                     L_cap: int | None = None, L_max: int | None = None, window: int = 0,
+                     scale: float | None = None, out=None, out_dtype=None, workspace=None,
+                     return_lse: bool = False, stream=None):
+    """q (B, h_q, s_q, d); seqlens int32 device (B,).
+    block_table None: caches (B, h_kv, L_cap, d).  Otherwise block_table int32
+    device (B, pages per sequence) and caches are page pools viewed as
+    (n_pages, h_kv, page_size, d).  window > 0: sliding window of that many
+    keys.  L_cap: longest sequence the cache holds (default: the cache's
+    length, or pages per sequence times page_size); L_max: an upper bound on
+    the lengths (default L_cap)."""
+    import torch
+    lib = load_library()
+    B, h_q, s_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    if block_table is None:
+        bt_stride, page_size = 0, 0
+        L_cap = k_cache.shape[2] if L_cap is None else int(L_cap)
+    else:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise TypeError("block_table must be an int32 (B, pages) tensor with contiguous rows")
+        page_size = int(page_size or k_cache.shape[2])
+        bt_stride = block_table.stride(0)
+        L_cap = block_table.shape[1] * page_size if L_cap is None else int(L_cap)
+    L_max = L_cap if L_max is None else int(L_max)
+    out_dtype = out_dtype or torch.bfloat16
+    o = out if out is not None else torch.empty((B, h_q, s_q, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=q.device) if return_lse else None
+    need = gqa_decode_paged_workspace_bytes(B, h_q, h_kv, s_q, L_max, int(window), d)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    _check(lib.gqa_decode_paged(_desc(q), _desc(k_cache), _desc(v_cache), _ptr(block_table), bt_stride,
+                                page_size, _ptr(seqlens), _desc(o), _ptr(lse), B, h_q, h_kv, s_q, L_cap,
+                                L_max, int(window), d, _dtype_code(q), _out_code(o.dtype),
+                                float(scale or 0.0), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)))
     return (o, lse) if return_lse else o
 
 

@@ -98,15 +98,32 @@ def decode_pairs(seqlens, s_q: int) -> int:
     return int(np.sum(s_q * L - s_q * (s_q - 1) // 2))
 
 
+def windowed_keys(seqlens, s_q: int, window: int) -> int:
+    """Cached keys some new query sees: all L_b, or with a sliding window the
+    last window + s_q - 1 of them."""
+    L = np.asarray(seqlens, dtype=np.int64)
+    return int(np.sum(L if window <= 0 else np.minimum(L, window + s_q - 1)))
+
+
+def windowed_pairs(seqlens, s_q: int, window: int) -> int:
+    """Visible (query, key) pairs of a decode step: query t of sequence b sees
+    L_b - s_q + t + 1 keys, at most `window` of them with a sliding window."""
+    if window <= 0:
+        return decode_pairs(seqlens, s_q)
+    L = np.asarray(seqlens, dtype=np.int64)
+    t = np.arange(s_q, dtype=np.int64)
+    return int(np.sum(np.minimum(L[:, None] - s_q + t[None, :] + 1, window)))
+
+
 def gqa_decode_bytes(seqlens, h_q, h_kv, s_q, d, in_bytes=BF16_BYTES,
-                     out_bytes=BF16_BYTES) -> float:
-    L = int(np.sum(np.asarray(seqlens, dtype=np.int64)))
+                     out_bytes=BF16_BYTES, window: int = 0) -> float:
+    L = windowed_keys(seqlens, s_q, window)
     B = len(seqlens)
     return float(L * h_kv * 2 * d * in_bytes + B * h_q * s_q * d * (in_bytes + out_bytes))
 
 
-def gqa_decode_flops(seqlens, h_q, s_q, d) -> float:
-    return 2.0 * h_q * decode_pairs(seqlens, s_q) * (d + d)
+def gqa_decode_flops(seqlens, h_q, s_q, d, window: int = 0) -> float:
+    return 2.0 * h_q * windowed_pairs(seqlens, s_q, window) * (d + d)
 
 
 def latent_decode_bytes(seqlens, h_q, s_q, r_kv, d_r, in_bytes=BF16_BYTES,

@@ -255,6 +255,86 @@ gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_
                   "gqa_decode");
 }
 
+// Keys a windowed sequence can touch, for the streaming plan: the window,
+// the new tokens and up to two chunks of alignment.
+int window_keys(int L_max_hint, int s_q, int window) {
+  if (window <= 0) return L_max_hint;
+  const int64_t k = (int64_t)window + s_q + 2 * gha::stream_decode_chunk();
+  return (int)std::min<int64_t>(L_max_hint, k);
+}
+
+size_t gqa_decode_paged_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint, int window, int d) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_max_hint < 1 || window < 0 || h_q % h_kv || d < 1) return 0;
+  if ((h_q / h_kv) * s_q > 32) return 0;
+  return stream_decode_ws(B, h_kv, 1, (h_q / h_kv) * s_q, window_keys(L_max_hint, s_q, window), d);
+}
+
+gha_status gqa_decode_paged(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
+                            const int32_t* block_table, int bt_stride, int page_size,
+                            const int32_t* seqlens_k, const gha_tensor* o, float* lse, int B, int h_q,
+                            int h_kv, int s_q, int L_cap, int L_max_hint, int window, int d,
+                            gha_dtype in_dtype, gha_dtype out_dtype, float scale, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
+    return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (h_q % h_kv) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
+  if (L_max_hint > L_cap || s_q > L_max_hint)
+    return fail(GHA_ERR_SHAPE, "need s_q <= L_max_hint <= L_cap (s_q=%d L_max_hint=%d L_cap=%d)", s_q, L_max_hint, L_cap);
+  if (window < 0) return fail(GHA_ERR_SHAPE, "window must be >= 0 (0: no window), got %d", window);
+  if ((h_q / h_kv) * s_q > 32)
+    return fail(GHA_ERR_SHAPE, "at most 32 query rows per KV head ((h_q / h_kv) * s_q = %d)", (h_q / h_kv) * s_q);
+  if (d != 64 && d != 128) return fail(GHA_ERR_HEAD_DIM, "head dim %d not in {64, 128}", d);
+  if (in_dtype != GHA_BF16 || (out_dtype != GHA_BF16 && out_dtype != GHA_F32))
+    return fail(GHA_ERR_DTYPE, "decode takes bf16 inputs and bf16 or f32 outputs");
+  if (seqlens_k == nullptr) return fail(GHA_ERR_NULL, "seqlens_k is null");
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (page_size < 32 || page_size % 32 != 0)
+      return fail(GHA_ERR_SHAPE, "page_size must be a positive multiple of 32 (got %d)", page_size);
+    if (bt_stride < 1 || (int64_t)bt_stride * page_size < L_cap)
+      return fail(GHA_ERR_SHAPE, "block table rows of %d pages of %d tokens do not cover L_cap=%d", bt_stride, page_size, L_cap);
+  }
+  gha_status s;
+  if ((s = check_view("q", q, in_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("k_cache", k_cache, in_dtype, true, h_kv > 1, true)) != GHA_OK) return s;
+  if ((s = check_view("v_cache", v_cache, in_dtype, true, h_kv > 1, true)) != GHA_OK) return s;
+  if ((s = check_view("o", o, out_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  if (k_cache->ss < d || v_cache->ss < d) return fail(GHA_ERR_STRIDE, "cache rows overlap (token stride < d)");
+  const int span_rows = paged ? page_size : L_cap;
+  if (!span_ok(span_rows, k_cache->ss) || !span_ok(span_rows, v_cache->ss))
+    return fail(GHA_ERR_STRIDE, "one %s spans 2 GiB or more", paged ? "page" : "sequence");
+  const int rows = (h_q / h_kv) * s_q;
+  const int L_plan = window_keys(L_max_hint, s_q, window);
+  const size_t need = stream_decode_ws(B, h_kv, 1, rows, L_plan, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
+  if ((int64_t)B * ((L_cap + 127) / 128) >= (1LL << 31))
+    return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  if ((s = check_device()) != GHA_OK) return s;
+
+  gha::StreamDecodeArgs sa{};
+  sa.q = q->ptr; sa.q_sb = q->sb; sa.q_sh = q->sh; sa.q_ss = q->ss;
+  sa.k = k_cache->ptr; sa.k_sb = k_cache->sb; sa.k_sh = k_cache->sh; sa.k_ss = k_cache->ss;
+  sa.v = v_cache->ptr; sa.v_sb = v_cache->sb; sa.v_sh = v_cache->sh; sa.v_ss = v_cache->ss;
+  sa.seqlens = seqlens_k;
+  sa.o = o->ptr; sa.o_sb = o->sb; sa.o_sh = o->sh; sa.o_ss = o->ss;
+  sa.lse = lse;
+  sa.B = B; sa.n_groups = h_kv; sa.qpg = h_q / h_kv; sa.s_q = s_q; sa.rows = rows; sa.L_cap = L_cap;
+  sa.team = 1;
+  sa.n_wg = stream_decode_wgs(B, h_kv, 1, L_plan);
+  stream_decode_carve(sa, workspace, d);
+  sa.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+  sa.window = window;
+  sa.block_table = block_table;
+  sa.bt_stride = paged ? bt_stride : 0;
+  sa.page_size = paged ? page_size : 0;
+  return launched(gha::launch_stream_decode(sa, d, 0, d, 1, out_dtype == GHA_F32,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                  "gqa_decode_paged");
+}
+
 gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, const gha_tensor* v,
                                     const gha_tensor* o, float* lse, int B, int h, int n_grp, int S,
                                     int d_qk, int d_v, gha_dtype in_dtype, gha_dtype out_dtype,

@@ -78,6 +78,15 @@ struct StreamDecodeArgs {
   int L_cap, n_wg;    // n_wg work-groups (teams of `team`) share all chunks equally
   int team;           // 1, or n_groups when the groups share a key part
   float scale;
+  // sliding window: with window > 0 query t of sequence b sees only keys
+  // L_b - s_q + t - window + 1 .. L_b - s_q + t
+  int window;
+  // paged cache (one key part, one value source): block_table != null means
+  // k and v are pages, indexed (page, group, token in page) by the k_sb / v_sb,
+  // k_sh / v_sh, k_ss / v_ss strides; key u of sequence b sits in page
+  // block_table[b * bt_stride + u / page_size] at token u % page_size
+  const int32_t* block_table;
+  int bt_stride, page_size;
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, bool out_f32, hipStream_t st);

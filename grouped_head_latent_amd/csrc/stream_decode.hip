@@ -67,9 +67,17 @@ struct SdLayout {
 
 constexpr int CH = 128;  // keys per scheduling chunk
 
+// first key any query row of a length-L sequence sees (sliding window), and
+// the chunk-aligned key the chunks of that sequence start from
+__device__ __forceinline__ int sd_first_key(const StreamDecodeArgs& a, int L) {
+  return a.window > 0 ? max(0, L - a.s_q + 1 - a.window) : 0;
+}
+__device__ __forceinline__ int sd_chunk0(const StreamDecodeArgs& a, int L) { return sd_first_key(a, L) / CH * CH; }
 // chunks of sequence b (0 past the batch); lengths are clamped to [0, L_cap]
 __device__ __forceinline__ int sd_chunks(const StreamDecodeArgs& a, int b) {
-  return b < a.B ? (min(max(a.seqlens[b], 0), a.L_cap) + CH - 1) / CH : 0;
+  if (b >= a.B) return 0;
+  const int L = min(max(a.seqlens[b], 0), a.L_cap);
+  return (L - sd_chunk0(a, L) + CH - 1) / CH;
 }
 
 template <int DK1, int DK2, int DVW, int NVS>
@@ -80,6 +88,16 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // B[4g .. 4g + 3][i], and receives D[4g + r][i] as the 16x16x32 form does
 __device__ __forceinline__ f32x4 mfma_k16(const u32x2& a, const u32x2& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// One int32 through the scalar cache, waited for in the same asm block.  A
+// plain load of the block table becomes a vector load here (the compiler
+// cannot prove the table unwritten), and waiting for it would wait for every
+// tile DMA in flight.
+__device__ __forceinline__ int scalar_load_i32(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
 }
 
 // unit swizzles (see above)
@@ -158,13 +176,14 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
 
   // ---- query rows: R = hh * s_q + t, head j * qpg + hh -----------------------
   u32x4 qf[QT][DS];
-  int kvis[QT];  // last key each lane's row sees (bottom-right causal)
+  int kvis[QT], kmin[QT];  // last and first key each lane's row sees (bottom-right causal, window)
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int R = 16 * qt + li;
     const bool ok = R < a.rows;
     const int hh = ok ? R / a.s_q : 0, tq = ok ? R % a.s_q : 0;
     kvis[qt] = L - a.s_q + tq;
+    kmin[qt] = a.window > 0 ? kvis[qt] - a.window + 1 : 0;
     const int head = j * a.qpg + hh;
     const __bf16* qp = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)head * a.q_sh + (int64_t)tq * a.q_ss;
 #pragma unroll
@@ -213,23 +232,52 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
 #pragma unroll
   for (int n = 0; n < Ly::NV; ++n) vo[n] = lane_ofs(Ly::VROW, vrow, n, false);
   const uint32_t ring = lds_offset(smem) + wave * Ly::WAVE;
+  const int klo = sd_first_key(a, L);
   // tile i of this wave (global tile i * 4 + w of the split) into slot i % NSLOT;
-  // tiles past the split read out of range (zeros), keeping DMA counts uniform
+  // tiles past the split or wholly before the window read out of range
+  // (zeros), keeping DMA counts uniform
   auto issue_tile = [&](int i) __attribute__((always_inline)) {
-    const bool ok = i < n_my;
-    const uint32_t key0 = (uint32_t)(start + (i * NWAVE + wave) * T);
+    const int key0 = start + (i * NWAVE + wave) * T;
+    const bool ok = i < n_my && key0 + T > klo;
     const uint32_t dst = ring + (uint32_t)(i % NSLOT) * Ly::SLOT;
+    if constexpr (DK2 == 0 && NVS == 1) {
+      if (a.block_table != nullptr) {
+        // the tile lies in one page (page_size is a multiple of 32 and tiles
+        // start at multiples of T); each tile gets buffers whose range ends at
+        // the page's last token of the sequence
+        int pidx = 0, rows = 0, u = 0;
+        if (ok) {
+          const int pg = key0 / a.page_size;
+          pidx = scalar_load_i32(a.block_table + __builtin_amdgcn_readfirstlane(b * a.bt_stride + pg));
+          rows = min(a.page_size, L - pg * a.page_size);
+          u = key0 - pg * a.page_size;
+        }
+        const __amdgpu_buffer_rsrc_t kp = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const __bf16*)a.k + (int64_t)pidx * a.k_sb + (int64_t)j * a.k_sh), 0,
+            rows > 0 ? (int)((uint32_t)(rows - 1) * k1row + (uint32_t)Ly::K1ROW) : 0, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t vp = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const __bf16*)a.v + (int64_t)pidx * a.v_sb + (int64_t)j * a.v_sh), 0,
+            rows > 0 ? (int)((uint32_t)(rows - 1) * vrow + (uint32_t)Ly::VROW) : 0, kBufferFlags);
+#pragma unroll
+        for (int n = 0; n < Ly::NK1; ++n)
+          lds_dma16(kp, dst + 1024 * n, k1o[n], ok ? (uint32_t)u * k1row : kOutOfRange);
+#pragma unroll
+        for (int n = 0; n < Ly::NV; ++n)
+          lds_dma16(vp, dst + Ly::K1B + 1024 * n, vo[n], ok ? (uint32_t)u * vrow : kOutOfRange);
+        return;
+      }
+    }
 #pragma unroll
     for (int n = 0; n < Ly::NK1; ++n)
-      lds_dma16(k1rs, dst + 1024 * n, k1o[n], ok ? key0 * k1row : kOutOfRange);
+      lds_dma16(k1rs, dst + 1024 * n, k1o[n], ok ? (uint32_t)key0 * k1row : kOutOfRange);
 #pragma unroll
     for (int n = 0; n < Ly::NK2; ++n)
-      lds_dma16(k2rs, dst + Ly::K1B + 1024 * n, k2o[n], ok ? key0 * k2row : kOutOfRange);
+      lds_dma16(k2rs, dst + Ly::K1B + 1024 * n, k2o[n], ok ? (uint32_t)key0 * k2row : kOutOfRange);
 #pragma unroll
     for (int vs = 0; vs < NVS; ++vs)
 #pragma unroll
       for (int n = 0; n < Ly::NV; ++n)
-        lds_dma16(vrs[vs], dst + Ly::K1B + Ly::K2B + vs * Ly::VB + 1024 * n, vo[n], ok ? key0 * vrow : kOutOfRange);
+        lds_dma16(vrs[vs], dst + Ly::K1B + Ly::K2B + vs * Ly::VB + 1024 * n, vo[n], ok ? (uint32_t)key0 * vrow : kOutOfRange);
   };
 
   // ---- fragment addresses ----------------------------------------------------------
@@ -301,7 +349,7 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = key0 + 16 * kt + 4 * lg + r;
-          if (key >= end || key > kvis[qt]) sacc[kt][qt][r] = kNegInf;
+          if (key >= end || key > kvis[qt] || key < kmin[qt]) sacc[kt][qt][r] = kNegInf;
           mx = fmaxf(mx, sacc[kt][qt][r]);
         }
       const float mx2 = group4_max(mx) * c2;
@@ -412,12 +460,13 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
   // falling
   for (int b = b0, P = P0; b < a.B && P < hi; ++b) {
     const int L = __builtin_amdgcn_readfirstlane(min(max(a.seqlens[b], 0), a.L_cap));
-    const int c = (L + CH - 1) / CH;
+    const int kc = sd_chunk0(a, L);
+    const int c = (L - kc + CH - 1) / CH;
     for (int jb = 0; jb < GZ; ++jb) {
       const int U0 = P + jb * c;
       const int s0 = max(lo, U0), s1 = min(hi, U0 + c);
       if (s0 < s1)
-        segment(b, jb * Z + m, L, (s0 - U0) * CH, min(L, (s1 - U0) * CH), (team + b * GZ + jb) * Z + m);
+        segment(b, jb * Z + m, L, kc + (s0 - U0) * CH, min(L, kc + (s1 - U0) * CH), (team + b * GZ + jb) * Z + m);
     }
     P += c * GZ;
   }

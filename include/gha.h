@@ -130,6 +130,39 @@ gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache,
 
 size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint, int d);
 
+/* One decode step of grouped-query attention against a paged KV cache, a
+ * sliding window, or both (GQA page, "GQA vs related techniques": paged
+ * attention allocates the cache in fixed-size blocks, and a sliding window
+ * bounds the tokens each query attends to; the GQLA page's section 2 names
+ * paged caches as complementary to the cache layout).
+ *   block_table NULL: k_cache, v_cache are contiguous (B, h_kv, L_cap, d) as
+ *   for gqa_decode, and bt_stride, page_size are ignored.
+ *   block_table non-NULL: device int32 (B, bt_stride); key u of sequence b
+ *   lives in page block_table[b * bt_stride + u / page_size] at token
+ *   u % page_size; k_cache, v_cache describe the page pool with (sb, sh, ss)
+ *   = (page, KV head, token in page) strides, e.g. (n_pages, h_kv,
+ *   page_size, d) or (n_pages, page_size, h_kv, d) views.  page_size is a
+ *   positive multiple of 32 and bt_stride * page_size >= L_cap.  Only the
+ *   entries of pages holding keys some query sees are read; they must be
+ *   valid page indices.
+ *   window: 0 for none; else query t of sequence b sees only keys
+ *   L_b - s_q + t - window + 1 .. L_b - s_q + t (its own key and the
+ *   window - 1 before it).
+ *   seqlens_k, q, o, lse, L_cap, L_max_hint, scale as in gqa_decode;
+ *   (h_q / h_kv) * s_q <= 32; d in {64, 128}; in BF16, out BF16 or F32.
+ * One page (or, unpaged, one sequence) of a cache must span less than 2 GiB.
+ * workspace: at least gqa_decode_paged_workspace_bytes(...) bytes. */
+gha_status gqa_decode_paged(const gha_tensor* q, const gha_tensor* k_cache,
+                            const gha_tensor* v_cache, const int32_t* block_table,
+                            int bt_stride, int page_size, const int32_t* seqlens_k,
+                            const gha_tensor* o, float* lse,
+                            int B, int h_q, int h_kv, int s_q, int L_cap, int L_max_hint,
+                            int window, int d, gha_dtype in_dtype, gha_dtype out_dtype,
+                            float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t gqa_decode_paged_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint,
+                                        int window, int d);
+
 /* GTA shared-score attention (GTA news article, grouped shared attention
  * matrix: a group computes its attention scores once and every head of the
  * group uses that same matrix).

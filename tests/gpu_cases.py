@@ -38,3 +38,38 @@ def tolerance_ok(got: np.ndarray, ref: np.ndarray, max_abs=1e-2, mean_abs=1e-3, 
     else:
         ok_max = bool(err.max(initial=0.0) <= max_abs)
     return ok_max and err.mean() <= mean_abs, float(err.max(initial=0.0)), float(err.mean())
+
+
+BF16_NAN = 0x7FC0
+
+
+def page_pool(cache: np.ndarray, seqlens, page_size: int, seed: int, *, window: int = 0, s_q: int = 1,
+              tokens_major: bool = False):
+    """Scatter a contiguous cache (B, H, L_cap, d) of bf16 bits into a shuffled
+    pool of pages.  Returns (pool, block_table): pool is (n_pages, H,
+    page_size, d), or (n_pages, page_size, H, d) with tokens_major; row b of
+    block_table (B, ceil(L_cap / page_size)) lists the pages of sequence b.
+    Page 0 of the pool is all NaN, and every table entry no query may read
+    (pages past the sequence end, and with a sliding window pages wholly
+    before the earliest visible key) points at it: a kernel that read such a
+    page would return NaN."""
+    B, H, L_cap, d = cache.shape
+    n_pps = (L_cap + page_size - 1) // page_size
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(B * n_pps) + 1            # page 0 is the NaN page
+    pool = np.full((B * n_pps + 1, H, page_size, d), BF16_NAN, dtype=np.uint16)
+    table = np.zeros((B, n_pps), dtype=np.int32)
+    padded = np.full((B, H, n_pps * page_size, d), BF16_NAN, dtype=np.uint16)
+    padded[:, :, :L_cap] = cache
+    for b in range(B):
+        L = int(seqlens[b])
+        first = max(0, L - s_q + 1 - window) if window > 0 else 0
+        for p in range(n_pps):
+            if p * page_size >= L or (p + 1) * page_size <= first:
+                continue
+            dst = order[b * n_pps + p]
+            table[b, p] = dst
+            pool[dst] = padded[b, :, p * page_size:(p + 1) * page_size]
+    if tokens_major:
+        pool = np.ascontiguousarray(pool.transpose(0, 2, 1, 3))
+    return pool, table

@@ -34,6 +34,7 @@ def test_exports_every_declared_function(lib):
             "gta_shared_score_decode", "gqla_gqa_decode", "gta_shared_score_decode_workspace_bytes",
             "gqla_gqa_decode_workspace_bytes",
             "gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
+            "gqa_decode_paged", "gqa_decode_paged_workspace_bytes",
             "gha_status_string", "gha_last_error", "gha_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -95,6 +96,54 @@ def decode(lib, **kw):
 ])
 def test_decode_rejects_bad_arguments(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def paged(lib, **kw):
+    a = dict(q=T(), k=T(sb=1 << 16, sh=1 << 13), v=T(sb=1 << 16, sh=1 << 13), bt=FAKE, bt_stride=64,
+             page=64, seq=FAKE, o=T(), B=2, h_q=32, h_kv=8, s_q=1, L_cap=4096, L_max=4096, window=0,
+             d=128, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.gqa_decode_paged(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                                ctypes.c_void_p(a["bt"]) if a["bt"] else None, a["bt_stride"], a["page"],
+                                ctypes.c_void_p(a["seq"]) if a["seq"] else None, ctypes.byref(a["o"]), None,
+                                a["B"], a["h_q"], a["h_kv"], a["s_q"], a["L_cap"], a["L_max"], a["window"],
+                                a["d"], gha.GHA_BF16, gha.GHA_BF16, 0.0,
+                                ctypes.c_void_p(a["ws"]) if a["ws"] else None, a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h_kv=5), 3),
+    (dict(page=48), 2),                     # not a multiple of 32
+    (dict(page=0), 2),
+    (dict(bt_stride=63), 2),                # 63 pages of 64 tokens do not cover 4096
+    (dict(window=-1), 2),
+    (dict(s_q=2), 2),
+    (dict(h_q=64, s_q=5), 2),               # 8 heads x 5 tokens = 40 rows > 32
+    (dict(seq=0), 1),
+    (dict(ws=0), 8),
+    (dict(ws_bytes=16), 8),
+    (dict(d=256), 7),
+    (dict(k=T(sb=1 << 16, sh=1 << 13, ss=64)), 4),   # rows overlap (token stride < d)
+    (dict(v=T(sb=(1 << 16) + 4)), 5),                 # page stride not a multiple of 16 bytes
+])
+def test_paged_decode_rejects_bad_arguments(lib, kw, status):
+    if kw == dict(s_q=2):
+        # 32 query heads over 8 KV heads at s_q = 2 is 8 rows per group: accepted
+        # by validation, so it reaches the device check (no GPU here) instead
+        assert paged(lib, **kw) in (0, 9)
+        return
+    assert paged(lib, **kw) == status
+    assert len(lib.gha_last_error()) > 0
+
+
+def test_paged_decode_workspace_follows_the_window(lib):
+    # one slot per work-group (256) and per (sequence, KV head), 16 padded rows
+    full = lib.gqa_decode_paged_workspace_bytes(64, 32, 8, 1, 32768, 0, 128)
+    assert full == (256 + 64 * 8) * 16 * 129 * 4 + 65 * 4
+    # a short window has fewer chunks: fewer work-groups are planned
+    short = lib.gqa_decode_paged_workspace_bytes(1, 4, 1, 1, 32768, 100, 128)
+    assert short == (3 + 1) * 16 * 129 * 4 + 2 * 4
+    assert lib.gqa_decode_paged_workspace_bytes(64, 40, 8, 8, 32768, 0, 128) == 0
 
 
 def test_workspace_sizes_cover_the_split_plan(lib):

@@ -59,3 +59,20 @@ def test_config_work_figures():
     assert abs(acc.gqa_prefill_flops(4, 32, 4096, 4096, 128) - 5.4993e11) / 5.4993e11 < 1e-4
     # GTA prefill at batch 8, 4 groups of 4 heads, seq 2048, dims 64
     assert abs(acc.gta_prefill_flops(8, 16, 4, 2048, 64, 64) - 4.2971e10) / 4.2971e10 < 1e-4
+
+
+def test_windowed_counts_by_enumeration():
+    seqlens, s_q = [1, 5, 9, 40], 3
+    seqlens_ok = [max(L, s_q) for L in seqlens]
+    for W in (0, 1, 2, 4, 7, 100):
+        keys, pairs = 0, 0
+        for L in seqlens_ok:
+            seen = set()
+            for t in range(s_q):
+                last = L - s_q + t
+                vis = [u for u in range(last + 1) if W <= 0 or u > last - W]
+                pairs += len(vis)
+                seen.update(vis)
+            keys += len(seen)
+        assert acc.windowed_keys(seqlens_ok, s_q, W) == keys
+        assert acc.windowed_pairs(seqlens_ok, s_q, W) == pairs

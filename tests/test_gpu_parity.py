@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_cases import (bf16_to_torch, cache_bits, latent_cache_bits, tolerance_ok,
+from tests.gpu_cases import (bf16_to_torch, cache_bits, latent_cache_bits, page_pool, tolerance_ok,
                              widen)
 
 pytestmark = pytest.mark.gpu
@@ -221,6 +221,84 @@ def test_gqa_decode_full_size_sampled(gha_lib, s_q):
         ref, _ = oracle.gqa_decode(widen(qb[b:b + 1]), widen(k_ref)[None], widen(v_ref)[None],
                                    np.array([L]))
         check(f"full decode b={b} L={L}", o[b:b + 1], ref)
+
+
+# ------------------------------------------------ paged and windowed decode
+
+PAGED_CASES = [
+    # B, h_q, h_kv, s_q, L_cap, seqlens, d, page_size (0: contiguous), window, tokens-major pool
+    (3, 32, 8, 1, 1100, [1, 700, 1100], 128, 64, 0, False),
+    (3, 32, 8, 2, 1100, [2, 333, 1099], 128, 32, 0, True),
+    (2, 8, 2, 2, 600, [64, 599], 64, 128, 0, False),
+    (3, 32, 8, 1, 1100, [1, 700, 1100], 128, 0, 100, False),
+    (3, 32, 8, 2, 1100, [2, 333, 1099], 128, 64, 257, False),
+    (2, 4, 1, 8, 800, [8, 790], 64, 256, 1, True),       # window 1: each row sees its own key
+    (2, 16, 2, 4, 2000, [1500, 2000], 128, 32, 1000, False),  # 32 rows per group
+    (2, 32, 8, 1, 500, [100, 500], 128, 0, 5000, False),  # window longer than every sequence
+    (2, 8, 8, 3, 700, [3, 650], 64, 96, 130, True),       # MHA, page of 96 tokens
+]
+
+
+@pytest.mark.parametrize("B,h_q,h_kv,s_q,L_cap,seqlens,d,page,window,tmajor", PAGED_CASES)
+def test_gqa_decode_paged(gha_lib, B, h_q, h_kv, s_q, L_cap, seqlens, d, page, window, tmajor):
+    say(f"paged decode B={B} h={h_q}/{h_kv} s_q={s_q} L_cap={L_cap} L={seqlens} d={d} "
+        f"page={page} window={window} tokens_major={tmajor}")
+    seqlens = np.array(seqlens, dtype=np.int32)
+    qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, 21)
+    q = bf16_to_torch(qb)
+    sl = torch.from_numpy(seqlens).cuda()
+    if page:
+        kp, table = page_pool(kb, seqlens, page, 5, window=window, s_q=s_q, tokens_major=tmajor)
+        vp, table_v = page_pool(vb, seqlens, page, 5, window=window, s_q=s_q, tokens_major=tmajor)
+        assert np.array_equal(table, table_v)
+        k, v = bf16_to_torch(kp), bf16_to_torch(vp)
+        if tmajor:
+            k, v = k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3)
+        bt = torch.from_numpy(table).cuda()
+        kw = dict(block_table=bt, page_size=page, L_cap=L_cap)
+    else:
+        k, v = bf16_to_torch(kb), bf16_to_torch(vb)
+        kw = {}
+    o32, lse = gha_lib.gqa_decode_paged(q, k, v, sl, window=window, out_dtype=torch.float32,
+                                        return_lse=True, **kw)
+    o16 = gha_lib.gqa_decode_paged(q, k, v, sl, window=window, **kw)
+    ref, ref_lse = oracle.gqa_decode(widen(qb), widen(kb), widen(vb), seqlens, window=window)
+    check("paged decode fp32", o32.cpu().numpy(), ref)
+    check("paged decode bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("paged decode lse", lse.cpu().numpy(), ref_lse)
+
+
+@pytest.mark.parametrize("page,window", [(128, 0), (256, 4096)])
+def test_gqa_decode_paged_full_size_sampled(gha_lib, page, window):
+    """The decode workload (batch 64, 32/8 heads, head dim 128, lengths uniform
+    in [1024, 32768]) with its cache scattered over a shuffled page pool."""
+    B, h_q, h_kv, d, L_cap, s_q = 64, 32, 8, 128, 32768, 1
+    say(f"full-size paged decode page={page} window={window}")
+    seqlens = synth.uniform_i32(B, 1024, 32768, 3, synth.STREAM["seqlens"])
+    qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, 3)
+    q = bf16_to_torch(qb)
+    n_pps = L_cap // page
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(B * n_pps)).cuda()
+    table = torch.empty(B * n_pps, dtype=torch.int32, device="cuda")
+    table[perm] = torch.arange(B * n_pps, dtype=torch.int32, device="cuda")
+    pools = []
+    for x in (kb, vb):
+        # page i of sequence b (pool row b * n_pps + i) goes to pool row table[b, i]
+        src = bf16_to_torch(x).view(B, h_kv, n_pps, page, d).permute(0, 2, 1, 3, 4).reshape(B * n_pps, h_kv, page, d)
+        pool = torch.empty_like(src)
+        pool[table.long()] = src
+        pools.append(pool)
+        del src
+    o = gha_lib.gqa_decode_paged(q, pools[0], pools[1], torch.from_numpy(seqlens).cuda(),
+                                 block_table=table.view(B, n_pps), page_size=page, window=window,
+                                 out_dtype=torch.float32).cpu().numpy()
+    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 17, 40]:
+        L = int(seqlens[b])
+        k_ref = np.stack([synth.normal_bf16((L, d), 3, 2, offset=((b * h_kv + j) * L_cap) * d) for j in range(h_kv)])
+        v_ref = np.stack([synth.normal_bf16((L, d), 3, 3, offset=((b * h_kv + j) * L_cap) * d) for j in range(h_kv)])
+        ref, _ = oracle.gqa_decode(widen(qb[b:b + 1]), widen(k_ref)[None], widen(v_ref)[None],
+                                   np.array([L]), window=window)
+        check(f"full paged decode b={b} L={L}", o[b:b + 1], ref)
 
 
 # -------------------------------------------------------------- GTA decode
