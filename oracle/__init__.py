@@ -52,7 +52,7 @@ import numpy as np
 
 __all__ = [
     "widen_bf16", "softmax_attention", "gqa_prefill", "gqa_decode",
-    "gta_prefill", "gta_decode", "latent_absorb_decode", "gqla_gqa_decode",
+    "gta_prefill", "gta_decode", "latent_absorb_decode", "gqla_gqa_decode", "gqla_gqa_prefill",
     "absorb_query", "absorb_output", "expand_latent",
 ]
 
@@ -258,6 +258,37 @@ def gqla_gqa_decode(q_c, q_r, k_c, k_r, v_cache, seqlens, *, scale: float,
         kj = np.concatenate([k_c[b, j, :L], k_r[b, :L]], axis=1)
         nvis = np.arange(s_q) + (L - s_q) + 1
         o[b, i], lse[b, i] = softmax_attention(qi, kj, v_cache[b, j, :L], nvis, scale)
+    return o, lse
+
+
+def gqla_gqa_prefill(q_c, q_r, k_c, k_r, v, *, scale: float, causal: bool = True,
+                     heads=None):
+    """GQLA's GQA path over a whole sequence, the compute-friendly form for
+    prefill (section 1; Eq. (1) of section 3.1 expands the latent into per-
+    group keys and values, with one decoupled RoPE key shared by the groups).
+    Head i of group j = g(i) attends with query [q^C_i; q^R_i] over keys
+    [k^C_j; k^R] (width d_h + d^R) and values v_j.
+
+    q_c: (B, h_q, S_q, d_h); q_r: (B, h_q, S_q, d_r); k_c: (B, g, S_k, d_h);
+    k_r: (B, S_k, d_r); v: (B, g, S_k, d_v).  Causal alignment is bottom-right
+    (query t sees keys 0 .. S_k - S_q + t).  Returns o (B, h_q, S_q, d_v) and
+    lse (B, h_q, S_q).
+    """
+    B, h_q, S_q, _ = q_c.shape
+    g, S_k = k_c.shape[1], k_c.shape[2]
+    if h_q % g:
+        raise ValueError("h_q must be a multiple of g")
+    if causal and S_q > S_k:
+        raise ValueError("causal needs S_q <= S_k")
+    o = np.full((B, h_q, S_q, v.shape[3]), np.nan)
+    lse = np.full((B, h_q, S_q), np.nan)
+    nvis = np.arange(S_q) + (S_k - S_q) + 1 if causal else np.full(S_q, S_k)
+    pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h_q)]
+    for b, i in pairs:
+        j = _group_of(i, h_q, g)
+        qi = np.concatenate([q_c[b, i], q_r[b, i]], axis=1)
+        kj = np.concatenate([k_c[b, j], k_r[b]], axis=1)
+        o[b, i], lse[b, i] = softmax_attention(qi, kj, v[b, j], nvis, scale)
     return o, lse
 
 

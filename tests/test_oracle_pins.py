@@ -424,6 +424,37 @@ def test_gqla_gqa_path_equals_absorbed_latent_path():
     np.testing.assert_allclose(lse_gqa.transpose(0, 2, 1), lse_lat, rtol=0, atol=1e-12)
 
 
+def test_gqla_gqa_prefill_matches_brute_force():
+    B, h_q, g, S, dh, dr = 1, 4, 2, 4, 3, 2
+    qc, qr = rnd((B, h_q, S, dh), 31, 1), rnd((B, h_q, S, dr), 31, 2)
+    kc, kr, v = rnd((B, g, S, dh), 31, 3), rnd((B, S, dr), 31, 4), rnd((B, g, S, dh), 31, 5)
+    scale = 0.37
+    for causal in (True, False):
+        o, lse = oracle.gqla_gqa_prefill(qc, qr, kc, kr, v, scale=scale, causal=causal)
+        for i in range(h_q):
+            j = i // 2
+            for t in range(S):
+                keys = range(t + 1) if causal else range(S)
+                # the score written out: group key part plus shared RoPE part
+                sc = [scale * (sum(qc[0, i, t, x] * kc[0, j, u, x] for x in range(dh))
+                               + sum(qr[0, i, t, x] * kr[0, u, x] for x in range(dr))) for u in keys]
+                mx = max(sc)
+                w = [math.exp(z - mx) for z in sc]
+                row = [sum(w[n] / sum(w) * v[0, j, u, x] for n, u in enumerate(keys)) for x in range(dh)]
+                np.testing.assert_allclose(o[0, i, t], row, atol=1e-13, rtol=0)
+                assert abs(lse[0, i, t] - (mx + math.log(sum(w)))) < 1e-13
+
+
+def test_gqla_gqa_decode_is_last_rows_of_gqla_prefill():
+    B, h_q, g, L, dh, dr, s_q = 2, 8, 2, 29, 16, 8, 3
+    qc, qr = rnd((B, h_q, L, dh), 32, 1), rnd((B, h_q, L, dr), 32, 2)
+    kc, kr, v = rnd((B, g, L, dh), 32, 3), rnd((B, L, dr), 32, 4), rnd((B, g, L, dh), 32, 5)
+    o_p, l_p = oracle.gqla_gqa_prefill(qc, qr, kc, kr, v, scale=0.2)
+    o_d, l_d = oracle.gqla_gqa_decode(qc[:, :, L - s_q:], qr[:, :, L - s_q:], kc, kr, v, np.array([L, L]), scale=0.2)
+    np.testing.assert_allclose(o_d, o_p[:, :, L - s_q:], atol=1e-14)
+    np.testing.assert_allclose(l_d, l_p[:, :, L - s_q:], atol=1e-14)
+
+
 def test_gta_decode_is_last_rows_of_gta_prefill():
     """Bottom-right alignment: decoding the last s_q tokens of a sequence gives
     the last s_q rows of the causal shared-score prefill."""
