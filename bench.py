@@ -41,6 +41,7 @@ LATENT = dict(B=64, h_q=128, r_kv=512, d_r=64, L_lo=8192, L_hi=65536, seed=5, d_
 # and the same with a 4096-key sliding window
 PAGED = dict(page=128, window=4096, seed=8)
 GTA_DECODE = dict(B=64, h=16, n_grp=4, d=64, L_lo=1024, L_hi=32768, seed=6)
+GQLA_PREFILL = dict(B=2, h_q=128, g=8, S=4096, d_h=128, d_r=64, seed=10, kv_std=0.45)
 GQLA_DECODE = dict(B=64, h_q=128, g=8, d_h=128, d_r=64, L_lo=8192, L_hi=65536, seed=7, kv_std=0.45)
 
 
@@ -197,6 +198,24 @@ def bench_decode_paged(gha, torch, steps, warmup, s_q, window):
                 keys=acc.windowed_keys(seqlens, s_q, window), page=page, window=window)
 
 
+def bench_gqla_prefill(gha, torch, steps, warmup):
+    c = GQLA_PREFILL
+    B, h_q, g, S, dh, dr = c["B"], c["h_q"], c["g"], c["S"], c["d_h"], c["d_r"]
+    qc = to_dev(synth.normal_bf16((B, h_q, S, dh), c["seed"], 1), torch)
+    qr = to_dev(synth.normal_bf16((B, h_q, S, dr), c["seed"], 2), torch)
+    kc = to_dev(synth.normal_bf16((B, g, S, dh), c["seed"], 3, c["kv_std"]), torch)
+    kr = to_dev(synth.normal_bf16((B, S, dr), c["seed"], 4), torch)
+    v = to_dev(synth.normal_bf16((B, g, S, dh), c["seed"], 5, c["kv_std"]), torch)
+    o = torch.empty((B, h_q, S, dh), dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / float(np.sqrt(dh + dr))
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    ms, wall = time_steps(lambda: gha.gqla_gqa_prefill(qc, qr, kc, kr, v, scale=scale, out=o), steps, warmup,
+                          torch, flush)
+    del flush
+    fl = acc.gqla_prefill_flops(B, h_q, S, S, dh, dr)
+    return dict(ms=ms, tflops=fl / ms / 1e9, flops=fl, bytes=acc.gqla_prefill_bytes(B, h_q, g, S, S, dh, dr))
+
+
 def bench_gta(gha, torch, steps, warmup):
     c = GTA
     B, h, g, S, d = c["B"], c["h"], c["n_grp"], c["S"], c["d"]
@@ -315,7 +334,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None,
-                    help="prefill|decode|paged|gta|latent|gta_decode|gqla_decode: time one workload")
+                    help="prefill|gqla_prefill|decode|paged|gta|latent|gta_decode|gqla_decode: time one workload")
     ap.add_argument("--spinup-s", type=float, default=1.0,
                     help="untimed seconds of the same workload before the warmup steps (clock ramp)")
     args = ap.parse_args()
@@ -345,6 +364,11 @@ def main():
             log("gta ...")
             extras["gta_prefill"] = bench_gta(gha, torch, args.steps, args.warmup)
             log(extras["gta_prefill"])
+        if only in (None, "gqla_prefill"):
+            log("gqla prefill ...")
+            extras["gqla_prefill"] = bench_gqla_prefill(gha, torch, args.steps, args.warmup)
+            log(extras["gqla_prefill"])
+            torch.cuda.empty_cache()
         if only in (None, "decode"):
             for s_q in (1, 2):
                 log(f"decode s_q={s_q} ...")

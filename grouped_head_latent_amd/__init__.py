@@ -21,7 +21,7 @@ import os
 
 __all__ = [
     "gqa_prefill", "gqa_decode", "gqa_decode_paged", "gta_shared_score_prefill", "gta_shared_score_decode",
-    "gqla_gqa_decode", "latent_absorb_decode",
+    "gqla_gqa_decode", "gqla_gqa_prefill", "latent_absorb_decode",
     "gqa_decode_workspace_bytes", "gqa_decode_paged_workspace_bytes", "gta_shared_score_decode_workspace_bytes",
     "gqla_gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
     "GhaError", "library_path", "load_library", "GHA_F32", "GHA_BF16",
@@ -85,6 +85,8 @@ def load_library():
     lib.gqla_gqa_decode.restype = I
     lib.gqla_gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.gqla_gqa_decode_workspace_bytes.restype = S
+    lib.gqla_gqa_prefill.argtypes = [P, P, P, P, P, P, V, I, I, I, I, I, I, I, I, I, F, I, V]
+    lib.gqla_gqa_prefill.restype = I
     lib.latent_absorb_decode.argtypes = [P, P, P, P, V, P, V, I, I, I, I, I, I, I, I, I, F, V, S, V]
     lib.latent_absorb_decode.restype = I
     lib.latent_absorb_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -304,6 +306,25 @@ def gqla_gqa_decode(q_c, q_r, k_c, k_r, v_cache, seqlens, *, scale: float, L_max
                                _ptr(seqlens), _desc(o), _ptr(lse), B, h_q, g, s_q, L_cap, L_max, d_h, d_r,
                                _dtype_code(q_c), _out_code(o.dtype), float(scale), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def gqla_gqa_prefill(q_c, q_r, k_c, k_r, v, *, scale: float, causal: bool = True, out=None,
+                     out_dtype=None, return_lse: bool = False, stream=None):
+    """q_c (B, h_q, S_q, d_h), q_r (B, h_q, S_q, d_r); k_c, v (B, g, S_k, d_h);
+    k_r (B, S_k, d_r) shared by the groups.  Returns o (B, h_q, S_q, d_h)
+    [and lse (B, h_q, S_q)]."""
+    import torch
+    lib = load_library()
+    B, h_q, S_q, d_h = q_c.shape
+    g, S_k = k_c.shape[1], k_c.shape[2]
+    d_r = q_r.shape[3]
+    out_dtype = out_dtype or torch.bfloat16
+    o = out if out is not None else torch.empty((B, h_q, S_q, d_h), dtype=out_dtype, device=q_c.device)
+    lse = torch.empty((B, h_q, S_q), dtype=torch.float32, device=q_c.device) if return_lse else None
+    _check(lib.gqla_gqa_prefill(_desc(q_c), _desc(q_r), _desc(k_c), _desc(k_r, (0, None, 1)), _desc(v), _desc(o),
+                                _ptr(lse), B, h_q, g, S_q, S_k, d_h, d_r, _dtype_code(q_c), _out_code(o.dtype),
+                                float(scale), int(bool(causal)), _stream(stream)))
     return (o, lse) if return_lse else o
 
 

@@ -163,5 +163,18 @@ def gqla_decode_bytes(seqlens, h_q, g, s_q, d_h, d_r, in_bytes=BF16_BYTES,
                  + B * s_q * h_q * ((d_h + d_r) * in_bytes + d_h * out_bytes))
 
 
+def gqla_prefill_flops(B, h_q, S_q, S_k, d_h, d_r, causal=True) -> float:
+    """Scores over the expanded key [k^C; k^R] (d_h + d^R) and values of d_h."""
+    return 2.0 * B * h_q * causal_pairs(S_q, S_k, causal) * ((d_h + d_r) + d_h)
+
+
+def gqla_prefill_bytes(B, h_q, g, S_q, S_k, d_h, d_r, in_bytes=BF16_BYTES,
+                       out_bytes=BF16_BYTES) -> float:
+    """Queries [q^C; q^R], per-group keys and values, the shared RoPE key, and
+    the outputs, each moved once."""
+    return float(B * (h_q * S_q * (d_h + d_r) * in_bytes + g * S_k * 2 * d_h * in_bytes
+                      + S_k * d_r * in_bytes + h_q * S_q * d_h * out_bytes))
+
+
 def gqla_decode_flops(seqlens, h_q, s_q, d_h, d_r) -> float:
     return 2.0 * h_q * decode_pairs(seqlens, s_q) * ((d_h + d_r) + d_h)

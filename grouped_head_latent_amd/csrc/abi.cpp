@@ -170,6 +170,55 @@ gha_status gqa_prefill(const gha_tensor* q, const gha_tensor* k, const gha_tenso
   return launched(gha::launch_prefill_bf16(a, d, out_dtype == GHA_F32, st), "gqa_prefill");
 }
 
+gha_status gqla_gqa_prefill(const gha_tensor* q_c, const gha_tensor* q_r, const gha_tensor* k_c,
+                            const gha_tensor* k_r, const gha_tensor* v, const gha_tensor* o, float* lse,
+                            int B, int h_q, int g, int S_q, int S_k, int d_h, int d_r,
+                            gha_dtype in_dtype, gha_dtype out_dtype, float scale, int causal,
+                            void* stream) {
+  if (B < 1 || h_q < 1 || g < 1 || S_q < 1 || S_k < 1)
+    return fail(GHA_ERR_SHAPE, "sizes must be positive (B=%d h_q=%d g=%d S_q=%d S_k=%d)", B, h_q, g, S_q, S_k);
+  if (h_q % g) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of g=%d", h_q, g);
+  if (causal && S_q > S_k) return fail(GHA_ERR_SHAPE, "causal needs S_q <= S_k (got %d > %d)", S_q, S_k);
+  if (d_h != 128 || d_r != 64) return fail(GHA_ERR_HEAD_DIM, "need d_h == 128 and d_r == 64 (got %d, %d)", d_h, d_r);
+  if (!(scale > 0.f)) return fail(GHA_ERR_SHAPE, "scale must be given (> 0): 1/sqrt(d_h + d_r) for the expanded key");
+  if (in_dtype != GHA_BF16 || (out_dtype != GHA_BF16 && out_dtype != GHA_F32))
+    return fail(GHA_ERR_DTYPE, "takes bf16 inputs and bf16 or f32 outputs");
+  gha_status s;
+  if ((s = check_view("q_c", q_c, in_dtype, B > 1, h_q > 1, S_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("q_r", q_r, in_dtype, B > 1, h_q > 1, S_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("k_c", k_c, in_dtype, B > 1, g > 1, S_k > 1)) != GHA_OK) return s;
+  if ((s = check_view("k_r", k_r, in_dtype, B > 1, false, S_k > 1)) != GHA_OK) return s;
+  if ((s = check_view("v", v, in_dtype, B > 1, g > 1, S_k > 1)) != GHA_OK) return s;
+  if ((s = check_view("o", o, out_dtype, B > 1, h_q > 1, S_q > 1)) != GHA_OK) return s;
+
+  gha::PrefillArgs a{};
+  a.q = q_c->ptr; a.q_sb = q_c->sb; a.q_sh = q_c->sh; a.q_ss = q_c->ss;
+  a.k = k_c->ptr; a.k_sb = k_c->sb; a.k_sh = k_c->sh; a.k_ss = k_c->ss;
+  a.v = v->ptr; a.v_sb = v->sb; a.v_sh = v->sh; a.v_ss = v->ss;
+  a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
+  a.dk2 = d_r;
+  a.q2 = q_r->ptr; a.q2_sb = q_r->sb; a.q2_sh = q_r->sh; a.q2_ss = q_r->ss;
+  a.k2 = k_r->ptr; a.k2_sb = k_r->sb; a.k2_sh = 0; a.k2_ss = k_r->ss;  // one RoPE key for every group
+  a.lse = lse; a.lse_heads = h_q;
+  a.S_q = S_q; a.S_k = S_k; a.h_kv = g; a.group = h_q / g;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale;
+  a.B = B;
+  if (!gha::prefill_d128_supported(a))
+    return fail(GHA_ERR_STRIDE, "rows overlap or one sequence spans 2 GiB or more");
+  if ((s = check_device()) != GHA_OK) return s;
+  const int G = a.group;
+  a.heads_per_wg = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
+  a.n_subgroups = G / a.heads_per_wg;
+  const int pos_per_wg = (4 / a.heads_per_wg) * gha::prefill_rows_per_wave();
+  a.n_qblocks = (S_q + pos_per_wg - 1) / pos_per_wg;
+  const int64_t nb = (int64_t)B * g * a.n_subgroups * a.n_qblocks;
+  if (nb > (1LL << 30)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  a.n_blocks = (int)nb;
+  return launched(gha::launch_prefill_d128(a, out_dtype == GHA_F32, reinterpret_cast<hipStream_t>(stream)),
+                  "gqla_gqa_prefill");
+}
+
 size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint, int d) {
   if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_max_hint < 1 || d < 1 || h_q % h_kv) return 0;
   const int n_rb = gqa_row_blocks(h_q, h_kv, s_q);

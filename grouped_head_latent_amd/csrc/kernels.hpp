@@ -23,6 +23,11 @@ struct PrefillArgs {
   int causal;
   int B;
   float scale;
+  // second key part (d = 128 kernel only): keys [k; k2] of width 128 + dk2
+  // against queries [q; q2]; dk2 = 0 for none
+  int dk2;
+  const void* q2; int64_t q2_sb, q2_sh, q2_ss;
+  const void* k2; int64_t k2_sb, k2_sh, k2_ss;
 };
 
 struct DecodeArgs {

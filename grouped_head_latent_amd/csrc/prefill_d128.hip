@@ -53,13 +53,25 @@ constexpr int TILEB = KB * ROWB;
 #define GHA_PF_ORDER 1
 #endif
 
-template <int QT, bool OUT_F32>
+// DK2 = 0: keys of width 128.  DK2 = 64: keys of width 192 made of a
+// per-head part k (128) and a part k2 (64) with its own strides (GQLA's
+// decoupled RoPE key, shared by all groups when its head stride is 0), and
+// queries [q; q2] to match; values stay 128 wide.  The second key part sits
+// in LDS rows of 128 bytes (8 units, unit u at u ^ ((r / 2) % 8)), two tile
+// buffers above the K and V buffers.
+template <int QT, bool OUT_F32, int DK2>
 __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(PrefillArgs a) {
   constexpr int D = 128;
-  constexpr int DS = D / 32;  // contraction steps of the score MFMA
-  constexpr int DT = D / 16;  // 16-wide output column tiles
+  constexpr int DS1 = D / 32;             // score contraction steps over k
+  constexpr int DS = DS1 + DK2 / 32;      // ... over [k; k2]
+  constexpr int DT = D / 16;              // 16-wide output column tiles
+  constexpr int NSTEP = 4 + DS;           // MFMA steps per tile: 4 value, DS score
+  constexpr int K2ROWB = 2 * DK2;         // bytes per k2 row in LDS
+  constexpr int K2TILEB = KB * K2ROWB;
+  constexpr int K2BASE = 4 * TILEB;
+  static_assert(DK2 == 0 || DK2 == 64, "second key part");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILEB + 2 * K2TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -102,7 +114,12 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
   for (int qt = 0; qt < QT; ++qt) {
     const int pos = min(pos0 + qt * 16 + li, a.S_q - 1);
 #pragma unroll
-    for (int s = 0; s < DS; ++s) qf[qt][s] = ld16(qbase + (int64_t)pos * a.q_ss + 32 * s + 8 * lg);
+    for (int s = 0; s < DS1; ++s) qf[qt][s] = ld16(qbase + (int64_t)pos * a.q_ss + 32 * s + 8 * lg);
+    if constexpr (DK2 > 0) {
+      const __bf16* q2p = (const __bf16*)a.q2 + (int64_t)b * a.q2_sb + (int64_t)qhead * a.q2_sh + (int64_t)pos * a.q2_ss;
+#pragma unroll
+      for (int s = DS1; s < DS; ++s) qf[qt][s] = ld16(q2p + 32 * (s - DS1) + 8 * lg);
+    }
   }
 
   // ---- tile loads: wave w fills rows 16 w .. 16 w + 15 of both tiles -------
@@ -124,6 +141,22 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
       (void*)kbase, 0, (int)((uint32_t)(a.S_k - 1) * (uint32_t)a.k_ss * 2u + 2u * D), kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)vbase, 0, (int)((uint32_t)(a.S_k - 1) * (uint32_t)a.v_ss * 2u + 2u * D), kBufferFlags);
+  // second key part: 8 rows per DMA instruction, lane l taking row l / 8 and
+  // LDS unit l % 8, so wave w fills rows 16 w .. 16 w + 15 with two
+  __amdgpu_buffer_rsrc_t k2rs = krs;
+  uint32_t k2ofs[2] = {0u, 0u};
+  if constexpr (DK2 > 0) {
+    const __bf16* k2base = (const __bf16*)a.k2 + (int64_t)b * a.k2_sb + (int64_t)kvh * a.k2_sh;
+    k2rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)k2base, 0, (int)((uint32_t)(a.S_k - 1) * (uint32_t)a.k2_ss * 2u + 2u * DK2), kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rr = 8 * i + (lane >> 3);  // row within the wave's 16
+      const int r = 16 * wave + rr;
+      k2ofs[i] = (uint32_t)(r * a.k2_ss + 8 * ((lane & 7) ^ ((rr >> 1) & 7))) * 2u;
+    }
+  }
+  const uint32_t k2_step = (uint32_t)a.k2_ss * (2u * KB);
   // LDS: K tiles in buffers 0/1 at 0 and 16 KiB, V tiles in buffers 0/1 at
   // 32 and 48 KiB; tile t goes to buffer t % 2.
   auto issue_k = [&](int t) {
@@ -131,6 +164,11 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
     const uint32_t so = (uint32_t)t * k_step;
 #pragma unroll
     for (int i = 0; i < 4; ++i) lds_dma16(krs, dst + 1024 * i, kofs[i], so);
+    if constexpr (DK2 > 0) {
+      const uint32_t dst2 = lds_offset(smem) + K2BASE + (t & 1) * K2TILEB + wave * 16 * K2ROWB;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma16(k2rs, dst2 + 1024 * i, k2ofs[i], (uint32_t)t * k2_step);
+    }
   };
   auto issue_v = [&](int t) {
     const uint32_t dst = lds_offset(smem) + 2 * TILEB + (t & 1) * TILEB + wave * 16 * ROWB;
@@ -144,6 +182,9 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
   // 4 s and lg occupy different bits, the byte address is
   // (li * 256 + 16 (lg ^ li)) ^ 64 s, plus 4096 kt.
   const uint32_t kfrag = li * ROWB + 16 * (lg ^ li);
+  // second key part: row 16 kt + li, unit 4 (s - DS1) + lg at
+  // (kfrag2 ^ 64 (s - DS1)) + 2048 kt
+  const uint32_t kfrag2 = K2BASE + li * K2ROWB + 16 * (lg ^ ((li >> 1) & 7));
   // V: source lane li of group lg reads row vr = 4 lg + li / 4 (+ 32 k2 + 16 h),
   // columns 16 dt + 4 (li % 4): logical unit 2 dt + (li / 2) % 2, byte 8 (li % 2)
   // of it, at slot 2 (dt ^ (vr & 7)) + (li / 2) % 2.  Bits 5..7 of the
@@ -171,19 +212,21 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
   const float c2 = a.scale * kLog2e;
   const u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
 
-  // The MFMA phase of iteration t runs in eight steps, each issuing the LDS
-  // reads of a later step (GHA_PF_PFD steps ahead) before its own MFMAs:
+  // The MFMA phase of iteration t runs in NSTEP steps (8, or 10 with a
+  // second key part), each issuing the LDS reads of a later step (GHA_PF_PFD
+  // steps ahead) before its own MFMAs:
   //   steps 0..3: O^T += V^T P^T for k2 = step / 2, column tiles 4 (step % 2) ..
   //               + 3 (V from buffer t % 2; step 0 also adds 1^T P^T to the
   //               normaliser, step 2 likewise for k2 = 1)
-  //   steps 4..7: S^T += K Q^T for contraction step s = step - 4 (K of tile
-  //               t + 1 from buffer (t + 1) % 2)
+  //   steps 4..:  S^T += K Q^T for contraction step s = step - 4 (K of tile
+  //               t + 1 from buffer (t + 1) % 2; steps past 7 read the second
+  //               key part)
   f32x4 sacc[4][QT];
   constexpr int NFR = GHA_PF_PFD + 1;  // fragment buffers (LDS reads run PFD steps ahead)
   // Order of the steps in the MFMA phase: PV and score steps alternate, so
   // that the transposing V reads (slow per wave) of one step overlap the
   // MFMAs of a score step, whose own K reads are few.
-  auto step_at = [](int j) { return GHA_PF_ORDER ? ((j & 1) ? 4 + (j >> 1) : (j >> 1)) : j; };
+  auto step_at = [](int j) { return (GHA_PF_ORDER && j < 8) ? ((j & 1) ? 4 + (j >> 1) : (j >> 1)) : j; };
   u32x4 fr[NFR][4];
   auto load_step = [&](int j, int t, u32x4 (&f)[4]) __attribute__((always_inline)) {
     if (j < 4) {
@@ -196,10 +239,14 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
         const u32x2 h1 = ld_tr(smem + va + k2 * 32 * ROWB + 16 * ROWB);
         f[i] = u32x4{h0[0], h0[1], h1[0], h1[1]};
       }
-    } else {
+    } else if (j - 4 < DS1) {
       const uint32_t kst = kfrag ^ (((t + 1) & 1) << 14);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) f[kt] = ld16(smem + (kst ^ ((j - 4) << 6)) + kt * 16 * ROWB);
+    } else {
+      const uint32_t kst = (kfrag2 ^ ((j - 4 - DS1) << 6)) + ((t + 1) & 1) * K2TILEB;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) f[kt] = ld16(smem + kst + kt * 16 * K2ROWB);
     }
   };
   auto mfma_step = [&](int j, const u32x4 (&f)[4], const u32x4 (&pf)[QT][2]) __attribute__((always_inline)) {
@@ -225,14 +272,14 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
           sacc[kt][qt] = mfma_bf16(f[kt], qf[qt][st], st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kt][qt]);
     }
   };
-  // scores of tile 0 (prologue): steps 4..7 of a phantom iteration -1
+  // scores of tile 0 (prologue): steps 4 .. NSTEP - 1 of a phantom iteration -1
   auto score0 = [&]() __attribute__((always_inline)) {
     const u32x4 nopf[QT][2] = {};
 #pragma unroll
     for (int j = 4; j < 4 + GHA_PF_PFD; ++j) load_step(j, -1, fr[j % NFR]);
 #pragma unroll
-    for (int j = 4; j < 8; ++j) {
-      if (j + GHA_PF_PFD < 8) load_step(j + GHA_PF_PFD, -1, fr[(j + GHA_PF_PFD) % NFR]);
+    for (int j = 4; j < NSTEP; ++j) {
+      if (j + GHA_PF_PFD < NSTEP) load_step(j + GHA_PF_PFD, -1, fr[(j + GHA_PF_PFD) % NFR]);
       mfma_step(j, fr[j % NFR], nopf);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -317,8 +364,8 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
       // P(t) V(t), then the scores of tile t + 1; past this wave's last tile
       // (or the last tile) those read a stale buffer and are never used
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j + GHA_PF_PFD < 8) load_step(step_at(j + GHA_PF_PFD), t, fr[(j + GHA_PF_PFD) % NFR]);
+      for (int j = 0; j < NSTEP; ++j) {
+        if (j + GHA_PF_PFD < NSTEP) load_step(step_at(j + GHA_PF_PFD), t, fr[(j + GHA_PF_PFD) % NFR]);
         mfma_step(step_at(j), fr[j % NFR], pf);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -361,17 +408,27 @@ bool prefill_d128_supported(const PrefillArgs& a) {
   // one (batch, head) sequence of K or V must span less than 2^31 bytes
   // (buffer offsets and range are 32-bit), and rows must not overlap, so
   // that the range check cuts exactly at the last key
-  const int64_t ss = a.k_ss > a.v_ss ? a.k_ss : a.v_ss;
+  int64_t ss = a.k_ss > a.v_ss ? a.k_ss : a.v_ss;
+  if (a.dk2 > 0) ss = ss > a.k2_ss ? ss : a.k2_ss;
   const int64_t span = ((int64_t)a.S_k + 4 * KB) * ss * 2;
-  return a.k_ss >= 128 && a.v_ss >= 128 && span < ((int64_t)1 << 31);
+  return a.k_ss >= 128 && a.v_ss >= 128 && (a.dk2 == 0 || a.k2_ss >= a.dk2) && span < ((int64_t)1 << 31);
 }
 
 hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t st) {
   const uint32_t padded = (uint32_t)((a.n_blocks + 7) / 8 * 8);
-  if (out_f32)
-    hipLaunchKernelGGL((prefill_d128_kernel<GHA_PF_QT, true>), dim3(padded), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((prefill_d128_kernel<GHA_PF_QT, false>), dim3(padded), dim3(256), 0, st, a);
+  if (a.dk2 == 64) {
+    if (out_f32)
+      hipLaunchKernelGGL((prefill_d128_kernel<GHA_PF_QT, true, 64>), dim3(padded), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_d128_kernel<GHA_PF_QT, false, 64>), dim3(padded), dim3(256), 0, st, a);
+  } else if (a.dk2 == 0) {
+    if (out_f32)
+      hipLaunchKernelGGL((prefill_d128_kernel<GHA_PF_QT, true, 0>), dim3(padded), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_d128_kernel<GHA_PF_QT, false, 0>), dim3(padded), dim3(256), 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -228,6 +228,26 @@ gha_status gqla_gqa_decode(const gha_tensor* q_c, const gha_tensor* q_r, const g
 
 size_t gqla_gqa_decode_workspace_bytes(int B, int h_q, int g, int s_q, int L_max_hint, int d_h);
 
+/* GQLA's GQA path over a whole sequence, the compute-friendly form used for
+ * prefill (GQLA section 1; section 3.1, Eq. (1): the latent is expanded into
+ * per-group keys k^C_j and values v_j, and one decoupled RoPE key k^R per
+ * token is shared by all groups).  Head i (group j = i / (h_q / g)) attends
+ * with query [q_c_i; q_r_i] over keys [k_c_j; k_r] and takes values v_j.
+ *   q_c (B, h_q, S_q, d_h), q_r (B, h_q, S_q, d_r);
+ *   k_c (B, g, S_k, d_h), v (B, g, S_k, d_h): per group;
+ *   k_r (B, S_k, d_r): shared (its head stride is ignored);
+ *   o (B, h_q, S_q, d_h); lse NULL or dense fp32 (B, h_q, S_q).
+ * Causal alignment is bottom-right (query t sees keys 0 .. S_k - S_q + t);
+ * requires S_q <= S_k when causal.  d_h == 128, d_r == 64; in BF16, out BF16
+ * or F32.  scale must be given (> 0): 1/sqrt(d_h + d_r) is the scale of the
+ * expanded key.  Rows must not overlap and one (batch, group) sequence must
+ * span less than 2 GiB. */
+gha_status gqla_gqa_prefill(const gha_tensor* q_c, const gha_tensor* q_r, const gha_tensor* k_c,
+                            const gha_tensor* k_r, const gha_tensor* v, const gha_tensor* o,
+                            float* lse, int B, int h_q, int g, int S_q, int S_k, int d_h, int d_r,
+                            gha_dtype in_dtype, gha_dtype out_dtype, float scale, int causal,
+                            void* stream);
+
 /* Absorbed latent decode (GQLA section 1 and Figure 2, right: with W^UK folded
  * into the query and W^UV into the output, all h_q heads attend directly over
  * the cache of r_kv + d_r elements per token, which serves as the one shared

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
             "gta_shared_score_decode", "gqla_gqa_decode", "gta_shared_score_decode_workspace_bytes",
             "gqla_gqa_decode_workspace_bytes",
             "gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
-            "gqa_decode_paged", "gqa_decode_paged_workspace_bytes",
+            "gqa_decode_paged", "gqa_decode_paged_workspace_bytes", "gqla_gqa_prefill",
             "gha_status_string", "gha_last_error", "gha_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -144,6 +144,32 @@ def test_paged_decode_workspace_follows_the_window(lib):
     short = lib.gqa_decode_paged_workspace_bytes(1, 4, 1, 1, 32768, 100, 128)
     assert short == (3 + 1) * 16 * 129 * 4 + 2 * 4
     assert lib.gqa_decode_paged_workspace_bytes(64, 40, 8, 8, 32768, 0, 128) == 0
+
+
+def gqla_prefill(lib, **kw):
+    a = dict(qc=T(), qr=T(ss=64), kc=T(), kr=T(ss=64), v=T(), o=T(), B=1, h_q=16, g=2, S_q=256, S_k=256,
+             d_h=128, d_r=64, i=gha.GHA_BF16, o_t=gha.GHA_F32, scale=0.07, causal=1)
+    a.update(kw)
+    return lib.gqla_gqa_prefill(ctypes.byref(a["qc"]), ctypes.byref(a["qr"]), ctypes.byref(a["kc"]),
+                                ctypes.byref(a["kr"]), ctypes.byref(a["v"]), ctypes.byref(a["o"]), None,
+                                a["B"], a["h_q"], a["g"], a["S_q"], a["S_k"], a["d_h"], a["d_r"], a["i"],
+                                a["o_t"], ctypes.c_float(a["scale"]), a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=3), 3),
+    (dict(d_h=64), 7),
+    (dict(d_r=32), 7),
+    (dict(scale=0.0), 2),                   # the expanded head width is not an argument
+    (dict(S_q=300), 2),                     # causal with S_q > S_k
+    (dict(i=gha.GHA_F32), 6),
+    (dict(kr=T(ptr=0)), 1),
+    (dict(kr=T(ss=32)), 4),                 # RoPE rows overlap
+    (dict(v=T(ss=100)), 5),
+])
+def test_gqla_prefill_rejects_bad_arguments(lib, kw, status):
+    assert gqla_prefill(lib, **kw) == status
+    assert len(lib.gha_last_error()) > 0
 
 
 def test_workspace_sizes_cover_the_split_plan(lib):

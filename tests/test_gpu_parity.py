@@ -301,6 +301,53 @@ def test_gqa_decode_paged_full_size_sampled(gha_lib, page, window):
         check(f"full paged decode b={b} L={L}", o[b:b + 1], ref)
 
 
+# ----------------------------------------------- GQLA GQA-path prefill
+
+GQLA_PREFILL_CASES = [
+    # B, h_q, g, S_q, S_k, causal
+    (2, 16, 2, 200, 200, True),     # ragged last tile
+    (1, 8, 8, 77, 77, True),        # one head per group
+    (1, 16, 4, 100, 300, True),     # bottom-right: queries are the last 100 positions
+    (1, 8, 2, 130, 130, False),
+    (1, 32, 8, 1, 40, True),        # a single query row
+]
+
+
+def gqla_prefill_case(B, h_q, g, S_q, S_k, seed, kv_std=0.45):
+    return (synth.normal_bf16((B, h_q, S_q, 128), seed, 1), synth.normal_bf16((B, h_q, S_q, 64), seed, 2),
+            synth.normal_bf16((B, g, S_k, 128), seed, 3, kv_std), synth.normal_bf16((B, S_k, 64), seed, 4),
+            synth.normal_bf16((B, g, S_k, 128), seed, 5, kv_std))
+
+
+@pytest.mark.parametrize("B,h_q,g,S_q,S_k,causal", GQLA_PREFILL_CASES)
+def test_gqla_gqa_prefill(gha_lib, B, h_q, g, S_q, S_k, causal):
+    say(f"gqla prefill B={B} h_q={h_q} g={g} S_q={S_q} S_k={S_k} causal={causal}")
+    bits = gqla_prefill_case(B, h_q, g, S_q, S_k, 23)
+    qc, qr, kc, kr, v = (bf16_to_torch(x) for x in bits)
+    scale = 1.0 / math.sqrt(192)
+    o32, lse = gha_lib.gqla_gqa_prefill(qc, qr, kc, kr, v, scale=scale, causal=causal,
+                                        out_dtype=torch.float32, return_lse=True)
+    o16 = gha_lib.gqla_gqa_prefill(qc, qr, kc, kr, v, scale=scale, causal=causal)
+    ref, ref_lse = oracle.gqla_gqa_prefill(*(widen(x) for x in bits), scale=scale, causal=causal)
+    check("gqla prefill fp32", o32.cpu().numpy(), ref)
+    check("gqla prefill bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("gqla prefill lse", lse.cpu().numpy(), ref_lse)
+
+
+def test_gqla_gqa_prefill_full_size_sampled(gha_lib):
+    """Batch 2, 128 query heads in 8 groups, 4096 tokens, d_h 128 + d^R 64."""
+    B, h_q, g, S = 2, 128, 8, 4096
+    say(f"full-size gqla prefill {B}x{h_q}/{g}x{S}")
+    bits = gqla_prefill_case(B, h_q, g, S, S, 10)
+    scale = 1.0 / math.sqrt(192)
+    o = gha_lib.gqla_gqa_prefill(*(bf16_to_torch(x) for x in bits), scale=scale,
+                                 out_dtype=torch.float32).cpu().numpy()
+    pairs = [(0, 0), (0, 77), (1, 63), (1, 127)]
+    ref, _ = oracle.gqla_gqa_prefill(*(widen(x) for x in bits), scale=scale, heads=pairs)
+    for b, i in pairs:
+        check(f"full gqla prefill (b={b}, head={i})", o[b, i], ref[b, i])
+
+
 # -------------------------------------------------------------- GTA decode
 
 GTA_DECODE_CASES = [
