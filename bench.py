@@ -296,6 +296,30 @@ def bench_latent(gha, torch, steps, warmup, s_q):
                 sum_L=int(seqlens.sum()))
 
 
+def bench_absorbing(gha, torch, steps, warmup, s_q):
+    """The latent workload with the absorption products on the device:
+    content queries q^C and per-group W^UK, W^UV (8 groups, N(0, 0.02^2))."""
+    c = LATENT
+    B, h_q, r, dr, dh, g = c["B"], c["h_q"], c["r_kv"], c["d_r"], c["d_h"], 8
+    L_cap = c["L_hi"]
+    seqlens = synth.uniform_i32(B, c["L_lo"], c["L_hi"], c["seed"], synth.STREAM["seqlens"])
+    cache = to_dev(synth.latent_cache_bf16(B, L_cap, r + dr, seqlens, c["seed"], synth.STREAM["latent"]), torch)
+    q_c = to_dev(synth.normal_bf16((B, s_q, h_q, dh), c["seed"], synth.STREAM["q_c"]), torch)
+    q_r = to_dev(synth.normal_bf16((B, s_q, h_q, dr), c["seed"], synth.STREAM["q_rope"]), torch)
+    w_uk = to_dev(synth.normal_bf16((g * dh, r), c["seed"], synth.STREAM["w_uk"], 0.02), torch)
+    w_uv = to_dev(synth.normal_bf16((g * dh, r), c["seed"], synth.STREAM["w_uv"], 0.02), torch)
+    sl = torch.from_numpy(seqlens).cuda()
+    o = torch.empty((B, s_q, h_q, dh), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gha.gqla_absorb_decode_workspace_bytes(B, h_q, s_q, L_cap, r), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(dh + dr)
+    ms, wall = time_steps(lambda: gha.gqla_absorb_decode(q_c, q_r, w_uk, w_uv, cache[..., :r], cache[..., r:], sl,
+                                                         g=g, scale=scale, out=o, workspace=ws), steps, warmup, torch)
+    by = acc.absorbing_decode_bytes(seqlens, h_q, g, s_q, dh, r, dr)
+    fl = acc.absorbing_decode_flops(seqlens, h_q, s_q, dh, r, dr)
+    del cache
+    return dict(ms=ms, gbps=by / ms / 1e6, tflops=fl / ms / 1e9, bytes=by, flops=fl, sum_L=int(seqlens.sum()))
+
+
 # ---------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(max_seconds=15.0):
@@ -334,7 +358,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None,
-                    help="prefill|gqla_prefill|decode|paged|gta|latent|gta_decode|gqla_decode: time one workload")
+                    help="prefill|gqla_prefill|decode|paged|gta|latent|absorbing|gta_decode|gqla_decode: "
+                         "time one workload")
     ap.add_argument("--spinup-s", type=float, default=1.0,
                     help="untimed seconds of the same workload before the warmup steps (clock ramp)")
     args = ap.parse_args()
@@ -387,6 +412,12 @@ def main():
                 log(f"latent s_q={s_q} ...")
                 extras[f"latent_decode_sq{s_q}"] = bench_latent(gha, torch, args.steps, args.warmup, s_q)
                 log(extras[f"latent_decode_sq{s_q}"])
+                torch.cuda.empty_cache()
+        if only in (None, "absorbing"):
+            for s_q in (1, 2):
+                log(f"absorbing latent decode s_q={s_q} ...")
+                extras[f"latent_absorbing_decode_sq{s_q}"] = bench_absorbing(gha, torch, args.steps, args.warmup, s_q)
+                log(extras[f"latent_absorbing_decode_sq{s_q}"])
                 torch.cuda.empty_cache()
         if only in (None, "gta_decode"):
             for s_q in (1, 2):

@@ -21,7 +21,7 @@ import os
 
 __all__ = [
     "gqa_prefill", "gqa_decode", "gqa_decode_paged", "gta_shared_score_prefill", "gta_shared_score_decode",
-    "gqla_gqa_decode", "gqla_gqa_prefill", "latent_absorb_decode",
+    "gqla_gqa_decode", "gqla_gqa_prefill", "latent_absorb_decode", "gqla_absorb_decode",
     "gqa_decode_workspace_bytes", "gqa_decode_paged_workspace_bytes", "gta_shared_score_decode_workspace_bytes",
     "gqla_gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
     "GhaError", "library_path", "load_library", "GHA_F32", "GHA_BF16",
@@ -91,6 +91,10 @@ def load_library():
     lib.latent_absorb_decode.restype = I
     lib.latent_absorb_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.latent_absorb_decode_workspace_bytes.restype = S
+    lib.gqla_absorb_decode.argtypes = [P, P, V, V, P, P, V, P, V, I, I, I, I, I, I, I, I, I, I, I, F, V, S, V]
+    lib.gqla_absorb_decode.restype = I
+    lib.gqla_absorb_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.gqla_absorb_decode_workspace_bytes.restype = S
     lib.gha_status_string.argtypes = [I]
     lib.gha_status_string.restype = ctypes.c_char_p
     lib.gha_last_error.argtypes = []
@@ -358,4 +362,39 @@ def latent_absorb_decode(q_lat, q_rope, c_kv, k_rope, seqlens, *, scale: float,
         _desc(k_rope, (0, None, 1)), _ptr(seqlens), _desc(o, (0, 2, 1)), _ptr(lse),
         B, h_q, s_q, L_cap, L_max, r_kv, d_r, _dtype_code(q_lat), _out_code(o.dtype),
         float(scale), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def gqla_absorb_decode_workspace_bytes(B, h_q, s_q, L_max, r_kv=512) -> int:
+    return int(load_library().gqla_absorb_decode_workspace_bytes(B, h_q, s_q, L_max, r_kv))
+
+
+def gqla_absorb_decode(q_c, q_rope, w_uk, w_uv, c_kv, k_rope, seqlens, *, g: int, scale: float,
+                       L_max: int | None = None, out=None, out_dtype=None, workspace=None,
+                       return_lse: bool = False, stream=None):
+    """q_c (B, s_q, h_q, d_h), q_rope (B, s_q, h_q, d_r); w_uk, w_uv (g*d_h,
+    r_kv) bf16; c_kv (B, L_cap, r_kv), k_rope (B, L_cap, d_r) (may be views of
+    one (B, L_cap, r_kv + d_r) buffer).  Returns O (B, s_q, h_q, d_h) [and lse
+    (B, s_q, h_q)]."""
+    import torch
+    lib = load_library()
+    B, s_q, h_q, d_h = q_c.shape
+    d_r = q_rope.shape[3]
+    L_cap, r_kv = c_kv.shape[1], c_kv.shape[2]
+    L_max = L_cap if L_max is None else int(L_max)
+    for w in (w_uk, w_uv):
+        if not w.is_contiguous() or w.shape != (g * d_h, r_kv):
+            raise ValueError("w_uk and w_uv must be contiguous (g * d_h, r_kv)")
+    out_dtype = out_dtype or torch.bfloat16
+    o = out if out is not None else torch.empty((B, s_q, h_q, d_h), dtype=out_dtype, device=q_c.device)
+    lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q_c.device) if return_lse else None
+    need = gqla_absorb_decode_workspace_bytes(B, h_q, s_q, L_max, r_kv)
+    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=q_c.device)
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    _check(lib.gqla_absorb_decode(
+        _desc(q_c, (0, 2, 1)), _desc(q_rope, (0, 2, 1)), _ptr(w_uk), _ptr(w_uv), _desc(c_kv, (0, None, 1)),
+        _desc(k_rope, (0, None, 1)), _ptr(seqlens), _desc(o, (0, 2, 1)), _ptr(lse), B, h_q, g, s_q, L_cap, L_max,
+        d_h, r_kv, d_r, _dtype_code(q_c), _out_code(o.dtype), float(scale), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
     return (o, lse) if return_lse else o

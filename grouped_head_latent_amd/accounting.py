@@ -138,6 +138,22 @@ def latent_decode_flops(seqlens, h_q, s_q, r_kv, d_r) -> float:
     return 2.0 * h_q * decode_pairs(seqlens, s_q) * ((r_kv + d_r) + r_kv)
 
 
+def absorbing_decode_bytes(seqlens, h_q, g, s_q, d_h, r_kv, d_r, in_bytes=BF16_BYTES,
+                           out_bytes=BF16_BYTES) -> float:
+    """The latent cache read once, the content and RoPE queries, both
+    up-projection blocks (g d_h x r_kv each), and the d_h-wide outputs."""
+    L = int(np.sum(np.asarray(seqlens, dtype=np.int64)))
+    B = len(seqlens)
+    return float(L * (r_kv + d_r) * in_bytes + 2 * g * d_h * r_kv * in_bytes
+                 + B * s_q * h_q * ((d_h + d_r) * in_bytes + d_h * out_bytes))
+
+
+def absorbing_decode_flops(seqlens, h_q, s_q, d_h, r_kv, d_r) -> float:
+    """Attention over the latent plus the two absorption products per row."""
+    B = len(seqlens)
+    return latent_decode_flops(seqlens, h_q, s_q, r_kv, d_r) + 2.0 * 2 * B * s_q * h_q * d_h * r_kv
+
+
 def gta_decode_bytes(seqlens, h, n_grp, s_q, d_qk, d_v, in_bytes=BF16_BYTES,
                      out_bytes=BF16_BYTES) -> float:
     """Per token one key per group and one value per head, read once; plus

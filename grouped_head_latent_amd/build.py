@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgha.so")
 OBJDIR = os.path.join(ROOT, "_build", "gha")
 SOURCES = ["abi.cpp", "prefill_bf16.hip", "prefill_d128.hip", "prefill_f32.hip", "gta.hip", "decode.hip",
-           "stream_decode.hip", "latent.hip"]
+           "stream_decode.hip", "latent.hip", "absorb.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

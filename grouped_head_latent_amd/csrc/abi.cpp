@@ -550,12 +550,16 @@ size_t latent_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_h
   return rows * (size_t)r_kv * 4 + rows * 4 + (size_t)(B + 1) * 4;
 }
 
-gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rope,
-                                const gha_tensor* c_kv, const gha_tensor* k_rope,
-                                const int32_t* seqlens_k, const gha_tensor* o_lat, float* lse,
-                                int B, int h_q, int s_q, int L_cap, int L_max_hint, int r_kv,
-                                int d_r, gha_dtype in_dtype, gha_dtype out_dtype, float scale,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// every argument check of latent_absorb_decode, nothing launched
+gha_status latent_absorb_decode_check(const gha_tensor* q_lat, const gha_tensor* q_rope,
+                                      const gha_tensor* c_kv, const gha_tensor* k_rope,
+                                      const int32_t* seqlens_k, const gha_tensor* o_lat,
+                                      int B, int h_q, int s_q, int L_cap, int L_max_hint, int r_kv,
+                                      int d_r, gha_dtype in_dtype, gha_dtype out_dtype, float scale,
+                                      void* workspace, size_t workspace_bytes) {
   if (B < 1 || h_q < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
     return fail(GHA_ERR_SHAPE, "sizes must be positive");
   if (L_max_hint > L_cap || s_q > L_max_hint)
@@ -583,6 +587,26 @@ gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rop
     return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
     return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
+  const int T = gha::latent_tile_tokens();
+  if ((int64_t)B * latent_row_blocks(h_q, s_q) * (gha::latent_rows_per_wg() / 4) > (1LL << 30) ||
+      (int64_t)B * ((L_cap + T - 1) / T) >= (1LL << 31))
+    return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  return GHA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rope,
+                                const gha_tensor* c_kv, const gha_tensor* k_rope,
+                                const int32_t* seqlens_k, const gha_tensor* o_lat, float* lse,
+                                int B, int h_q, int s_q, int L_cap, int L_max_hint, int r_kv,
+                                int d_r, gha_dtype in_dtype, gha_dtype out_dtype, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  gha_status s = latent_absorb_decode_check(q_lat, q_rope, c_kv, k_rope, seqlens_k, o_lat, B, h_q, s_q, L_cap,
+                                            L_max_hint, r_kv, d_r, in_dtype, out_dtype, scale, workspace,
+                                            workspace_bytes);
+  if (s != GHA_OK) return s;
   if ((s = check_device()) != GHA_OK) return s;
 
   gha::LatentArgs a{};
@@ -603,10 +627,78 @@ gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rop
   a.ws_lse = a.ws_o + n_part * r_kv;
   a.ws_tiles = reinterpret_cast<int32_t*>(a.ws_lse + n_part);
   a.scale = scale;
-  if ((int64_t)B * a.n_rb * (gha::latent_rows_per_wg() / 4) > (1LL << 30) || (int64_t)B * ((L_cap + T - 1) / T) >= (1LL << 31))
-    return fail(GHA_ERR_SHAPE, "problem too large for one launch");
   return launched(gha::launch_latent_decode(a, out_dtype == GHA_F32, reinterpret_cast<hipStream_t>(stream)),
                   "latent_absorb_decode");
+}
+
+size_t gqla_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_hint, int r_kv) {
+  const size_t lat = latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_max_hint, r_kv);
+  if (lat == 0) return 0;
+  const size_t rows = (size_t)B * s_q * h_q;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  // latent workspace, q~ and o_lat (bf16 each), W^UK transposed (at most
+  // h_q groups of 128 x r_kv)
+  return up(lat) + up(rows * r_kv * 2) + up(rows * r_kv * 2) + (size_t)h_q * 128 * r_kv * 2;
+}
+
+gha_status gqla_absorb_decode(const gha_tensor* q_c, const gha_tensor* q_rope, const void* w_uk,
+                              const void* w_uv, const gha_tensor* c_kv, const gha_tensor* k_rope,
+                              const int32_t* seqlens_k, const gha_tensor* o, float* lse, int B, int h_q,
+                              int g, int s_q, int L_cap, int L_max_hint, int d_h, int r_kv, int d_r,
+                              gha_dtype in_dtype, gha_dtype out_dtype, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (B < 1 || h_q < 1 || g < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
+    return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (h_q % g) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of g=%d", h_q, g);
+  if (d_h != 128 || r_kv != 512 || d_r != 64)
+    return fail(GHA_ERR_HEAD_DIM, "need d_h == 128, r_kv == 512 and d_r == 64 (got %d, %d, %d)", d_h, r_kv, d_r);
+  if (in_dtype != GHA_BF16 || (out_dtype != GHA_BF16 && out_dtype != GHA_F32))
+    return fail(GHA_ERR_DTYPE, "takes bf16 inputs and bf16 or f32 outputs");
+  if (w_uk == nullptr || w_uv == nullptr) return fail(GHA_ERR_NULL, "w_uk or w_uv is null");
+  if ((reinterpret_cast<uintptr_t>(w_uk) & 15u) || (reinterpret_cast<uintptr_t>(w_uv) & 15u))
+    return fail(GHA_ERR_ALIGN, "w_uk and w_uv must be 16-byte aligned");
+  if ((int64_t)B * s_q * h_q >= (1LL << 26)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
+  gha_status s;
+  if ((s = check_view("q_c", q_c, in_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  if ((s = check_view("o", o, out_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
+  const size_t need = gqla_absorb_decode_workspace_bytes(B, h_q, s_q, L_max_hint, r_kv);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GHA_ERR_ALIGN, "workspace not 256-byte aligned");
+  // carve: the latent decode's own workspace, then q~ and o_lat (bf16), then
+  // W^UK transposed
+  const size_t rows = (size_t)B * s_q * h_q;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t lat_ws = latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_max_hint, r_kv);
+  unsigned char* base = reinterpret_cast<unsigned char*>(workspace);
+  void* q_abs = base + up(lat_ws);
+  void* o_lat = base + up(lat_ws) + up(rows * r_kv * 2);
+  void* w_t = base + up(lat_ws) + 2 * up(rows * r_kv * 2);
+  const gha_tensor q_lat_t{q_abs, (int64_t)s_q * h_q * r_kv, (int64_t)r_kv, (int64_t)h_q * r_kv};
+  const gha_tensor o_lat_t{o_lat, (int64_t)s_q * h_q * r_kv, (int64_t)r_kv, (int64_t)h_q * r_kv};
+  // the attention part is validated in full before anything is launched
+  if ((s = latent_absorb_decode_check(&q_lat_t, q_rope, c_kv, k_rope, seqlens_k, &o_lat_t, B, h_q, s_q, L_cap,
+                                      L_max_hint, r_kv, d_r, in_dtype, GHA_BF16, scale, base, lat_ws)) != GHA_OK)
+    return s;
+  if ((s = check_device()) != GHA_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  gha::AbsorbArgs ab{};
+  ab.in = q_c->ptr; ab.in_sb = q_c->sb; ab.in_sh = q_c->sh; ab.in_ss = q_c->ss;
+  ab.w = w_uk;
+  ab.wt = w_t;
+  ab.out = q_abs;
+  ab.B = B; ab.s_q = s_q; ab.h_q = h_q; ab.g = g;
+  if ((s = launched(gha::launch_absorb_query(ab, st), "gqla_absorb_decode(query)")) != GHA_OK) return s;
+  if ((s = latent_absorb_decode(&q_lat_t, q_rope, c_kv, k_rope, seqlens_k, &o_lat_t, lse, B, h_q, s_q, L_cap,
+                                L_max_hint, r_kv, d_r, in_dtype, GHA_BF16, scale, base, lat_ws, stream)) != GHA_OK)
+    return s;
+  gha::AbsorbArgs ao{};
+  ao.w = w_uv;
+  ao.lat = o_lat;
+  ao.out = o->ptr; ao.o_sb = o->sb; ao.o_sh = o->sh; ao.o_ss = o->ss;
+  ao.B = B; ao.s_q = s_q; ao.h_q = h_q; ao.g = g;
+  return launched(gha::launch_absorb_output(ao, out_dtype == GHA_F32, st), "gqla_absorb_decode(output)");
 }
 
 }  // extern "C"

@@ -94,6 +94,20 @@ struct StreamDecodeArgs {
   int bt_stride, page_size;
 };
 
+// The per-group absorption products of the latent decode (d_h = 128,
+// r_kv = 512): rows are (batch, new token, head) with head in group
+// head / (h_q / g).
+struct AbsorbArgs {
+  const void* in; int64_t in_sb, in_sh, in_ss;  // q^C (B, s_q, h_q, d_h) by (batch, head, token) strides
+  const void* w;                                // W^UK or W^UV, (g * d_h, r_kv) row-major bf16
+  void* wt;                                     // workspace for W^UK transposed, (g, r_kv, d_h) bf16
+  const void* lat;                              // o_lat, dense bf16 (B, s_q, h_q, r_kv)
+  void* out; int64_t o_sb, o_sh, o_ss;          // q~ dense bf16 (B, s_q, h_q, r_kv), or O by strides
+  int B, s_q, h_q, g;
+};
+hipError_t launch_absorb_query(const AbsorbArgs& a, hipStream_t st);
+hipError_t launch_absorb_output(const AbsorbArgs& a, bool out_f32, hipStream_t st);
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, bool out_f32, hipStream_t st);
 bool prefill_d128_supported(const PrefillArgs& a);
 hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t st);

@@ -279,6 +279,29 @@ gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rop
 size_t latent_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_hint,
                                             int r_kv);
 
+/* The absorbed latent decode with both absorption products done on the
+ * device (GQLA section 3.1, Eq. (1), and Figure 2, right: the query of head i
+ * in group j = i / (h_q / g) is folded into the latent space as
+ * q~_i = (W^UK_j)^T q_c_i, attention runs over the cached latent as in
+ * latent_absorb_decode, and the head's output is O_i = W^UV_j o_lat_i).
+ *   q_c (B, s_q, h_q, d_h): content queries, strides as for q_lat;
+ *   q_rope (B, s_q, h_q, d_r); c_kv, k_rope, seqlens_k as latent_absorb_decode;
+ *   w_uk, w_uv: device bf16, (g * d_h, r_kv) row-major each, rows
+ *   j * d_h .. j * d_h + d_h - 1 being group j's block; 16-byte aligned;
+ *   o (B, s_q, h_q, d_h); lse NULL or dense fp32 (B, s_q, h_q).
+ * d_h == 128, r_kv == 512, d_r == 64; h_q % g == 0; in BF16, out BF16 or F32;
+ * scale required (> 0).  q~ is rounded to bf16 before attention.
+ * workspace: at least gqla_absorb_decode_workspace_bytes(...) bytes,
+ * 256-byte aligned (the latent decode's workspace, q~ and o_lat). */
+gha_status gqla_absorb_decode(const gha_tensor* q_c, const gha_tensor* q_rope, const void* w_uk,
+                              const void* w_uv, const gha_tensor* c_kv, const gha_tensor* k_rope,
+                              const int32_t* seqlens_k, const gha_tensor* o, float* lse,
+                              int B, int h_q, int g, int s_q, int L_cap, int L_max_hint,
+                              int d_h, int r_kv, int d_r, gha_dtype in_dtype, gha_dtype out_dtype,
+                              float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t gqla_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_hint, int r_kv);
+
 /* Status name, thread-local detail of the last error, library version. */
 const char* gha_status_string(gha_status s);
 const char* gha_last_error(void);

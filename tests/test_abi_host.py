@@ -35,6 +35,7 @@ def test_exports_every_declared_function(lib):
             "gqla_gqa_decode_workspace_bytes",
             "gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
             "gqa_decode_paged", "gqa_decode_paged_workspace_bytes", "gqla_gqa_prefill",
+            "gqla_absorb_decode", "gqla_absorb_decode_workspace_bytes",
             "gha_status_string", "gha_last_error", "gha_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -170,6 +171,46 @@ def gqla_prefill(lib, **kw):
 def test_gqla_prefill_rejects_bad_arguments(lib, kw, status):
     assert gqla_prefill(lib, **kw) == status
     assert len(lib.gha_last_error()) > 0
+
+
+def absorbing(lib, **kw):
+    a = dict(qc=T(ss=128 * 128, sh=128), qr=T(ss=64 * 128, sh=64), wuk=FAKE, wuv=FAKE, c=T(ss=576), kr=T(ss=576),
+             seq=FAKE, o=T(ss=128 * 128, sh=128), B=2, h_q=128, g=8, s_q=1, L_cap=4096, L_max=4096, d_h=128,
+             r=512, d_r=64, scale=0.07, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.gqla_absorb_decode(ctypes.byref(a["qc"]), ctypes.byref(a["qr"]),
+                                  ctypes.c_void_p(a["wuk"]) if a["wuk"] else None,
+                                  ctypes.c_void_p(a["wuv"]) if a["wuv"] else None,
+                                  ctypes.byref(a["c"]), ctypes.byref(a["kr"]),
+                                  ctypes.c_void_p(a["seq"]) if a["seq"] else None, ctypes.byref(a["o"]), None,
+                                  a["B"], a["h_q"], a["g"], a["s_q"], a["L_cap"], a["L_max"], a["d_h"], a["r"],
+                                  a["d_r"], gha.GHA_BF16, gha.GHA_BF16, ctypes.c_float(a["scale"]),
+                                  ctypes.c_void_p(a["ws"]) if a["ws"] else None, a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=3), 3),
+    (dict(d_h=64), 7),
+    (dict(r=256), 7),
+    (dict(wuk=0), 1),
+    (dict(wuv=FAKE + 8), 5),                # weights not 16-byte aligned
+    (dict(scale=0.0), 2),
+    (dict(seq=0), 1),
+    (dict(ws_bytes=4096), 8),
+    (dict(ws=FAKE + 16), 5),                # workspace not 256-byte aligned
+])
+def test_absorbing_decode_rejects_bad_arguments(lib, kw, status):
+    assert absorbing(lib, **kw) == status
+    assert len(lib.gha_last_error()) > 0
+
+
+def test_absorbing_decode_workspace_adds_query_and_latent_output(lib):
+    lat = lib.latent_absorb_decode_workspace_bytes(64, 128, 1, 65536, 512)
+    up = lambda x: (x + 255) // 256 * 256
+    rows = 64 * 128
+    # the latent decode's workspace, q~ and o_lat (bf16 each), W^UK transposed
+    assert lib.gqla_absorb_decode_workspace_bytes(64, 128, 1, 65536, 512) == (
+        up(lat) + 2 * up(rows * 512 * 2) + 128 * 128 * 512 * 2)
 
 
 def test_workspace_sizes_cover_the_split_plan(lib):

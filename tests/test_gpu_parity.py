@@ -645,12 +645,51 @@ def test_latent_growing_scores_restart(gha_lib, heads):
     assert np.allclose(ref[:, :, jumped], 4.0)
 
 
+
+ABSORB_CASES = [
+    # B, h_q, s_q, L_cap, seqlens, g
+    (2, 128, 1, 700, [1, 700], 8),
+    (2, 128, 2, 600, [2, 555], 8),
+    (1, 16, 1, 300, [299], 2),
+    (2, 32, 3, 400, [37, 400], 32),   # one head per group (MLA's per-head up-projections)
+    (1, 40, 1, 90, [90], 5),          # rows not a multiple of 32
+]
+
+
+@pytest.mark.parametrize("B,h_q,s_q,L_cap,seqlens,g", ABSORB_CASES)
+def test_gqla_absorb_decode(gha_lib, B, h_q, s_q, L_cap, seqlens, g):
+    say(f"absorbing decode B={B} h_q={h_q} s_q={s_q} L={seqlens} g={g}")
+    seqlens = np.array(seqlens, dtype=np.int32)
+    q_c, q_r, cache, w_uk, w_uv, _ = latent_inputs(B, s_q, h_q, L_cap, seqlens, 33, g=g)
+    w_bits = [synth.normal_bf16((g * 128, 512), 33, synth.STREAM[n], 0.02) for n in ("w_uk", "w_uv")]
+    dcache = bf16_to_torch(cache)
+    scale = 1 / math.sqrt(128 + 64)
+    o32, lse = gha_lib.gqla_absorb_decode(bf16_to_torch(q_c), bf16_to_torch(q_r), bf16_to_torch(w_bits[0]),
+                                          bf16_to_torch(w_bits[1]), dcache[..., :512], dcache[..., 512:],
+                                          torch.from_numpy(seqlens).cuda(), g=g, scale=scale,
+                                          out_dtype=torch.float32, return_lse=True)
+    o16 = gha_lib.gqla_absorb_decode(bf16_to_torch(q_c), bf16_to_torch(q_r), bf16_to_torch(w_bits[0]),
+                                     bf16_to_torch(w_bits[1]), dcache[..., :512], dcache[..., 512:],
+                                     torch.from_numpy(seqlens).cuda(), g=g, scale=scale)
+    c = widen(cache)
+    # oracle: absorb in fp64 (no bf16 rounding of the absorbed query), attend,
+    # apply W^UV
+    q_abs = oracle.absorb_query(widen(q_c), w_uk, g)
+    o_lat, ref_lse = oracle.latent_absorb_decode(q_abs, widen(q_r), c[..., :512], c[..., 512:], seqlens, scale=scale)
+    ref = oracle.absorb_output(o_lat, w_uv, g, 128)
+    check("absorbing decode fp32", o32.cpu().numpy(), ref)
+    check("absorbing decode bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("absorbing decode lse", lse.cpu().numpy(), ref_lse)
+
+
 @pytest.mark.parametrize("s_q", [1, 2])
 def test_latent_full_size_sampled_and_expanded_path(gha_lib, s_q):
     """h_q 128, r_kv 512, RoPE 64, batch 64, lengths uniform in [8192, 65536],
     W^UK/W^UV per 8 groups ~ N(0, 0.02).  o_lat is checked against the
     absorbed oracle on sampled sequences, and W^UV o_lat (host, fp64) against
-    the expanded per-group GQA oracle (GQLA: the two paths are equal)."""
+    the expanded per-group GQA oracle (GQLA: the two paths are equal); so is
+    the output of gqla_absorb_decode, which does both absorption products on
+    the device."""
     B, h_q, L_cap, g, d_h = 64, 128, 65536, 8, 128
     say(f"full-size latent s_q={s_q}")
     seqlens = synth.uniform_i32(B, 8192, 65536, 5, synth.STREAM["seqlens"])
@@ -660,6 +699,11 @@ def test_latent_full_size_sampled_and_expanded_path(gha_lib, s_q):
     o = gha_lib.latent_absorb_decode(bf16_to_torch(q_lat), bf16_to_torch(q_r), dcache[..., :512],
                                      dcache[..., 512:], torch.from_numpy(seqlens).cuda(), scale=scale,
                                      out_dtype=torch.float32).cpu().numpy()
+    w_bits = [synth.normal_bf16((g * d_h, 512), 5, synth.STREAM[n], 0.02) for n in ("w_uk", "w_uv")]
+    o_fused = gha_lib.gqla_absorb_decode(bf16_to_torch(q_c), bf16_to_torch(q_r), bf16_to_torch(w_bits[0]),
+                                         bf16_to_torch(w_bits[1]), dcache[..., :512], dcache[..., 512:],
+                                         torch.from_numpy(seqlens).cuda(), g=g, scale=scale,
+                                         out_dtype=torch.float32).cpu().numpy()
     for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 30]:
         L = int(seqlens[b])
         c = widen(cache[b:b + 1, :L])
@@ -672,3 +716,4 @@ def test_latent_full_size_sampled_and_expanded_path(gha_lib, s_q):
         O_exp, _ = oracle.gqa_decode(qf, K, V, np.array([L]), scale=scale)
         O_gpu = oracle.absorb_output(o[b:b + 1], w_uv, g, d_h)
         check(f"expanded path b={b}", O_gpu, O_exp.transpose(0, 2, 1, 3))
+        check(f"device absorption b={b}", o_fused[b:b + 1], O_exp.transpose(0, 2, 1, 3))
