@@ -53,6 +53,7 @@ import numpy as np
 __all__ = [
     "widen_bf16", "softmax_attention", "gqa_prefill", "gqa_decode",
     "gta_prefill", "gta_decode", "latent_absorb_decode", "gqla_gqa_decode", "gqla_gqa_prefill",
+    "decode_e4m3", "gqa_decode_fp8",
     "absorb_query", "absorb_output", "expand_latent",
 ]
 
@@ -170,6 +171,31 @@ def gqa_decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
         o[b, i], lse[b, i] = softmax_attention(q[b, i], k_cache[b, j, :L],
                                                v_cache[b, j, :L], nvis, scale, first)
     return o, lse
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """8-bit floating point codes, E4M3 as in the OCP 8-bit floating point
+    format (the quantized KV storage that the GQLA page's section 2 names as
+    complementary; the format is a reading): sign bit, 4-bit exponent with
+    bias 7, 3-bit mantissa; exponent 0 holds subnormals m/8 * 2^-6; the code
+    S.1111.111 is NaN and there are no infinities.  Returns float64."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    subnormal = (m / 8.0) * 2.0 ** -6
+    v = sign * np.where(e == 0, subnormal, normal)
+    return np.where((e == 15) & ((b & 7) == 7), np.nan, v)
+
+
+def gqa_decode_fp8(q, k_codes, v_codes, k_scale: float, v_scale: float, seqlens, *,
+                   scale: float | None = None, heads=None, window: int = 0):
+    """GQA decode over an 8-bit cache: key u is decode_e4m3(k_codes[u]) * k_scale
+    and value u is decode_e4m3(v_codes[u]) * v_scale (one scale per tensor, a
+    reading); otherwise exactly gqa_decode."""
+    return gqa_decode(q, decode_e4m3(k_codes) * k_scale, decode_e4m3(v_codes) * v_scale, seqlens,
+                      scale=scale, heads=heads, window=window)
 
 
 def gta_prefill(q, k, v, *, causal: bool = True, scale: float | None = None,

@@ -132,6 +132,43 @@ def test_windowed_decode_equals_decode_of_the_window():
             np.testing.assert_array_equal(o_1[b, i, 0], vc[b, i // 2, L - 1])
 
 
+def test_e4m3_decoder_against_the_format_and_torch():
+    # values the OCP 8-bit float format fixes for E4M3
+    fixed = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x30: 0.5, 0x7E: 448.0, 0xFE: -448.0,
+             0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x3C: 1.5, 0x81: -(2.0 ** -9)}
+    for c, v in fixed.items():
+        assert oracle.decode_e4m3([c])[0] == v, hex(c)
+    assert np.isnan(oracle.decode_e4m3([0x7F, 0xFF])).all()
+    assert np.signbit(oracle.decode_e4m3([0x80])[0])
+    # every code against torch's float8_e4m3fn
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.decode_e4m3(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def test_fp8_decode_is_decode_of_the_dequantized_cache():
+    B, h_q, h_kv, s_q, d, L_cap = 2, 4, 2, 2, 8, 30
+    rng = np.random.default_rng(3)
+    q = rnd((B, h_q, s_q, d), 16, 1)
+    kc = rng.integers(0, 256, (B, h_kv, L_cap, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, (B, h_kv, L_cap, d)).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    vc[(vc & 0x7F) == 0x7F] = 0x38
+    seqlens = np.array([7, 30])
+    o, lse = oracle.gqa_decode_fp8(q, kc, vc, 0.01, 0.25, seqlens, window=9)
+    for b in range(B):
+        L = int(seqlens[b])
+        for i in range(h_q):
+            j = i // 2
+            k = (torch.from_numpy(kc[b, j, :L].copy()).view(torch.float8_e4m3fn).to(torch.float64) * 0.01).tolist()
+            v = (torch.from_numpy(vc[b, j, :L].copy()).view(torch.float8_e4m3fn).to(torch.float64) * 0.25).tolist()
+            bo, bl = brute_attention(q[b, i].tolist(), k, v, 1 / math.sqrt(d), causal_offset=L - s_q, window=9)
+            np.testing.assert_allclose(o[b, i], bo, atol=1e-12, rtol=1e-12)
+            np.testing.assert_allclose(lse[b, i], bl, atol=1e-12, rtol=1e-12)
+
+
 def test_latent_matches_brute_force():
     B, s_q, h_q, r, dr, L_cap = 1, 2, 3, 4, 2, 4
     ql = rnd((B, s_q, h_q, r), 13, 1)
