@@ -198,6 +198,31 @@ def bench_decode_paged(gha, torch, steps, warmup, s_q, window):
                 keys=acc.windowed_keys(seqlens, s_q, window), page=page, window=window)
 
 
+def bench_decode_fp8(gha, torch, steps, warmup, s_q):
+    """The decode workload with its caches stored as E4M3 codes (scales 1/64)."""
+    c = DECODE
+    B, h_q, h_kv, d = c["B"], c["h_q"], c["h_kv"], c["d"]
+    L_cap = c["L_hi"]
+    seqlens = synth.uniform_i32(B, c["L_lo"], c["L_hi"], c["seed"], synth.STREAM["seqlens"])
+    ks = vs = 1.0 / 64
+    caches = []
+    for stream, sc in ((2, ks), (3, vs)):
+        x = to_dev(synth.cache_bf16(B, h_kv, L_cap, d, seqlens, c["seed"], stream), torch)
+        caches.append((x.float() / sc).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8))
+        del x
+    q = to_dev(synth.normal_bf16((B, h_q, s_q, d), c["seed"], 1), torch)
+    sl = torch.from_numpy(seqlens).cuda()
+    o = torch.empty((B, h_q, s_q, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gha.gqa_decode_paged_workspace_bytes(B, h_q, h_kv, s_q, L_cap, 0, d), dtype=torch.uint8,
+                     device="cuda")
+    ms, wall = time_steps(lambda: gha.gqa_decode_fp8(q, caches[0], caches[1], sl, k_scale=ks, v_scale=vs, out=o,
+                                                     workspace=ws), steps, warmup, torch)
+    by = acc.gqa_decode_fp8_bytes(seqlens, h_q, h_kv, s_q, d)
+    fl = acc.gqa_decode_flops(seqlens, h_q, s_q, d)
+    del caches
+    return dict(ms=ms, gbps=by / ms / 1e6, tflops=fl / ms / 1e9, bytes=by, flops=fl, sum_L=int(seqlens.sum()))
+
+
 def bench_gqla_prefill(gha, torch, steps, warmup):
     c = GQLA_PREFILL
     B, h_q, g, S, dh, dr = c["B"], c["h_q"], c["g"], c["S"], c["d_h"], c["d_r"]
@@ -358,7 +383,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None,
-                    help="prefill|gqla_prefill|decode|paged|gta|latent|absorbing|gta_decode|gqla_decode: "
+                    help="prefill|gqla_prefill|decode|paged|fp8|gta|latent|absorbing|gta_decode|gqla_decode: "
                          "time one workload")
     ap.add_argument("--spinup-s", type=float, default=1.0,
                     help="untimed seconds of the same workload before the warmup steps (clock ramp)")
@@ -406,6 +431,12 @@ def main():
                 log(f"{name} ...")
                 extras[name] = bench_decode_paged(gha, torch, args.steps, args.warmup, s_q, window)
                 log(extras[name])
+                torch.cuda.empty_cache()
+        if only in (None, "fp8"):
+            for s_q in (1, 2):
+                log(f"fp8 decode s_q={s_q} ...")
+                extras[f"gqa_decode_fp8_sq{s_q}"] = bench_decode_fp8(gha, torch, args.steps, args.warmup, s_q)
+                log(extras[f"gqa_decode_fp8_sq{s_q}"])
                 torch.cuda.empty_cache()
         if only in (None, "latent"):
             for s_q in (1, 2):

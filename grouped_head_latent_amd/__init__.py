@@ -20,7 +20,7 @@ import math
 import os
 
 __all__ = [
-    "gqa_prefill", "gqa_decode", "gqa_decode_paged", "gta_shared_score_prefill", "gta_shared_score_decode",
+    "gqa_prefill", "gqa_decode", "gqa_decode_paged", "gqa_decode_fp8", "gta_shared_score_prefill", "gta_shared_score_decode",
     "gqla_gqa_decode", "gqla_gqa_prefill", "latent_absorb_decode", "gqla_absorb_decode",
     "gqa_decode_workspace_bytes", "gqa_decode_paged_workspace_bytes", "gta_shared_score_decode_workspace_bytes",
     "gqla_gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
@@ -75,6 +75,8 @@ def load_library():
     lib.gqa_decode_paged.restype = I
     lib.gqa_decode_paged_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.gqa_decode_paged_workspace_bytes.restype = S
+    lib.gqa_decode_fp8.argtypes = [P, P, P, F, F, V, I, I, V, P, V, I, I, I, I, I, I, I, I, I, F, V, S, V]
+    lib.gqa_decode_fp8.restype = I
     lib.gta_shared_score_prefill.argtypes = [P, P, P, P, V, I, I, I, I, I, I, I, I, F, I, V]
     lib.gta_shared_score_prefill.restype = I
     lib.gta_shared_score_decode.argtypes = [P, P, P, V, P, V, I, I, I, I, I, I, I, I, I, I, F, V, S, V]
@@ -235,6 +237,43 @@ def gqa_decode_paged(q, k_cache, v_cache, seqlens, *, block_table=None, page_siz
                                 L_max, int(window), d, _dtype_code(q), _out_code(o.dtype),
                                 float(scale or 0.0), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def gqa_decode_fp8(q, k_codes, v_codes, seqlens, *, k_scale: float, v_scale: float, block_table=None,
+                   page_size: int = 0, L_cap: int | None = None, L_max: int | None = None, window: int = 0,
+                   scale: float | None = None, out=None, out_dtype=None, workspace=None,
+                   return_lse: bool = False, stream=None):
+    """gqa_decode_paged over caches of OCP E4M3 codes (uint8 tensors of the
+    same shapes as the bf16 caches); key = code * k_scale, value = code *
+    v_scale."""
+    import torch
+    lib = load_library()
+    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise TypeError("the caches hold uint8 E4M3 codes")
+    B, h_q, s_q, d = q.shape
+    h_kv = k_codes.shape[1]
+    if block_table is None:
+        bt_stride, page_size = 0, 0
+        L_cap = k_codes.shape[2] if L_cap is None else int(L_cap)
+    else:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise TypeError("block_table must be an int32 (B, pages) tensor with contiguous rows")
+        page_size = int(page_size or k_codes.shape[2])
+        bt_stride = block_table.stride(0)
+        L_cap = block_table.shape[1] * page_size if L_cap is None else int(L_cap)
+    L_max = L_cap if L_max is None else int(L_max)
+    out_dtype = out_dtype or torch.bfloat16
+    o = out if out is not None else torch.empty((B, h_q, s_q, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=q.device) if return_lse else None
+    need = gqa_decode_paged_workspace_bytes(B, h_q, h_kv, s_q, L_max, int(window), d)
+    ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    _check(lib.gqa_decode_fp8(_desc(q), _desc(k_codes), _desc(v_codes), float(k_scale), float(v_scale),
+                              _ptr(block_table), bt_stride, page_size, _ptr(seqlens), _desc(o), _ptr(lse), B, h_q,
+                              h_kv, s_q, L_cap, L_max, int(window), d, _out_code(o.dtype), float(scale or 0.0),
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return (o, lse) if return_lse else o
 
 

@@ -122,6 +122,14 @@ def gqa_decode_bytes(seqlens, h_q, h_kv, s_q, d, in_bytes=BF16_BYTES,
     return float(L * h_kv * 2 * d * in_bytes + B * h_q * s_q * d * (in_bytes + out_bytes))
 
 
+def gqa_decode_fp8_bytes(seqlens, h_q, h_kv, s_q, d, window: int = 0) -> float:
+    """As gqa_decode_bytes with one byte per cached element (bf16 queries and
+    outputs)."""
+    L = windowed_keys(seqlens, s_q, window)
+    B = len(seqlens)
+    return float(L * h_kv * 2 * d + B * h_q * s_q * d * (BF16_BYTES + BF16_BYTES))
+
+
 def gqa_decode_flops(seqlens, h_q, s_q, d, window: int = 0) -> float:
     return 2.0 * h_q * windowed_pairs(seqlens, s_q, window) * (d + d)
 

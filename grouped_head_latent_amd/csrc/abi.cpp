@@ -24,7 +24,7 @@ gha_status fail(gha_status s, const char* fmt, ...) {
   return s;
 }
 
-int elem_size(gha_dtype t) { return t == GHA_F32 ? 4 : 2; }
+int elem_size(gha_dtype t) { return t == GHA_F32 ? 4 : t == GHA_FP8_E4M3 ? 1 : 2; }
 
 // A view must be present, non-negative and keep every row 16-byte aligned.
 gha_status check_view(const char* name, const gha_tensor* t, gha_dtype dt, bool use_sb,
@@ -318,12 +318,18 @@ size_t gqa_decode_paged_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L
   return stream_decode_ws(B, h_kv, 1, (h_q / h_kv) * s_q, window_keys(L_max_hint, s_q, window), d);
 }
 
-gha_status gqa_decode_paged(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
-                            const int32_t* block_table, int bt_stride, int page_size,
-                            const int32_t* seqlens_k, const gha_tensor* o, float* lse, int B, int h_q,
-                            int h_kv, int s_q, int L_cap, int L_max_hint, int window, int d,
-                            gha_dtype in_dtype, gha_dtype out_dtype, float scale, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// GQA decode on the streaming kernel over a contiguous or paged cache of
+// bf16 or E4M3 elements, with an optional sliding window
+gha_status stream_gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
+                             const int32_t* block_table, int bt_stride, int page_size,
+                             const int32_t* seqlens_k, const gha_tensor* o, float* lse, int B, int h_q,
+                             int h_kv, int s_q, int L_cap, int L_max_hint, int window, int d,
+                             gha_dtype in_dtype, gha_dtype cache_dtype, gha_dtype out_dtype, float scale,
+                             float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                             void* stream, const char* name) {
   if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
     return fail(GHA_ERR_SHAPE, "sizes must be positive");
   if (h_q % h_kv) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
@@ -345,12 +351,13 @@ gha_status gqa_decode_paged(const gha_tensor* q, const gha_tensor* k_cache, cons
   }
   gha_status s;
   if ((s = check_view("q", q, in_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
-  if ((s = check_view("k_cache", k_cache, in_dtype, true, h_kv > 1, true)) != GHA_OK) return s;
-  if ((s = check_view("v_cache", v_cache, in_dtype, true, h_kv > 1, true)) != GHA_OK) return s;
+  if ((s = check_view("k_cache", k_cache, cache_dtype, true, h_kv > 1, true)) != GHA_OK) return s;
+  if ((s = check_view("v_cache", v_cache, cache_dtype, true, h_kv > 1, true)) != GHA_OK) return s;
   if ((s = check_view("o", o, out_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
   if (k_cache->ss < d || v_cache->ss < d) return fail(GHA_ERR_STRIDE, "cache rows overlap (token stride < d)");
   const int span_rows = paged ? page_size : L_cap;
-  if (!span_ok(span_rows, k_cache->ss) || !span_ok(span_rows, v_cache->ss))
+  const int64_t eb = elem_size(cache_dtype);
+  if (((int64_t)span_rows + 64) * std::max(k_cache->ss, v_cache->ss) * eb >= ((int64_t)1 << 31))
     return fail(GHA_ERR_STRIDE, "one %s spans 2 GiB or more", paged ? "page" : "sequence");
   const int rows = (h_q / h_kv) * s_q;
   const int L_plan = window_keys(L_max_hint, s_q, window);
@@ -374,14 +381,41 @@ gha_status gqa_decode_paged(const gha_tensor* q, const gha_tensor* k_cache, cons
   sa.team = 1;
   sa.n_wg = stream_decode_wgs(B, h_kv, 1, L_plan);
   stream_decode_carve(sa, workspace, d);
-  sa.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+  sa.scale = (scale > 0.f ? scale : 1.0f / std::sqrt((float)d)) * k_scale;
+  sa.v_scale = v_scale;
   sa.window = window;
   sa.block_table = block_table;
   sa.bt_stride = paged ? bt_stride : 0;
   sa.page_size = paged ? page_size : 0;
   return launched(gha::launch_stream_decode(sa, d, 0, d, 1, out_dtype == GHA_F32,
-                                            reinterpret_cast<hipStream_t>(stream)),
-                  "gqa_decode_paged");
+                                            reinterpret_cast<hipStream_t>(stream), cache_dtype == GHA_FP8_E4M3),
+                  name);
+}
+}  // namespace
+
+extern "C" {
+
+gha_status gqa_decode_paged(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
+                            const int32_t* block_table, int bt_stride, int page_size,
+                            const int32_t* seqlens_k, const gha_tensor* o, float* lse, int B, int h_q,
+                            int h_kv, int s_q, int L_cap, int L_max_hint, int window, int d,
+                            gha_dtype in_dtype, gha_dtype out_dtype, float scale, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return stream_gqa_decode(q, k_cache, v_cache, block_table, bt_stride, page_size, seqlens_k, o, lse, B, h_q,
+                           h_kv, s_q, L_cap, L_max_hint, window, d, in_dtype, in_dtype, out_dtype, scale, 1.f, 1.f,
+                           workspace, workspace_bytes, stream, "gqa_decode_paged");
+}
+
+gha_status gqa_decode_fp8(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
+                          float k_scale, float v_scale, const int32_t* block_table, int bt_stride, int page_size,
+                          const int32_t* seqlens_k, const gha_tensor* o, float* lse, int B, int h_q, int h_kv,
+                          int s_q, int L_cap, int L_max_hint, int window, int d, gha_dtype out_dtype, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(GHA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  return stream_gqa_decode(q, k_cache, v_cache, block_table, bt_stride, page_size, seqlens_k, o, lse, B, h_q,
+                           h_kv, s_q, L_cap, L_max_hint, window, d, GHA_BF16, GHA_FP8_E4M3, out_dtype, scale,
+                           k_scale, v_scale, workspace, workspace_bytes, stream, "gqa_decode_fp8");
 }
 
 gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, const gha_tensor* v,

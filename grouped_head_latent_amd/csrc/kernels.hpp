@@ -92,6 +92,9 @@ struct StreamDecodeArgs {
   // block_table[b * bt_stride + u / page_size] at token u % page_size
   const int32_t* block_table;
   int bt_stride, page_size;
+  // 8-bit caches: k and v hold E4M3 codes; the key scale is folded into
+  // `scale`, the value scale multiplies the outputs
+  float v_scale;
 };
 
 // The per-group absorption products of the latent decode (d_h = 128,
@@ -121,7 +124,7 @@ bool gta_layout_supported(const PrefillArgs& a, int d_qk, int d_v);
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, int d, bool out_f32, hipStream_t st);
 hipError_t launch_stream_decode(const StreamDecodeArgs& a, int dk1, int dk2, int dvw, int nvs, bool out_f32,
-                                hipStream_t st);
+                                hipStream_t st, bool fp8 = false);
 int stream_decode_chunk();  // keys per scheduling chunk of the streaming decode
 hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st);
 int latent_rows_per_wg();    // query rows per work-group of the split kernel

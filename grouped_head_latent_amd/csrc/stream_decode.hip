@@ -48,19 +48,28 @@ namespace gha {
 namespace {
 
 // T keys per tile: 32 (one 16x16x32 value MFMA step) or 16 (one 16x16x16
-// step), whichever lets a wave keep more tiles in flight
-template <int DK1, int DK2, int DVW, int NVS, int T>
+// step), whichever lets a wave keep more tiles in flight.  EB is the bytes
+// per cached element: 2 (bf16 tiles feed the MFMAs straight from the ring)
+// or 1 (8-bit tiles land in the ring and are expanded into one bf16 tile per
+// wave before use).
+template <int DK1, int DK2, int DVW, int NVS, int T, int EB = 2>
 struct SdLayout {
+  // the bf16 tile the MFMAs read (swizzled rows)
   static constexpr int K1ROW = 2 * DK1, K2ROW = 2 * DK2, VROW = 2 * DVW;
   static constexpr int K1B = T * K1ROW, K2B = T * K2ROW, VB = T * VROW;
-  static constexpr int SLOT = K1B + K2B + NVS * VB;            // one tile
+  static constexpr int TILE = K1B + K2B + NVS * VB;
+  // the tile as it arrives from HBM
+  static constexpr int RK1ROW = EB * DK1, RK2ROW = EB * DK2, RVROW = EB * DVW;
+  static constexpr int RK1B = T * RK1ROW, RK2B = T * RK2ROW, RVB = T * RVROW;
+  static constexpr int SLOT = RK1B + RK2B + NVS * RVB;          // one ring slot
+  static constexpr int STAGE = EB == 2 ? 0 : TILE;              // the expanded tile
   // four waves per work-group when each can keep two tiles, else two
-  static constexpr int NW = 8 * SLOT <= 160 * 1024 ? 4 : 2;
-  static constexpr int NSLOT_FIT = (160 * 1024) / (NW * SLOT);
+  static constexpr int NW = 4 * (2 * SLOT + STAGE) <= 160 * 1024 ? 4 : 2;
+  static constexpr int NSLOT_FIT = ((160 * 1024) / NW - STAGE) / SLOT;
   static constexpr int NSLOT = NSLOT_FIT > 6 ? 6 : NSLOT_FIT;  // ring slots per wave
-  static constexpr int WAVE = NSLOT * SLOT;
+  static constexpr int WAVE = NSLOT * SLOT + STAGE;
   static constexpr int BYTES = NW * WAVE;
-  static constexpr int NK1 = K1B / 1024, NK2 = K2B / 1024, NV = VB / 1024;
+  static constexpr int NK1 = RK1B / 1024, NK2 = RK2B / 1024, NV = RVB / 1024;
   static constexpr int NDMA = NK1 + NK2 + NVS * NV;            // DMA instructions per tile
   static constexpr int DV = NVS * DVW;                         // output width of a row
 };
@@ -80,8 +89,8 @@ __device__ __forceinline__ int sd_chunks(const StreamDecodeArgs& a, int b) {
   return (L - sd_chunk0(a, L) + CH - 1) / CH;
 }
 
-template <int DK1, int DK2, int DVW, int NVS>
-constexpr int sd_tile_keys() { return SdLayout<DK1, DK2, DVW, NVS, 32>::NSLOT >= 3 ? 32 : 16; }
+template <int DK1, int DK2, int DVW, int NVS, int EB = 2>
+constexpr int sd_tile_keys() { return SdLayout<DK1, DK2, DVW, NVS, 32, EB>::NSLOT >= 3 ? 32 : 16; }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 // v_mfma_f32_16x16x16_bf16: lane (i, g) supplies A[i][4g .. 4g + 3] and
@@ -104,10 +113,11 @@ __device__ __forceinline__ int scalar_load_i32(const int32_t* p) {
 __device__ __forceinline__ int key_swz(int row_bytes, int r) { return row_bytes == 128 ? ((r >> 1) & 7) : (r & 15); }
 __device__ __forceinline__ int val_swz(int row_bytes, int r) { return row_bytes == 128 ? 2 * ((r >> 1) & 3) : 2 * (r & 7); }
 
-template <int DK1, int DK2, int DVW, int NVS, int T, int QT>
-__global__ __launch_bounds__((64 * SdLayout<DK1, DK2, DVW, NVS, T>::NW), 1)
+template <int DK1, int DK2, int DVW, int NVS, int T, int QT, int EB>
+__global__ __launch_bounds__((64 * SdLayout<DK1, DK2, DVW, NVS, T, EB>::NW), 1)
 void stream_decode_split_kernel(StreamDecodeArgs a) {
-  using Ly = SdLayout<DK1, DK2, DVW, NVS, T>;
+  using Ly = SdLayout<DK1, DK2, DVW, NVS, T, EB>;
+  static_assert(EB == 2 || (EB == 1 && DK2 == 0 && NVS == 1 && DK1 == DVW), "8-bit caches: one key part, one value");
   constexpr int NWAVE = Ly::NW;
   constexpr int KT = T / 16;  // 16-key score tiles per tile
   static_assert(T == 16 || T == 32, "tile keys");
@@ -202,35 +212,38 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
   // rows past it read as zeros.  One instruction moves 1 KiB: 1024 / row_bytes
   // rows, lane l taking row l / (row_bytes / 16), unit position
   // l % (row_bytes / 16) and fetching the global unit that belongs there.
-  const uint32_t k1row = (uint32_t)a.k_ss * 2u, k2row = (uint32_t)a.k2_ss * 2u, vrow = (uint32_t)a.v_ss * 2u;
+  const uint32_t k1row = (uint32_t)a.k_ss * EB, k2row = (uint32_t)a.k2_ss * EB, vrow = (uint32_t)a.v_ss * EB;
   const uint32_t lastk = (uint32_t)(L - 1);
+  // (strides count elements of EB bytes)
   const __amdgpu_buffer_rsrc_t k1rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)j * a.k_sh), 0,
-      (int)(lastk * k1row + (uint32_t)Ly::K1ROW), kBufferFlags);
+      (void*)((const unsigned char*)a.k + ((int64_t)b * a.k_sb + (int64_t)j * a.k_sh) * EB), 0,
+      (int)(lastk * k1row + (uint32_t)Ly::RK1ROW), kBufferFlags);
   __amdgpu_buffer_rsrc_t k2rs = k1rs;
   if constexpr (DK2 > 0)
     k2rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const __bf16*)a.k2 + (int64_t)b * a.k2_sb), 0,
-                                             (int)(lastk * k2row + (uint32_t)Ly::K2ROW), kBufferFlags);
+                                             (int)(lastk * k2row + (uint32_t)Ly::RK2ROW), kBufferFlags);
   __amdgpu_buffer_rsrc_t vrs[NVS];
 #pragma unroll
   for (int vs = 0; vs < NVS; ++vs)
     vrs[vs] = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)(j * NVS + vs) * a.v_sh), 0,
-        (int)(lastk * vrow + (uint32_t)Ly::VROW), kBufferFlags);
+        (void*)((const unsigned char*)a.v + ((int64_t)b * a.v_sb + (int64_t)(j * NVS + vs) * a.v_sh) * EB), 0,
+        (int)(lastk * vrow + (uint32_t)Ly::RVROW), kBufferFlags);
   // per-lane offsets of the instructions of one tile (they repeat every tile)
+  // (8-bit tiles are stored unswizzled: they are only read row-major, by the
+  // expansion into the bf16 tile)
   auto lane_ofs = [&](int row_bytes, uint32_t gl_row, int n, bool is_key) -> uint32_t {
     const int upr = row_bytes / 16, rpi = 1024 / row_bytes;
     const int r = n * rpi + lane / upr;  // row in the tile
-    const int sw = is_key ? key_swz(row_bytes, r) : val_swz(row_bytes, r);
+    const int sw = EB == 1 ? 0 : is_key ? key_swz(row_bytes, r) : val_swz(row_bytes, r);
     return (uint32_t)r * gl_row + 16u * (uint32_t)((lane % upr) ^ sw);
   };
   uint32_t k1o[Ly::NK1], k2o[Ly::NK2 > 0 ? Ly::NK2 : 1], vo[Ly::NV];
 #pragma unroll
-  for (int n = 0; n < Ly::NK1; ++n) k1o[n] = lane_ofs(Ly::K1ROW, k1row, n, true);
+  for (int n = 0; n < Ly::NK1; ++n) k1o[n] = lane_ofs(Ly::RK1ROW, k1row, n, true);
 #pragma unroll
-  for (int n = 0; n < Ly::NK2; ++n) k2o[n] = lane_ofs(Ly::K2ROW, k2row, n, true);
+  for (int n = 0; n < Ly::NK2; ++n) k2o[n] = lane_ofs(Ly::RK2ROW, k2row, n, true);
 #pragma unroll
-  for (int n = 0; n < Ly::NV; ++n) vo[n] = lane_ofs(Ly::VROW, vrow, n, false);
+  for (int n = 0; n < Ly::NV; ++n) vo[n] = lane_ofs(Ly::RVROW, vrow, n, false);
   const uint32_t ring = lds_offset(smem) + wave * Ly::WAVE;
   const int klo = sd_first_key(a, L);
   // tile i of this wave (global tile i * 4 + w of the split) into slot i % NSLOT;
@@ -253,17 +266,17 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
           u = key0 - pg * a.page_size;
         }
         const __amdgpu_buffer_rsrc_t kp = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const __bf16*)a.k + (int64_t)pidx * a.k_sb + (int64_t)j * a.k_sh), 0,
-            rows > 0 ? (int)((uint32_t)(rows - 1) * k1row + (uint32_t)Ly::K1ROW) : 0, kBufferFlags);
+            (void*)((const unsigned char*)a.k + ((int64_t)pidx * a.k_sb + (int64_t)j * a.k_sh) * EB), 0,
+            rows > 0 ? (int)((uint32_t)(rows - 1) * k1row + (uint32_t)Ly::RK1ROW) : 0, kBufferFlags);
         const __amdgpu_buffer_rsrc_t vp = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const __bf16*)a.v + (int64_t)pidx * a.v_sb + (int64_t)j * a.v_sh), 0,
-            rows > 0 ? (int)((uint32_t)(rows - 1) * vrow + (uint32_t)Ly::VROW) : 0, kBufferFlags);
+            (void*)((const unsigned char*)a.v + ((int64_t)pidx * a.v_sb + (int64_t)j * a.v_sh) * EB), 0,
+            rows > 0 ? (int)((uint32_t)(rows - 1) * vrow + (uint32_t)Ly::RVROW) : 0, kBufferFlags);
 #pragma unroll
         for (int n = 0; n < Ly::NK1; ++n)
           lds_dma16(kp, dst + 1024 * n, k1o[n], ok ? (uint32_t)u * k1row : kOutOfRange);
 #pragma unroll
         for (int n = 0; n < Ly::NV; ++n)
-          lds_dma16(vp, dst + Ly::K1B + 1024 * n, vo[n], ok ? (uint32_t)u * vrow : kOutOfRange);
+          lds_dma16(vp, dst + Ly::RK1B + 1024 * n, vo[n], ok ? (uint32_t)u * vrow : kOutOfRange);
         return;
       }
     }
@@ -272,12 +285,12 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
       lds_dma16(k1rs, dst + 1024 * n, k1o[n], ok ? (uint32_t)key0 * k1row : kOutOfRange);
 #pragma unroll
     for (int n = 0; n < Ly::NK2; ++n)
-      lds_dma16(k2rs, dst + Ly::K1B + 1024 * n, k2o[n], ok ? (uint32_t)key0 * k2row : kOutOfRange);
+      lds_dma16(k2rs, dst + Ly::RK1B + 1024 * n, k2o[n], ok ? (uint32_t)key0 * k2row : kOutOfRange);
 #pragma unroll
     for (int vs = 0; vs < NVS; ++vs)
 #pragma unroll
       for (int n = 0; n < Ly::NV; ++n)
-        lds_dma16(vrs[vs], dst + Ly::K1B + Ly::K2B + vs * Ly::VB + 1024 * n, vo[n], ok ? (uint32_t)key0 * vrow : kOutOfRange);
+        lds_dma16(vrs[vs], dst + Ly::RK1B + Ly::RK2B + vs * Ly::RVB + 1024 * n, vo[n], ok ? (uint32_t)key0 * vrow : kOutOfRange);
   };
 
   // ---- fragment addresses ----------------------------------------------------------
@@ -319,6 +332,38 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
     issue_tile(i + NSLOT - 1);                       // into the slot of tile i - 1
     wait_vmem_at_most<Ly::NDMA * (NSLOT - 1)>();     // tile i has landed
     const unsigned char* sl = smem + wave * Ly::WAVE + (i % NSLOT) * Ly::SLOT;
+    if constexpr (EB == 1) {
+      // expand the 8-bit tile into this wave's bf16 tile, row by row in
+      // 16-code chunks (exact: every E4M3 value is a bf16 value), into the
+      // swizzled layout the MFMA reads expect
+      unsigned char* st = smem + wave * Ly::WAVE + NSLOT * Ly::SLOT;
+      constexpr int CPR = DK1 / 16;  // 16-code chunks per row (keys and values alike)
+      auto cvt_lo = [](uint32_t w) -> uint32_t {  // codes 0, 1 of the word
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+      };
+      auto cvt_hi = [](uint32_t w) -> uint32_t {  // codes 2, 3
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+      };
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+#pragma unroll
+        for (int c0 = 0; c0 < T * CPR; c0 += 64) {
+          const int c = c0 + lane, r = c / CPR, u8 = c % CPR;
+          const u32x4 w = ld16(sl + part * Ly::RK1B + 16 * c);
+          const u32x4 lo = {cvt_lo(w[0]), cvt_hi(w[0]), cvt_lo(w[1]), cvt_hi(w[1])};
+          const u32x4 hi = {cvt_lo(w[2]), cvt_hi(w[2]), cvt_lo(w[3]), cvt_hi(w[3])};
+          const int sw = part == 0 ? key_swz(Ly::K1ROW, r) : val_swz(Ly::VROW, r);
+          unsigned char* row = st + part * Ly::K1B + r * Ly::K1ROW;
+          st16(row + 16 * ((2 * u8) ^ sw), lo);
+          st16(row + 16 * ((2 * u8 + 1) ^ sw), hi);
+        }
+      }
+      // the wave's LDS operations run in order, so its reads below see these
+      // writes; keep the compiler from moving a read above a write whose
+      // address it cannot relate (another lane's)
+      asm volatile("" ::: "memory");
+      sl = st;
+    }
     const int key0 = start + (i * NWAVE + wave) * T;
 
     // S^T = K Q^T: keys key0 + 16 kt + 4 lg + r in sacc[kt][qt][r]
@@ -439,7 +484,8 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
       wt[v] = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
       Lsum += wt[v] * s_l[v * RP + row];
     }
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    // (8-bit values carry their tensor scale, applied here)
+    const float inv = (Lsum > 0.f ? 1.f / Lsum : 0.f) * (EB == 1 ? a.v_scale : 1.f);
     const int64_t pidx = (int64_t)slot * RP + row;
     float* wo = a.ws_o + pidx * DV + f0;
 #pragma unroll
@@ -537,13 +583,13 @@ __global__ __launch_bounds__(256) void stream_decode_merge_kernel(StreamDecodeAr
     a.lse[((int64_t)b * a.n_groups * a.qpg + qhead) * a.s_q + tq] = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
 }
 
-template <int DK1, int DK2, int DVW, int NVS, int QT>
+template <int DK1, int DK2, int DVW, int NVS, int QT, int EB>
 hipError_t launch_cfg(const StreamDecodeArgs& a, bool out_f32, hipStream_t st) {
   constexpr int DV = NVS * DVW;
-  constexpr int T = sd_tile_keys<DK1, DK2, DVW, NVS>();
+  constexpr int T = sd_tile_keys<DK1, DK2, DVW, NVS, EB>();
   const uint32_t padded = (uint32_t)(a.n_wg + 7) / 8 * 8;
-  hipLaunchKernelGGL((stream_decode_split_kernel<DK1, DK2, DVW, NVS, T, QT>), dim3(padded),
-                     dim3(64 * SdLayout<DK1, DK2, DVW, NVS, T>::NW), 0, st, a);
+  hipLaunchKernelGGL((stream_decode_split_kernel<DK1, DK2, DVW, NVS, T, QT, EB>), dim3(padded),
+                     dim3(64 * SdLayout<DK1, DK2, DVW, NVS, T, EB>::NW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (out_f32)
@@ -553,10 +599,10 @@ hipError_t launch_cfg(const StreamDecodeArgs& a, bool out_f32, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int DK1, int DK2, int DVW, int NVS>
+template <int DK1, int DK2, int DVW, int NVS, int EB = 2>
 hipError_t launch_qt(const StreamDecodeArgs& a, bool out_f32, hipStream_t st) {
-  if (a.rows <= 16) return launch_cfg<DK1, DK2, DVW, NVS, 1>(a, out_f32, st);
-  if (a.rows <= 32) return launch_cfg<DK1, DK2, DVW, NVS, 2>(a, out_f32, st);
+  if (a.rows <= 16) return launch_cfg<DK1, DK2, DVW, NVS, 1, EB>(a, out_f32, st);
+  if (a.rows <= 32) return launch_cfg<DK1, DK2, DVW, NVS, 2, EB>(a, out_f32, st);
   return hipErrorInvalidValue;
 }
 
@@ -565,7 +611,12 @@ hipError_t launch_qt(const StreamDecodeArgs& a, bool out_f32, hipStream_t st) {
 int stream_decode_chunk() { return CH; }
 
 hipError_t launch_stream_decode(const StreamDecodeArgs& a, int dk1, int dk2, int dvw, int nvs, bool out_f32,
-                                hipStream_t st) {
+                                hipStream_t st, bool fp8) {
+  if (fp8) {
+    if (dk1 == 64 && dk2 == 0 && dvw == 64 && nvs == 1) return launch_qt<64, 0, 64, 1, 1>(a, out_f32, st);
+    if (dk1 == 128 && dk2 == 0 && dvw == 128 && nvs == 1) return launch_qt<128, 0, 128, 1, 1>(a, out_f32, st);
+    return hipErrorInvalidValue;
+  }
 #define GHA_SD_CASE(K1, K2, VW, NV) \
   if (dk1 == K1 && dk2 == K2 && dvw == VW && nvs == NV) return launch_qt<K1, K2, VW, NV>(a, out_f32, st);
   GHA_SD_CASE(64, 0, 64, 1)

@@ -87,7 +87,7 @@ typedef enum {
   GHA_ERR_HIP = 9        /* no usable device, or a launch failed */
 } gha_status;
 
-typedef enum { GHA_F32 = 0, GHA_BF16 = 1 } gha_dtype;
+typedef enum { GHA_F32 = 0, GHA_BF16 = 1, GHA_FP8_E4M3 = 2 } gha_dtype;  /* E4M3: caches of gqa_decode_fp8 */
 
 /* A strided view: element (b, h, s, c) lives at ptr[b*sb + h*sh + s*ss + c]. */
 typedef struct {
@@ -162,6 +162,22 @@ gha_status gqa_decode_paged(const gha_tensor* q, const gha_tensor* k_cache,
 
 size_t gqa_decode_paged_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint,
                                         int window, int d);
+
+/* gqa_decode_paged over caches of 8-bit floats (the GQLA page's section 2
+ * names quantized KV storage as complementary to the cache layout): k_cache
+ * and v_cache hold OCP E4M3 codes (1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits; no infinities), one byte per element, strides in
+ * elements; key u is code * k_scale and value u is code * v_scale, one scale
+ * per tensor (k_scale, v_scale > 0).  Everything else (contiguous or paged
+ * layout, window, q in BF16, out BF16 or F32, scale <= 0 meaning 1/sqrt(d))
+ * as gqa_decode_paged; d in {64, 128}.  The workspace is that of
+ * gqa_decode_paged_workspace_bytes(...). */
+gha_status gqa_decode_fp8(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
+                          float k_scale, float v_scale, const int32_t* block_table, int bt_stride,
+                          int page_size, const int32_t* seqlens_k, const gha_tensor* o, float* lse,
+                          int B, int h_q, int h_kv, int s_q, int L_cap, int L_max_hint, int window,
+                          int d, gha_dtype out_dtype, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* GTA shared-score attention (GTA news article, grouped shared attention
  * matrix: a group computes its attention scores once and every head of the

@@ -41,6 +41,7 @@ def tolerance_ok(got: np.ndarray, ref: np.ndarray, max_abs=1e-2, mean_abs=1e-3, 
 
 
 BF16_NAN = 0x7FC0
+E4M3_NAN = 0x7F
 
 
 def page_pool(cache: np.ndarray, seqlens, page_size: int, seed: int, *, window: int = 0, s_q: int = 1,
@@ -57,9 +58,10 @@ def page_pool(cache: np.ndarray, seqlens, page_size: int, seed: int, *, window: 
     n_pps = (L_cap + page_size - 1) // page_size
     rng = np.random.default_rng(seed)
     order = rng.permutation(B * n_pps) + 1            # page 0 is the NaN page
-    pool = np.full((B * n_pps + 1, H, page_size, d), BF16_NAN, dtype=np.uint16)
+    nan = BF16_NAN if cache.dtype == np.uint16 else E4M3_NAN  # bf16 bits or E4M3 codes
+    pool = np.full((B * n_pps + 1, H, page_size, d), nan, dtype=cache.dtype)
     table = np.zeros((B, n_pps), dtype=np.int32)
-    padded = np.full((B, H, n_pps * page_size, d), BF16_NAN, dtype=np.uint16)
+    padded = np.full((B, H, n_pps * page_size, d), nan, dtype=cache.dtype)
     padded[:, :, :L_cap] = cache
     for b in range(B):
         L = int(seqlens[b])
@@ -73,3 +75,12 @@ def page_pool(cache: np.ndarray, seqlens, page_size: int, seed: int, *, window: 
     if tokens_major:
         pool = np.ascontiguousarray(pool.transpose(0, 2, 1, 3))
     return pool, table
+
+
+def e4m3_codes(bits: np.ndarray, scale: float) -> np.ndarray:
+    """bf16 bits -> OCP E4M3 codes of value / scale (round to nearest, clamped
+    to +-448; NaN stays NaN), made with torch's float8_e4m3fn on the host."""
+    import torch
+    x = widen(bits) / scale
+    x = np.where(np.isnan(x), np.nan, np.clip(x, -448.0, 448.0))
+    return torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()

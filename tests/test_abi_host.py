@@ -35,7 +35,7 @@ def test_exports_every_declared_function(lib):
             "gqla_gqa_decode_workspace_bytes",
             "gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
             "gqa_decode_paged", "gqa_decode_paged_workspace_bytes", "gqla_gqa_prefill",
-            "gqla_absorb_decode", "gqla_absorb_decode_workspace_bytes",
+            "gqla_absorb_decode", "gqla_absorb_decode_workspace_bytes", "gqa_decode_fp8",
             "gha_status_string", "gha_last_error", "gha_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -211,6 +211,35 @@ def test_absorbing_decode_workspace_adds_query_and_latent_output(lib):
     # the latent decode's workspace, q~ and o_lat (bf16 each), W^UK transposed
     assert lib.gqla_absorb_decode_workspace_bytes(64, 128, 1, 65536, 512) == (
         up(lat) + 2 * up(rows * 512 * 2) + 128 * 128 * 512 * 2)
+
+
+def fp8(lib, **kw):
+    a = dict(q=T(), k=T(sb=1 << 20, sh=1 << 17, ss=128), v=T(sb=1 << 20, sh=1 << 17, ss=128), ks=0.05, vs=0.02,
+             bt=0, bt_stride=0, page=0, seq=FAKE, o=T(), B=2, h_q=32, h_kv=8, s_q=1, L_cap=1024, L_max=1024,
+             window=0, d=128, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.gqa_decode_fp8(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                              ctypes.c_float(a["ks"]), ctypes.c_float(a["vs"]),
+                              ctypes.c_void_p(a["bt"]) if a["bt"] else None, a["bt_stride"], a["page"],
+                              ctypes.c_void_p(a["seq"]) if a["seq"] else None, ctypes.byref(a["o"]), None,
+                              a["B"], a["h_q"], a["h_kv"], a["s_q"], a["L_cap"], a["L_max"], a["window"], a["d"],
+                              gha.GHA_BF16, ctypes.c_float(0.0),
+                              ctypes.c_void_p(a["ws"]) if a["ws"] else None, a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=0.0), 2),
+    (dict(vs=float("inf")), 2),
+    (dict(d=96), 7),
+    (dict(k=T(sb=1 << 20, sh=1 << 17, ss=112)), 4),         # 112-byte rows of 128 codes overlap
+    (dict(v=T(sb=1 << 20, sh=1 << 17, ss=136)), 5),         # 136-byte rows: not 16-byte multiples
+    (dict(h_kv=3), 3),
+    (dict(bt=FAKE, bt_stride=16, page=48), 2),
+    (dict(ws_bytes=16), 8),
+])
+def test_fp8_decode_rejects_bad_arguments(lib, kw, status):
+    assert fp8(lib, **kw) == status
+    assert len(lib.gha_last_error()) > 0
 
 
 def test_workspace_sizes_cover_the_split_plan(lib):

@@ -11,8 +11,8 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_cases import (bf16_to_torch, cache_bits, latent_cache_bits, page_pool, tolerance_ok,
-                             widen)
+from tests.gpu_cases import (bf16_to_torch, cache_bits, e4m3_codes, latent_cache_bits, page_pool,
+                             tolerance_ok, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -299,6 +299,68 @@ def test_gqa_decode_paged_full_size_sampled(gha_lib, page, window):
         ref, _ = oracle.gqa_decode(widen(qb[b:b + 1]), widen(k_ref)[None], widen(v_ref)[None],
                                    np.array([L]), window=window)
         check(f"full paged decode b={b} L={L}", o[b:b + 1], ref)
+
+
+# ------------------------------------------------------- 8-bit caches
+
+FP8_CASES = [
+    # B, h_q, h_kv, s_q, L_cap, seqlens, d, page_size (0: contiguous), window
+    (3, 32, 8, 1, 1100, [1, 700, 1100], 128, 0, 0),
+    (3, 32, 8, 2, 1100, [2, 333, 1099], 128, 64, 0),
+    (2, 8, 2, 2, 600, [64, 599], 64, 0, 0),
+    (2, 16, 2, 4, 2000, [1500, 2000], 128, 32, 1000),   # 32 rows per group, paged, windowed
+    (2, 8, 8, 3, 700, [3, 650], 64, 96, 130),
+]
+
+
+@pytest.mark.parametrize("B,h_q,h_kv,s_q,L_cap,seqlens,d,page,window", FP8_CASES)
+def test_gqa_decode_fp8(gha_lib, B, h_q, h_kv, s_q, L_cap, seqlens, d, page, window):
+    say(f"fp8 decode B={B} h={h_q}/{h_kv} s_q={s_q} L={seqlens} d={d} page={page} window={window}")
+    seqlens = np.array(seqlens, dtype=np.int32)
+    qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, 25)
+    ks, vs = 1 / 64, 1 / 48
+    kc, vc = e4m3_codes(kb, ks), e4m3_codes(vb, vs)
+    q = bf16_to_torch(qb)
+    sl = torch.from_numpy(seqlens).cuda()
+    if page:
+        kp, table = page_pool(kc, seqlens, page, 7, window=window, s_q=s_q)
+        vp, _ = page_pool(vc, seqlens, page, 7, window=window, s_q=s_q)
+        k, v = torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda()
+        kw = dict(block_table=torch.from_numpy(table).cuda(), page_size=page, L_cap=L_cap)
+    else:
+        k, v = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
+        kw = {}
+    o32, lse = gha_lib.gqa_decode_fp8(q, k, v, sl, k_scale=ks, v_scale=vs, window=window,
+                                      out_dtype=torch.float32, return_lse=True, **kw)
+    o16 = gha_lib.gqa_decode_fp8(q, k, v, sl, k_scale=ks, v_scale=vs, window=window, **kw)
+    ref, ref_lse = oracle.gqa_decode_fp8(widen(qb), kc, vc, ks, vs, seqlens, window=window)
+    check("fp8 decode fp32", o32.cpu().numpy(), ref)
+    check("fp8 decode bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("fp8 decode lse", lse.cpu().numpy(), ref_lse)
+
+
+def test_gqa_decode_fp8_full_size_sampled(gha_lib):
+    """The decode workload (batch 64, 32/8 heads, head dim 128, lengths uniform
+    in [1024, 32768]) with its cache quantized to E4M3."""
+    B, h_q, h_kv, d, L_cap, s_q = 64, 32, 8, 128, 32768, 1
+    say("full-size fp8 decode")
+    seqlens = synth.uniform_i32(B, 1024, 32768, 3, synth.STREAM["seqlens"])
+    qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, 3)
+    ks, vs = 1 / 64, 1 / 64
+    kc = torch.from_numpy(kb).view(torch.bfloat16).cuda()
+    vc = torch.from_numpy(vb).view(torch.bfloat16).cuda()
+    del kb, vb
+    # quantize on the device (input preparation; the same rounding as the host helper)
+    k8 = (kc.float() / ks).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = (vc.float() / vs).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    del kc, vc
+    o = gha_lib.gqa_decode_fp8(bf16_to_torch(qb), k8, v8, torch.from_numpy(seqlens).cuda(), k_scale=ks,
+                               v_scale=vs, out_dtype=torch.float32).cpu().numpy()
+    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 17, 40]:
+        L = int(seqlens[b])
+        kk, vv = k8[b, :, :L].cpu().numpy(), v8[b, :, :L].cpu().numpy()
+        ref, _ = oracle.gqa_decode_fp8(widen(qb[b:b + 1]), kk[None], vv[None], ks, vs, np.array([L]))
+        check(f"full fp8 decode b={b} L={L}", o[b:b + 1], ref)
 
 
 # ----------------------------------------------- GQLA GQA-path prefill
