@@ -489,7 +489,7 @@ def main():
                    "global_batch": PREFILL["B"], "seq_len": PREFILL["S"], "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(head["tflops"], 2), "peak": acc.PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(head["tflops"] / acc.PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_d128_kernel<2, false>"),
+                     "traffic": measured_traffic("prefill_d128_kernel<2, false, 0>"),
                      "algorithmic_bytes": head["bytes"]},
     }
     if not args.no_cpu:
