@@ -104,12 +104,18 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
   const int li = lane & 15, lg = lane >> 4;
 
   // ---- which positions of which group -----------------------------------------
-  const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  // Work-groups start in blockIdx order as CUs free up, and causal q-blocks
+  // differ in work (q-block qb walks 2 qb + 2 key tiles), with only about
+  // two work-groups per CU: number them heaviest first (every (batch, group)
+  // of the last q-block, then of the one before, ...), so that light blocks
+  // fill in behind heavy ones instead of two heavy ones meeting on one CU.
+  const uint32_t lid = blockIdx.x;
   if (lid >= (uint32_t)a.n_blocks) return;
   const int n_qb = a.n_qblocks;
-  const int qb = __builtin_amdgcn_readfirstlane(n_qb - 1 - (int)(lid % n_qb));  // heavy (late) blocks first
-  const int grp = __builtin_amdgcn_readfirstlane((int)(lid / n_qb) % a.h_kv);
-  const int b = __builtin_amdgcn_readfirstlane((int)(lid / n_qb) / a.h_kv);
+  const int n_bg = a.B * a.h_kv;
+  const int qb = __builtin_amdgcn_readfirstlane(n_qb - 1 - (int)(lid / n_bg));
+  const int grp = __builtin_amdgcn_readfirstlane((int)(lid % n_bg) % a.h_kv);
+  const int b = __builtin_amdgcn_readfirstlane((int)(lid % n_bg) / a.h_kv);
   const int S = a.S_q;
   const int pos_wg = qb * ROWS;
   const int hv = wave / HW;          // value phase: head hv of the group
