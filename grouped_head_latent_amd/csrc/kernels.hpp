@@ -20,6 +20,7 @@ struct PrefillArgs {
   int n_subgroups;    // group / heads_per_wg
   int n_qblocks;      // position blocks per (batch, head set)
   int n_blocks;       // work-groups with work
+  int pair_qblocks;   // d = 128 kernel: a work-group takes q-blocks n_qblocks - 1 - i and i
   int causal;
   int B;
   float scale;

@@ -27,6 +27,7 @@
 #include "kernels.hpp"
 #include "lds_pipe.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace gha {
@@ -79,21 +80,36 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
   const int li = lane & 15;
   const int lg = lane >> 4;
 
-  // ---- which work this work-group does (as in the generic kernel) ---------
+  // ---- which work this work-group does -------------------------------------
+  // Under the causal mask q-block qb costs about qb + 1 key tiles.  With
+  // paired blocks a work-group takes q-block n_qb - 1 - i and then q-block i,
+  // so every work-group does the same work and the grid has no tail of heavy
+  // blocks; otherwise it takes one block, heavy (late) blocks first.
+  // Consecutive work-groups share (batch, KV head), so their K/V tiles meet
+  // in one XCD's L2.
   const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
   if (lid >= (uint32_t)a.n_blocks) return;
   const int n_qb = a.n_qblocks;
-  const int qb = n_qb - 1 - (int)(lid % n_qb);  // heavy (late) blocks first
-  int rest = (int)(lid / n_qb);
+  const int n_slot = a.pair_qblocks ? (n_qb + 1) / 2 : n_qb;
+  const int qi = (int)(lid % n_slot);
+  int rest = (int)(lid / n_slot);
   const int sg = rest % a.n_subgroups;  rest /= a.n_subgroups;
   const int kvh = rest % a.h_kv;
   const int b = rest / a.h_kv;
+  const int n_pass = (a.pair_qblocks && qi != n_qb - 1 - qi) ? 2 : 1;
 
   const int wph = 4 / a.heads_per_wg;
   const int pos_per_wg = wph * QT * 16;
   const int qhead = kvh * a.group + sg * a.heads_per_wg + wave / wph;
-  const int pos0 = qb * pos_per_wg + (wave % wph) * QT * 16;
   const int off = a.S_k - a.S_q;  // bottom-right causal offset
+
+  const __bf16* qbase = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)qhead * a.q_sh;
+  const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
+  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
+
+  for (int pass = 0; pass < n_pass; ++pass) {
+  const int qb = pass == 0 ? n_qb - 1 - qi : qi;
+  const int pos0 = qb * pos_per_wg + (wave % wph) * QT * 16;
 
   int k_end = a.S_k;
   int wave_kmax = a.S_k - 1;
@@ -103,10 +119,6 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
     wave_kmax = min(a.S_k - 1, min(pos0 + QT * 16 - 1, a.S_q - 1) + off);
   }
   const int n_kb = (k_end + KB - 1) / KB;
-
-  const __bf16* qbase = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)qhead * a.q_sh;
-  const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
-  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
 
   // ---- resident Q^T fragments ---------------------------------------------
   u32x4 qf[QT][DS];
@@ -400,6 +412,7 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
       }
     }
   }
+  }  // pass
 }
 
 }  // namespace
@@ -414,7 +427,35 @@ bool prefill_d128_supported(const PrefillArgs& a) {
   return a.k_ss >= 128 && a.v_ss >= 128 && (a.dk2 == 0 || a.k2_ss >= a.dk2) && span < ((int64_t)1 << 31);
 }
 
-hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t st) {
+namespace {
+// Work-groups of this kernel resident at once on the current device, or 0 if
+// the device cannot be queried.
+int resident_wgs() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = -1;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n > 0 ? n * GHA_PF_MIN_WG : 0;
+}
+}  // namespace
+
+hipError_t launch_prefill_d128(const PrefillArgs& args, bool out_f32, hipStream_t st) {
+  // Pair heavy and light causal q-blocks once the grid outgrows one round of
+  // resident work-groups: every work-group then does the same work.  Within
+  // one round, single blocks finish sooner.
+  PrefillArgs a = args;
+  a.pair_qblocks = 0;
+  if (a.causal && a.n_qblocks > 1) {
+    const int slots = resident_wgs();
+    if (slots > 0 && a.n_blocks > slots) {
+      a.pair_qblocks = 1;
+      a.n_blocks = a.n_blocks / a.n_qblocks * ((a.n_qblocks + 1) / 2);
+    }
+  }
   const uint32_t padded = (uint32_t)((a.n_blocks + 7) / 8 * 8);
   if (a.dk2 == 64) {
     if (out_f32)

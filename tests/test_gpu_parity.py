@@ -88,6 +88,10 @@ PREFILL_CASES = [
     (1, 8, 2, 1, 1, 128, True),       # one token
     (1, 8, 2, 70, 300, 128, True),    # chunked prefill: bottom-right causal
     (1, 8, 2, 90, 150, 128, False),   # no mask
+    # grids larger than the resident work-groups: heavy and light causal
+    # q-blocks paired in one work-group, 35 blocks so the middle one is alone
+    (2, 32, 8, 1100, 1100, 128, True),
+    (2, 32, 8, 1090, 1400, 128, True),  # paired, bottom-right offset
 ]
 
 
@@ -372,6 +376,7 @@ GQLA_PREFILL_CASES = [
     (1, 16, 4, 100, 300, True),     # bottom-right: queries are the last 100 positions
     (1, 8, 2, 130, 130, False),
     (1, 32, 8, 1, 40, True),        # a single query row
+    (1, 64, 4, 1090, 1090, True),   # 560 work-groups: paired q-blocks, 35 of them
 ]
 
 
