@@ -570,6 +570,7 @@ GTA_CASES = [
     (1, 8, 4, 129, 64, 64),
     (1, 4, 4, 70, 64, 64),
     (1, 8, 2, 100, 128, 64),
+    (4, 16, 4, 520, 64, 64),  # 16 (batch, group) units of 5 q-blocks: 80 work-groups
 ]
 
 
