@@ -67,23 +67,28 @@ void gqa_decode_plan(int B, int h_kv, int n_rb, int L_max, int* split_len, int* 
 
 int gqa_row_blocks(int h_q, int h_kv, int s_q) { return ((h_q / h_kv) * s_q + 15) / 16; }
 
-// Plan of the streaming decode: teams of Z work-groups, about GHA_SD_WGS
-// work-groups in all (one per CU, a single round), share all 128-key chunks
-// of all units equally; fewer teams when there are fewer chunks than that.
+// Plan of the streaming decode: teams of Z work-groups, about `target`
+// work-groups in all (a single round: GHA_SD_WGS = one per CU for bf16
+// caches, GHA_SD_WGS_8BIT = two per CU for 8-bit caches, whose kernel sizes
+// its LDS for two), share all 128-key chunks of all units equally; fewer
+// teams when there are fewer chunks than that.
 // Z = 1 (units are (sequence, group)) unless the groups share a key part,
 // then Z = G (units are sequences, member j serves group j).  Partials: one
 // slot per team and per unit for each member, 16 or 32 padded rows each.
 #ifndef GHA_SD_WGS
 #define GHA_SD_WGS 256
 #endif
-int stream_decode_wgs(int B, int G, int Z, int L_max) {
+#ifndef GHA_SD_WGS_8BIT
+#define GHA_SD_WGS_8BIT 512
+#endif
+int stream_decode_wgs(int B, int G, int Z, int L_max, int target = GHA_SD_WGS) {
   const int64_t chunks = (int64_t)B * (G / Z) * ((L_max + gha::stream_decode_chunk() - 1) / gha::stream_decode_chunk());
-  const int64_t teams = std::max<int64_t>(1, std::min<int64_t>(GHA_SD_WGS / Z, chunks));
+  const int64_t teams = std::max<int64_t>(1, std::min<int64_t>(target / Z, chunks));
   return (int)(teams * Z);
 }
-size_t stream_decode_ws(int B, int G, int Z, int rows, int L_max, int dv) {
+size_t stream_decode_ws(int B, int G, int Z, int rows, int L_max, int dv, int target = GHA_SD_WGS) {
   const size_t rp = rows <= 16 ? 16 : 32;
-  const size_t n = ((size_t)stream_decode_wgs(B, G, Z, L_max) + (size_t)B * G) * rp;
+  const size_t n = ((size_t)stream_decode_wgs(B, G, Z, L_max, target) + (size_t)B * G) * rp;
   return n * (size_t)dv * 4 + n * 4 + (size_t)(B + 1) * 4;
 }
 // workspace carve-up: partial outputs, their log2-sum-exp, the chunk prefix sums
@@ -315,7 +320,8 @@ int window_keys(int L_max_hint, int s_q, int window) {
 size_t gqa_decode_paged_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint, int window, int d) {
   if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_max_hint < 1 || window < 0 || h_q % h_kv || d < 1) return 0;
   if ((h_q / h_kv) * s_q > 32) return 0;
-  return stream_decode_ws(B, h_kv, 1, (h_q / h_kv) * s_q, window_keys(L_max_hint, s_q, window), d);
+  // enough for either cache type (the 8-bit plan has more work-groups)
+  return stream_decode_ws(B, h_kv, 1, (h_q / h_kv) * s_q, window_keys(L_max_hint, s_q, window), d, GHA_SD_WGS_8BIT);
 }
 
 }  // extern "C"
@@ -361,7 +367,8 @@ gha_status stream_gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, con
     return fail(GHA_ERR_STRIDE, "one %s spans 2 GiB or more", paged ? "page" : "sequence");
   const int rows = (h_q / h_kv) * s_q;
   const int L_plan = window_keys(L_max_hint, s_q, window);
-  const size_t need = stream_decode_ws(B, h_kv, 1, rows, L_plan, d);
+  const int target = cache_dtype == GHA_FP8_E4M3 ? GHA_SD_WGS_8BIT : GHA_SD_WGS;
+  const size_t need = stream_decode_ws(B, h_kv, 1, rows, L_plan, d, target);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
@@ -379,7 +386,7 @@ gha_status stream_gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, con
   sa.lse = lse;
   sa.B = B; sa.n_groups = h_kv; sa.qpg = h_q / h_kv; sa.s_q = s_q; sa.rows = rows; sa.L_cap = L_cap;
   sa.team = 1;
-  sa.n_wg = stream_decode_wgs(B, h_kv, 1, L_plan);
+  sa.n_wg = stream_decode_wgs(B, h_kv, 1, L_plan, target);
   stream_decode_carve(sa, workspace, d);
   sa.scale = (scale > 0.f ? scale : 1.0f / std::sqrt((float)d)) * k_scale;
   sa.v_scale = v_scale;

@@ -63,9 +63,13 @@ struct SdLayout {
   static constexpr int RK1B = T * RK1ROW, RK2B = T * RK2ROW, RVB = T * RVROW;
   static constexpr int SLOT = RK1B + RK2B + NVS * RVB;          // one ring slot
   static constexpr int STAGE = EB == 2 ? 0 : TILE;              // the expanded tile
+  // LDS per work-group: all of a CU's for 16-bit tiles (one work-group per
+  // CU); half for 8-bit ones, so that two work-groups share a CU and one's
+  // expansion and softmax run beside the other's MFMAs
+  static constexpr int BUDGET = EB == 1 ? 80 * 1024 : 160 * 1024;
   // four waves per work-group when each can keep two tiles, else two
-  static constexpr int NW = 4 * (2 * SLOT + STAGE) <= 160 * 1024 ? 4 : 2;
-  static constexpr int NSLOT_FIT = ((160 * 1024) / NW - STAGE) / SLOT;
+  static constexpr int NW = 4 * (2 * SLOT + STAGE) <= BUDGET ? 4 : 2;
+  static constexpr int NSLOT_FIT = (BUDGET / NW - STAGE) / SLOT;
   static constexpr int NSLOT = NSLOT_FIT > 6 ? 6 : NSLOT_FIT;  // ring slots per wave
   static constexpr int WAVE = NSLOT * SLOT + STAGE;
   static constexpr int BYTES = NW * WAVE;
@@ -90,7 +94,9 @@ __device__ __forceinline__ int sd_chunks(const StreamDecodeArgs& a, int b) {
 }
 
 template <int DK1, int DK2, int DVW, int NVS, int EB = 2>
-constexpr int sd_tile_keys() { return SdLayout<DK1, DK2, DVW, NVS, 32, EB>::NSLOT >= 3 ? 32 : 16; }
+constexpr int sd_tile_keys() {
+  return EB == 1 ? 16 : (SdLayout<DK1, DK2, DVW, NVS, 32, EB>::NSLOT >= 3 ? 32 : 16);
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 // v_mfma_f32_16x16x16_bf16: lane (i, g) supplies A[i][4g .. 4g + 3] and
@@ -332,11 +338,12 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
     issue_tile(i + NSLOT - 1);                       // into the slot of tile i - 1
     wait_vmem_at_most<Ly::NDMA * (NSLOT - 1)>();     // tile i has landed
     const unsigned char* sl = smem + wave * Ly::WAVE + (i % NSLOT) * Ly::SLOT;
-    if constexpr (EB == 1) {
-      // expand the 8-bit tile into this wave's bf16 tile, row by row in
-      // 16-code chunks (exact: every E4M3 value is a bf16 value), into the
-      // swizzled layout the MFMA reads expect
-      unsigned char* st = smem + wave * Ly::WAVE + NSLOT * Ly::SLOT;
+    // expand part `part` (0: keys, 1: values) of the 8-bit tile into this
+    // wave's bf16 tile, row by row in 16-code chunks (exact: every E4M3
+    // value is a bf16 value), into the swizzled layout the MFMA reads expect
+    unsigned char* st = smem + wave * Ly::WAVE + NSLOT * Ly::SLOT;
+    const unsigned char* sl8 = sl;
+    auto expand = [&](int part) __attribute__((always_inline)) {
       constexpr int CPR = DK1 / 16;  // 16-code chunks per row (keys and values alike)
       auto cvt_lo = [](uint32_t w) -> uint32_t {  // codes 0, 1 of the word
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
@@ -345,11 +352,9 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
       };
 #pragma unroll
-      for (int part = 0; part < 2; ++part) {
-#pragma unroll
         for (int c0 = 0; c0 < T * CPR; c0 += 64) {
           const int c = c0 + lane, r = c / CPR, u8 = c % CPR;
-          const u32x4 w = ld16(sl + part * Ly::RK1B + 16 * c);
+          const u32x4 w = ld16(sl8 + part * Ly::RK1B + 16 * c);
           const u32x4 lo = {cvt_lo(w[0]), cvt_hi(w[0]), cvt_lo(w[1]), cvt_hi(w[1])};
           const u32x4 hi = {cvt_lo(w[2]), cvt_hi(w[2]), cvt_lo(w[3]), cvt_hi(w[3])};
           const int sw = part == 0 ? key_swz(Ly::K1ROW, r) : val_swz(Ly::VROW, r);
@@ -357,11 +362,16 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
           st16(row + 16 * ((2 * u8) ^ sw), lo);
           st16(row + 16 * ((2 * u8 + 1) ^ sw), hi);
         }
-      }
-      // the wave's LDS operations run in order, so its reads below see these
+      // the wave's LDS operations run in order, so its later reads see these
       // writes; keep the compiler from moving a read above a write whose
       // address it cannot relate (another lane's)
       asm volatile("" ::: "memory");
+    };
+    // keys now; values once the score MFMAs are issued, so that their
+    // expansion runs while the matrix core works (and its stores do not sit
+    // in the wave's LDS queue ahead of the key reads)
+    if constexpr (EB == 1) {
+      expand(0);
       sl = st;
     }
     const int key0 = start + (i * NWAVE + wave) * T;
@@ -382,6 +392,8 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
         for (int qt = 0; qt < QT; ++qt)
           sacc[kt][qt] = mfma_bf16(kf[kt], qf[qt][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kt][qt]);
     }
+
+    if constexpr (EB == 1) expand(1);
 
     // online softmax per row, running maximum moved lazily (log2 units); the
     // bf16 probabilities of a row are the value MFMA's P^T operand as they lie

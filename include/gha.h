@@ -160,6 +160,8 @@ gha_status gqa_decode_paged(const gha_tensor* q, const gha_tensor* k_cache,
                             int window, int d, gha_dtype in_dtype, gha_dtype out_dtype,
                             float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes for gqa_decode_paged and gqa_decode_fp8 with these sizes
+ * (the larger of the two plans; 0 for sizes either call rejects). */
 size_t gqa_decode_paged_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint,
                                         int window, int d);
 

@@ -138,9 +138,10 @@ def test_paged_decode_rejects_bad_arguments(lib, kw, status):
 
 
 def test_paged_decode_workspace_follows_the_window(lib):
-    # one slot per work-group (256) and per (sequence, KV head), 16 padded rows
+    # one slot per work-group and per (sequence, KV head), 16 padded rows; the
+    # size covers the 8-bit caches' plan of two work-groups per CU (512)
     full = lib.gqa_decode_paged_workspace_bytes(64, 32, 8, 1, 32768, 0, 128)
-    assert full == (256 + 64 * 8) * 16 * 129 * 4 + 65 * 4
+    assert full == (512 + 64 * 8) * 16 * 129 * 4 + 65 * 4
     # a short window has fewer chunks: fewer work-groups are planned
     short = lib.gqa_decode_paged_workspace_bytes(1, 4, 1, 1, 32768, 100, 128)
     assert short == (3 + 1) * 16 * 129 * 4 + 2 * 4
