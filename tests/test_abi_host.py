@@ -354,3 +354,17 @@ def test_valid_call_without_device_reports_hip_error(lib):
         pytest.skip("a GPU is present")
     assert prefill(lib) == 9
     assert b"device" in lib.gha_last_error()
+
+
+def test_fp8_decode_plans_two_work_groups_per_cu(lib):
+    # 8-bit caches plan 512 work-groups (two per CU) where 16-bit ones plan 256,
+    # so the bf16 plan's workspace is too small for them and the paged query
+    # covers both
+    big = dict(k=T(sb=1 << 26, sh=1 << 22, ss=128), v=T(sb=1 << 26, sh=1 << 22, ss=128),
+               L_cap=32768, L_max=32768)
+    full = lib.gqa_decode_paged_workspace_bytes(2, 32, 8, 1, 32768, 0, 128)
+    assert full == (512 + 2 * 8) * 16 * 129 * 4 + 3 * 4
+    bf16_plan = (256 + 2 * 8) * 16 * 129 * 4 + 3 * 4
+    assert fp8(lib, ws_bytes=bf16_plan, **big) == 8
+    assert fp8(lib, ws_bytes=full - 1, **big) == 8
+    assert fp8(lib, ws_bytes=full, **big) != 8   # passes the workspace check (then needs a GPU)
