@@ -107,6 +107,9 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
   const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)kvh * a.k_sh;
   const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)kvh * a.v_sh;
 
+  // A second pass reuses the LDS tile buffers: its first DMAs are issued
+  // after the first pass's last tile iteration, whose closing barrier every
+  // wave has passed once done reading them (its epilogue reads registers).
   for (int pass = 0; pass < n_pass; ++pass) {
   const int qb = pass == 0 ? n_qb - 1 - qi : qi;
   const int pos0 = qb * pos_per_wg + (wave % wph) * QT * 16;
