@@ -58,6 +58,8 @@ constexpr float kLatentSlack = 96.f;              // see the running state below
 #define GHA_LAT_SOFT_SLOTS 48
 #endif
 constexpr int kSoftSlots = GHA_LAT_SOFT_SLOTS;     // value MFMAs that carry the softmax (< 64)
+// the value MFMA after the last softmax slot publishes P^T, so one must follow
+static_assert(kSoftSlots > 0 && kSoftSlots < 64, "softmax slots must leave a value MFMA to publish after");
 
 // chunk swizzles of the LDS rows (see the layout above)
 __host__ __device__ constexpr int lat_sw(int k) { return ((k & 7) << 1) | ((k >> 3) & 1); }
