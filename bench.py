@@ -2,15 +2,22 @@
 """Benchmark of the grouped-head attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+                    [--only WORKLOAD]
 
 One step is one call of the path over one batch of synthetic input, already
 resident in HBM.  The headline workload is causal GQA prefill at batch 4,
 32 query heads over 8 KV heads, 4096 tokens, head dim 128, bf16 inputs with
 fp32 accumulation; `value` is its algorithmic attention TFLOP/s (the causal
 pair count times 4*d FLOP, whatever the kernel actually executes).  The other
-workloads (GQA decode, GTA shared-score prefill and decode, latent-absorbed
-decode, GQLA's per-group GQA-path decode) are timed the same way and reported
-under "extras".
+workloads (the fp32 worked-example shape, GQA decode, GTA shared-score
+prefill and decode, latent-absorbed decode, GQLA's per-group paths, paged,
+windowed and 8-bit caches) are timed the same way and reported under
+"extras".
+
+The CPU leg runs the fp64 oracle (test infrastructure, imported only there)
+after each timed GPU workload of the five reference shapes, on the same
+seeded inputs: it reports the oracle's own rate ("cpu_baseline") and the
+parity of the timed GPU output against it.
 
 Rank 0 prints one JSON line.  Only one GPU is used: --gpus above 1 exits.
 """
@@ -31,6 +38,7 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 from grouped_head_latent_amd import accounting as acc  # noqa: E402
 
+TINY = dict(B=1, h_q=8, h_kv=2, S=16, d=64, seed=0)
 PREFILL = dict(B=4, h_q=32, h_kv=8, S=4096, d=128, seed=2)
 DECODE = dict(B=64, h_q=32, h_kv=8, d=128, L_lo=1024, L_hi=32768, seed=3)
 GTA = dict(B=8, h=16, n_grp=4, S=2048, d=64, seed=4)
@@ -130,6 +138,21 @@ def time_steps(fn, steps, warmup, torch, flush=None):
 
 # ------------------------------------------------------------------ workloads
 
+def bench_tiny(gha, torch, steps, warmup):
+    """The GQA page's worked example shape in fp32: latency of one call."""
+    c = TINY
+    B, h_q, h_kv, S, d = c["B"], c["h_q"], c["h_kv"], c["S"], c["d"]
+    host = [synth.normal_f32(shp, c["seed"], synth.STREAM[n]) for shp, n in
+            (((B, h_q, S, d), "q"), ((B, h_kv, S, d), "k"), ((B, h_kv, S, d), "v"))]
+    q, k, v = (torch.from_numpy(x).cuda() for x in host)
+    o = torch.empty((B, h_q, S, d), dtype=torch.float32, device="cuda")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    ms, wall = time_steps(lambda: gha.gqa_prefill(q, k, v, causal=True, out=o), steps, warmup, torch, flush)
+    del flush
+    flops = acc.gqa_prefill_flops(B, h_q, S, S, d)
+    return dict(us=ms * 1e3, ms=ms, flops=flops, _host=host, _out=o.cpu().numpy())
+
+
 def bench_prefill(gha, torch, steps, warmup):
     c = PREFILL
     B, h_q, h_kv, S, d = c["B"], c["h_q"], c["h_kv"], c["S"], c["d"]
@@ -141,8 +164,9 @@ def bench_prefill(gha, torch, steps, warmup):
     ms, wall = time_steps(lambda: gha.gqa_prefill(q, k, v, causal=True, out=o), steps, warmup, torch, flush)
     del flush
     flops = acc.gqa_prefill_flops(B, h_q, S, S, d)
+    # the output of the last timed call (every call writes the same values)
     return dict(ms=ms, wall=wall, flops=flops, tflops=flops / ms / 1e9,
-                bytes=acc.gqa_prefill_bytes(B, h_q, h_kv, S, S, d))
+                bytes=acc.gqa_prefill_bytes(B, h_q, h_kv, S, S, d), _out=o.float().cpu().numpy())
 
 
 def bench_decode(gha, torch, steps, warmup, s_q):
@@ -150,9 +174,10 @@ def bench_decode(gha, torch, steps, warmup, s_q):
     B, h_q, h_kv, d = c["B"], c["h_q"], c["h_kv"], c["d"]
     L_cap = c["L_hi"]
     seqlens = synth.uniform_i32(B, c["L_lo"], c["L_hi"], c["seed"], synth.STREAM["seqlens"])
-    kc = to_dev(synth.cache_bf16(B, h_kv, L_cap, d, seqlens, c["seed"], 2), torch)
-    vc = to_dev(synth.cache_bf16(B, h_kv, L_cap, d, seqlens, c["seed"], 3), torch)
-    q = to_dev(synth.normal_bf16((B, h_q, s_q, d), c["seed"], 1), torch)
+    kb = synth.cache_bf16(B, h_kv, L_cap, d, seqlens, c["seed"], 2)
+    vb = synth.cache_bf16(B, h_kv, L_cap, d, seqlens, c["seed"], 3)
+    qb = synth.normal_bf16((B, h_q, s_q, d), c["seed"], 1)
+    kc, vc, q = to_dev(kb, torch), to_dev(vb, torch), to_dev(qb, torch)
     sl = torch.from_numpy(seqlens).cuda()
     o = torch.empty((B, h_q, s_q, d), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(gha.gqa_decode_workspace_bytes(B, h_q, h_kv, s_q, L_cap, d), dtype=torch.uint8, device="cuda")
@@ -161,7 +186,7 @@ def bench_decode(gha, torch, steps, warmup, s_q):
     fl = acc.gqa_decode_flops(seqlens, h_q, s_q, d)
     del kc, vc
     return dict(ms=ms, gbps=by / ms / 1e6, tflops=fl / ms / 1e9, bytes=by, flops=fl,
-                sum_L=int(seqlens.sum()))
+                sum_L=int(seqlens.sum()), _host=(qb, kb, vb, seqlens), _out=o.float().cpu().numpy())
 
 
 def bench_decode_paged(gha, torch, steps, warmup, s_q, window):
@@ -244,15 +269,16 @@ def bench_gqla_prefill(gha, torch, steps, warmup):
 def bench_gta(gha, torch, steps, warmup):
     c = GTA
     B, h, g, S, d = c["B"], c["h"], c["n_grp"], c["S"], c["d"]
-    q = to_dev(synth.normal_bf16((B, g, S, d), c["seed"], 1), torch)
-    k = to_dev(synth.normal_bf16((B, g, S, d), c["seed"], 2), torch)
-    v = to_dev(synth.normal_bf16((B, h, S, d), c["seed"], 3), torch)
+    host = (synth.normal_bf16((B, g, S, d), c["seed"], 1), synth.normal_bf16((B, g, S, d), c["seed"], 2),
+            synth.normal_bf16((B, h, S, d), c["seed"], 3))
+    q, k, v = (to_dev(x, torch) for x in host)
     o = torch.empty((B, h, S, d), dtype=torch.bfloat16, device="cuda")
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     ms, wall = time_steps(lambda: gha.gta_shared_score_prefill(q, k, v, out=o), steps, warmup, torch, flush)
     del flush
     fl = acc.gta_prefill_flops(B, h, g, S, d, d)
-    return dict(ms=ms, tflops=fl / ms / 1e9, flops=fl)
+    return dict(ms=ms, tflops=fl / ms / 1e9, flops=fl, bytes=acc.gta_prefill_bytes(B, h, g, S, d, d),
+                _host=host, _out=o.float().cpu().numpy())
 
 
 def bench_gta_decode(gha, torch, steps, warmup, s_q):
@@ -305,9 +331,10 @@ def bench_latent(gha, torch, steps, warmup, s_q):
     B, h_q, r, dr = c["B"], c["h_q"], c["r_kv"], c["d_r"]
     L_cap = c["L_hi"]
     seqlens = synth.uniform_i32(B, c["L_lo"], c["L_hi"], c["seed"], synth.STREAM["seqlens"])
-    cache = to_dev(synth.latent_cache_bf16(B, L_cap, r + dr, seqlens, c["seed"], synth.STREAM["latent"]), torch)
-    q_lat = to_dev(synth.normal_bf16((B, s_q, h_q, r), c["seed"], synth.STREAM["q"], 0.25), torch)
-    q_r = to_dev(synth.normal_bf16((B, s_q, h_q, dr), c["seed"], synth.STREAM["q_rope"]), torch)
+    cb = synth.latent_cache_bf16(B, L_cap, r + dr, seqlens, c["seed"], synth.STREAM["latent"])
+    qb = synth.normal_bf16((B, s_q, h_q, r), c["seed"], synth.STREAM["q"], 0.25)
+    qrb = synth.normal_bf16((B, s_q, h_q, dr), c["seed"], synth.STREAM["q_rope"])
+    cache, q_lat, q_r = to_dev(cb, torch), to_dev(qb, torch), to_dev(qrb, torch)
     sl = torch.from_numpy(seqlens).cuda()
     o = torch.empty((B, s_q, h_q, r), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(gha.latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_cap, r), dtype=torch.uint8, device="cuda")
@@ -318,7 +345,7 @@ def bench_latent(gha, torch, steps, warmup, s_q):
     fl = acc.latent_decode_flops(seqlens, h_q, s_q, r, dr)
     del cache
     return dict(ms=ms, gbps=by / ms / 1e6, tflops=fl / ms / 1e9, bytes=by, flops=fl,
-                sum_L=int(seqlens.sum()))
+                sum_L=int(seqlens.sum()), _host=(qb, qrb, cb, seqlens, scale), _out=o.float().cpu().numpy())
 
 
 def bench_absorbing(gha, torch, steps, warmup, s_q):
@@ -345,34 +372,192 @@ def bench_absorbing(gha, torch, steps, warmup, s_q):
     return dict(ms=ms, gbps=by / ms / 1e6, tflops=fl / ms / 1e9, bytes=by, flops=fl, sum_L=int(seqlens.sum()))
 
 
-# ---------------------------------------------------------------- CPU oracle
+# ------------------------------------------------------- CPU leg: the oracle
+# The fp64 oracle is test infrastructure; it is imported and run only in the
+# functions of this section, on the host, after a workload's GPU timing, on
+# the same seeded inputs.  Each leg times the oracle on the full output (or a
+# stated bounded sample) and compares the timed GPU output with it.
 
-def cpu_baseline(max_seconds=15.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the headline
-    workload: whole (batch, head) slices of the causal prefill, as many as
-    fit in about `max_seconds`, scaled to TFLOP/s with the same algorithmic
-    count as the GPU figure."""
-    import oracle
+def _cpu_threads() -> int:
     from threadpoolctl import threadpool_info
+    return max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+
+
+class Parity:
+    """Running max and mean |GPU - oracle| over the compared elements.  For
+    bf16 outputs an element also passes when it is within half a bf16 ulp of
+    the reference (the output rounding alone reaches 1e-2 at |o| >= 4)."""
+
+    def __init__(self, bf16_out: bool, max_abs: float = 1e-2, mean_abs: float = 1e-3):
+        self.bf16_out, self.max_bar, self.mean_bar = bf16_out, max_abs, mean_abs
+        self.max, self.sum, self.n, self.over, self.nonfinite = 0.0, 0.0, 0, 0, 0
+
+    def add(self, got, ref):
+        got = np.asarray(got, dtype=np.float64)
+        self.nonfinite += int((~np.isfinite(got)).sum())
+        err = np.abs(got - ref)
+        allowed = self.max_bar
+        if self.bf16_out:
+            allowed = np.maximum(self.max_bar, 0.5 * np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7))
+        self.over += int((err > allowed).sum())
+        self.max = max(self.max, float(np.nanmax(err)) if err.size else 0.0)
+        self.sum += float(np.nansum(err))
+        self.n += err.size
+
+    def record(self, what: str):
+        mean = self.sum / max(self.n, 1)
+        ok = self.over == 0 and self.nonfinite == 0 and mean <= self.mean_bar
+        return {"max_abs": self.max, "mean_abs": mean, "elements": self.n, "over_bar": self.over,
+                "nonfinite": self.nonfinite, "ok": ok, "compared": what,
+                "bar": f"max <= {self.max_bar:g}" + (" or half a bf16 ulp" if self.bf16_out else "")
+                       + f", mean <= {self.mean_bar:g}"}
+
+
+def cpu_tiny(res):
+    import oracle
+    q, k, v = (x.astype(np.float64) for x in res["_host"])
+    t0 = time.perf_counter()
+    ref, _ = oracle.gqa_prefill(q, k, v, causal=True)
+    t = time.perf_counter() - t0
+    par = Parity(False, max_abs=1e-5, mean_abs=1e-5)
+    par.add(res["_out"], ref)
+    return ({"value": t * 1e6, "unit": "us", "cores": _cpu_threads(), "kind": "oracle",
+             "sample": "the full output (1 x 8 x 16 x 64, fp32 in, fp64 oracle)"},
+            par.record("every element of the timed output"))
+
+
+def cpu_prefill(res, budget_s=40.0):
+    """The oracle on whole (batch, head) slices of the causal prefill, all 128
+    unless `budget_s` of oracle time runs out first; the same slices of the
+    timed GPU output are compared with it."""
+    import oracle
     c = PREFILL
     B, h_q, h_kv, S, d = c["B"], c["h_q"], c["h_kv"], c["S"], c["d"]
     G = h_q // h_kv
+    par = Parity(True)
     done, t_total = 0, 0.0
     pairs = [(b, i) for b in range(B) for i in range(h_q)]
-    while done < len(pairs) and t_total < max_seconds:
+    while done < len(pairs) and t_total < budget_s:
         b, i = pairs[done]
         q = oracle.widen_bf16(synth.normal_bf16_rows((B, h_q, S, d), c["seed"], 1, (b, i)))
         k = oracle.widen_bf16(synth.normal_bf16_rows((B, h_kv, S, d), c["seed"], 2, (b, i // G)))
         v = oracle.widen_bf16(synth.normal_bf16_rows((B, h_kv, S, d), c["seed"], 3, (b, i // G)))
         t0 = time.perf_counter()
-        oracle.gqa_prefill(q[None, None], k[None, None], v[None, None], causal=True)
+        ref, _ = oracle.gqa_prefill(q[None, None], k[None, None], v[None, None], causal=True)
         t_total += time.perf_counter() - t0
+        par.add(res["_out"][b, i], ref[0, 0])
         done += 1
     flops = done * acc.gqa_prefill_flops(1, 1, S, S, d)
-    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {B * h_q} (batch, head) slices of the causal prefill "
-                      f"(4096 x 4096 x 128 each), fp64 numpy, {t_total:.1f} s"}
+    what = "all" if done == len(pairs) else f"{done} of {len(pairs)}"
+    return ({"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": _cpu_threads(), "kind": "oracle",
+             "seconds": t_total,
+             "sample": f"{what} (batch, head) slices of the causal prefill ({S} x {S} x {d} each), "
+                       f"fp64 numpy, {t_total:.1f} s"},
+            par.record(f"{what} (batch, head) slices of the timed bf16 output"))
+
+
+def _decode_rate(by, t, done, total):
+    what = "all" if done == total else f"{done} of {total}"
+    return {"value": by / t / 1e9, "unit": "GB/s", "cores": _cpu_threads(), "kind": "oracle", "seconds": t,
+            "sample": f"{what} sequences ({by / 1e9:.2f} GB of algorithmic traffic), fp64 numpy, {t:.1f} s"}
+
+
+def cpu_decode(res, s_q, budget_s=60.0):
+    import oracle
+    c = DECODE
+    qb, kb, vb, seqlens = res["_host"]
+    par = Parity(True)
+    t, done, by = 0.0, 0, 0.0
+    for b in range(c["B"]):
+        if t >= budget_s:
+            break
+        L = int(seqlens[b])
+        q, k, v = oracle.widen_bf16(qb[b:b + 1]), oracle.widen_bf16(kb[b:b + 1, :, :L]), oracle.widen_bf16(vb[b:b + 1, :, :L])
+        t0 = time.perf_counter()
+        ref, _ = oracle.gqa_decode(q, k, v, np.array([L]))
+        t += time.perf_counter() - t0
+        par.add(res["_out"][b:b + 1], ref)
+        by += acc.gqa_decode_bytes(seqlens[b:b + 1], c["h_q"], c["h_kv"], s_q, c["d"])
+        done += 1
+    return _decode_rate(by, t, done, c["B"]), par.record(f"{done} of {c['B']} sequences of the timed bf16 output")
+
+
+def cpu_gta(res):
+    import oracle
+    qb, kb, vb = res["_host"]
+    q, k, v = (oracle.widen_bf16(x) for x in (qb, kb, vb))
+    t0 = time.perf_counter()
+    ref, _ = oracle.gta_prefill(q, k, v, causal=True)
+    t = time.perf_counter() - t0
+    par = Parity(True)
+    par.add(res["_out"], ref)
+    return ({"value": res["flops"] / t / 1e12, "unit": "TFLOP/s", "cores": _cpu_threads(), "kind": "oracle",
+             "seconds": t, "sample": f"the full output, fp64 numpy, {t:.1f} s"},
+            par.record("every element of the timed bf16 output"))
+
+
+def cpu_latent(res, s_q, budget_s=60.0):
+    import oracle
+    c = LATENT
+    qb, qrb, cb, seqlens, scale = res["_host"]
+    r = c["r_kv"]
+    par = Parity(True)
+    t, done, by = 0.0, 0, 0.0
+    for b in range(c["B"]):
+        if t >= budget_s:
+            break
+        L = int(seqlens[b])
+        cache = oracle.widen_bf16(cb[b:b + 1, :L])
+        q, qr = oracle.widen_bf16(qb[b:b + 1]), oracle.widen_bf16(qrb[b:b + 1])
+        t0 = time.perf_counter()
+        ref, _ = oracle.latent_absorb_decode(q, qr, cache[..., :r], cache[..., r:], np.array([L]), scale=scale)
+        t += time.perf_counter() - t0
+        par.add(res["_out"][b:b + 1], ref)
+        by += acc.latent_decode_bytes(seqlens[b:b + 1], c["h_q"], s_q, r, c["d_r"])
+        done += 1
+    return _decode_rate(by, t, done, c["B"]), par.record(f"{done} of {c['B']} sequences of the timed bf16 output")
+
+
+# ------------------------------------------------------------------ provenance
+
+def provenance(torch):
+    """CPU model and threads, GPU name and clocks, ROCm and torch versions."""
+    import ctypes
+    import platform
+    env = {"host": platform.node()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            env["cpu_model"] = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        env["cpu_model"] = None
+    env["cpu_threads_available"] = len(os.sched_getaffinity(0))
+    p = torch.cuda.get_device_properties(0)
+    env["gpu_name"] = p.name
+    env["gpu_arch"] = getattr(p, "gcnArchName", None)
+    env["gpu_cus"] = p.multi_processor_count
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int()
+        # hipDeviceAttributeClockRate = 5, hipDeviceAttributeMemoryClockRate = 60
+        # (enum hipDeviceAttribute_t in hip_runtime_api.h), both in kHz
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) == 0:
+            env["gpu_peak_sclk_mhz"] = val.value / 1000
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 60, 0) == 0:
+            env["gpu_peak_mclk_mhz"] = val.value / 1000
+    except OSError:
+        pass
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        env["rocm"] = None
+    env["torch"] = torch.__version__
+    env["torch_hip"] = torch.version.hip
+    return env
+
+
+def strip(res):
+    """A workload's record without the host arrays the CPU leg used."""
+    return {k: v for k, v in res.items() if not k.startswith("_")}
 
 
 def main():
@@ -381,9 +566,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs (and their parity)")
     ap.add_argument("--only", default=None,
-                    help="prefill|gqla_prefill|decode|paged|fp8|gta|latent|absorbing|gta_decode|gqla_decode: "
+                    help="tiny|prefill|gqla_prefill|decode|paged|fp8|gta|latent|absorbing|gta_decode|gqla_decode: "
                          "time one workload")
     ap.add_argument("--spinup-s", type=float, default=1.0,
                     help="untimed seconds of the same workload before the warmup steps (clock ramp)")
@@ -403,72 +588,78 @@ def main():
     gha.load_library()
 
     only = args.only
+    cpu = not args.no_cpu
     extras = {}
     head = None
+    head_cpu = head_parity = None
+
+    def run(name, fn, cpu_fn=None):
+        log(f"{name} ...")
+        res = fn()
+        if cpu and cpu_fn is not None:
+            log(f"{name}: oracle ...")
+            res["cpu_baseline"], res["parity"] = cpu_fn(res)
+        res = strip(res)
+        log(f"{name}: {res}")
+        torch.cuda.empty_cache()
+        return res
+
+    want = lambda w: only == w or (only is None and not args.no_extras)
+    steps, warmup = args.steps, args.warmup
+    if want("tiny"):
+        extras["tiny_gqa_fp32"] = run("tiny", lambda: bench_tiny(gha, torch, steps, warmup), cpu_tiny)
     if only in (None, "prefill"):
         log("prefill ...")
-        head = bench_prefill(gha, torch, args.steps, args.warmup)
+        head = bench_prefill(gha, torch, steps, warmup)
         log(f"prefill {head['ms']:.4f} ms {head['tflops']:.1f} TFLOP/s")
-    if not args.no_extras or only is not None:
-        if only in (None, "gta"):
-            log("gta ...")
-            extras["gta_prefill"] = bench_gta(gha, torch, args.steps, args.warmup)
-            log(extras["gta_prefill"])
-        if only in (None, "gqla_prefill"):
-            log("gqla prefill ...")
-            extras["gqla_prefill"] = bench_gqla_prefill(gha, torch, args.steps, args.warmup)
-            log(extras["gqla_prefill"])
-            torch.cuda.empty_cache()
-        if only in (None, "decode"):
-            for s_q in (1, 2):
-                log(f"decode s_q={s_q} ...")
-                extras[f"gqa_decode_sq{s_q}"] = bench_decode(gha, torch, args.steps, args.warmup, s_q)
-                log(extras[f"gqa_decode_sq{s_q}"])
-                torch.cuda.empty_cache()
-        if only in (None, "paged"):
-            for s_q, window in ((1, 0), (2, 0), (1, PAGED["window"])):
-                name = f"gqa_decode_paged{PAGED['page']}" + (f"_window{window}" if window else "") + f"_sq{s_q}"
-                log(f"{name} ...")
-                extras[name] = bench_decode_paged(gha, torch, args.steps, args.warmup, s_q, window)
-                log(extras[name])
-                torch.cuda.empty_cache()
-        if only in (None, "fp8"):
-            for s_q in (1, 2):
-                log(f"fp8 decode s_q={s_q} ...")
-                extras[f"gqa_decode_fp8_sq{s_q}"] = bench_decode_fp8(gha, torch, args.steps, args.warmup, s_q)
-                log(extras[f"gqa_decode_fp8_sq{s_q}"])
-                torch.cuda.empty_cache()
-        if only in (None, "latent"):
-            for s_q in (1, 2):
-                log(f"latent s_q={s_q} ...")
-                extras[f"latent_decode_sq{s_q}"] = bench_latent(gha, torch, args.steps, args.warmup, s_q)
-                log(extras[f"latent_decode_sq{s_q}"])
-                torch.cuda.empty_cache()
-        if only in (None, "absorbing"):
-            for s_q in (1, 2):
-                log(f"absorbing latent decode s_q={s_q} ...")
-                extras[f"latent_absorbing_decode_sq{s_q}"] = bench_absorbing(gha, torch, args.steps, args.warmup, s_q)
-                log(extras[f"latent_absorbing_decode_sq{s_q}"])
-                torch.cuda.empty_cache()
-        if only in (None, "gta_decode"):
-            for s_q in (1, 2):
-                log(f"gta decode s_q={s_q} ...")
-                extras[f"gta_decode_sq{s_q}"] = bench_gta_decode(gha, torch, args.steps, args.warmup, s_q)
-                log(extras[f"gta_decode_sq{s_q}"])
-                torch.cuda.empty_cache()
-        if only in (None, "gqla_decode"):
-            for s_q in (1, 2):
-                log(f"gqla decode s_q={s_q} ...")
-                extras[f"gqla_decode_sq{s_q}"] = bench_gqla_decode(gha, torch, args.steps, args.warmup, s_q)
-                log(extras[f"gqla_decode_sq{s_q}"])
-                torch.cuda.empty_cache()
-    for k_, e in extras.items():
+        if cpu:
+            log("prefill: oracle ...")
+            head_cpu, head_parity = cpu_prefill(head)
+        head = strip(head)
+        torch.cuda.empty_cache()
+    if want("gta"):
+        extras["gta_prefill"] = run("gta", lambda: bench_gta(gha, torch, steps, warmup), cpu_gta)
+    if want("gqla_prefill"):
+        extras["gqla_prefill"] = run("gqla prefill", lambda: bench_gqla_prefill(gha, torch, steps, warmup))
+    if want("decode"):
+        for s_q in (1, 2):
+            extras[f"gqa_decode_sq{s_q}"] = run(f"decode s_q={s_q}",
+                                                lambda: bench_decode(gha, torch, steps, warmup, s_q),
+                                                lambda r: cpu_decode(r, s_q))
+    if want("paged"):
+        for s_q, window in ((1, 0), (2, 0), (1, PAGED["window"])):
+            name = f"gqa_decode_paged{PAGED['page']}" + (f"_window{window}" if window else "") + f"_sq{s_q}"
+            extras[name] = run(name, lambda: bench_decode_paged(gha, torch, steps, warmup, s_q, window))
+    if want("fp8"):
+        for s_q in (1, 2):
+            extras[f"gqa_decode_fp8_sq{s_q}"] = run(f"fp8 decode s_q={s_q}",
+                                                    lambda: bench_decode_fp8(gha, torch, steps, warmup, s_q))
+    if want("latent"):
+        for s_q in (1, 2):
+            extras[f"latent_decode_sq{s_q}"] = run(f"latent s_q={s_q}",
+                                                   lambda: bench_latent(gha, torch, steps, warmup, s_q),
+                                                   lambda r: cpu_latent(r, s_q))
+    if want("absorbing"):
+        for s_q in (1, 2):
+            extras[f"latent_absorbing_decode_sq{s_q}"] = run(
+                f"absorbing latent decode s_q={s_q}", lambda: bench_absorbing(gha, torch, steps, warmup, s_q))
+    if want("gta_decode"):
+        for s_q in (1, 2):
+            extras[f"gta_decode_sq{s_q}"] = run(f"gta decode s_q={s_q}",
+                                                lambda: bench_gta_decode(gha, torch, steps, warmup, s_q))
+    if want("gqla_decode"):
+        for s_q in (1, 2):
+            extras[f"gqla_decode_sq{s_q}"] = run(f"gqla decode s_q={s_q}",
+                                                 lambda: bench_gqla_decode(gha, torch, steps, warmup, s_q))
+    for e in extras.values():
         if "gbps" in e:
             e["hbm_frac"] = e["gbps"] / acc.PEAK_HBM_GBPS
-        e["mfma_frac"] = e["tflops"] / acc.PEAK_BF16_TFLOPS
+        if "tflops" in e:
+            e["mfma_frac"] = e["tflops"] / acc.PEAK_BF16_TFLOPS
 
+    env = provenance(torch)
     if head is None:
-        print(json.dumps({"extras": extras}))
+        print(json.dumps({"extras": extras, "env": env}))
         return
     out = {
         "metric": "decode HBM GB/s (% of peak) + prefill attention TFLOPS (% of MFMA peak)",
@@ -492,11 +683,12 @@ def main():
                      "traffic": measured_traffic("prefill_d128_kernel<2, false, 0>"),
                      "algorithmic_bytes": head["bytes"]},
     }
-    if not args.no_cpu:
-        log("cpu baseline ...")
-        out["cpu_baseline"] = cpu_baseline()
+    if head_cpu is not None:
+        out["cpu_baseline"] = head_cpu
+        out["parity"] = head_parity
     if extras:
         out["extras"] = extras
+    out["env"] = env
     print(json.dumps(out))
 
 

@@ -9,9 +9,12 @@ the library's HIP kernels; there is no fallback of any kind.  If the library
 is missing or cannot be loaded, every call raises.
 
 Entry points (same names as the C ABI):
-  gqa_prefill, gqa_decode, gta_shared_score_prefill, gta_shared_score_decode,
-  gqla_gqa_decode, latent_absorb_decode, and the *_workspace_bytes queries of
-  the decode calls.
+  gqa_prefill, gqa_decode, gqa_decode_paged, gqa_decode_fp8,
+  gta_shared_score_prefill, gta_shared_score_decode, gqla_gqa_decode,
+  gqla_gqa_prefill, latent_absorb_decode, gqla_absorb_decode, and the
+  *_workspace_bytes queries of the decode calls.  Every wrapper checks, before
+  the library is called, that all tensors sit on the query's GPU and carry
+  the dtypes the call expects.
 """
 from __future__ import annotations
 
@@ -146,7 +149,49 @@ def _ptr(t):
 
 def _out_code(out_dtype):
     import torch
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"outputs are bf16 or fp32, not {out_dtype}")
     return GHA_F32 if out_dtype == torch.float32 else GHA_BF16
+
+
+def _same_device(ref, **tensors):
+    """Every given tensor must live on `ref`'s GPU: a host tensor or one on
+    another device would hand the kernels a pointer they cannot read."""
+    if not ref.is_cuda:
+        raise ValueError("inputs must be GPU tensors")
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, not on {ref.device} with the query")
+
+
+def _need_dtype(allowed, **tensors):
+    """Each given tensor must have one of the `allowed` dtypes."""
+    for name, t in tensors.items():
+        if t is not None and t.dtype not in allowed:
+            raise TypeError(f"{name} has dtype {t.dtype}; expected one of {allowed}")
+
+
+def _need_same_dtype(ref_name, ref, **tensors):
+    for name, t in tensors.items():
+        if t.dtype != ref.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype} but {ref_name} has {ref.dtype}")
+
+
+def _check_common(q, q_name, *, inputs, seqlens=None, extra=None, out=None, out_dtype=None, workspace=None):
+    """The checks every wrapper makes before calling the library: all tensors
+    on q's GPU, inputs of q's dtype (bf16), int32 lengths, bf16 or fp32
+    outputs, a byte workspace."""
+    import torch
+    _need_same_dtype(q_name, q, **inputs)
+    if seqlens is not None and seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    _need_dtype((torch.bfloat16, torch.float32), out=out)
+    if out_dtype is not None:
+        _out_code(out_dtype)
+    _need_dtype((torch.int32,), **{k: t for k, t in (extra or {}).items() if k == "block_table"})
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _same_device(q, **inputs, **(extra or {}), seqlens=seqlens, out=out, workspace=workspace)
 
 
 # ------------------------------------------------------------------ wrappers
@@ -157,6 +202,8 @@ def gqa_prefill(q, k, v, *, causal: bool = True, scale: float | None = None, out
     for the fp32 path).  Returns o (B, h_q, S_q, d) [and lse (B, h_q, S_q)]."""
     import torch
     lib = load_library()
+    _need_dtype((torch.bfloat16, torch.float32), q=q)
+    _check_common(q, "q", inputs=dict(k=k, v=v), out=out, out_dtype=out_dtype)
     B, h_q, S_q, d = q.shape
     h_kv, S_k = k.shape[1], k.shape[2]
     out_dtype = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
@@ -179,6 +226,9 @@ def gqa_decode(q, k_cache, v_cache, seqlens, *, L_max: int | None = None,
     L_max: an upper bound on the lengths (default L_cap)."""
     import torch
     lib = load_library()
+    _need_dtype((torch.bfloat16,), q=q)
+    _check_common(q, "q", inputs=dict(k_cache=k_cache, v_cache=v_cache), seqlens=seqlens, out=out, out_dtype=out_dtype,
+                  workspace=workspace)
     B, h_q, s_q, d = q.shape
     h_kv, L_cap = k_cache.shape[1], k_cache.shape[2]
     L_max = L_cap if L_max is None else int(L_max)
@@ -187,8 +237,6 @@ def gqa_decode(q, k_cache, v_cache, seqlens, *, L_max: int | None = None,
     lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=q.device) if return_lse else None
     need = gqa_decode_workspace_bytes(B, h_q, h_kv, s_q, L_max, d)
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if seqlens.dtype != torch.int32:
-        raise TypeError("seqlens must be int32")
     _check(lib.gqa_decode(_desc(q), _desc(k_cache), _desc(v_cache), _ptr(seqlens), _desc(o),
                           _ptr(lse), B, h_q, h_kv, s_q, L_cap, L_max, d, _dtype_code(q),
                           _out_code(o.dtype), float(scale or 0.0), _ptr(ws), ws.numel() * ws.element_size(),
@@ -213,6 +261,9 @@ def gqa_decode_paged(q, k_cache, v_cache, seqlens, *, block_table=None, page_siz
     the lengths (default L_cap)."""
     import torch
     lib = load_library()
+    _need_dtype((torch.bfloat16,), q=q)
+    _check_common(q, "q", inputs=dict(k_cache=k_cache, v_cache=v_cache), seqlens=seqlens, out=out, out_dtype=out_dtype,
+                  workspace=workspace, extra=dict(block_table=block_table))
     B, h_q, s_q, d = q.shape
     h_kv = k_cache.shape[1]
     if block_table is None:
@@ -230,8 +281,6 @@ def gqa_decode_paged(q, k_cache, v_cache, seqlens, *, block_table=None, page_siz
     lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=q.device) if return_lse else None
     need = gqa_decode_paged_workspace_bytes(B, h_q, h_kv, s_q, L_max, int(window), d)
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if seqlens.dtype != torch.int32:
-        raise TypeError("seqlens must be int32")
     _check(lib.gqa_decode_paged(_desc(q), _desc(k_cache), _desc(v_cache), _ptr(block_table), bt_stride,
                                 page_size, _ptr(seqlens), _desc(o), _ptr(lse), B, h_q, h_kv, s_q, L_cap,
                                 L_max, int(window), d, _dtype_code(q), _out_code(o.dtype),
@@ -251,6 +300,9 @@ def gqa_decode_fp8(q, k_codes, v_codes, seqlens, *, k_scale: float, v_scale: flo
     lib = load_library()
     if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
         raise TypeError("the caches hold uint8 E4M3 codes")
+    _need_dtype((torch.bfloat16,), q=q)
+    _check_common(q, "q", inputs={}, seqlens=seqlens, out=out, out_dtype=out_dtype, workspace=workspace,
+                  extra=dict(k_codes=k_codes, v_codes=v_codes, block_table=block_table))
     B, h_q, s_q, d = q.shape
     h_kv = k_codes.shape[1]
     if block_table is None:
@@ -268,8 +320,6 @@ def gqa_decode_fp8(q, k_codes, v_codes, seqlens, *, k_scale: float, v_scale: flo
     lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=q.device) if return_lse else None
     need = gqa_decode_paged_workspace_bytes(B, h_q, h_kv, s_q, L_max, int(window), d)
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if seqlens.dtype != torch.int32:
-        raise TypeError("seqlens must be int32")
     _check(lib.gqa_decode_fp8(_desc(q), _desc(k_codes), _desc(v_codes), float(k_scale), float(v_scale),
                               _ptr(block_table), bt_stride, page_size, _ptr(seqlens), _desc(o), _ptr(lse), B, h_q,
                               h_kv, s_q, L_cap, L_max, int(window), d, _out_code(o.dtype), float(scale or 0.0),
@@ -283,6 +333,8 @@ def gta_shared_score_prefill(q, k, v, *, causal: bool = True, scale: float | Non
     [and lse (B, n_grp, S)]."""
     import torch
     lib = load_library()
+    _need_dtype((torch.bfloat16,), q=q)
+    _check_common(q, "q", inputs=dict(k=k, v=v), out=out, out_dtype=out_dtype)
     B, n_grp, S, d_qk = q.shape
     h, d_v = v.shape[1], v.shape[3]
     out_dtype = out_dtype or torch.bfloat16
@@ -306,6 +358,9 @@ def gta_shared_score_decode(q, k_cache, v_cache, seqlens, *, L_max: int | None =
     [and lse (B, n_grp, s_q)]."""
     import torch
     lib = load_library()
+    _need_dtype((torch.bfloat16,), q=q)
+    _check_common(q, "q", inputs=dict(k_cache=k_cache, v_cache=v_cache), seqlens=seqlens, out=out, out_dtype=out_dtype,
+                  workspace=workspace)
     B, n_grp, s_q, d_qk = q.shape
     h, L_cap, d_v = v_cache.shape[1], v_cache.shape[2], v_cache.shape[3]
     L_max = L_cap if L_max is None else int(L_max)
@@ -314,8 +369,6 @@ def gta_shared_score_decode(q, k_cache, v_cache, seqlens, *, L_max: int | None =
     lse = torch.empty((B, n_grp, s_q), dtype=torch.float32, device=q.device) if return_lse else None
     need = gta_shared_score_decode_workspace_bytes(B, h, n_grp, s_q, L_max, d_v)
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if seqlens.dtype != torch.int32:
-        raise TypeError("seqlens must be int32")
     _check(lib.gta_shared_score_decode(_desc(q), _desc(k_cache), _desc(v_cache), _ptr(seqlens), _desc(o),
                                        _ptr(lse), B, h, n_grp, s_q, L_cap, L_max, d_qk, d_v, _dtype_code(q),
                                        _out_code(o.dtype), float(scale or 0.0), _ptr(ws),
@@ -334,6 +387,9 @@ def gqla_gqa_decode(q_c, q_r, k_c, k_r, v_cache, seqlens, *, scale: float, L_max
     Returns o (B, h_q, s_q, d_h) [and lse (B, h_q, s_q)]."""
     import torch
     lib = load_library()
+    _need_dtype((torch.bfloat16,), q_c=q_c)
+    _check_common(q_c, "q_c", inputs=dict(q_r=q_r, k_c=k_c, k_r=k_r, v_cache=v_cache), seqlens=seqlens,
+                  out=out, out_dtype=out_dtype, workspace=workspace)
     B, h_q, s_q, d_h = q_c.shape
     d_r = q_r.shape[3]
     g, L_cap = k_c.shape[1], k_c.shape[2]
@@ -343,8 +399,6 @@ def gqla_gqa_decode(q_c, q_r, k_c, k_r, v_cache, seqlens, *, scale: float, L_max
     lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=q_c.device) if return_lse else None
     need = gqla_gqa_decode_workspace_bytes(B, h_q, g, s_q, L_max, d_h)
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q_c.device)
-    if seqlens.dtype != torch.int32:
-        raise TypeError("seqlens must be int32")
     _check(lib.gqla_gqa_decode(_desc(q_c), _desc(q_r), _desc(k_c), _desc(k_r, (0, None, 1)), _desc(v_cache),
                                _ptr(seqlens), _desc(o), _ptr(lse), B, h_q, g, s_q, L_cap, L_max, d_h, d_r,
                                _dtype_code(q_c), _out_code(o.dtype), float(scale), _ptr(ws),
@@ -359,6 +413,8 @@ def gqla_gqa_prefill(q_c, q_r, k_c, k_r, v, *, scale: float, causal: bool = True
     [and lse (B, h_q, S_q)]."""
     import torch
     lib = load_library()
+    _need_dtype((torch.bfloat16,), q_c=q_c)
+    _check_common(q_c, "q_c", inputs=dict(q_r=q_r, k_c=k_c, k_r=k_r, v=v), out=out, out_dtype=out_dtype)
     B, h_q, S_q, d_h = q_c.shape
     g, S_k = k_c.shape[1], k_c.shape[2]
     d_r = q_r.shape[3]
@@ -384,6 +440,9 @@ def latent_absorb_decode(q_lat, q_rope, c_kv, k_rope, seqlens, *, scale: float,
     (B, s_q, h_q)]."""
     import torch
     lib = load_library()
+    _need_dtype((torch.bfloat16,), q_lat=q_lat)
+    _check_common(q_lat, "q_lat", inputs=dict(q_rope=q_rope, c_kv=c_kv, k_rope=k_rope), seqlens=seqlens,
+                  out=out, out_dtype=out_dtype, workspace=workspace)
     B, s_q, h_q, r_kv = q_lat.shape
     d_r = q_rope.shape[3]
     L_cap = c_kv.shape[1]
@@ -393,8 +452,6 @@ def latent_absorb_decode(q_lat, q_rope, c_kv, k_rope, seqlens, *, scale: float,
     lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q_lat.device) if return_lse else None
     need = latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_max, r_kv)
     ws = workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=q_lat.device)
-    if seqlens.dtype != torch.int32:
-        raise TypeError("seqlens must be int32")
     # (batch, head, token) axes: q-like tensors are (B, s_q, h_q, .), caches (B, L, .)
     _check(lib.latent_absorb_decode(
         _desc(q_lat, (0, 2, 1)), _desc(q_rope, (0, 2, 1)), _desc(c_kv, (0, None, 1)),
@@ -417,6 +474,9 @@ def gqla_absorb_decode(q_c, q_rope, w_uk, w_uv, c_kv, k_rope, seqlens, *, g: int
     (B, s_q, h_q)]."""
     import torch
     lib = load_library()
+    _need_dtype((torch.bfloat16,), q_c=q_c)
+    _check_common(q_c, "q_c", inputs=dict(q_rope=q_rope, w_uk=w_uk, w_uv=w_uv, c_kv=c_kv, k_rope=k_rope),
+                  seqlens=seqlens, out=out, out_dtype=out_dtype, workspace=workspace)
     B, s_q, h_q, d_h = q_c.shape
     d_r = q_rope.shape[3]
     L_cap, r_kv = c_kv.shape[1], c_kv.shape[2]
@@ -429,8 +489,6 @@ def gqla_absorb_decode(q_c, q_rope, w_uk, w_uv, c_kv, k_rope, seqlens, *, g: int
     lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q_c.device) if return_lse else None
     need = gqla_absorb_decode_workspace_bytes(B, h_q, s_q, L_max, r_kv)
     ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=q_c.device)
-    if seqlens.dtype != torch.int32:
-        raise TypeError("seqlens must be int32")
     _check(lib.gqla_absorb_decode(
         _desc(q_c, (0, 2, 1)), _desc(q_rope, (0, 2, 1)), _ptr(w_uk), _ptr(w_uv), _desc(c_kv, (0, None, 1)),
         _desc(k_rope, (0, None, 1)), _ptr(seqlens), _desc(o, (0, 2, 1)), _ptr(lse), B, h_q, g, s_q, L_cap, L_max,

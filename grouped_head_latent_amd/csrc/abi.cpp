@@ -295,7 +295,7 @@ gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_
   a.seqlens = seqlens_k;
   a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
   a.lse = lse;
-  a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.s_q = s_q; a.group = h_q / h_kv;
+  a.B = B; a.h_q = h_q; a.h_kv = h_kv; a.s_q = s_q; a.group = h_q / h_kv; a.L_cap = L_cap;
   a.rows = a.group * s_q;
   a.n_rb = gqa_row_blocks(h_q, h_kv, s_q);
   gqa_decode_plan(B, h_kv, a.n_rb, L_max_hint, &a.split_len, &a.n_splits);

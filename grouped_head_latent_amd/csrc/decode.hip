@@ -43,7 +43,9 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_split_kernel(DecodeArgs a) 
   const int rb = unit % a.n_rb;
   const int j = (unit / a.n_rb) % a.h_kv;
   const int b = unit / (a.n_rb * a.h_kv);
-  const int L = a.seqlens[b];
+  // a length outside [0, L_cap] breaks the documented precondition; clamping
+  // keeps every read inside the sequence's slice of the cache
+  const int L = min(max(a.seqlens[b], 0), a.L_cap);
   const int start = split * a.split_len;
   if (start >= L) return;  // the merge ignores splits past the sequence end
   const int end = min(L, start + a.split_len);
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(256) void gqa_decode_merge_kernel(DecodeArgs a) {
   const int row = tid / TPR, f0 = (tid % TPR) * FPT;
   const int R = rb * 16 + row;
   if (R >= a.rows) return;
-  const int L = a.seqlens[b];
+  const int L = min(max(a.seqlens[b], 0), a.L_cap);
   // lengths above the plan's bound are a precondition violation; never read
   // partials the plan did not allot
   const int ns = min((L + a.split_len - 1) / a.split_len, a.n_splits);
@@ -246,7 +248,8 @@ __global__ __launch_bounds__(256) void gqa_decode_merge_kernel(DecodeArgs a) {
       acc[f] += w * x[0]; acc[f + 1] += w * x[1]; acc[f + 2] += w * x[2]; acc[f + 3] += w * x[3];
     }
   }
-  const float inv = 1.f / den;
+  // a row with no visible key (only when L_b < s_q) gets zeros and lse -inf
+  const float inv = den > 0.f ? 1.f / den : 0.f;
   const int hh = R / a.s_q, tq = R % a.s_q;
   const int head = j * a.group + hh;
   const int64_t obase = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh + (int64_t)tq * a.o_ss + f0;
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(256) void gqa_decode_merge_kernel(DecodeArgs a) {
           u32x2{pack_bf16(acc[f] * inv, acc[f + 1] * inv), pack_bf16(acc[f + 2] * inv, acc[f + 3] * inv)};
   }
   if (a.lse != nullptr && (tid % TPR) == 0)
-    a.lse[((int64_t)b * a.h_q + head) * a.s_q + tq] = (M + fast_log2(den)) * kLn2;
+    a.lse[((int64_t)b * a.h_q + head) * a.s_q + tq] = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
 }
 
 template <int D>

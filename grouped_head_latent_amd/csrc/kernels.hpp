@@ -41,6 +41,7 @@ struct DecodeArgs {
   float* ws_o;        // (units, n_splits, 16, d) fp32 partial outputs
   float* ws_lse;      // (units, n_splits, 16) fp32 partial log2-sum-exp
   int B, h_q, h_kv, s_q, group;
+  int L_cap;          // cache capacity: lengths are clamped to [0, L_cap]
   int rows;           // group * s_q query rows per KV head
   int n_rb;           // 16-row blocks per KV head
   int split_len;      // keys per split (multiple of 256)

@@ -109,6 +109,17 @@ def _group_of(head: int, heads: int, groups: int) -> int:
     return head // (heads // groups)
 
 
+def _heads_by_unit(pairs, unit_of):
+    """Group the requested (b, head) pairs by the unit whose keys they read:
+    {unit: [heads...]} in first-seen order.  Rows are independent, so the
+    rows of one unit's heads can be evaluated in one call; the arithmetic of
+    each row is unchanged."""
+    units = {}
+    for b, i in pairs:
+        units.setdefault(unit_of(b, i), []).append(i)
+    return units
+
+
 def gqa_prefill(q, k, v, *, causal: bool = True, scale: float | None = None,
                 heads=None):
     """Grouped-query attention ("How GQA works").
@@ -161,15 +172,17 @@ def gqa_decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
     o = np.full((B, h_q, s_q, v_cache.shape[3]), np.nan)
     lse = np.full((B, h_q, s_q), np.nan)
     pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h_q)]
-    for b, i in pairs:
+    for (b, j), hs in _heads_by_unit(pairs, lambda b, i: (b, _group_of(i, h_q, h_kv))).items():
         L = int(seqlens[b])
         if not (s_q <= L <= k_cache.shape[2]):
             raise ValueError("need s_q <= L_b <= L_cap")
-        j = _group_of(i, h_q, h_kv)
-        nvis = np.arange(s_q) + (L - s_q) + 1
+        # rows (head, t) of the group's requested heads over the group's keys
+        nvis = np.tile(np.arange(s_q) + (L - s_q) + 1, len(hs))
         first = np.maximum(nvis - window, 0) if window > 0 else None
-        o[b, i], lse[b, i] = softmax_attention(q[b, i], k_cache[b, j, :L],
-                                               v_cache[b, j, :L], nvis, scale, first)
+        ob, lb = softmax_attention(q[b, hs].reshape(len(hs) * s_q, d), k_cache[b, j, :L],
+                                   v_cache[b, j, :L], nvis, scale, first)
+        o[b, hs] = ob.reshape(len(hs), s_q, -1)
+        lse[b, hs] = lb.reshape(len(hs), s_q)
     return o, lse
 
 
@@ -275,15 +288,17 @@ def gqla_gqa_decode(q_c, q_r, k_c, k_r, v_cache, seqlens, *, scale: float,
     o = np.full((B, h_q, s_q, v_cache.shape[3]), np.nan)
     lse = np.full((B, h_q, s_q), np.nan)
     pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h_q)]
-    for b, i in pairs:
+    for (b, j), hs in _heads_by_unit(pairs, lambda b, i: (b, _group_of(i, h_q, g))).items():
         L = int(seqlens[b])
         if not (s_q <= L <= k_c.shape[2]):
             raise ValueError("need s_q <= L_b <= L_cap")
-        j = _group_of(i, h_q, g)
-        qi = np.concatenate([q_c[b, i], q_r[b, i]], axis=1)
+        # rows (head, t): query [q^C_i; q^R_i]; keys [k^C_j; k^R] of the group
+        qi = np.concatenate([q_c[b, hs], q_r[b, hs]], axis=2).reshape(len(hs) * s_q, -1)
         kj = np.concatenate([k_c[b, j, :L], k_r[b, :L]], axis=1)
-        nvis = np.arange(s_q) + (L - s_q) + 1
-        o[b, i], lse[b, i] = softmax_attention(qi, kj, v_cache[b, j, :L], nvis, scale)
+        nvis = np.tile(np.arange(s_q) + (L - s_q) + 1, len(hs))
+        ob, lb = softmax_attention(qi, kj, v_cache[b, j, :L], nvis, scale)
+        o[b, hs] = ob.reshape(len(hs), s_q, -1)
+        lse[b, hs] = lb.reshape(len(hs), s_q)
     return o, lse
 
 
@@ -310,11 +325,11 @@ def gqla_gqa_prefill(q_c, q_r, k_c, k_r, v, *, scale: float, causal: bool = True
     lse = np.full((B, h_q, S_q), np.nan)
     nvis = np.arange(S_q) + (S_k - S_q) + 1 if causal else np.full(S_q, S_k)
     pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h_q)]
-    for b, i in pairs:
-        j = _group_of(i, h_q, g)
-        qi = np.concatenate([q_c[b, i], q_r[b, i]], axis=1)
-        kj = np.concatenate([k_c[b, j], k_r[b]], axis=1)
-        o[b, i], lse[b, i] = softmax_attention(qi, kj, v[b, j], nvis, scale)
+    for (b, j), hs in _heads_by_unit(pairs, lambda b, i: (b, _group_of(i, h_q, g))).items():
+        kj = np.concatenate([k_c[b, j], k_r[b]], axis=1)   # the group's key [k^C_j; k^R]
+        for i in hs:
+            qi = np.concatenate([q_c[b, i], q_r[b, i]], axis=1)
+            o[b, i], lse[b, i] = softmax_attention(qi, kj, v[b, j], nvis, scale)
     return o, lse
 
 
@@ -337,14 +352,17 @@ def latent_absorb_decode(q_lat, q_rope, c_kv, k_rope, seqlens, *, scale: float,
     o = np.full((B, s_q, h_q, r_kv), np.nan)
     lse = np.full((B, s_q, h_q), np.nan)
     pairs = heads if heads is not None else [(b, i) for b in range(B) for i in range(h_q)]
-    for b, i in pairs:
+    for b, hs in _heads_by_unit(pairs, lambda b, i: b).items():
         L = int(seqlens[b])
         if not (s_q <= L <= c_kv.shape[1]):
             raise ValueError("need s_q <= L_b <= L_cap")
-        qi = np.concatenate([q_lat[b, :, i], q_rope[b, :, i]], axis=1)
+        # rows (t, head) of every requested head over the one shared cache
+        qi = np.concatenate([q_lat[b][:, hs], q_rope[b][:, hs]], axis=2).reshape(s_q * len(hs), -1)
         kb = np.concatenate([c_kv[b, :L], k_rope[b, :L]], axis=1)
-        nvis = np.arange(s_q) + (L - s_q) + 1
-        o[b, :, i], lse[b, :, i] = softmax_attention(qi, kb, c_kv[b, :L], nvis, scale)
+        nvis = np.repeat(np.arange(s_q) + (L - s_q) + 1, len(hs))
+        ob, lb = softmax_attention(qi, kb, c_kv[b, :L], nvis, scale)
+        o[b][:, hs] = ob.reshape(s_q, len(hs), -1)
+        lse[b][:, hs] = lb.reshape(s_q, len(hs))
     return o, lse
 
 

@@ -118,7 +118,9 @@ def paged(lib, **kw):
     (dict(page=0), 2),
     (dict(bt_stride=63), 2),                # 63 pages of 64 tokens do not cover 4096
     (dict(window=-1), 2),
-    (dict(s_q=2), 2),
+    # 32 query heads over 8 KV heads at s_q = 2 is 8 rows per group: the row
+    # check passes and the call stops at the (too small) workspace instead
+    (dict(s_q=2, ws_bytes=16), 8),
     (dict(h_q=64, s_q=5), 2),               # 8 heads x 5 tokens = 40 rows > 32
     (dict(seq=0), 1),
     (dict(ws=0), 8),
@@ -128,11 +130,6 @@ def paged(lib, **kw):
     (dict(v=T(sb=(1 << 16) + 4)), 5),                 # page stride not a multiple of 16 bytes
 ])
 def test_paged_decode_rejects_bad_arguments(lib, kw, status):
-    if kw == dict(s_q=2):
-        # 32 query heads over 8 KV heads at s_q = 2 is 8 rows per group: accepted
-        # by validation, so it reaches the device check (no GPU here) instead
-        assert paged(lib, **kw) in (0, 9)
-        return
     assert paged(lib, **kw) == status
     assert len(lib.gha_last_error()) > 0
 
@@ -367,4 +364,5 @@ def test_fp8_decode_plans_two_work_groups_per_cu(lib):
     bf16_plan = (256 + 2 * 8) * 16 * 129 * 4 + 3 * 4
     assert fp8(lib, ws_bytes=bf16_plan, **big) == 8
     assert fp8(lib, ws_bytes=full - 1, **big) == 8
-    assert fp8(lib, ws_bytes=full, **big) != 8   # passes the workspace check (then needs a GPU)
+    # a call with the full workspace would pass every check and launch on the
+    # fake pointers, so it is never made here

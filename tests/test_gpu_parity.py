@@ -1,8 +1,12 @@
 """GPU parity: every entry point of the C ABI against the fp64 oracle on the
 same seeded inputs.  Each case prints its name first so a failure is easy to
 place.  Tolerances: fp32 inputs 1e-5 max abs; bf16 inputs with fp32
-accumulation 1e-2 max / 1e-3 mean abs (fp32 outputs), plus half a bf16 ulp of
-the reference for bf16 outputs."""
+accumulation 1e-2 max / 1e-3 mean abs (fp32 outputs); for bf16 outputs an
+element may instead be off by half a bf16 ulp of the reference,
+max(1e-2, ulp/2).  Every call is made twice and the two results must be
+bitwise equal (fixed split plans, no atomics).  At the workloads' full sizes
+the whole output must be finite and the oracle checks every sequence (decode)
+or every (batch, head) slice (prefill) unless a test says otherwise."""
 import math
 import sys
 
@@ -41,6 +45,23 @@ def check(name, got, ref, bf16_out=False, **kw):
     ok, mx, mean = tolerance_ok(got, ref, bf16_out=bf16_out, **kw)
     say(f"{name}: max_abs={mx:.3e} mean_abs={mean:.3e}")
     assert ok, f"{name}: max_abs={mx:.3e} mean_abs={mean:.3e}"
+
+
+def twice(name, fn):
+    """Call `fn` twice; the results (a tensor or a tuple of tensors) must be
+    bitwise equal.  Returns the first."""
+    a = fn()
+    b = fn()
+    torch.cuda.synchronize()
+    for x, y in zip(a if isinstance(a, tuple) else (a,), b if isinstance(b, tuple) else (b,)):
+        assert torch.equal(x, y), f"{name}: two calls differ"
+    return a
+
+
+def all_finite(name, t):
+    bad = int((~torch.isfinite(t)).sum().item())
+    say(f"{name}: {t.numel()} outputs, {bad} non-finite")
+    assert bad == 0
 
 
 # ----------------------------------------------------------------- fp32 path
@@ -100,8 +121,9 @@ def test_gqa_prefill_bf16(gha_lib, B, h_q, h_kv, S_q, S_k, d, causal):
     say(f"bf16 prefill B={B} h={h_q}/{h_kv} S_q={S_q} S_k={S_k} d={d} causal={causal}")
     qb, kb, vb = gen((B, h_q, S_q, d), 8, 1), gen((B, h_kv, S_k, d), 8, 2), gen((B, h_kv, S_k, d), 8, 3)
     q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
-    o32, lse = gha_lib.gqa_prefill(q, k, v, causal=causal, out_dtype=torch.float32, return_lse=True)
-    o16 = gha_lib.gqa_prefill(q, k, v, causal=causal)
+    o32, lse = twice("prefill", lambda: gha_lib.gqa_prefill(q, k, v, causal=causal, out_dtype=torch.float32,
+                                                            return_lse=True))
+    o16 = twice("prefill bf16", lambda: gha_lib.gqa_prefill(q, k, v, causal=causal))
     ref, ref_lse = oracle.gqa_prefill(widen(qb), widen(kb), widen(vb), causal=causal)
     check("o fp32", o32.cpu().numpy(), ref)
     check("o bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
@@ -136,23 +158,25 @@ def test_prefill_invariants(gha_lib):
         assert torch.allclose(o1[0, i, 0], v[0, i // 4, 0].float(), atol=0, rtol=0)
 
 
-def test_gqa_prefill_full_size_sampled(gha_lib):
+def test_gqa_prefill_full_size(gha_lib):
     """Batch 4, 32 query heads over 8 KV heads, 4096 tokens, head dim 128, in
     the launch configuration the benchmark times; the oracle evaluates every
-    row of four sampled (batch, head) pairs."""
+    row of every (batch, head) slice."""
     B, h_q, h_kv, S, d = 4, 32, 8, 4096, 128
     say(f"full-size prefill {B}x{h_q}/{h_kv}x{S}x{d}")
     qb, kb, vb = gen((B, h_q, S, d), 2, 1), gen((B, h_kv, S, d), 2, 2), gen((B, h_kv, S, d), 2, 3)
     q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
-    o = gha_lib.gqa_prefill(q, k, v, out_dtype=torch.float32)
-    o16 = gha_lib.gqa_prefill(q, k, v)
-    pairs = [(0, 0), (1, 13), (2, 22), (3, 31)]
-    ref, _ = oracle.gqa_prefill(widen(qb), widen(kb), widen(vb), heads=pairs)
+    o = twice("full prefill", lambda: gha_lib.gqa_prefill(q, k, v, out_dtype=torch.float32))
+    o16 = twice("full prefill bf16", lambda: gha_lib.gqa_prefill(q, k, v))
+    all_finite("full prefill", o)
+    all_finite("full prefill bf16", o16)
     o = o.cpu().numpy()
     o16 = o16.float().cpu().numpy()
-    for b, i in pairs:
-        check(f"full prefill (b={b}, head={i})", o[b, i], ref[b, i])
-        check(f"full prefill bf16 (b={b}, head={i})", o16[b, i], ref[b, i], bf16_out=True)
+    wq, wk, wv = widen(qb), widen(kb), widen(vb)
+    for b in range(B):
+        ref, _ = oracle.gqa_prefill(wq[b:b + 1], wk[b:b + 1], wv[b:b + 1])
+        check(f"full prefill b={b}", o[b:b + 1], ref)
+        check(f"full prefill bf16 b={b}", o16[b:b + 1], ref, bf16_out=True)
 
 
 # ------------------------------------------------------------------- decode
@@ -185,8 +209,8 @@ def test_gqa_decode(gha_lib, B, h_q, h_kv, s_q, L_cap, seqlens, d):
     qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, 12)
     q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
     sl = torch.from_numpy(seqlens).cuda()
-    o32, lse = gha_lib.gqa_decode(q, k, v, sl, out_dtype=torch.float32, return_lse=True)
-    o16 = gha_lib.gqa_decode(q, k, v, sl)
+    o32, lse = twice("decode", lambda: gha_lib.gqa_decode(q, k, v, sl, out_dtype=torch.float32, return_lse=True))
+    o16 = twice("decode bf16", lambda: gha_lib.gqa_decode(q, k, v, sl))
     ref, ref_lse = oracle.gqa_decode(widen(qb), widen(kb), widen(vb), seqlens)
     check("decode fp32", o32.cpu().numpy(), ref)
     check("decode bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
@@ -203,28 +227,51 @@ def test_gqa_decode_single_key_returns_value(gha_lib):
     assert np.abs(o.cpu().numpy() - ref).max() <= 1e-6
 
 
+@pytest.mark.parametrize("h_q,h_kv,s_q", [(32, 1, 2), (32, 8, 1)])
+def test_gqa_decode_empty_sequence_gives_zeros(gha_lib, h_q, h_kv, s_q):
+    """A sequence of length 0 breaks the documented precondition s_q <= L_b;
+    both decode kernels (64 rows per KV head: the register-operand kernel;
+    4 rows: the streaming kernel) still return zeros and lse = -inf for it
+    and leave the other sequences exact."""
+    B, L_cap, d = 2, 300, 128
+    say(f"decode with an empty sequence h={h_q}/{h_kv} s_q={s_q}")
+    seqlens = np.array([0, 299], dtype=np.int32)
+    qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, 31)
+    o, lse = twice("empty sequence", lambda: gha_lib.gqa_decode(*(bf16_to_torch(x) for x in (qb, kb, vb)),
+                                                                torch.from_numpy(seqlens).cuda(),
+                                                                out_dtype=torch.float32, return_lse=True))
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(o[0] == 0.0) and np.all(lse[0] == -np.inf)
+    ref, ref_lse = oracle.gqa_decode(widen(qb[1:]), widen(kb[1:]), widen(vb[1:]), seqlens[1:])
+    check("non-empty sequence", o[1:], ref)
+    check("non-empty sequence lse", lse[1:], ref_lse)
+
+
 @pytest.mark.parametrize("s_q", [1, 2])
-def test_gqa_decode_full_size_sampled(gha_lib, s_q):
+def test_gqa_decode_full_size(gha_lib, s_q):
     """Batch 64, 32/8 heads, head dim 128, lengths uniform in [1024, 32768],
-    cache capacity 32768 with NaN beyond each length."""
+    cache capacity 32768 with NaN beyond each length; every sequence is
+    checked against the oracle (output and lse)."""
     B, h_q, h_kv, d, L_cap = 64, 32, 8, 128, 32768
     say(f"full-size decode s_q={s_q}")
     seqlens = synth.uniform_i32(B, 1024, 32768, 3, synth.STREAM["seqlens"])
     qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, 3)
     q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
-    del kb, vb
-    o = gha_lib.gqa_decode(q, k, v, torch.from_numpy(seqlens).cuda(), out_dtype=torch.float32).cpu().numpy()
-    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 17, 40]:
-        kh = k[b].view(torch.int16).cpu().numpy().view(np.uint16)
-        vh = v[b].view(torch.int16).cpu().numpy().view(np.uint16)
-        # the oracle gets host-generated values: regenerate this sequence's slice
+    sl = torch.from_numpy(seqlens).cuda()
+    ws = torch.empty(gha_lib.gqa_decode_workspace_bytes(B, h_q, h_kv, s_q, L_cap, d), dtype=torch.uint8,
+                     device="cuda")
+    o, lse = twice("full decode", lambda: gha_lib.gqa_decode(q, k, v, sl, out_dtype=torch.float32, workspace=ws,
+                                                             return_lse=True))
+    all_finite("full decode", o)
+    del q, k, v
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    wq = widen(qb)
+    for b in range(B):
         L = int(seqlens[b])
-        k_ref = np.stack([synth.normal_bf16((L, d), 3, 2, offset=((b * h_kv + j) * L_cap) * d) for j in range(h_kv)])
-        v_ref = np.stack([synth.normal_bf16((L, d), 3, 3, offset=((b * h_kv + j) * L_cap) * d) for j in range(h_kv)])
-        assert np.array_equal(kh[:, :L], k_ref) and np.array_equal(vh[:, :L], v_ref)
-        ref, _ = oracle.gqa_decode(widen(qb[b:b + 1]), widen(k_ref)[None], widen(v_ref)[None],
-                                   np.array([L]))
+        ref, ref_lse = oracle.gqa_decode(wq[b:b + 1], widen(kb[b:b + 1, :, :L]), widen(vb[b:b + 1, :, :L]),
+                                         np.array([L]))
         check(f"full decode b={b} L={L}", o[b:b + 1], ref)
+        check(f"full decode lse b={b}", lse[b:b + 1], ref_lse)
 
 
 # ------------------------------------------------ paged and windowed decode
@@ -263,9 +310,9 @@ def test_gqa_decode_paged(gha_lib, B, h_q, h_kv, s_q, L_cap, seqlens, d, page, w
     else:
         k, v = bf16_to_torch(kb), bf16_to_torch(vb)
         kw = {}
-    o32, lse = gha_lib.gqa_decode_paged(q, k, v, sl, window=window, out_dtype=torch.float32,
-                                        return_lse=True, **kw)
-    o16 = gha_lib.gqa_decode_paged(q, k, v, sl, window=window, **kw)
+    o32, lse = twice("paged", lambda: gha_lib.gqa_decode_paged(q, k, v, sl, window=window, out_dtype=torch.float32,
+                                                               return_lse=True, **kw))
+    o16 = twice("paged bf16", lambda: gha_lib.gqa_decode_paged(q, k, v, sl, window=window, **kw))
     ref, ref_lse = oracle.gqa_decode(widen(qb), widen(kb), widen(vb), seqlens, window=window)
     check("paged decode fp32", o32.cpu().numpy(), ref)
     check("paged decode bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
@@ -293,15 +340,19 @@ def test_gqa_decode_paged_full_size_sampled(gha_lib, page, window):
         pool[table.long()] = src
         pools.append(pool)
         del src
-    o = gha_lib.gqa_decode_paged(q, pools[0], pools[1], torch.from_numpy(seqlens).cuda(),
-                                 block_table=table.view(B, n_pps), page_size=page, window=window,
-                                 out_dtype=torch.float32).cpu().numpy()
-    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 17, 40]:
+    sl = torch.from_numpy(seqlens).cuda()
+    o = twice("full paged", lambda: gha_lib.gqa_decode_paged(q, pools[0], pools[1], sl,
+                                                             block_table=table.view(B, n_pps), page_size=page,
+                                                             window=window, out_dtype=torch.float32))
+    all_finite("full paged decode", o)
+    del pools
+    o = o.cpu().numpy()
+    wq = widen(qb)
+    for b in range(B):
         L = int(seqlens[b])
-        k_ref = np.stack([synth.normal_bf16((L, d), 3, 2, offset=((b * h_kv + j) * L_cap) * d) for j in range(h_kv)])
-        v_ref = np.stack([synth.normal_bf16((L, d), 3, 3, offset=((b * h_kv + j) * L_cap) * d) for j in range(h_kv)])
-        ref, _ = oracle.gqa_decode(widen(qb[b:b + 1]), widen(k_ref)[None], widen(v_ref)[None],
-                                   np.array([L]), window=window)
+        lo = max(0, L - s_q + 1 - window) if window else 0   # keys no row can see are not widened
+        ref, _ = oracle.gqa_decode(wq[b:b + 1], widen(kb[b:b + 1, :, lo:L]), widen(vb[b:b + 1, :, lo:L]),
+                                   np.array([L - lo]), window=window)
         check(f"full paged decode b={b} L={L}", o[b:b + 1], ref)
 
 
@@ -334,18 +385,48 @@ def test_gqa_decode_fp8(gha_lib, B, h_q, h_kv, s_q, L_cap, seqlens, d, page, win
     else:
         k, v = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
         kw = {}
-    o32, lse = gha_lib.gqa_decode_fp8(q, k, v, sl, k_scale=ks, v_scale=vs, window=window,
-                                      out_dtype=torch.float32, return_lse=True, **kw)
-    o16 = gha_lib.gqa_decode_fp8(q, k, v, sl, k_scale=ks, v_scale=vs, window=window, **kw)
+    o32, lse = twice("fp8", lambda: gha_lib.gqa_decode_fp8(q, k, v, sl, k_scale=ks, v_scale=vs, window=window,
+                                                           out_dtype=torch.float32, return_lse=True, **kw))
+    o16 = twice("fp8 bf16", lambda: gha_lib.gqa_decode_fp8(q, k, v, sl, k_scale=ks, v_scale=vs, window=window,
+                                                           **kw))
     ref, ref_lse = oracle.gqa_decode_fp8(widen(qb), kc, vc, ks, vs, seqlens, window=window)
     check("fp8 decode fp32", o32.cpu().numpy(), ref)
     check("fp8 decode bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
     check("fp8 decode lse", lse.cpu().numpy(), ref_lse)
 
 
-def test_gqa_decode_fp8_full_size_sampled(gha_lib):
+@pytest.mark.parametrize("d,page", [(128, 0), (64, 0), (128, 64)])
+def test_gqa_decode_fp8_many_chunks_per_work_group(gha_lib, d, page):
+    """Batch 8, 32/8 heads, lengths up to 8192: 8 x 8 x 64 = 4096 chunks of
+    128 keys over the 8-bit plan's 512 work-groups, so every work-group's
+    share spans several chunks and the merge combines partials across team
+    boundaries; every sequence and the lse are checked."""
+    B, h_q, h_kv, s_q, L_cap = 8, 32, 8, 1, 8192
+    say(f"fp8 decode, many chunks per work-group, d={d} page={page}")
+    seqlens = np.array([8192, 1, 4097, 8000, 333, 7777, 129, 6000], dtype=np.int32)
+    qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L_cap, seqlens, d, 27)
+    ks, vs = 1 / 32, 1 / 40
+    kc, vc = e4m3_codes(kb, ks), e4m3_codes(vb, vs)
+    sl = torch.from_numpy(seqlens).cuda()
+    if page:
+        kp, table = page_pool(kc, seqlens, page, 11)
+        vp, _ = page_pool(vc, seqlens, page, 11)
+        k, v = torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda()
+        kw = dict(block_table=torch.from_numpy(table).cuda(), page_size=page, L_cap=L_cap)
+    else:
+        k, v = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
+        kw = {}
+    o, lse = twice("fp8 many chunks", lambda: gha_lib.gqa_decode_fp8(
+        bf16_to_torch(qb), k, v, sl, k_scale=ks, v_scale=vs, out_dtype=torch.float32, return_lse=True, **kw))
+    ref, ref_lse = oracle.gqa_decode_fp8(widen(qb), kc, vc, ks, vs, seqlens)
+    check("fp8 many chunks", o.cpu().numpy(), ref)
+    check("fp8 many chunks lse", lse.cpu().numpy(), ref_lse)
+
+
+def test_gqa_decode_fp8_full_size(gha_lib):
     """The decode workload (batch 64, 32/8 heads, head dim 128, lengths uniform
-    in [1024, 32768]) with its cache quantized to E4M3."""
+    in [1024, 32768]) with its cache quantized to E4M3; every sequence is
+    checked."""
     B, h_q, h_kv, d, L_cap, s_q = 64, 32, 8, 128, 32768, 1
     say("full-size fp8 decode")
     seqlens = synth.uniform_i32(B, 1024, 32768, 3, synth.STREAM["seqlens"])
@@ -358,9 +439,12 @@ def test_gqa_decode_fp8_full_size_sampled(gha_lib):
     k8 = (kc.float() / ks).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
     v8 = (vc.float() / vs).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
     del kc, vc
-    o = gha_lib.gqa_decode_fp8(bf16_to_torch(qb), k8, v8, torch.from_numpy(seqlens).cuda(), k_scale=ks,
-                               v_scale=vs, out_dtype=torch.float32).cpu().numpy()
-    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 17, 40]:
+    q, sl = bf16_to_torch(qb), torch.from_numpy(seqlens).cuda()
+    o = twice("full fp8", lambda: gha_lib.gqa_decode_fp8(q, k8, v8, sl, k_scale=ks, v_scale=vs,
+                                                         out_dtype=torch.float32))
+    all_finite("full fp8 decode", o)
+    o = o.cpu().numpy()
+    for b in range(B):
         L = int(seqlens[b])
         kk, vv = k8[b, :, :L].cpu().numpy(), v8[b, :, :L].cpu().numpy()
         ref, _ = oracle.gqa_decode_fp8(widen(qb[b:b + 1]), kk[None], vv[None], ks, vs, np.array([L]))
@@ -370,13 +454,15 @@ def test_gqa_decode_fp8_full_size_sampled(gha_lib):
 # ----------------------------------------------- GQLA GQA-path prefill
 
 GQLA_PREFILL_CASES = [
-    # B, h_q, g, S_q, S_k, causal
-    (2, 16, 2, 200, 200, True),     # ragged last tile
-    (1, 8, 8, 77, 77, True),        # one head per group
-    (1, 16, 4, 100, 300, True),     # bottom-right: queries are the last 100 positions
-    (1, 8, 2, 130, 130, False),
-    (1, 32, 8, 1, 40, True),        # a single query row
-    (1, 64, 4, 1090, 1090, True),   # 560 work-groups: paired q-blocks, 35 of them
+    # B, h_q, g, S_q, S_k, causal, kv_std
+    (2, 16, 2, 200, 200, True, 0.45),     # ragged last tile
+    (1, 8, 8, 77, 77, True, 0.45),        # one head per group
+    (1, 16, 4, 100, 300, True, 0.45),     # bottom-right: queries are the last 100 positions
+    (1, 8, 2, 130, 130, False, 0.45),
+    (1, 32, 8, 1, 40, True, 0.45),        # a single query row
+    (1, 64, 4, 1090, 1090, True, 0.45),   # 560 work-groups: paired q-blocks, 35 of them
+    (2, 16, 2, 300, 300, True, 1.0),      # N(0, 1) keys and values: larger scores
+    (1, 64, 4, 1090, 1200, True, 1.0),    # N(0, 1), paired q-blocks, bottom-right
 ]
 
 
@@ -386,15 +472,16 @@ def gqla_prefill_case(B, h_q, g, S_q, S_k, seed, kv_std=0.45):
             synth.normal_bf16((B, g, S_k, 128), seed, 5, kv_std))
 
 
-@pytest.mark.parametrize("B,h_q,g,S_q,S_k,causal", GQLA_PREFILL_CASES)
-def test_gqla_gqa_prefill(gha_lib, B, h_q, g, S_q, S_k, causal):
-    say(f"gqla prefill B={B} h_q={h_q} g={g} S_q={S_q} S_k={S_k} causal={causal}")
-    bits = gqla_prefill_case(B, h_q, g, S_q, S_k, 23)
+@pytest.mark.parametrize("B,h_q,g,S_q,S_k,causal,kv_std", GQLA_PREFILL_CASES)
+def test_gqla_gqa_prefill(gha_lib, B, h_q, g, S_q, S_k, causal, kv_std):
+    say(f"gqla prefill B={B} h_q={h_q} g={g} S_q={S_q} S_k={S_k} causal={causal} kv_std={kv_std}")
+    bits = gqla_prefill_case(B, h_q, g, S_q, S_k, 23, kv_std)
     qc, qr, kc, kr, v = (bf16_to_torch(x) for x in bits)
     scale = 1.0 / math.sqrt(192)
-    o32, lse = gha_lib.gqla_gqa_prefill(qc, qr, kc, kr, v, scale=scale, causal=causal,
-                                        out_dtype=torch.float32, return_lse=True)
-    o16 = gha_lib.gqla_gqa_prefill(qc, qr, kc, kr, v, scale=scale, causal=causal)
+    o32, lse = twice("gqla prefill", lambda: gha_lib.gqla_gqa_prefill(qc, qr, kc, kr, v, scale=scale, causal=causal,
+                                                                      out_dtype=torch.float32, return_lse=True))
+    o16 = twice("gqla prefill bf16", lambda: gha_lib.gqla_gqa_prefill(qc, qr, kc, kr, v, scale=scale,
+                                                                      causal=causal))
     ref, ref_lse = oracle.gqla_gqa_prefill(*(widen(x) for x in bits), scale=scale, causal=causal)
     check("gqla prefill fp32", o32.cpu().numpy(), ref)
     check("gqla prefill bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
@@ -402,14 +489,19 @@ def test_gqla_gqa_prefill(gha_lib, B, h_q, g, S_q, S_k, causal):
 
 
 def test_gqla_gqa_prefill_full_size_sampled(gha_lib):
-    """Batch 2, 128 query heads in 8 groups, 4096 tokens, d_h 128 + d^R 64."""
+    """Batch 2, 128 query heads in 8 groups, 4096 tokens, d_h 128 + d^R 64.
+    The whole output must be finite; the oracle evaluates every row of 16
+    (batch, head) slices, two in each group (the full output would take the
+    oracle about a minute)."""
     B, h_q, g, S = 2, 128, 8, 4096
     say(f"full-size gqla prefill {B}x{h_q}/{g}x{S}")
     bits = gqla_prefill_case(B, h_q, g, S, S, 10)
     scale = 1.0 / math.sqrt(192)
-    o = gha_lib.gqla_gqa_prefill(*(bf16_to_torch(x) for x in bits), scale=scale,
-                                 out_dtype=torch.float32).cpu().numpy()
-    pairs = [(0, 0), (0, 77), (1, 63), (1, 127)]
+    dev = [bf16_to_torch(x) for x in bits]
+    o = twice("full gqla prefill", lambda: gha_lib.gqla_gqa_prefill(*dev, scale=scale, out_dtype=torch.float32))
+    all_finite("full gqla prefill", o)
+    o = o.cpu().numpy()
+    pairs = [(j % 2, 16 * j + (5 * j + 3) % 16) for j in range(8)] + [((j + 1) % 2, 16 * j + 15 - j) for j in range(8)]
     ref, _ = oracle.gqla_gqa_prefill(*(widen(x) for x in bits), scale=scale, heads=pairs)
     for b, i in pairs:
         check(f"full gqla prefill (b={b}, head={i})", o[b, i], ref[b, i])
@@ -438,8 +530,9 @@ def test_gta_shared_score_decode(gha_lib, B, h, n_grp, s_q, L_cap, seqlens, d_qk
     vb = cache_bits(B, h, L_cap, 64, seqlens, 22, 3)
     q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
     sl = torch.from_numpy(seqlens).cuda()
-    o32, lse = gha_lib.gta_shared_score_decode(q, k, v, sl, out_dtype=torch.float32, return_lse=True)
-    o16 = gha_lib.gta_shared_score_decode(q, k, v, sl)
+    o32, lse = twice("gta decode", lambda: gha_lib.gta_shared_score_decode(q, k, v, sl, out_dtype=torch.float32,
+                                                                           return_lse=True))
+    o16 = twice("gta decode bf16", lambda: gha_lib.gta_shared_score_decode(q, k, v, sl))
     ref, ref_lse = oracle.gta_decode(widen(qb), widen(kb), widen(vb), seqlens)
     check("gta decode fp32", o32.cpu().numpy(), ref)
     check("gta decode bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
@@ -458,9 +551,10 @@ def test_gta_decode_single_key_returns_value(gha_lib):
 
 
 @pytest.mark.parametrize("s_q", [1, 2])
-def test_gta_decode_full_size_sampled(gha_lib, s_q):
+def test_gta_decode_full_size(gha_lib, s_q):
     """Batch 64, 16 heads in 4 groups, dims 64, lengths uniform in
-    [1024, 32768], capacity 32768 with NaN beyond each length."""
+    [1024, 32768], capacity 32768 with NaN beyond each length; every sequence
+    is checked."""
     B, h, n_grp, d, L_cap = 64, 16, 4, 64, 32768
     say(f"full-size GTA decode s_q={s_q}")
     seqlens = synth.uniform_i32(B, 1024, 32768, 6, synth.STREAM["seqlens"])
@@ -468,9 +562,12 @@ def test_gta_decode_full_size_sampled(gha_lib, s_q):
     kb = cache_bits(B, n_grp, L_cap, d, seqlens, 6, 2)
     vb = cache_bits(B, h, L_cap, d, seqlens, 6, 3)
     q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
-    o = gha_lib.gta_shared_score_decode(q, k, v, torch.from_numpy(seqlens).cuda(),
-                                        out_dtype=torch.float32).cpu().numpy()
-    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 21]:
+    sl = torch.from_numpy(seqlens).cuda()
+    o = twice("full gta decode", lambda: gha_lib.gta_shared_score_decode(q, k, v, sl, out_dtype=torch.float32))
+    all_finite("full GTA decode", o)
+    del q, k, v
+    o = o.cpu().numpy()
+    for b in range(B):
         L = int(seqlens[b])
         ref, _ = oracle.gta_decode(widen(qb[b:b + 1]), widen(kb[b:b + 1, :, :L]), widen(vb[b:b + 1, :, :L]),
                                    np.array([L]))
@@ -504,8 +601,9 @@ def test_gqla_gqa_decode(gha_lib, B, h_q, g, s_q, L_cap, seqlens):
     qc, qr, kc, kr, v = gqla_case(B, h_q, g, s_q, L_cap, seqlens, 24)
     scale = 1 / math.sqrt(128 + 64)
     args = [bf16_to_torch(x) for x in (qc, qr, kc, kr, v)] + [torch.from_numpy(seqlens).cuda()]
-    o32, lse = gha_lib.gqla_gqa_decode(*args, scale=scale, out_dtype=torch.float32, return_lse=True)
-    o16 = gha_lib.gqla_gqa_decode(*args, scale=scale)
+    o32, lse = twice("gqla decode", lambda: gha_lib.gqla_gqa_decode(*args, scale=scale, out_dtype=torch.float32,
+                                                                    return_lse=True))
+    o16 = twice("gqla decode bf16", lambda: gha_lib.gqla_gqa_decode(*args, scale=scale))
     ref, ref_lse = oracle.gqla_gqa_decode(*(widen(x) for x in (qc, qr, kc, kr, v)), seqlens, scale=scale)
     check("gqla fp32", o32.cpu().numpy(), ref)
     check("gqla bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
@@ -541,20 +639,23 @@ def test_gqla_gqa_path_matches_absorbed_path_on_gpu(gha_lib):
 
 
 @pytest.mark.parametrize("s_q", [1, 2])
-def test_gqla_decode_full_size_sampled(gha_lib, s_q):
+def test_gqla_decode_full_size(gha_lib, s_q):
     """h_q 128 in g = 8 groups, d_h 128, RoPE 64, batch 64, lengths uniform in
     [8192, 65536]: the per-group expanded cache of the latent workload (key
-    and value spread 0.45, that of W^UK c with W ~ N(0, 0.02))."""
+    and value spread 0.45, that of W^UK c with W ~ N(0, 0.02)); every
+    sequence is checked."""
     B, h_q, g, L_cap = 64, 128, 8, 65536
     say(f"full-size GQLA decode s_q={s_q}")
     seqlens = synth.uniform_i32(B, 8192, 65536, 7, synth.STREAM["seqlens"])
     qc, qr, kc, kr, v = gqla_case(B, h_q, g, s_q, L_cap, seqlens, 7, kv_std=0.45)
     args = [bf16_to_torch(x) for x in (qc, qr, kc, kr, v)]
     scale = 1 / math.sqrt(128 + 64)
-    o = gha_lib.gqla_gqa_decode(*args, torch.from_numpy(seqlens).cuda(), scale=scale,
-                                out_dtype=torch.float32).cpu().numpy()
+    sl = torch.from_numpy(seqlens).cuda()
+    o = twice("full gqla decode", lambda: gha_lib.gqla_gqa_decode(*args, sl, scale=scale, out_dtype=torch.float32))
+    all_finite("full GQLA decode", o)
     del args
-    for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 9]:
+    o = o.cpu().numpy()
+    for b in range(B):
         L = int(seqlens[b])
         ref, _ = oracle.gqla_gqa_decode(widen(qc[b:b + 1]), widen(qr[b:b + 1]), widen(kc[b:b + 1, :, :L]),
                                         widen(kr[b:b + 1, :L]), widen(v[b:b + 1, :, :L]), np.array([L]),
@@ -579,8 +680,9 @@ def test_gta_shared_score(gha_lib, B, h, n_grp, S, d_qk, d_v):
     say(f"GTA B={B} h={h} groups={n_grp} S={S} d_qk={d_qk} d_v={d_v}")
     qb, kb, vb = gen((B, n_grp, S, d_qk), 14, 1), gen((B, n_grp, S, d_qk), 14, 2), gen((B, h, S, d_v), 14, 3)
     q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
-    o, lse = gha_lib.gta_shared_score_prefill(q, k, v, out_dtype=torch.float32, return_lse=True)
-    o16 = gha_lib.gta_shared_score_prefill(q, k, v)
+    o, lse = twice("gta", lambda: gha_lib.gta_shared_score_prefill(q, k, v, out_dtype=torch.float32,
+                                                                   return_lse=True))
+    o16 = twice("gta bf16", lambda: gha_lib.gta_shared_score_prefill(q, k, v))
     ref, ref_lse = oracle.gta_prefill(widen(qb), widen(kb), widen(vb))
     check("gta fp32", o.cpu().numpy(), ref)
     check("gta bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
@@ -620,17 +722,22 @@ def test_gta_growing_scores_restart(gha_lib):
     check("gta restart", o.cpu().numpy(), ref)
 
 
-def test_gta_full_size_sampled(gha_lib):
-    """Batch 8, 16 heads in 4 groups of 4, 2048 tokens, dims 64."""
+def test_gta_full_size(gha_lib):
+    """Batch 8, 16 heads in 4 groups of 4, 2048 tokens, dims 64; every
+    (batch, head) slice and the per-group lse are checked."""
     B, h, n_grp, S, d = 8, 16, 4, 2048, 64
     say("full-size GTA")
     qb, kb, vb = gen((B, n_grp, S, d), 4, 1), gen((B, n_grp, S, d), 4, 2), gen((B, h, S, d), 4, 3)
-    o = gha_lib.gta_shared_score_prefill(*(bf16_to_torch(x) for x in (qb, kb, vb)),
-                                         out_dtype=torch.float32).cpu().numpy()
-    pairs = [(0, 0), (0, 3), (3, 6), (7, 15)]
-    ref, _ = oracle.gta_prefill(widen(qb), widen(kb), widen(vb), heads=pairs)
-    for b, i in pairs:
-        check(f"full GTA (b={b}, head={i})", o[b, i], ref[b, i])
+    dev = [bf16_to_torch(x) for x in (qb, kb, vb)]
+    o, lse = twice("full gta", lambda: gha_lib.gta_shared_score_prefill(*dev, out_dtype=torch.float32,
+                                                                        return_lse=True))
+    o16 = twice("full gta bf16", lambda: gha_lib.gta_shared_score_prefill(*dev))
+    all_finite("full GTA", o)
+    all_finite("full GTA bf16", o16)
+    ref, ref_lse = oracle.gta_prefill(widen(qb), widen(kb), widen(vb))
+    check("full GTA", o.cpu().numpy(), ref)
+    check("full GTA bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("full GTA lse", lse.cpu().numpy(), ref_lse)
 
 
 # ------------------------------------------------------------------- latent
@@ -664,11 +771,12 @@ def test_latent_absorb_decode(gha_lib, B, h_q, s_q, L_cap, seqlens):
     q_c, q_r, cache, w_uk, w_uv, q_lat = latent_inputs(B, s_q, h_q, L_cap, seqlens, 15, g=g)
     dcache = bf16_to_torch(cache)
     scale = 1 / math.sqrt(128 + 64)
-    o32, lse = gha_lib.latent_absorb_decode(bf16_to_torch(q_lat), bf16_to_torch(q_r), dcache[..., :512],
-                                            dcache[..., 512:], torch.from_numpy(seqlens).cuda(),
-                                            scale=scale, out_dtype=torch.float32, return_lse=True)
-    o16 = gha_lib.latent_absorb_decode(bf16_to_torch(q_lat), bf16_to_torch(q_r), dcache[..., :512],
-                                       dcache[..., 512:], torch.from_numpy(seqlens).cuda(), scale=scale)
+    dq, dr, sl = bf16_to_torch(q_lat), bf16_to_torch(q_r), torch.from_numpy(seqlens).cuda()
+    o32, lse = twice("latent", lambda: gha_lib.latent_absorb_decode(dq, dr, dcache[..., :512], dcache[..., 512:], sl,
+                                                                    scale=scale, out_dtype=torch.float32,
+                                                                    return_lse=True))
+    o16 = twice("latent bf16", lambda: gha_lib.latent_absorb_decode(dq, dr, dcache[..., :512], dcache[..., 512:], sl,
+                                                                    scale=scale))
     c = widen(cache)
     ref, ref_lse = oracle.latent_absorb_decode(widen(q_lat), widen(q_r), c[..., :512], c[..., 512:],
                                                seqlens, scale=scale)
@@ -732,13 +840,13 @@ def test_gqla_absorb_decode(gha_lib, B, h_q, s_q, L_cap, seqlens, g):
     w_bits = [synth.normal_bf16((g * 128, 512), 33, synth.STREAM[n], 0.02) for n in ("w_uk", "w_uv")]
     dcache = bf16_to_torch(cache)
     scale = 1 / math.sqrt(128 + 64)
-    o32, lse = gha_lib.gqla_absorb_decode(bf16_to_torch(q_c), bf16_to_torch(q_r), bf16_to_torch(w_bits[0]),
-                                          bf16_to_torch(w_bits[1]), dcache[..., :512], dcache[..., 512:],
-                                          torch.from_numpy(seqlens).cuda(), g=g, scale=scale,
-                                          out_dtype=torch.float32, return_lse=True)
-    o16 = gha_lib.gqla_absorb_decode(bf16_to_torch(q_c), bf16_to_torch(q_r), bf16_to_torch(w_bits[0]),
-                                     bf16_to_torch(w_bits[1]), dcache[..., :512], dcache[..., 512:],
-                                     torch.from_numpy(seqlens).cuda(), g=g, scale=scale)
+    dev = [bf16_to_torch(x) for x in (q_c, q_r, w_bits[0], w_bits[1])]
+    sl = torch.from_numpy(seqlens).cuda()
+    o32, lse = twice("absorbing", lambda: gha_lib.gqla_absorb_decode(*dev, dcache[..., :512], dcache[..., 512:], sl,
+                                                                     g=g, scale=scale, out_dtype=torch.float32,
+                                                                     return_lse=True))
+    o16 = twice("absorbing bf16", lambda: gha_lib.gqla_absorb_decode(*dev, dcache[..., :512], dcache[..., 512:], sl,
+                                                                     g=g, scale=scale))
     c = widen(cache)
     # oracle: absorb in fp64 (no bf16 rounding of the absorbed query), attend,
     # apply W^UV
@@ -751,33 +859,43 @@ def test_gqla_absorb_decode(gha_lib, B, h_q, s_q, L_cap, seqlens, g):
 
 
 @pytest.mark.parametrize("s_q", [1, 2])
-def test_latent_full_size_sampled_and_expanded_path(gha_lib, s_q):
+def test_latent_full_size_and_expanded_path(gha_lib, s_q):
     """h_q 128, r_kv 512, RoPE 64, batch 64, lengths uniform in [8192, 65536],
-    W^UK/W^UV per 8 groups ~ N(0, 0.02).  o_lat is checked against the
-    absorbed oracle on sampled sequences, and W^UV o_lat (host, fp64) against
-    the expanded per-group GQA oracle (GQLA: the two paths are equal); so is
-    the output of gqla_absorb_decode, which does both absorption products on
-    the device."""
+    W^UK/W^UV per 8 groups ~ N(0, 0.02).  o_lat and its lse are checked
+    against the absorbed oracle on every sequence; on three sequences W^UV
+    o_lat (host, fp64) is also checked against the expanded per-group GQA
+    oracle (GQLA: the two paths are equal), and so is the output of
+    gqla_absorb_decode, which does both absorption products on the device."""
     B, h_q, L_cap, g, d_h = 64, 128, 65536, 8, 128
     say(f"full-size latent s_q={s_q}")
     seqlens = synth.uniform_i32(B, 8192, 65536, 5, synth.STREAM["seqlens"])
     q_c, q_r, cache, w_uk, w_uv, q_lat = latent_inputs(B, s_q, h_q, L_cap, seqlens, 5)
     dcache = bf16_to_torch(cache)
     scale = 1 / math.sqrt(d_h + 64)
-    o = gha_lib.latent_absorb_decode(bf16_to_torch(q_lat), bf16_to_torch(q_r), dcache[..., :512],
-                                     dcache[..., 512:], torch.from_numpy(seqlens).cuda(), scale=scale,
-                                     out_dtype=torch.float32).cpu().numpy()
+    dq, dr, sl = bf16_to_torch(q_lat), bf16_to_torch(q_r), torch.from_numpy(seqlens).cuda()
+    o, lse = twice("full latent", lambda: gha_lib.latent_absorb_decode(dq, dr, dcache[..., :512], dcache[..., 512:],
+                                                                       sl, scale=scale, out_dtype=torch.float32,
+                                                                       return_lse=True))
+    all_finite("full latent", o)
     w_bits = [synth.normal_bf16((g * d_h, 512), 5, synth.STREAM[n], 0.02) for n in ("w_uk", "w_uv")]
-    o_fused = gha_lib.gqla_absorb_decode(bf16_to_torch(q_c), bf16_to_torch(q_r), bf16_to_torch(w_bits[0]),
-                                         bf16_to_torch(w_bits[1]), dcache[..., :512], dcache[..., 512:],
-                                         torch.from_numpy(seqlens).cuda(), g=g, scale=scale,
-                                         out_dtype=torch.float32).cpu().numpy()
+    dev = [bf16_to_torch(x) for x in (q_c, q_r, w_bits[0], w_bits[1])]
+    o_fused = twice("full absorbing", lambda: gha_lib.gqla_absorb_decode(*dev, dcache[..., :512], dcache[..., 512:],
+                                                                         sl, g=g, scale=scale,
+                                                                         out_dtype=torch.float32))
+    all_finite("full absorbing", o_fused)
+    del dcache
+    o, lse, o_fused = o.cpu().numpy(), lse.cpu().numpy(), o_fused.cpu().numpy()
+    wq, wr = widen(q_lat), widen(q_r)
+    for b in range(B):
+        L = int(seqlens[b])
+        c = widen(cache[b:b + 1, :L])
+        ref, ref_lse = oracle.latent_absorb_decode(wq[b:b + 1], wr[b:b + 1], c[..., :512], c[..., 512:],
+                                                   np.array([L]), scale=scale)
+        check(f"full latent b={b} L={L}", o[b:b + 1], ref)
+        check(f"full latent lse b={b}", lse[b:b + 1], ref_lse)
     for b in [int(np.argmin(seqlens)), int(np.argmax(seqlens)), 30]:
         L = int(seqlens[b])
         c = widen(cache[b:b + 1, :L])
-        ref, _ = oracle.latent_absorb_decode(widen(q_lat[b:b + 1]), widen(q_r[b:b + 1]), c[..., :512],
-                                             c[..., 512:], np.array([L]), scale=scale)
-        check(f"full latent b={b} L={L}", o[b:b + 1], ref)
         # expanded per-group GQA path from the un-absorbed query
         K, V = oracle.expand_latent(c[..., :512], c[..., 512:], w_uk, w_uv, g)
         qf = np.concatenate([widen(q_c[b:b + 1]), widen(q_r[b:b + 1])], -1).transpose(0, 2, 1, 3)

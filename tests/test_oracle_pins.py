@@ -132,6 +132,49 @@ def test_windowed_decode_equals_decode_of_the_window():
             np.testing.assert_array_equal(o_1[b, i, 0], vc[b, i // 2, L - 1])
 
 
+def bf16_widening_matches(widen) -> bool:
+    """bf16 is the top 16 bits of an IEEE-754 binary32 word (sign, 8 exponent
+    bits with bias 127, 7 mantissa bits).  Checks `widen` on values the format
+    fixes, then on every one of the 65,536 bit patterns against torch's
+    bfloat16 -> float64, and on a strided 2-D view."""
+    fixed = {0x0000: 0.0, 0x3F80: 1.0, 0x4000: 2.0, 0x3F00: 0.5, 0xBF80: -1.0, 0x3FC0: 1.5,
+             0x4080: 4.0, 0x3F81: 1.0 + 2.0 ** -7, 0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126,
+             0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0x7F80: math.inf, 0xFF80: -math.inf}
+    for bits, v in fixed.items():
+        if widen(np.array([bits], dtype=np.uint16))[0] != v:
+            return False
+    if not np.signbit(widen(np.array([0x8000], dtype=np.uint16))[0]):
+        return False
+    if not np.isnan(widen(np.array([0x7FC0, 0xFFC1, 0x7F81], dtype=np.uint16))).all():
+        return False
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = widen(allbits)
+    keep = ~np.isnan(ref)
+    if got.dtype != np.float64 or not np.array_equal(np.isnan(got), ~keep):
+        return False
+    if not (np.array_equal(got[keep], ref[keep]) and np.array_equal(np.signbit(got[keep]), np.signbit(ref[keep]))):
+        return False
+    grid, rgrid = allbits.reshape(256, 256)[:, ::3], ref.reshape(256, 256)[:, ::3]
+    g = widen(grid)
+    return g.shape == grid.shape and np.array_equal(g[~np.isnan(rgrid)], rgrid[~np.isnan(rgrid)])
+
+
+def test_bf16_widening_against_the_format_and_torch():
+    assert bf16_widening_matches(oracle.widen_bf16)
+
+
+@pytest.mark.parametrize("wrong", [
+    lambda b: np.asarray(b).astype(np.float64),                                          # integer value
+    lambda b: (np.asarray(b, np.uint32) << 15).view(np.float32).astype(np.float64),        # shift by 15
+    lambda b: np.abs((np.asarray(b, np.uint32) << 16).view(np.float32).astype(np.float64)),  # sign dropped
+    lambda b: (np.asarray(b, np.uint32) << 16).view(np.float32).astype(np.float16).astype(np.float64),  # narrowed
+])
+def test_planted_bf16_widening_mistakes_are_caught(wrong):
+    """Plausible slips in the widening each fail the pin above."""
+    assert not bf16_widening_matches(wrong)
+
+
 def test_e4m3_decoder_against_the_format_and_torch():
     # values the OCP 8-bit float format fixes for E4M3
     fixed = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x30: 0.5, 0x7E: 448.0, 0xFE: -448.0,
@@ -555,3 +598,34 @@ def test_planted_top_left_decode_alignment_is_caught():
     o_pre, _ = oracle.gqa_prefill(q_full, k, v)
     wrong = oracle.softmax_attention(q_full[0, 0, L - s_q:], k[0, 0], v[0, 0], np.arange(s_q) + 1, 1 / math.sqrt(d))[0]
     assert np.max(np.abs(wrong - o_pre[0, 0, L - s_q:])) > 1e-3
+
+
+def test_row_subsets_equal_the_full_evaluation():
+    """Evaluating a subset of (batch, head) rows gives exactly those rows of
+    the full evaluation (rows are independent), in every decode form that
+    evaluates a unit's heads together; rows outside the subset stay NaN."""
+    B, h_q, h_kv, s_q, d, L_cap = 2, 8, 2, 2, 4, 9
+    q = rnd((B, h_q, s_q, d), 40, 1)
+    kc, vc = rnd((B, h_kv, L_cap, d), 40, 2), rnd((B, h_kv, L_cap, d), 40, 3)
+    seqlens = np.array([3, 9])
+    pairs = [(1, 6), (0, 1), (1, 0), (1, 7)]
+    full, full_lse = oracle.gqa_decode(q, kc, vc, seqlens)
+    part, part_lse = oracle.gqa_decode(q, kc, vc, seqlens, heads=pairs)
+    for b, i in pairs:
+        np.testing.assert_array_equal(part[b, i], full[b, i])
+        np.testing.assert_array_equal(part_lse[b, i], full_lse[b, i])
+    assert np.isnan(part[0, 0]).all()
+    ql, qr = rnd((B, s_q, h_q, 6), 40, 4), rnd((B, s_q, h_q, 2), 40, 5)
+    c, kr = rnd((B, L_cap, 6), 40, 6), rnd((B, L_cap, 2), 40, 7)
+    full, full_lse = oracle.latent_absorb_decode(ql, qr, c, kr, seqlens, scale=0.4)
+    part, part_lse = oracle.latent_absorb_decode(ql, qr, c, kr, seqlens, scale=0.4, heads=pairs)
+    for b, i in pairs:
+        np.testing.assert_allclose(part[b, :, i], full[b, :, i], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(part_lse[b, :, i], full_lse[b, :, i], rtol=0, atol=1e-15)
+    assert np.isnan(part[0, :, 0]).all()
+    qc, qrr = rnd((B, h_q, s_q, 4), 40, 8), rnd((B, h_q, s_q, 2), 40, 9)
+    kcc, krr, vv = rnd((B, h_kv, L_cap, 4), 40, 10), rnd((B, L_cap, 2), 40, 11), rnd((B, h_kv, L_cap, 3), 40, 12)
+    full, _ = oracle.gqla_gqa_decode(qc, qrr, kcc, krr, vv, seqlens, scale=0.4)
+    part, _ = oracle.gqla_gqa_decode(qc, qrr, kcc, krr, vv, seqlens, scale=0.4, heads=pairs)
+    for b, i in pairs:
+        np.testing.assert_allclose(part[b, i], full[b, i], rtol=0, atol=1e-15)
