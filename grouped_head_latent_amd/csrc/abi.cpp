@@ -105,6 +105,36 @@ int latent_row_blocks(int h_q, int s_q) {
   return (h_q * s_q + r - 1) / r;
 }
 
+// GTA value sources: the kernels apply a group's scores to value sources of
+// `dvw` columns, a head of d_v columns being d_v / dvw of them.  A launch
+// takes `nvs` sources (the largest of 4, 2, 1 that divides the group's
+// `nsrc`, within `max_cols` columns); `launches` launches cover the group.
+struct GtaSources {
+  int dvw, sph, nsrc, nvs, launches;
+};
+GtaSources gta_sources(int per, int d_v, int dvw, int max_cols) {
+  GtaSources p{};
+  p.dvw = dvw;
+  p.sph = d_v / dvw;
+  p.nsrc = per * p.sph;
+  p.nvs = 1;
+  for (int n : {4, 2})
+    if (n * dvw <= max_cols && p.nsrc % n == 0) {
+      p.nvs = n;
+      break;
+    }
+  p.launches = p.nsrc / p.nvs;
+  return p;
+}
+// prefill: 64-column sources, up to four per work-group
+GtaSources gta_prefill_sources(int per, int d_v) { return gta_sources(per, d_v, 64, 256); }
+// decode: 64-column sources for d_v = 64, else 128; a 16-row q-tile holds up
+// to 512 accumulated columns, a 32-row one up to 256
+GtaSources gta_decode_sources(int per, int d_v, int s_q) {
+  return gta_sources(per, d_v, d_v == 64 ? 64 : 128, s_q <= 16 ? 512 : 256);
+}
+bool gta_dv_ok(int d_v) { return d_v == 64 || d_v == 128 || d_v == 256; }
+
 }  // namespace
 
 extern "C" {
@@ -277,6 +307,7 @@ gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_
     sa.o = o->ptr; sa.o_sb = o->sb; sa.o_sh = o->sh; sa.o_ss = o->ss;
     sa.lse = lse;
     sa.B = B; sa.n_groups = h_kv; sa.qpg = h_q / h_kv; sa.s_q = s_q; sa.rows = rows; sa.L_cap = L_cap;
+    sa.v_hpg = 1; sa.v_sph = 1;
     sa.team = 1;
     sa.n_wg = stream_decode_wgs(B, h_kv, 1, L_max_hint);
     stream_decode_carve(sa, workspace, d);
@@ -385,6 +416,7 @@ gha_status stream_gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, con
   sa.o = o->ptr; sa.o_sb = o->sb; sa.o_sh = o->sh; sa.o_ss = o->ss;
   sa.lse = lse;
   sa.B = B; sa.n_groups = h_kv; sa.qpg = h_q / h_kv; sa.s_q = s_q; sa.rows = rows; sa.L_cap = L_cap;
+  sa.v_hpg = 1; sa.v_sph = 1;
   sa.team = 1;
   sa.n_wg = stream_decode_wgs(B, h_kv, 1, L_plan, target);
   stream_decode_carve(sa, workspace, d);
@@ -432,9 +464,8 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
   if (B < 1 || h < 1 || n_grp < 1 || S < 1) return fail(GHA_ERR_SHAPE, "sizes must be positive");
   if (h % n_grp) return fail(GHA_ERR_GROUPING, "h=%d is not a multiple of n_grp=%d", h, n_grp);
   const int per = h / n_grp;
-  const int DV = per * d_v;
-  if ((d_qk != 64 && d_qk != 128) || d_v != 64 || (DV != 64 && DV != 128 && DV != 256))
-    return fail(GHA_ERR_HEAD_DIM, "need d_qk in {64,128}, d_v == 64 and (h/n_grp)*d_v in {64,128,256} (d_qk=%d d_v=%d per=%d)", d_qk, d_v, per);
+  if ((d_qk != 64 && d_qk != 128) || !gta_dv_ok(d_v))
+    return fail(GHA_ERR_HEAD_DIM, "need d_qk in {64,128} and d_v in {64,128,256} (d_qk=%d d_v=%d)", d_qk, d_v);
   if (in_dtype != GHA_BF16 || (out_dtype != GHA_BF16 && out_dtype != GHA_F32))
     return fail(GHA_ERR_DTYPE, "GTA takes bf16 inputs and bf16 or f32 outputs");
   gha_status s;
@@ -452,6 +483,8 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
   a.lse = lse; a.lse_heads = n_grp;
   a.S_q = S; a.S_k = S; a.h_kv = n_grp; a.group = per;
   a.heads_per_wg = 1; a.n_subgroups = 1;
+  const GtaSources src = gta_prefill_sources(per, d_v);
+  a.v_hpg = per; a.v_sph = src.sph;
   const int pos_per_wg = gha::gta_positions_per_wg();
   a.n_qblocks = (S + pos_per_wg - 1) / pos_per_wg;
   const int64_t nb = (int64_t)B * n_grp * a.n_qblocks;
@@ -463,13 +496,30 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
   if (!gha::gta_layout_supported(a, d_qk, d_v))
     return fail(GHA_ERR_STRIDE, "k/v rows overlap or one sequence spans 2 GiB or more (k ss=%lld, v ss=%lld, S=%d)",
                 (long long)k->ss, (long long)v->ss, S);
-  return launched(gha::launch_gta(a, d_qk, per, out_dtype == GHA_F32, reinterpret_cast<hipStream_t>(stream)),
-                  "gta_shared_score_prefill");
+  // launch l applies the scores to sources l nvs .. of every group: the v and
+  // o views start at that source's head and column; the lse is written once
+  const int64_t ob = elem_size(out_dtype);
+  for (int l = 0; l < src.launches; ++l) {
+    const int s0 = l * src.nvs;
+    const int64_t vofs = (int64_t)(s0 / src.sph) * v->sh + (int64_t)(s0 % src.sph) * src.dvw;
+    const int64_t oofs = (int64_t)(s0 / src.sph) * o->sh + (int64_t)(s0 % src.sph) * src.dvw;
+    a.v = static_cast<const unsigned char*>(v->ptr) + vofs * 2;
+    a.o = static_cast<unsigned char*>(o->ptr) + oofs * ob;
+    a.lse = l == 0 ? lse : nullptr;
+    const gha_status st = launched(gha::launch_gta(a, d_qk, src.nvs, out_dtype == GHA_F32,
+                                                   reinterpret_cast<hipStream_t>(stream)),
+                                   "gta_shared_score_prefill");
+    if (st != GHA_OK) return st;
+  }
+  return GHA_OK;
 }
 
 size_t gta_shared_score_decode_workspace_bytes(int B, int h, int n_grp, int s_q, int L_max_hint, int d_v) {
-  if (B < 1 || h < 1 || n_grp < 1 || s_q < 1 || s_q > 32 || L_max_hint < 1 || d_v < 1 || h % n_grp) return 0;
-  return stream_decode_ws(B, n_grp, 1, s_q, L_max_hint, (h / n_grp) * d_v);
+  if (B < 1 || h < 1 || n_grp < 1 || s_q < 1 || s_q > 32 || L_max_hint < 1 || !gta_dv_ok(d_v) || h % n_grp) return 0;
+  // the launches over a group's value sources run one after another on the
+  // stream and reuse one launch's workspace
+  const GtaSources src = gta_decode_sources(h / n_grp, d_v, s_q);
+  return stream_decode_ws(B, n_grp, 1, s_q, L_max_hint, src.nvs * src.dvw);
 }
 
 gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_tensor* v_cache,
@@ -484,8 +534,8 @@ gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cach
   if (L_max_hint > L_cap || s_q > L_max_hint)
     return fail(GHA_ERR_SHAPE, "need s_q <= L_max_hint <= L_cap (s_q=%d L_max_hint=%d L_cap=%d)", s_q, L_max_hint, L_cap);
   if (s_q > 32) return fail(GHA_ERR_SHAPE, "s_q=%d above 32 new tokens per step", s_q);
-  if ((d_qk != 64 && d_qk != 128) || d_v != 64 || (per != 1 && per != 2 && per != 4))
-    return fail(GHA_ERR_HEAD_DIM, "need d_qk in {64,128}, d_v == 64 and h/n_grp in {1,2,4} (d_qk=%d d_v=%d per=%d)", d_qk, d_v, per);
+  if ((d_qk != 64 && d_qk != 128) || !gta_dv_ok(d_v))
+    return fail(GHA_ERR_HEAD_DIM, "need d_qk in {64,128} and d_v in {64,128,256} (d_qk=%d d_v=%d)", d_qk, d_v);
   if (in_dtype != GHA_BF16 || (out_dtype != GHA_BF16 && out_dtype != GHA_F32))
     return fail(GHA_ERR_DTYPE, "GTA decode takes bf16 inputs and bf16 or f32 outputs");
   if (seqlens_k == nullptr) return fail(GHA_ERR_NULL, "seqlens_k is null");
@@ -512,14 +562,29 @@ gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cach
   a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
   a.lse = lse;
   a.B = B; a.n_groups = n_grp; a.qpg = 1; a.s_q = s_q; a.rows = s_q; a.L_cap = L_cap;
+  const GtaSources src = gta_decode_sources(per, d_v, s_q);
+  a.v_hpg = per; a.v_sph = src.sph;
   a.team = 1;
   a.n_wg = stream_decode_wgs(B, n_grp, 1, L_max_hint);
-  stream_decode_carve(a, workspace, per * d_v);
+  stream_decode_carve(a, workspace, src.nvs * src.dvw);
   a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d_qk);
   if ((int64_t)B * ((L_cap + 127) / 128) >= (1LL << 31)) return fail(GHA_ERR_SHAPE, "problem too large for one launch");
-  return launched(gha::launch_stream_decode(a, d_qk, 0, d_v, per, out_dtype == GHA_F32,
-                                            reinterpret_cast<hipStream_t>(stream)),
-                  "gta_shared_score_decode");
+  // launch l covers sources l nvs .. of every group (views start at that
+  // source's head and column); the per-group lse is written once
+  const int64_t ob = elem_size(out_dtype);
+  for (int l = 0; l < src.launches; ++l) {
+    const int s0 = l * src.nvs;
+    const int64_t vofs = (int64_t)(s0 / src.sph) * v_cache->sh + (int64_t)(s0 % src.sph) * src.dvw;
+    const int64_t oofs = (int64_t)(s0 / src.sph) * o->sh + (int64_t)(s0 % src.sph) * src.dvw;
+    a.v = static_cast<const unsigned char*>(v_cache->ptr) + vofs * 2;
+    a.o = static_cast<unsigned char*>(o->ptr) + oofs * ob;
+    a.lse = l == 0 ? lse : nullptr;
+    const gha_status st = launched(gha::launch_stream_decode(a, d_qk, 0, src.dvw, src.nvs, out_dtype == GHA_F32,
+                                                             reinterpret_cast<hipStream_t>(stream)),
+                                   "gta_shared_score_decode");
+    if (st != GHA_OK) return st;
+  }
+  return GHA_OK;
 }
 
 size_t gqla_gqa_decode_workspace_bytes(int B, int h_q, int g, int s_q, int L_max_hint, int d_h) {
@@ -572,6 +637,7 @@ gha_status gqla_gqa_decode(const gha_tensor* q_c, const gha_tensor* q_r, const g
   a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
   a.lse = lse;
   a.B = B; a.n_groups = g; a.qpg = h_q / g; a.s_q = s_q; a.rows = rows; a.L_cap = L_cap;
+  a.v_hpg = 1; a.v_sph = 1;
   a.team = g;  // every group reads the shared RoPE key
   a.n_wg = stream_decode_wgs(B, g, g, L_max_hint);
   stream_decode_carve(a, workspace, d_h);

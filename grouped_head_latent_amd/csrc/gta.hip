@@ -3,17 +3,20 @@
 // "GTA: Grouped-head latenT Attention" news article, grouped shared attention
 // matrix mechanism: the heads of a group share one attention matrix, computed
 // once and applied to the values of every head in the group.  Per group there
-// is one query and one key (d_qk wide) and one 64-wide value per head.
+// is one query and one key (d_qk wide) and one value per head (d_v wide).
+// The kernel applies the scores to H value sources of 64 columns each
+// (a head of d_v = 128 or 256 is two or four sources); a group with more than
+// four sources is covered by several launches, each recomputing the scores.
 //
 // One work-group (eight waves, two per SIMD) owns 128 positions of one group
 // and walks the keys in tiles of 64:
 //   score: wave w computes S^T = K Q^T for positions 16 w .. 16 w + 15 (K
 //          from LDS, Q^T resident in VGPRs), runs their softmax and publishes
 //          the bf16 probabilities as P^T operand fragments in LDS;
-//   value: the waves split the group's heads and positions (with four heads,
-//          wave w takes head w / 2 for positions 64 (w % 2) .. + 63) and
-//          accumulate O^T += V^T P^T: V^T fragments come from transposing LDS
-//          reads of the head's V tile, P^T fragments from LDS.
+//   value: the waves split the value sources and positions (with four
+//          sources, wave w takes source w / 2 for positions 64 (w % 2) .. + 63)
+//          and accumulate O^T += V^T P^T: V^T fragments come from transposing
+//          LDS reads of the source's V tile, P^T fragments from LDS.
 // So the score matrix is computed once per group and every K or V tile is
 // fetched once per work-group.  Two waves per SIMD let one wave's softmax and
 // LDS traffic overlap the other's matrix work.
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
   constexpr int NBS = 3 * NB / 4;   // the softmax shares the first NBS of them
   constexpr int U = Ly::KROW / 16;  // 16-byte units per K row
   constexpr int NS = Ly::NS;
-  static_assert(H == 1 || H == 2 || H == 4, "heads per group");
+  static_assert(H == 1 || H == 2 || H == 4, "value sources per work-group");
   static_assert(QT == 1, "one score tile per wave");
   static_assert(RT == 1 || RT == 2 || RT == 4, "row tiles per wave");
   static_assert(Ly::KDMA >= 1 && Ly::KDMA <= DS && Ly::VDMA >= 1 && NB % Ly::VDMA == 0, "DMA slots");
@@ -135,7 +138,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
 
   const __bf16* qbase = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)grp * a.q_sh;
   const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)grp * a.k_sh;
-  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)(grp * H + hv) * a.v_sh;
+  // value source hv: columns 64 (hv % v_sph) .. + 63 of head grp v_hpg + hv / v_sph
+  const int vhead = grp * a.v_hpg + hv / a.v_sph, vcol = 64 * (hv % a.v_sph);
+  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)vhead * a.v_sh + vcol;
 
   // ---- Q^T fragments of this wave's score rows ----------------------------------
   u32x4 qf[QT][DS];
@@ -443,14 +448,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
     }
   }
   __syncthreads();
-  const int head = grp * H + hv;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = 16 * (rt0 + rt) + li;
     const int pos = pos_wg + row;
     if (pos >= S) continue;
     const float inv = stats[row];
-    const int64_t obase = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh + (int64_t)pos * a.o_ss + 4 * lg;
+    const int64_t obase = (int64_t)b * a.o_sb + (int64_t)vhead * a.o_sh + (int64_t)pos * a.o_ss + vcol + 4 * lg;
     // oacc[ct][rt][r] is feature 16 ct + 4 lg + r of this row
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -486,9 +490,9 @@ bool gta_layout_supported(const PrefillArgs& a, int d_qk, int d_v) {
   return a.k_ss >= d_qk && a.v_ss >= d_v && span_k < ((int64_t)1 << 31) && span_v < ((int64_t)1 << 31);
 }
 
-hipError_t launch_gta(const PrefillArgs& a, int d_qk, int heads_per_group, bool out_f32, hipStream_t st) {
+hipError_t launch_gta(const PrefillArgs& a, int d_qk, int sources, bool out_f32, hipStream_t st) {
 #define GHA_GTA_CASE(DQ, HH) \
-  if (d_qk == DQ && heads_per_group == HH) return launch_h<DQ, HH>(a, out_f32, st);
+  if (d_qk == DQ && sources == HH) return launch_h<DQ, HH>(a, out_f32, st);
   GHA_GTA_CASE(64, 4)
   GHA_GTA_CASE(64, 2)
   GHA_GTA_CASE(64, 1)

@@ -27,6 +27,10 @@ struct PrefillArgs {
   // second key part (d = 128 kernel only): keys [k; k2] of width 128 + dk2
   // against queries [q; q2]; dk2 = 0 for none
   int dk2;
+  // GTA: value heads per group, and 64-wide value sources per head (d_v / 64);
+  // the kernel's value source s of group j is columns 64 (s % v_sph) .. + 63
+  // of head j v_hpg + s / v_sph
+  int v_hpg, v_sph;
   const void* q2; int64_t q2_sb, q2_sh, q2_ss;
   const void* k2; int64_t k2_sb, k2_sh, k2_ss;
 };
@@ -74,9 +78,14 @@ struct StreamDecodeArgs {
   const void* q2; int64_t q2_sb, q2_sh, q2_ss; // query part 2: (B, G * qpg, s_q, dk2), if dk2 > 0
   const void* k;  int64_t k_sb, k_sh, k_ss;    // per-group key cache (B, G, L_cap, dk1)
   const void* k2; int64_t k2_sb, k2_ss;        // shared key cache (B, L_cap, dk2), if dk2 > 0
-  const void* v;  int64_t v_sb, v_sh, v_ss;    // value heads (B, G * nvs, L_cap, dvw)
+  const void* v;  int64_t v_sb, v_sh, v_ss;    // value heads (B, G * v_hpg, L_cap, v_sph * dvw)
+  // value source s (of nvs, each dvw wide) of group j is columns
+  // dvw (s % v_sph) .. + dvw - 1 of value head j v_hpg + s / v_sph; output
+  // row (hh, t) of group j writes that source to head (j qpg + hh) v_hpg +
+  // s / v_sph at the same columns
+  int v_hpg, v_sph;
   const int32_t* seqlens;
-  void* o;        int64_t o_sb, o_sh, o_ss;    // (B, G * qpg * nvs, s_q, dvw)
+  void* o;        int64_t o_sb, o_sh, o_ss;    // (B, G * qpg * v_hpg, s_q, v_sph * dvw)
   float* lse;         // dense (B, G * qpg, s_q) or null
   float* ws_o;        // (n_wg + B * G slots, rows padded to 16 or 32, nvs * dvw) partials
   float* ws_lse;      // (n_wg + B * G slots, padded rows)
@@ -119,7 +128,7 @@ hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t s
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
 int prefill_rows_per_wave();
 int prefill_bf16_waves(const PrefillArgs& a, int d);  // waves per work-group of the kernel chosen for a
-hipError_t launch_gta(const PrefillArgs& a, int d_qk, int heads_per_group, bool out_f32, hipStream_t st);
+hipError_t launch_gta(const PrefillArgs& a, int d_qk, int sources, bool out_f32, hipStream_t st);
 int gta_positions_per_wg();
 // K/V spans and row pitches the GTA kernel's 32-bit buffer addressing covers
 bool gta_layout_supported(const PrefillArgs& a, int d_qk, int d_v);

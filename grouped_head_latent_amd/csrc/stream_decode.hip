@@ -4,7 +4,9 @@
 //   * GTA shared-score decode ("GTA: Grouped-head latenT Attention" news
 //     article, grouped shared attention matrix): per group one query and one
 //     cached key (d_qk wide) per token, so one score vector per new token, and
-//     the cached values of the group's H heads (H x 64 wide) that all use it;
+//     the cached values of the group's heads that all use it (value sources
+//     of 64 or 128 columns of a head; a group wider than one launch's sources
+//     is covered by several launches);
 //   * GQLA's GQA-path decode ("GQLA: Group-Query Latent Attention ...",
 //     section 1 and section 3.1, Eq. (1)): per group a cached key k^C and a
 //     cached value, plus one decoupled RoPE key k^R per token that every group
@@ -232,7 +234,9 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
 #pragma unroll
   for (int vs = 0; vs < NVS; ++vs)
     vrs[vs] = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const unsigned char*)a.v + ((int64_t)b * a.v_sb + (int64_t)(j * NVS + vs) * a.v_sh) * EB), 0,
+        (void*)((const unsigned char*)a.v +
+                ((int64_t)b * a.v_sb + (int64_t)(j * a.v_hpg + vs / a.v_sph) * a.v_sh + (vs % a.v_sph) * DVW) * EB),
+        0,
         (int)(lastk * vrow + (uint32_t)Ly::RVROW), kBufferFlags);
   // per-lane offsets of the instructions of one tile (they repeat every tile)
   // (8-bit tiles are stored unswizzled: they are only read row-major, by the
@@ -582,9 +586,10 @@ __global__ __launch_bounds__(256) void stream_decode_merge_kernel(StreamDecodeAr
 #pragma unroll
   for (int f = 0; f < FPT; f += 4) {
     // features f0 + f .. + 3 lie in one value source (DVW is a multiple of FPT)
-    const int fe = f0 + f;
-    const int head = qhead * (DV / DVW) + fe / DVW;
-    const int64_t o = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh + (int64_t)tq * a.o_ss + fe % DVW;
+    const int fe = f0 + f, src = fe / DVW;
+    const int head = qhead * a.v_hpg + src / a.v_sph;
+    const int64_t o = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh + (int64_t)tq * a.o_ss +
+                      (src % a.v_sph) * DVW + fe % DVW;
     if constexpr (OUT_F32)
       *reinterpret_cast<f32x4*>((float*)a.o + o) = f32x4{acc[f] * inv, acc[f + 1] * inv, acc[f + 2] * inv, acc[f + 3] * inv};
     else
@@ -614,7 +619,10 @@ hipError_t launch_cfg(const StreamDecodeArgs& a, bool out_f32, hipStream_t st) {
 template <int DK1, int DK2, int DVW, int NVS, int EB = 2>
 hipError_t launch_qt(const StreamDecodeArgs& a, bool out_f32, hipStream_t st) {
   if (a.rows <= 16) return launch_cfg<DK1, DK2, DVW, NVS, 1, EB>(a, out_f32, st);
-  if (a.rows <= 32) return launch_cfg<DK1, DK2, DVW, NVS, 2, EB>(a, out_f32, st);
+  // 32 rows keep an accumulator of NVS * DVW / 16 tiles per q-tile: at most
+  // 256 columns, so that it fits the accumulation registers
+  if constexpr (NVS * DVW <= 256)
+    if (a.rows <= 32) return launch_cfg<DK1, DK2, DVW, NVS, 2, EB>(a, out_f32, st);
   return hipErrorInvalidValue;
 }
 
@@ -639,6 +647,11 @@ hipError_t launch_stream_decode(const StreamDecodeArgs& a, int dk1, int dk2, int
   GHA_SD_CASE(128, 0, 64, 4)
   GHA_SD_CASE(128, 64, 128, 1)
   GHA_SD_CASE(128, 0, 128, 1)
+  GHA_SD_CASE(64, 0, 128, 1)
+  GHA_SD_CASE(64, 0, 128, 2)
+  GHA_SD_CASE(64, 0, 128, 4)
+  GHA_SD_CASE(128, 0, 128, 2)
+  GHA_SD_CASE(128, 0, 128, 4)
 #undef GHA_SD_CASE
   return hipErrorInvalidValue;
 }

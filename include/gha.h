@@ -187,9 +187,11 @@ gha_status gqa_decode_fp8(const gha_tensor* q, const gha_tensor* k_cache, const 
  *   q, k (B, n_grp, S, d_qk): one query and one key per group;
  *   v (B, h, S, d_v), o (B, h, S, d_v): per head; head i is in group
  *   i / (h / n_grp); lse NULL or dense fp32 (B, n_grp, S), one per group.
- * Requires h % n_grp == 0, d_qk in {64, 128}, d_v == 64,
- * (h / n_grp) * d_v in {64, 128, 256}; in BF16, out BF16 or F32.
- * scale <= 0 means 1/sqrt(d_qk). */
+ * Requires h % n_grp == 0, d_qk in {64, 128}, d_v in {64, 128, 256}; any
+ * number of heads per group; in BF16, out BF16 or F32.  scale <= 0 means
+ * 1/sqrt(d_qk).  The scores are applied to the group's values in slices of
+ * at most 256 columns; a group with more value columns than that takes
+ * several launches on `stream`, each recomputing the group's scores. */
 gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k,
                                     const gha_tensor* v, const gha_tensor* o, float* lse,
                                     int B, int h, int n_grp, int S, int d_qk, int d_v,
@@ -206,11 +208,15 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k,
  *   seqlens_k: device int32 (B,), s_q <= seqlens_k[b] <= L_cap, counting the
  *   new tokens (bottom-right alignment as in gqa_decode);
  *   o (B, h, s_q, d_v); lse NULL or dense fp32 (B, n_grp, s_q), one per group.
- * d_qk in {64, 128}, d_v == 64, h / n_grp in {1, 2, 4}, s_q <= 32; in BF16,
- * out BF16 or F32; scale <= 0 means 1/sqrt(d_qk).  Rows of a cache must not
- * overlap (ss >= width) and one (batch, group or head) sequence must span less
- * than 2 GiB.  workspace: at least gta_shared_score_decode_workspace_bytes(...)
- * bytes of device memory; its contents on entry do not matter. */
+ * d_qk in {64, 128}, d_v in {64, 128, 256}, any number of heads per group,
+ * s_q <= 32; in BF16, out BF16 or F32; scale <= 0 means 1/sqrt(d_qk).  Rows
+ * of a cache must not overlap (ss >= width) and one (batch, group or head)
+ * sequence must span less than 2 GiB.  The scores are applied to the group's
+ * values in slices of at most 512 columns (256 when s_q > 16); a wider group
+ * takes several launches on `stream`, each reading the group's keys again.
+ * workspace: at least gta_shared_score_decode_workspace_bytes(...) bytes of
+ * device memory (one slice's partials, reused by the launches in turn); its
+ * contents on entry do not matter. */
 gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cache,
                                    const gha_tensor* v_cache, const int32_t* seqlens_k,
                                    const gha_tensor* o, float* lse,

@@ -282,7 +282,7 @@ def gta(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(n_grp=3), 3), (dict(d_v=128), 7), (dict(h=32, n_grp=4), 7), (dict(d_qk=96), 7),
+    (dict(n_grp=3), 3), (dict(d_v=96), 7), (dict(d_v=512), 7), (dict(d_v=32), 7), (dict(d_qk=96), 7),
 ])
 def test_gta_rejects_bad_arguments(lib, kw, status):
     assert gta(lib, **kw) == status
@@ -300,8 +300,11 @@ def gta_dec(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(n_grp=3), 3), (dict(d_v=128), 7), (dict(h=32, n_grp=4), 7), (dict(d_qk=96), 7),
+    (dict(n_grp=3), 3), (dict(d_v=96), 7), (dict(d_v=512), 7), (dict(d_qk=96), 7),
     (dict(s_q=33, L_max=64), 2), (dict(L_max=8192), 2), (dict(seq=0), 1), (dict(ws_bytes=16), 8),
+    # wider values and more heads per group are accepted; these stop at the workspace
+    (dict(d_v=256, v=T(ss=256), ws_bytes=16), 8), (dict(h=32, n_grp=4, d_v=128, ws_bytes=16), 8),
+    (dict(d_v=256), 4),                     # value rows of 256 elements would overlap (ss = 128)
     (dict(k=T(ss=32)), 4),                  # key rows of 64 elements would overlap
     (dict(v=T(ss=1 << 20)), 2),             # a sequence spanning 8 GiB
 ])
@@ -340,6 +343,21 @@ def test_stream_decode_workspace_sizes(lib):
     assert lib.gqla_gqa_decode_workspace_bytes(64, 128, 8, 3, 65536, 128) == 0
     # a tiny problem has no more work-groups than chunks
     assert lib.gta_shared_score_decode_workspace_bytes(1, 4, 1, 1, 100, 64) == (1 + 1) * 16 * 257 * 4 + 2 * 4
+
+
+def test_gta_decode_workspace_follows_the_value_sources(lib):
+    # value sources of 128 columns for d_v >= 128: a launch takes up to 512
+    # columns when one q-tile holds the rows (s_q <= 16), else up to 256; the
+    # launches over a group's sources reuse one launch's workspace
+    def ws(rows_padded, dv, units=64 * 4, wgs=256):
+        n = (wgs + units) * rows_padded
+        return n * dv * 4 + n * 4 + 65 * 4
+    assert lib.gta_shared_score_decode_workspace_bytes(64, 16, 4, 1, 32768, 64) == ws(16, 256)
+    assert lib.gta_shared_score_decode_workspace_bytes(64, 16, 4, 1, 32768, 128) == ws(16, 512)
+    assert lib.gta_shared_score_decode_workspace_bytes(64, 16, 4, 2, 32768, 256) == ws(16, 512)
+    assert lib.gta_shared_score_decode_workspace_bytes(64, 16, 4, 17, 32768, 128) == ws(32, 256)
+    assert lib.gta_shared_score_decode_workspace_bytes(64, 12, 4, 1, 32768, 64) == ws(16, 64)   # 3 heads: 1 source a launch
+    assert lib.gta_shared_score_decode_workspace_bytes(64, 16, 4, 1, 32768, 96) == 0
 
 
 def test_valid_call_without_device_reports_hip_error(lib):

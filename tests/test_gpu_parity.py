@@ -510,24 +510,31 @@ def test_gqla_gqa_prefill_full_size_sampled(gha_lib):
 # -------------------------------------------------------------- GTA decode
 
 GTA_DECODE_CASES = [
-    # B, h, n_grp, s_q, L_cap, seqlens, d_qk
-    (3, 16, 4, 1, 1100, [1, 700, 1100], 64),
-    (3, 16, 4, 2, 1100, [2, 333, 1099], 64),
-    (2, 8, 4, 1, 600, [64, 599], 64),        # two heads per group
-    (2, 4, 4, 2, 300, [5, 300], 64),         # one head per group
-    (2, 8, 2, 1, 500, [3, 480], 128),        # d_qk 128: two waves per work-group
-    (1, 16, 4, 16, 400, [390], 64),          # 16 new tokens
-    (1, 4, 4, 20, 400, [390], 64),           # 20 rows: two row tiles
+    # B, h, n_grp, s_q, L_cap, seqlens, d_qk, d_v
+    (3, 16, 4, 1, 1100, [1, 700, 1100], 64, 64),
+    (3, 16, 4, 2, 1100, [2, 333, 1099], 64, 64),
+    (2, 8, 4, 1, 600, [64, 599], 64, 64),        # two heads per group
+    (2, 4, 4, 2, 300, [5, 300], 64, 64),         # one head per group
+    (2, 8, 2, 1, 500, [3, 480], 128, 64),        # d_qk 128: two waves per work-group
+    (1, 16, 4, 16, 400, [390], 64, 64),          # 16 new tokens
+    (1, 4, 4, 20, 400, [390], 64, 64),           # 20 rows: two row tiles
+    (2, 12, 4, 1, 300, [100, 300], 64, 64),      # three heads per group: one value source a launch
+    # wider values: sources of 128 columns, several launches per group
+    (2, 8, 4, 1, 600, [64, 599], 64, 128),       # 2 sources, one launch
+    (2, 16, 4, 2, 500, [3, 480], 64, 128),       # 4 sources (512 columns), one launch
+    (2, 16, 4, 1, 400, [1, 399], 128, 256),      # 8 sources, two launches
+    (1, 8, 4, 20, 300, [290], 64, 128),          # 20 rows: at most 256 columns a launch
+    (1, 4, 1, 17, 300, [250], 64, 256),          # 8 sources of 17 rows: four launches
 ]
 
 
-@pytest.mark.parametrize("B,h,n_grp,s_q,L_cap,seqlens,d_qk", GTA_DECODE_CASES)
-def test_gta_shared_score_decode(gha_lib, B, h, n_grp, s_q, L_cap, seqlens, d_qk):
-    say(f"GTA decode B={B} h={h} groups={n_grp} s_q={s_q} L_cap={L_cap} L={seqlens} d_qk={d_qk}")
+@pytest.mark.parametrize("B,h,n_grp,s_q,L_cap,seqlens,d_qk,d_v", GTA_DECODE_CASES)
+def test_gta_shared_score_decode(gha_lib, B, h, n_grp, s_q, L_cap, seqlens, d_qk, d_v):
+    say(f"GTA decode B={B} h={h} groups={n_grp} s_q={s_q} L_cap={L_cap} L={seqlens} d_qk={d_qk} d_v={d_v}")
     seqlens = np.array(seqlens, dtype=np.int32)
     qb = gen((B, n_grp, s_q, d_qk), 22, 1)
     kb = cache_bits(B, n_grp, L_cap, d_qk, seqlens, 22, 2)
-    vb = cache_bits(B, h, L_cap, 64, seqlens, 22, 3)
+    vb = cache_bits(B, h, L_cap, d_v, seqlens, 22, 3)
     q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
     sl = torch.from_numpy(seqlens).cuda()
     o32, lse = twice("gta decode", lambda: gha_lib.gta_shared_score_decode(q, k, v, sl, out_dtype=torch.float32,
@@ -672,6 +679,13 @@ GTA_CASES = [
     (1, 4, 4, 70, 64, 64),
     (1, 8, 2, 100, 128, 64),
     (4, 16, 4, 520, 64, 64),  # 16 (batch, group) units of 5 q-blocks: 80 work-groups
+    (1, 6, 2, 100, 64, 64),   # three heads per group: one 64-column source a launch
+    # wider values: 64-column sources, up to four a launch
+    (2, 8, 4, 300, 64, 128),  # 4 sources, one launch
+    (1, 16, 4, 200, 64, 128), # 8 sources, two launches
+    (1, 4, 4, 150, 64, 256),  # one head of 256: 4 sources
+    (1, 8, 2, 130, 128, 256), # 16 sources, four launches, d_qk 128
+    (1, 6, 2, 100, 64, 128),  # 6 sources, three launches of 2
 ]
 
 
