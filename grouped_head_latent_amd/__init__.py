@@ -25,6 +25,7 @@ import os
 __all__ = [
     "gqa_prefill", "gqa_decode", "gqa_decode_paged", "gqa_decode_fp8", "gta_shared_score_prefill", "gta_shared_score_decode",
     "gqla_gqa_decode", "gqla_gqa_prefill", "latent_absorb_decode", "gqla_absorb_decode",
+    "gqa_decode_noalloc", "gqa_decode_noalloc_scratch_bytes",
     "gqa_decode_workspace_bytes", "gqa_decode_paged_workspace_bytes", "gta_shared_score_decode_workspace_bytes",
     "gqla_gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
     "GhaError", "library_path", "load_library", "GHA_F32", "GHA_BF16",
@@ -100,6 +101,10 @@ def load_library():
     lib.gqla_absorb_decode.restype = I
     lib.gqla_absorb_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.gqla_absorb_decode_workspace_bytes.restype = S
+    lib.gqa_decode_noalloc.argtypes = [P, P, P, V, P, V, I, I, I, I, I, I, I, I, I, F, V]
+    lib.gqa_decode_noalloc.restype = I
+    lib.gqa_decode_noalloc_scratch_bytes.argtypes = []
+    lib.gqa_decode_noalloc_scratch_bytes.restype = S
     lib.gha_status_string.argtypes = [I]
     lib.gha_status_string.restype = ctypes.c_char_p
     lib.gha_last_error.argtypes = []
@@ -242,6 +247,31 @@ def gqa_decode(q, k_cache, v_cache, seqlens, *, L_max: int | None = None,
                           _out_code(o.dtype), float(scale or 0.0), _ptr(ws), ws.numel() * ws.element_size(),
                           _stream(stream)))
     return (o, lse) if return_lse else o
+
+
+def gqa_decode_noalloc(q, k_cache, v_cache, seqlens, *, out, L_max: int | None = None,
+                       scale: float | None = None, lse=None, stream=None):
+    """gqa_decode with its workspace in the library's static per-GPU scratch
+    array: allocates nothing, so `out` (and `lse`, if wanted) must be given.
+    q (B, h_q, s_q, d); caches (B, h_kv, L_cap, d); seqlens int32 device (B,).
+    Calls on one GPU that overlap in time race on the shared scratch."""
+    import torch
+    lib = load_library()
+    _need_dtype((torch.bfloat16,), q=q)
+    _check_common(q, "q", inputs=dict(k_cache=k_cache, v_cache=v_cache), seqlens=seqlens, out=out,
+                  extra=dict(lse=lse))
+    _need_dtype((torch.float32,), lse=lse)
+    B, h_q, s_q, d = q.shape
+    h_kv, L_cap = k_cache.shape[1], k_cache.shape[2]
+    L_max = L_cap if L_max is None else int(L_max)
+    _check(lib.gqa_decode_noalloc(_desc(q), _desc(k_cache), _desc(v_cache), _ptr(seqlens), _desc(out), _ptr(lse),
+                                  B, h_q, h_kv, s_q, L_cap, L_max, d, _dtype_code(q), _out_code(out.dtype),
+                                  float(scale or 0.0), _stream(stream)))
+    return out
+
+
+def gqa_decode_noalloc_scratch_bytes() -> int:
+    return int(load_library().gqa_decode_noalloc_scratch_bytes())
 
 
 def gqa_decode_paged_workspace_bytes(B, h_q, h_kv, s_q, L_max, window, d) -> int:

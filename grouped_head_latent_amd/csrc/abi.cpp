@@ -137,6 +137,12 @@ bool gta_dv_ok(int d_v) { return d_v == 64 || d_v == 128 || d_v == 256; }
 
 }  // namespace
 
+namespace gha {
+// the thread-local detail string of gha_last_error(), for entry points
+// defined in other source files
+void set_last_error(const char* msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
+}  // namespace gha
+
 extern "C" {
 
 const char* gha_status_string(gha_status s) {
@@ -254,14 +260,49 @@ gha_status gqla_gqa_prefill(const gha_tensor* q_c, const gha_tensor* q_r, const 
                   "gqla_gqa_prefill");
 }
 
-size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint, int d) {
-  if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_max_hint < 1 || d < 1 || h_q % h_kv) return 0;
+}  // extern "C"
+
+namespace {
+// gqa_decode's choice of kernel: up to 32 query rows per group (heads per
+// group times new tokens) and caches the 32-bit buffer addressing covers go
+// to the streaming kernel (one pass over each group's cache with every row of
+// the group), anything else to the register-fed kernel with 16-row blocks
+bool gqa_decode_streams(const gha_tensor* k_cache, const gha_tensor* v_cache, int h_q, int h_kv, int s_q,
+                        int L_cap, int d) {
+  return (h_q / h_kv) * s_q <= 32 && k_cache->ss >= d && v_cache->ss >= d && span_ok(L_cap, k_cache->ss) &&
+         span_ok(L_cap, v_cache->ss);
+}
+// workspace of the register-fed kernel's split plan
+size_t gqa_decode_register_ws(int B, int h_q, int h_kv, int s_q, int L_max_hint, int d) {
   const int n_rb = gqa_row_blocks(h_q, h_kv, s_q);
   int sl, ns;
   gqa_decode_plan(B, h_kv, n_rb, L_max_hint, &sl, &ns);
   const size_t rows = (size_t)B * h_kv * n_rb * ns * 16;
-  size_t need = rows * (size_t)d * 4 + rows * 4;
-  // the streaming kernel takes up to 32 query rows per group
+  return rows * (size_t)d * 4 + rows * 4;
+}
+bool gqa_decode_sizes_ok(int B, int h_q, int h_kv, int s_q, int L_max_hint, int d) {
+  return B >= 1 && h_q >= 1 && h_kv >= 1 && s_q >= 1 && L_max_hint >= 1 && d >= 1 && h_q % h_kv == 0;
+}
+}  // namespace
+
+namespace gha {
+// the workspace gqa_decode needs for these cache views (the kernel it takes
+// depends on their strides); 0 for arguments it rejects
+size_t gqa_decode_path_workspace(const gha_tensor* k_cache, const gha_tensor* v_cache, int B, int h_q, int h_kv,
+                                 int s_q, int L_cap, int L_max_hint, int d) {
+  if (!gqa_decode_sizes_ok(B, h_q, h_kv, s_q, L_max_hint, d) || k_cache == nullptr || v_cache == nullptr) return 0;
+  if (gqa_decode_streams(k_cache, v_cache, h_q, h_kv, s_q, L_cap, d))
+    return stream_decode_ws(B, h_kv, 1, (h_q / h_kv) * s_q, L_max_hint, d);
+  return gqa_decode_register_ws(B, h_q, h_kv, s_q, L_max_hint, d);
+}
+}  // namespace gha
+
+extern "C" {
+
+size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint, int d) {
+  if (!gqa_decode_sizes_ok(B, h_q, h_kv, s_q, L_max_hint, d)) return 0;
+  // enough for either kernel: which one runs depends on the cache strides
+  size_t need = gqa_decode_register_ws(B, h_q, h_kv, s_q, L_max_hint, d);
   if ((h_q / h_kv) * s_q <= 32) need = std::max(need, stream_decode_ws(B, h_kv, 1, (h_q / h_kv) * s_q, L_max_hint, d));
   return need;
 }
@@ -285,20 +326,17 @@ gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_
   if ((s = check_view("k_cache", k_cache, in_dtype, B > 1, h_kv > 1, true)) != GHA_OK) return s;
   if ((s = check_view("v_cache", v_cache, in_dtype, B > 1, h_kv > 1, true)) != GHA_OK) return s;
   if ((s = check_view("o", o, out_dtype, B > 1, h_q > 1, s_q > 1)) != GHA_OK) return s;
-  const size_t need = gqa_decode_workspace_bytes(B, h_q, h_kv, s_q, L_max_hint, d);
+  // the workspace of the kernel these views take (at most the size that
+  // gqa_decode_workspace_bytes reports)
+  const size_t need = gha::gqa_decode_path_workspace(k_cache, v_cache, B, h_q, h_kv, s_q, L_cap, L_max_hint, d);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
     return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
   if ((s = check_device()) != GHA_OK) return s;
 
-  // Up to 32 query rows per group (heads per group times new tokens) and
-  // caches the 32-bit buffer addressing covers: the streaming kernel (one
-  // pass over each group's cache with every row of the group); otherwise the
-  // register-fed kernel with 16-row blocks.
   const int rows = (h_q / h_kv) * s_q;
-  if (rows <= 32 && k_cache->ss >= d && v_cache->ss >= d && span_ok(L_cap, k_cache->ss) &&
-      span_ok(L_cap, v_cache->ss)) {
+  if (gqa_decode_streams(k_cache, v_cache, h_q, h_kv, s_q, L_cap, d)) {
     gha::StreamDecodeArgs sa{};
     sa.q = q->ptr; sa.q_sb = q->sb; sa.q_sh = q->sh; sa.q_ss = q->ss;
     sa.k = k_cache->ptr; sa.k_sb = k_cache->sb; sa.k_sh = k_cache->sh; sa.k_ss = k_cache->ss;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/gha.h"
+
 namespace gha {
 
 struct PrefillArgs {
@@ -128,6 +130,12 @@ hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t s
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
 int prefill_rows_per_wave();
 int prefill_bf16_waves(const PrefillArgs& a, int d);  // waves per work-group of the kernel chosen for a
+// sets the detail string gha_last_error() returns (defined in abi.cpp)
+void set_last_error(const char* msg);
+// the workspace gqa_decode needs for these cache views (defined in abi.cpp)
+size_t gqa_decode_path_workspace(const gha_tensor* k_cache, const gha_tensor* v_cache, int B, int h_q, int h_kv,
+                                 int s_q, int L_cap, int L_max_hint, int d);
+
 hipError_t launch_gta(const PrefillArgs& a, int d_qk, int sources, bool out_f32, hipStream_t st);
 int gta_positions_per_wg();
 // K/V spans and row pitches the GTA kernel's 32-bit buffer addressing covers

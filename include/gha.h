@@ -326,6 +326,25 @@ gha_status gqla_absorb_decode(const gha_tensor* q_c, const gha_tensor* q_rope, c
 
 size_t gqla_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_hint, int r_kv);
 
+/* gqa_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, which comes instead from one
+ * static device array of gqa_decode_noalloc_scratch_bytes() (16 MiB) per GPU,
+ * held from the library's load until the process ends.  Sizes whose split
+ * partials (for the kernel these cache views take) exceed it return
+ * GHA_ERR_WORKSPACE and launch nothing; otherwise errors and results are
+ * those of gqa_decode.  The call allocates and frees nothing.  Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams or threads) race and give undefined results. */
+gha_status gqa_decode_noalloc(const gha_tensor* q, const gha_tensor* k_cache,
+                              const gha_tensor* v_cache, const int32_t* seqlens_k,
+                              const gha_tensor* o, float* lse,
+                              int B, int h_q, int h_kv, int s_q, int L_cap, int L_max_hint,
+                              int d, gha_dtype in_dtype, gha_dtype out_dtype, float scale,
+                              void* stream);
+
+size_t gqa_decode_noalloc_scratch_bytes(void);
+
 /* Status name, thread-local detail of the last error, library version. */
 const char* gha_status_string(gha_status s);
 const char* gha_last_error(void);
