@@ -568,8 +568,11 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs (and their parity)")
     ap.add_argument("--only", default=None,
-                    help="tiny|prefill|gqla_prefill|decode|paged|fp8|gta|latent|absorbing|gta_decode|gqla_decode: "
+                    help="tiny|prefill|gqla_prefill|decode|paged|paged_window|fp8|gta|latent|absorbing|gta_decode|"
+                         "gqla_decode: "
                          "time one workload")
+    ap.add_argument("--sq", type=int, default=None, choices=(1, 2),
+                    help="decode workloads: time only this many new tokens per sequence")
     ap.add_argument("--spinup-s", type=float, default=1.0,
                     help="untimed seconds of the same workload before the warmup steps (clock ramp)")
     args = ap.parse_args()
@@ -605,6 +608,7 @@ def main():
         return res
 
     want = lambda w: only == w or (only is None and not args.no_extras)
+    sqs = (1, 2) if args.sq is None else (args.sq,)
     steps, warmup = args.steps, args.warmup
     if want("tiny"):
         extras["tiny_gqa_fp32"] = run("tiny", lambda: bench_tiny(gha, torch, steps, warmup), cpu_tiny)
@@ -622,33 +626,36 @@ def main():
     if want("gqla_prefill"):
         extras["gqla_prefill"] = run("gqla prefill", lambda: bench_gqla_prefill(gha, torch, steps, warmup))
     if want("decode"):
-        for s_q in (1, 2):
+        for s_q in sqs:
             extras[f"gqa_decode_sq{s_q}"] = run(f"decode s_q={s_q}",
                                                 lambda: bench_decode(gha, torch, steps, warmup, s_q),
                                                 lambda r: cpu_decode(r, s_q))
-    if want("paged"):
-        for s_q, window in ((1, 0), (2, 0), (1, PAGED["window"])):
+    if want("paged") or only == "paged_window":
+        variants = [(s_q, 0) for s_q in sqs] if only != "paged_window" else []
+        if only in (None, "paged_window") and 1 in sqs:
+            variants.append((1, PAGED["window"]))
+        for s_q, window in variants:
             name = f"gqa_decode_paged{PAGED['page']}" + (f"_window{window}" if window else "") + f"_sq{s_q}"
             extras[name] = run(name, lambda: bench_decode_paged(gha, torch, steps, warmup, s_q, window))
     if want("fp8"):
-        for s_q in (1, 2):
+        for s_q in sqs:
             extras[f"gqa_decode_fp8_sq{s_q}"] = run(f"fp8 decode s_q={s_q}",
                                                     lambda: bench_decode_fp8(gha, torch, steps, warmup, s_q))
     if want("latent"):
-        for s_q in (1, 2):
+        for s_q in sqs:
             extras[f"latent_decode_sq{s_q}"] = run(f"latent s_q={s_q}",
                                                    lambda: bench_latent(gha, torch, steps, warmup, s_q),
                                                    lambda r: cpu_latent(r, s_q))
     if want("absorbing"):
-        for s_q in (1, 2):
+        for s_q in sqs:
             extras[f"latent_absorbing_decode_sq{s_q}"] = run(
                 f"absorbing latent decode s_q={s_q}", lambda: bench_absorbing(gha, torch, steps, warmup, s_q))
     if want("gta_decode"):
-        for s_q in (1, 2):
+        for s_q in sqs:
             extras[f"gta_decode_sq{s_q}"] = run(f"gta decode s_q={s_q}",
                                                 lambda: bench_gta_decode(gha, torch, steps, warmup, s_q))
     if want("gqla_decode"):
-        for s_q in (1, 2):
+        for s_q in sqs:
             extras[f"gqla_decode_sq{s_q}"] = run(f"gqla decode s_q={s_q}",
                                                  lambda: bench_gqla_decode(gha, torch, steps, warmup, s_q))
     for e in extras.values():

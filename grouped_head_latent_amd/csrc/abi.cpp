@@ -523,6 +523,7 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
   a.heads_per_wg = 1; a.n_subgroups = 1;
   const GtaSources src = gta_prefill_sources(per, d_v);
   a.v_hpg = per; a.v_sph = src.sph;
+  // both GTA kernels take 128 positions per work-group
   const int pos_per_wg = gha::gta_positions_per_wg();
   a.n_qblocks = (S + pos_per_wg - 1) / pos_per_wg;
   const int64_t nb = (int64_t)B * n_grp * a.n_qblocks;
@@ -534,6 +535,13 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
   if (!gha::gta_layout_supported(a, d_qk, d_v))
     return fail(GHA_ERR_STRIDE, "k/v rows overlap or one sequence spans 2 GiB or more (k ss=%lld, v ss=%lld, S=%d)",
                 (long long)k->ss, (long long)v->ss, S);
+  // Kernel choice (measured on the GTA workloads): the one-stream kernel,
+  // two work-groups per CU, is the faster one unless a causal grid fits in
+  // one round of them; then its heaviest q-blocks run out the clock alone,
+  // and the exchange kernel, one work-group per CU and two rounds, balances
+  // better.
+  const int cus = gha::device_cus();
+  const bool use_fused = !causal || cus <= 0 || a.n_blocks > 2 * cus;
   // launch l applies the scores to sources l nvs .. of every group: the v and
   // o views start at that source's head and column; the lse is written once
   const int64_t ob = elem_size(out_dtype);
@@ -544,9 +552,11 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
     a.v = static_cast<const unsigned char*>(v->ptr) + vofs * 2;
     a.o = static_cast<unsigned char*>(o->ptr) + oofs * ob;
     a.lse = l == 0 ? lse : nullptr;
-    const gha_status st = launched(gha::launch_gta(a, d_qk, src.nvs, out_dtype == GHA_F32,
-                                                   reinterpret_cast<hipStream_t>(stream)),
-                                   "gta_shared_score_prefill");
+    const hipError_t e = use_fused ? gha::launch_gta_fused(a, d_qk, src.nvs, out_dtype == GHA_F32,
+                                                           reinterpret_cast<hipStream_t>(stream))
+                                   : gha::launch_gta(a, d_qk, src.nvs, out_dtype == GHA_F32,
+                                                     reinterpret_cast<hipStream_t>(stream));
+    const gha_status st = launched(e, "gta_shared_score_prefill");
     if (st != GHA_OK) return st;
   }
   return GHA_OK;

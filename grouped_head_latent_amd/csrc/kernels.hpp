@@ -33,6 +33,10 @@ struct PrefillArgs {
   // the kernel's value source s of group j is columns 64 (s % v_sph) .. + 63
   // of head j v_hpg + s / v_sph
   int v_hpg, v_sph;
+  // GTA one-stream kernel: 1 when the grid is exactly two work-groups per CU
+  // (n_cus CUs); then work-group b shares its CU with b + n_cus and the pair
+  // takes complementary causal blocks.  0: heaviest blocks first.
+  int wg_order, n_cus;
   const void* q2; int64_t q2_sb, q2_sh, q2_ss;
   const void* k2; int64_t k2_sb, k2_sh, k2_ss;
 };
@@ -130,6 +134,8 @@ hipError_t launch_prefill_d128(const PrefillArgs& a, bool out_f32, hipStream_t s
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
 int prefill_rows_per_wave();
 int prefill_bf16_waves(const PrefillArgs& a, int d);  // waves per work-group of the kernel chosen for a
+// compute units of the current device, 0 if it cannot be queried
+int device_cus();
 // sets the detail string gha_last_error() returns (defined in abi.cpp)
 void set_last_error(const char* msg);
 // the workspace gqa_decode needs for these cache views (defined in abi.cpp)
@@ -137,6 +143,8 @@ size_t gqa_decode_path_workspace(const gha_tensor* k_cache, const gha_tensor* v_
                                  int s_q, int L_cap, int L_max_hint, int d);
 
 hipError_t launch_gta(const PrefillArgs& a, int d_qk, int sources, bool out_f32, hipStream_t st);
+// the one-stream GTA prefill kernel: same arguments, also 128 positions per work-group
+hipError_t launch_gta_fused(const PrefillArgs& a, int d_qk, int sources, bool out_f32, hipStream_t st);
 int gta_positions_per_wg();
 // K/V spans and row pitches the GTA kernel's 32-bit buffer addressing covers
 bool gta_layout_supported(const PrefillArgs& a, int d_qk, int d_v);

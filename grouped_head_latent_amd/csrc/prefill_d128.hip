@@ -430,10 +430,7 @@ bool prefill_d128_supported(const PrefillArgs& a) {
   return a.k_ss >= 128 && a.v_ss >= 128 && (a.dk2 == 0 || a.k2_ss >= a.dk2) && span < ((int64_t)1 << 31);
 }
 
-namespace {
-// Work-groups of this kernel resident at once on the current device, or 0 if
-// the device cannot be queried.
-int resident_wgs() {
+int device_cus() {
   static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -442,8 +439,13 @@ int resident_wgs() {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = -1;
     cus[dev].store(n, std::memory_order_relaxed);
   }
-  return n > 0 ? n * GHA_PF_MIN_WG : 0;
+  return n > 0 ? n : 0;
 }
+
+namespace {
+// Work-groups of this kernel resident at once on the current device, or 0 if
+// the device cannot be queried.
+int resident_wgs() { return device_cus() * GHA_PF_MIN_WG; }
 }  // namespace
 
 hipError_t launch_prefill_d128(const PrefillArgs& args, bool out_f32, hipStream_t st) {

@@ -1,7 +1,9 @@
 """Turn rocprofv3 output into the short text summaries kept under profiles/.
 
-    # per-kernel durations (rocprofv3 --kernel-trace --stats ... --output-format csv)
-    python -m grouped_head_latent_amd.rocprof_summary trace <out_dir> <summary.md> --command "..."
+    # per-kernel durations (rocprofv3 --kernel-trace --stats ... --output-format csv);
+    # with the traced bench.py run's JSON line, also the workload's rate from the trace
+    python -m grouped_head_latent_amd.rocprof_summary trace <out_dir> <summary.md> --command "..." \\
+        [--bench-json <bench_stdout>]
     # counters of one --pmc run (FETCH_SIZE, WRITE_SIZE, SQ_* ...)
     python -m grouped_head_latent_amd.rocprof_summary pmc <out_dir> <summary.md> --command "..."
     # a plain copy of known size, profiled to calibrate FETCH_SIZE / WRITE_SIZE
@@ -65,13 +67,45 @@ def pmc_summary(out_dir: str) -> dict:
     return {k: {c: statistics.mean(v) for c, v in d.items()} for k, d in per.items()}
 
 
-def _md_trace(rows, command):
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2516.6
+
+
+def _md_trace(rows, command, bench=None):
     out = ["# rocprofv3 kernel trace", "", f"Command: `{command}`", "",
            "| kernel | calls | avg us | min us | max us | total us |", "|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{_short(r['kernel'])}` | {r['calls']} | {r['avg_us']:.1f} | {r['min_us']:.1f} | "
                    f"{r['max_us']:.1f} | {r['total_us']:.1f} |")
+    if bench:
+        # one workload per traced run: a call of the path is one dispatch of
+        # each of the library's kernels, so its time from the trace is the sum
+        # of their average durations (torch's input-preparation kernels left out)
+        lib = [r for r in rows if r["kernel"].lstrip().split("(")[0].split("<")[0].split()[-1].startswith("gha::")]
+        t_us = sum(r["avg_us"] for r in lib)
+        out += ["", "Roofline from this trace (algorithmic work of the workload from the same run's bench line; "
+                "the path's time per call = the sum of the library kernels' average durations above):", "",
+                "| workload | HIP-event ms per call | trace us per call | algorithmic | rate from trace | of peak |",
+                "|---|---|---|---|---|---|"]
+        for name, e in bench.items():
+            if "gbps" in e:
+                work, rate = f"{e['bytes']:.4g} B", e["bytes"] / (t_us * 1e3)
+                frac, unit = rate / PEAK_HBM_GBPS, "GB/s"
+            else:
+                work, rate = f"{e['flops']:.4g} FLOP", e["flops"] / (t_us * 1e6)
+                frac, unit = rate / PEAK_BF16_TFLOPS, "TFLOP/s"
+            out.append(f"| {name} | {e['ms']:.4f} | {t_us:.1f} | {work} | {rate:.1f} {unit} | {frac:.3f} |")
     return "\n".join(out) + "\n"
+
+
+def _bench_workloads(path):
+    """The workloads of one bench.py JSON line: {name: record}."""
+    line = [l for l in open(path) if l.startswith("{")][-1]
+    d = json.loads(line)
+    w = dict(d.get("extras", {}))
+    if "ms_per_step" in d:
+        w["gqa_prefill"] = {"ms": d["ms_per_step"], "flops": d["roofline"]["achieved"] * d["ms_per_step"] * 1e9}
+    return w
 
 
 def _md_pmc(d, command):
@@ -142,6 +176,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace"); t.add_argument("out_dir"); t.add_argument("md"); t.add_argument("--command", default="")
+    t.add_argument("--bench-json", default=None, help="the traced bench.py run's JSON line (one workload)")
     p = sub.add_parser("pmc"); p.add_argument("out_dir"); p.add_argument("md"); p.add_argument("--command", default="")
     sub.add_parser("copy")
     tr = sub.add_parser("traffic")
@@ -149,7 +184,8 @@ def main(argv=None):
         tr.add_argument(n)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        open(a.md, "w").write(_md_trace(trace_summary(a.out_dir), a.command))
+        bench = _bench_workloads(a.bench_json) if a.bench_json else None
+        open(a.md, "w").write(_md_trace(trace_summary(a.out_dir), a.command, bench))
     elif a.cmd == "pmc":
         open(a.md, "w").write(_md_pmc(pmc_summary(a.out_dir), a.command))
     elif a.cmd == "copy":

@@ -703,6 +703,32 @@ def test_gta_shared_score(gha_lib, B, h, n_grp, S, d_qk, d_v):
     check("gta lse", lse.cpu().numpy(), ref_lse)
 
 
+# GTA shapes that take the one-stream kernel: grids of more than one round of
+# two work-groups per CU (above 512 work-groups on 256 CUs), or no mask
+GTA_ONE_STREAM_CASES = [
+    # B, h, n_grp, S, d_qk, d_v, causal
+    (4, 32, 16, 1100, 64, 64, True),    # 576 work-groups, two heads per group
+    (8, 16, 8, 1100, 64, 128, True),    # 576 work-groups, 128-wide values
+    (2, 16, 4, 300, 64, 256, False),    # four 256-wide heads: four launches
+    (1, 8, 2, 130, 128, 128, False),    # d_qk 128, two launches of four sources
+]
+
+
+@pytest.mark.parametrize("B,h,n_grp,S,d_qk,d_v,causal", GTA_ONE_STREAM_CASES)
+def test_gta_one_stream_kernel(gha_lib, B, h, n_grp, S, d_qk, d_v, causal):
+    say(f"GTA (one-stream kernel) B={B} h={h} groups={n_grp} S={S} d_qk={d_qk} d_v={d_v} causal={causal}")
+    qb, kb, vb = gen((B, n_grp, S, d_qk), 17, 1), gen((B, n_grp, S, d_qk), 17, 2), gen((B, h, S, d_v), 17, 3)
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    o, lse = twice("gta one-stream", lambda: gha_lib.gta_shared_score_prefill(q, k, v, causal=causal,
+                                                                              out_dtype=torch.float32,
+                                                                              return_lse=True))
+    o16 = twice("gta one-stream bf16", lambda: gha_lib.gta_shared_score_prefill(q, k, v, causal=causal))
+    ref, ref_lse = oracle.gta_prefill(widen(qb), widen(kb), widen(vb), causal=causal)
+    check("gta one-stream fp32", o.cpu().numpy(), ref)
+    check("gta one-stream bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
+    check("gta one-stream lse", lse.cpu().numpy(), ref_lse)
+
+
 def test_gta_not_causal(gha_lib):
     """Every position sees all S keys; S ragged against the 64-key tiles."""
     B, h, n_grp, S, d = 1, 8, 2, 200, 64
