@@ -84,17 +84,21 @@ def _md_trace(rows, command, bench=None):
         lib = [r for r in rows if r["kernel"].lstrip().split("(")[0].split("<")[0].split()[-1].startswith("gha::")]
         t_us = sum(r["avg_us"] for r in lib)
         out += ["", "Roofline from this trace (algorithmic work of the workload from the same run's bench line; "
-                "the path's time per call = the sum of the library kernels' average durations above):", "",
-                "| workload | HIP-event ms per call | trace us per call | algorithmic | rate from trace | of peak |",
-                "|---|---|---|---|---|---|"]
+                "the path's time per call = the sum of the library kernels' average durations above; the bound "
+                "is MFMA when FLOP per byte exceeds the ridge of the two peaks, else HBM):", "",
+                "| workload | HIP-event ms per call | trace us per call | algorithmic | bound | rate from trace | of peak |",
+                "|---|---|---|---|---|---|---|"]
+        ridge = PEAK_BF16_TFLOPS * 1e3 / PEAK_HBM_GBPS  # FLOP per byte
         for name, e in bench.items():
-            if "gbps" in e:
-                work, rate = f"{e['bytes']:.4g} B", e["bytes"] / (t_us * 1e3)
-                frac, unit = rate / PEAK_HBM_GBPS, "GB/s"
+            nbytes, flops = e.get("bytes"), e.get("flops")
+            work = " + ".join(x for x in (f"{nbytes:.4g} B" if nbytes else "", f"{flops:.4g} FLOP" if flops else "") if x)
+            if nbytes and not (flops and flops / nbytes > ridge):
+                rate = nbytes / (t_us * 1e3)
+                bound, frac, unit = "HBM", rate / PEAK_HBM_GBPS, "GB/s"
             else:
-                work, rate = f"{e['flops']:.4g} FLOP", e["flops"] / (t_us * 1e6)
-                frac, unit = rate / PEAK_BF16_TFLOPS, "TFLOP/s"
-            out.append(f"| {name} | {e['ms']:.4f} | {t_us:.1f} | {work} | {rate:.1f} {unit} | {frac:.3f} |")
+                rate = (flops or 0.0) / (t_us * 1e6)
+                bound, frac, unit = "MFMA", rate / PEAK_BF16_TFLOPS, "TFLOP/s"
+            out.append(f"| {name} | {e['ms']:.4f} | {t_us:.1f} | {work} | {bound} | {rate:.1f} {unit} | {frac:.3f} |")
     return "\n".join(out) + "\n"
 
 
