@@ -12,9 +12,10 @@ Entry points (same names as the C ABI):
   gqa_prefill, gqa_decode, gqa_decode_paged, gqa_decode_fp8,
   gta_shared_score_prefill, gta_shared_score_decode, gqla_gqa_decode,
   gqla_gqa_prefill, latent_absorb_decode, gqla_absorb_decode, and the
-  *_workspace_bytes queries of the decode calls.  Every wrapper checks, before
-  the library is called, that all tensors sit on the query's GPU and carry
-  the dtypes the call expects.
+  *_workspace_bytes queries of the decode calls; set_debug_checks and
+  debug_checks switch the device-side check of the decode lengths.  Every
+  wrapper checks, before the library is called, that all tensors sit on the
+  query's GPU and carry the dtypes the call expects.
 """
 from __future__ import annotations
 
@@ -28,6 +29,7 @@ __all__ = [
     "gqa_decode_noalloc", "gqa_decode_noalloc_scratch_bytes",
     "gqa_decode_workspace_bytes", "gqa_decode_paged_workspace_bytes", "gta_shared_score_decode_workspace_bytes",
     "gqla_gqa_decode_workspace_bytes", "latent_absorb_decode_workspace_bytes",
+    "set_debug_checks", "debug_checks",
     "GhaError", "library_path", "load_library", "GHA_F32", "GHA_BF16",
 ]
 
@@ -36,7 +38,8 @@ _LIB_PATH = os.path.join(_HERE, "libgha.so")
 
 GHA_F32, GHA_BF16 = 0, 1
 STATUS = ["GHA_OK", "GHA_ERR_NULL", "GHA_ERR_SHAPE", "GHA_ERR_GROUPING", "GHA_ERR_STRIDE",
-          "GHA_ERR_ALIGN", "GHA_ERR_DTYPE", "GHA_ERR_HEAD_DIM", "GHA_ERR_WORKSPACE", "GHA_ERR_HIP"]
+          "GHA_ERR_ALIGN", "GHA_ERR_DTYPE", "GHA_ERR_HEAD_DIM", "GHA_ERR_WORKSPACE", "GHA_ERR_HIP",
+          "GHA_ERR_PRECONDITION"]
 
 
 class GhaError(RuntimeError):
@@ -111,8 +114,25 @@ def load_library():
     lib.gha_last_error.restype = ctypes.c_char_p
     lib.gha_version.argtypes = []
     lib.gha_version.restype = I
+    lib.gha_set_debug_checks.argtypes = [I]
+    lib.gha_set_debug_checks.restype = None
+    lib.gha_debug_checks.argtypes = []
+    lib.gha_debug_checks.restype = I
     _lib = lib
     return lib
+
+
+def set_debug_checks(on: bool) -> None:
+    """Switch the device-side check s_q <= seqlens_k[b] <= L_cap of every
+    decode call on or off, for the whole process (gha_set_debug_checks).
+    With it on, a decode call waits for the check and raises GhaError
+    (GHA_ERR_PRECONDITION) before anything else runs on a bad length."""
+    load_library().gha_set_debug_checks(1 if on else 0)
+
+
+def debug_checks() -> bool:
+    """Whether the device-side length checks are on (gha_debug_checks)."""
+    return bool(load_library().gha_debug_checks())
 
 
 def _check(status: int):

@@ -4,9 +4,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/gha.h"
@@ -26,11 +28,33 @@ gha_status fail(gha_status s, const char* fmt, ...) {
 
 int elem_size(gha_dtype t) { return t == GHA_F32 ? 4 : t == GHA_FP8_E4M3 ? 1 : 2; }
 
+// Upper limits on sizes.  Within them every size, grid and workspace formula
+// in this file stays inside 64-bit arithmetic and every row count (heads per
+// group times new tokens) inside 32-bit; larger arguments are refused
+// (GHA_ERR_SHAPE, and 0 from the workspace queries).
+constexpr int kMaxBatch = 1 << 20;
+constexpr int kMaxHeads = 1 << 12;
+constexpr int kMaxNewTokens = 1 << 16;
+constexpr int kMaxLen = 1 << 30;
+bool within_limits(int B, int heads_a, int heads_b, int s_q, int len_a, int len_b) {
+  return B <= kMaxBatch && heads_a <= kMaxHeads && heads_b <= kMaxHeads && s_q <= kMaxNewTokens &&
+         len_a <= kMaxLen && len_b <= kMaxLen;
+}
+gha_status limits_fail() {
+  return fail(GHA_ERR_SHAPE, "a size exceeds the library's limits (B <= %d, heads <= %d, s_q <= %d, lengths <= %d)",
+              kMaxBatch, kMaxHeads, kMaxNewTokens, kMaxLen);
+}
+
 // A view must be present, non-negative and keep every row 16-byte aligned.
+// Strides above 2^48 elements cannot address real memory and are refused,
+// which also keeps the offset arithmetic of the launches within 64 bits.
+constexpr int64_t kMaxStride = (int64_t)1 << 48;
 gha_status check_view(const char* name, const gha_tensor* t, gha_dtype dt, bool use_sb,
                       bool use_sh, bool use_ss) {
   if (t == nullptr || t->ptr == nullptr) return fail(GHA_ERR_NULL, "%s: null tensor or pointer", name);
   if (t->sb < 0 || t->sh < 0 || t->ss < 0) return fail(GHA_ERR_STRIDE, "%s: negative stride", name);
+  if (t->sb > kMaxStride || t->sh > kMaxStride || t->ss > kMaxStride)
+    return fail(GHA_ERR_STRIDE, "%s: a stride exceeds 2^48 elements", name);
   const int64_t es = elem_size(dt);
   if ((reinterpret_cast<uintptr_t>(t->ptr) & 15u) != 0)
     return fail(GHA_ERR_ALIGN, "%s: pointer not 16-byte aligned", name);
@@ -43,6 +67,42 @@ gha_status check_device() {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(GHA_ERR_HIP, "no HIP device: %s", hipGetErrorString(e));
+  return GHA_OK;
+}
+
+// Debug checks: -1 until first asked for, then 0 or 1 (gha_set_debug_checks,
+// else the environment variable GHA_DEBUG_CHECKS).
+std::atomic<int> g_debug_checks{-1};
+
+bool debug_checks_on() {
+  int v = g_debug_checks.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* env = std::getenv("GHA_DEBUG_CHECKS");
+    int expected = -1;
+    g_debug_checks.compare_exchange_strong(expected, (env != nullptr && std::atoi(env) != 0) ? 1 : 0);
+    v = g_debug_checks.load();
+  }
+  return v != 0;
+}
+
+// With debug checks on: has the device test s_q <= seqlens_k[b] <= L_cap for
+// every b, answering in the first 8 bytes of `scratch` (the call's
+// workspace, 16-byte aligned and larger than that), waits for the answer and
+// refuses the call if a length is out of range.  Nothing else has been
+// launched by then.
+gha_status check_lengths_on_device(const int32_t* seqlens, int B, int s_q, int L_cap, void* scratch,
+                                   void* stream, const char* what) {
+  if (!debug_checks_on()) return GHA_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int32_t* answer = reinterpret_cast<int32_t*>(scratch);
+  int32_t h[2] = {-1, 0};
+  hipError_t e = gha::launch_check_lengths(seqlens, B, s_q, L_cap, answer, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(h, answer, sizeof(h), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(GHA_ERR_HIP, "%s: debug length check failed: %s", what, hipGetErrorString(e));
+  if (h[0] >= 0)
+    return fail(GHA_ERR_PRECONDITION, "%s: seqlens_k[%d] = %d is outside [s_q, L_cap] = [%d, %d]", what, h[0],
+                h[1], s_q, L_cap);
   return GHA_OK;
 }
 
@@ -99,7 +159,7 @@ void stream_decode_carve(gha::StreamDecodeArgs& a, void* workspace, int dv) {
   a.ws_pref = reinterpret_cast<int32_t*>(a.ws_lse + n);
 }
 // one (batch, head) sequence of a cache read through 32-bit buffer offsets
-bool span_ok(int L_cap, int64_t ss) { return ((int64_t)L_cap + 64) * ss * 2 < ((int64_t)1 << 31); }
+bool span_ok(int L_cap, int64_t ss) { return gha::span_below((int64_t)L_cap + 64, ss, 2, (int64_t)1 << 31); }
 int latent_row_blocks(int h_q, int s_q) {
   const int r = gha::latent_rows_per_wg();
   return (h_q * s_q + r - 1) / r;
@@ -157,11 +217,16 @@ const char* gha_status_string(gha_status s) {
     case GHA_ERR_HEAD_DIM: return "GHA_ERR_HEAD_DIM";
     case GHA_ERR_WORKSPACE: return "GHA_ERR_WORKSPACE";
     case GHA_ERR_HIP: return "GHA_ERR_HIP";
+    case GHA_ERR_PRECONDITION: return "GHA_ERR_PRECONDITION";
   }
   return "GHA_ERR_UNKNOWN";
 }
 
 const char* gha_last_error(void) { return g_err; }
+
+void gha_set_debug_checks(int on) { g_debug_checks.store(on != 0 ? 1 : 0); }
+
+int gha_debug_checks(void) { return debug_checks_on() ? 1 : 0; }
 
 int gha_version(void) { return 100; }  // 0.1.0
 
@@ -171,6 +236,7 @@ gha_status gqa_prefill(const gha_tensor* q, const gha_tensor* k, const gha_tenso
                        int causal, void* stream) {
   if (B < 1 || h_q < 1 || h_kv < 1 || S_q < 1 || S_k < 1)
     return fail(GHA_ERR_SHAPE, "sizes must be positive (B=%d h_q=%d h_kv=%d S_q=%d S_k=%d)", B, h_q, h_kv, S_q, S_k);
+  if (!within_limits(B, h_q, h_kv, 1, S_q, S_k)) return limits_fail();
   if (h_q % h_kv) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
   if (causal && S_q > S_k) return fail(GHA_ERR_SHAPE, "causal needs S_q <= S_k (got %d > %d)", S_q, S_k);
   if (d != 64 && d != 128) return fail(GHA_ERR_HEAD_DIM, "head dim %d not in {64, 128}", d);
@@ -218,6 +284,7 @@ gha_status gqla_gqa_prefill(const gha_tensor* q_c, const gha_tensor* q_r, const 
                             void* stream) {
   if (B < 1 || h_q < 1 || g < 1 || S_q < 1 || S_k < 1)
     return fail(GHA_ERR_SHAPE, "sizes must be positive (B=%d h_q=%d g=%d S_q=%d S_k=%d)", B, h_q, g, S_q, S_k);
+  if (!within_limits(B, h_q, g, 1, S_q, S_k)) return limits_fail();
   if (h_q % g) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of g=%d", h_q, g);
   if (causal && S_q > S_k) return fail(GHA_ERR_SHAPE, "causal needs S_q <= S_k (got %d > %d)", S_q, S_k);
   if (d_h != 128 || d_r != 64) return fail(GHA_ERR_HEAD_DIM, "need d_h == 128 and d_r == 64 (got %d, %d)", d_h, d_r);
@@ -281,7 +348,8 @@ size_t gqa_decode_register_ws(int B, int h_q, int h_kv, int s_q, int L_max_hint,
   return rows * (size_t)d * 4 + rows * 4;
 }
 bool gqa_decode_sizes_ok(int B, int h_q, int h_kv, int s_q, int L_max_hint, int d) {
-  return B >= 1 && h_q >= 1 && h_kv >= 1 && s_q >= 1 && L_max_hint >= 1 && d >= 1 && h_q % h_kv == 0;
+  return B >= 1 && h_q >= 1 && h_kv >= 1 && s_q >= 1 && L_max_hint >= 1 && (d == 64 || d == 128) &&
+         h_q % h_kv == 0 && within_limits(B, h_q, h_kv, s_q, L_max_hint, 1);
 }
 }  // namespace
 
@@ -314,6 +382,7 @@ gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_
                       void* stream) {
   if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
     return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (!within_limits(B, h_q, h_kv, s_q, L_cap, L_max_hint)) return limits_fail();
   if (h_q % h_kv) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
   if (L_max_hint > L_cap || s_q > L_max_hint)
     return fail(GHA_ERR_SHAPE, "need s_q <= L_max_hint <= L_cap (s_q=%d L_max_hint=%d L_cap=%d)", s_q, L_max_hint, L_cap);
@@ -334,6 +403,7 @@ gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
     return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
   if ((s = check_device()) != GHA_OK) return s;
+  if ((s = check_lengths_on_device(seqlens_k, B, s_q, L_cap, workspace, stream, "gqa_decode")) != GHA_OK) return s;
 
   const int rows = (h_q / h_kv) * s_q;
   if (gqa_decode_streams(k_cache, v_cache, h_q, h_kv, s_q, L_cap, d)) {
@@ -380,14 +450,16 @@ gha_status gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, const gha_
 
 // Keys a windowed sequence can touch, for the streaming plan: the window,
 // the new tokens and up to two chunks of alignment.
-int window_keys(int L_max_hint, int s_q, int window) {
+static int window_keys(int L_max_hint, int s_q, int window) {
   if (window <= 0) return L_max_hint;
   const int64_t k = (int64_t)window + s_q + 2 * gha::stream_decode_chunk();
   return (int)std::min<int64_t>(L_max_hint, k);
 }
 
 size_t gqa_decode_paged_workspace_bytes(int B, int h_q, int h_kv, int s_q, int L_max_hint, int window, int d) {
-  if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_max_hint < 1 || window < 0 || h_q % h_kv || d < 1) return 0;
+  if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_max_hint < 1 || window < 0 || h_q % h_kv || (d != 64 && d != 128))
+    return 0;
+  if (!within_limits(B, h_q, h_kv, s_q, L_max_hint, window)) return 0;
   if ((h_q / h_kv) * s_q > 32) return 0;
   // enough for either cache type (the 8-bit plan has more work-groups)
   return stream_decode_ws(B, h_kv, 1, (h_q / h_kv) * s_q, window_keys(L_max_hint, s_q, window), d, GHA_SD_WGS_8BIT);
@@ -407,6 +479,7 @@ gha_status stream_gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, con
                              void* stream, const char* name) {
   if (B < 1 || h_q < 1 || h_kv < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
     return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (!within_limits(B, h_q, h_kv, s_q, L_cap, L_max_hint)) return limits_fail();
   if (h_q % h_kv) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
   if (L_max_hint > L_cap || s_q > L_max_hint)
     return fail(GHA_ERR_SHAPE, "need s_q <= L_max_hint <= L_cap (s_q=%d L_max_hint=%d L_cap=%d)", s_q, L_max_hint, L_cap);
@@ -432,7 +505,7 @@ gha_status stream_gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, con
   if (k_cache->ss < d || v_cache->ss < d) return fail(GHA_ERR_STRIDE, "cache rows overlap (token stride < d)");
   const int span_rows = paged ? page_size : L_cap;
   const int64_t eb = elem_size(cache_dtype);
-  if (((int64_t)span_rows + 64) * std::max(k_cache->ss, v_cache->ss) * eb >= ((int64_t)1 << 31))
+  if (!gha::span_below((int64_t)span_rows + 64, std::max(k_cache->ss, v_cache->ss), eb, (int64_t)1 << 31))
     return fail(GHA_ERR_STRIDE, "one %s spans 2 GiB or more", paged ? "page" : "sequence");
   const int rows = (h_q / h_kv) * s_q;
   const int L_plan = window_keys(L_max_hint, s_q, window);
@@ -445,6 +518,7 @@ gha_status stream_gqa_decode(const gha_tensor* q, const gha_tensor* k_cache, con
   if ((int64_t)B * ((L_cap + 127) / 128) >= (1LL << 31))
     return fail(GHA_ERR_SHAPE, "problem too large for one launch");
   if ((s = check_device()) != GHA_OK) return s;
+  if ((s = check_lengths_on_device(seqlens_k, B, s_q, L_cap, workspace, stream, name)) != GHA_OK) return s;
 
   gha::StreamDecodeArgs sa{};
   sa.q = q->ptr; sa.q_sb = q->sb; sa.q_sh = q->sh; sa.q_ss = q->ss;
@@ -500,6 +574,7 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
                                     int d_qk, int d_v, gha_dtype in_dtype, gha_dtype out_dtype,
                                     float scale, int causal, void* stream) {
   if (B < 1 || h < 1 || n_grp < 1 || S < 1) return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (!within_limits(B, h, n_grp, 1, S, 1)) return limits_fail();
   if (h % n_grp) return fail(GHA_ERR_GROUPING, "h=%d is not a multiple of n_grp=%d", h, n_grp);
   const int per = h / n_grp;
   if ((d_qk != 64 && d_qk != 128) || !gta_dv_ok(d_v))
@@ -564,6 +639,7 @@ gha_status gta_shared_score_prefill(const gha_tensor* q, const gha_tensor* k, co
 
 size_t gta_shared_score_decode_workspace_bytes(int B, int h, int n_grp, int s_q, int L_max_hint, int d_v) {
   if (B < 1 || h < 1 || n_grp < 1 || s_q < 1 || s_q > 32 || L_max_hint < 1 || !gta_dv_ok(d_v) || h % n_grp) return 0;
+  if (!within_limits(B, h, n_grp, s_q, L_max_hint, 1)) return 0;
   // the launches over a group's value sources run one after another on the
   // stream and reuse one launch's workspace
   const GtaSources src = gta_decode_sources(h / n_grp, d_v, s_q);
@@ -577,6 +653,7 @@ gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cach
                                    size_t workspace_bytes, void* stream) {
   if (B < 1 || h < 1 || n_grp < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
     return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (!within_limits(B, h, n_grp, s_q, L_cap, L_max_hint)) return limits_fail();
   if (h % n_grp) return fail(GHA_ERR_GROUPING, "h=%d is not a multiple of n_grp=%d", h, n_grp);
   const int per = h / n_grp;
   if (L_max_hint > L_cap || s_q > L_max_hint)
@@ -601,6 +678,7 @@ gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cach
     return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
   if ((s = check_device()) != GHA_OK) return s;
+  if ((s = check_lengths_on_device(seqlens_k, B, s_q, L_cap, workspace, stream, "gta_shared_score_decode")) != GHA_OK) return s;
 
   gha::StreamDecodeArgs a{};
   a.q = q->ptr; a.q_sb = q->sb; a.q_sh = q->sh; a.q_ss = q->ss;
@@ -636,7 +714,8 @@ gha_status gta_shared_score_decode(const gha_tensor* q, const gha_tensor* k_cach
 }
 
 size_t gqla_gqa_decode_workspace_bytes(int B, int h_q, int g, int s_q, int L_max_hint, int d_h) {
-  if (B < 1 || h_q < 1 || g < 1 || s_q < 1 || L_max_hint < 1 || d_h < 1 || h_q % g || (h_q / g) * s_q > 32) return 0;
+  if (B < 1 || h_q < 1 || g < 1 || s_q < 1 || L_max_hint < 1 || d_h != 128 || h_q % g) return 0;
+  if (!within_limits(B, h_q, g, s_q, L_max_hint, 1) || (h_q / g) * s_q > 32) return 0;
   return stream_decode_ws(B, g, g, (h_q / g) * s_q, L_max_hint, d_h);
 }
 
@@ -647,6 +726,7 @@ gha_status gqla_gqa_decode(const gha_tensor* q_c, const gha_tensor* q_r, const g
                            float scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 1 || h_q < 1 || g < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
     return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (!within_limits(B, h_q, g, s_q, L_cap, L_max_hint)) return limits_fail();
   if (h_q % g) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of g=%d", h_q, g);
   if (L_max_hint > L_cap || s_q > L_max_hint)
     return fail(GHA_ERR_SHAPE, "need s_q <= L_max_hint <= L_cap (s_q=%d L_max_hint=%d L_cap=%d)", s_q, L_max_hint, L_cap);
@@ -674,6 +754,7 @@ gha_status gqla_gqa_decode(const gha_tensor* q_c, const gha_tensor* q_r, const g
     return fail(GHA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
   if ((s = check_device()) != GHA_OK) return s;
+  if ((s = check_lengths_on_device(seqlens_k, B, s_q, L_cap, workspace, stream, "gqla_gqa_decode")) != GHA_OK) return s;
 
   gha::StreamDecodeArgs a{};
   a.q = q_c->ptr; a.q_sb = q_c->sb; a.q_sh = q_c->sh; a.q_ss = q_c->ss;
@@ -697,7 +778,8 @@ gha_status gqla_gqa_decode(const gha_tensor* q_c, const gha_tensor* q_r, const g
 }
 
 size_t latent_absorb_decode_workspace_bytes(int B, int h_q, int s_q, int L_max_hint, int r_kv) {
-  if (B < 1 || h_q < 1 || s_q < 1 || L_max_hint < 1 || r_kv < 1) return 0;
+  if (B < 1 || h_q < 1 || s_q < 1 || L_max_hint < 1 || r_kv != 512) return 0;
+  if (!within_limits(B, h_q, 1, s_q, L_max_hint, 1)) return 0;
   const int n_rb = latent_row_blocks(h_q, s_q);
   const int T = gha::latent_tile_tokens();
   const int n_wg = gha::latent_plan_wgs(n_rb, (int64_t)B * ((L_max_hint + T - 1) / T));
@@ -717,6 +799,7 @@ gha_status latent_absorb_decode_check(const gha_tensor* q_lat, const gha_tensor*
                                       void* workspace, size_t workspace_bytes) {
   if (B < 1 || h_q < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
     return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (!within_limits(B, h_q, 1, s_q, L_cap, L_max_hint)) return limits_fail();
   if (L_max_hint > L_cap || s_q > L_max_hint)
     return fail(GHA_ERR_SHAPE, "need s_q <= L_max_hint <= L_cap (s_q=%d L_max_hint=%d L_cap=%d)", s_q, L_max_hint, L_cap);
   if (r_kv != 512 || d_r != 64) return fail(GHA_ERR_HEAD_DIM, "need r_kv == 512 and d_r == 64 (got %d, %d)", r_kv, d_r);
@@ -735,7 +818,7 @@ gha_status latent_absorb_decode_check(const gha_tensor* q_lat, const gha_tensor*
   // span less than 2^31 bytes
   if (c_kv->ss < r_kv || k_rope->ss < d_r)
     return fail(GHA_ERR_STRIDE, "cache rows overlap (c_kv ss=%lld, k_rope ss=%lld)", (long long)c_kv->ss, (long long)k_rope->ss);
-  if ((int64_t)(L_cap + gha::latent_tile_tokens()) * std::max(c_kv->ss, k_rope->ss) * 2 >= (1LL << 31))
+  if (!gha::span_below((int64_t)L_cap + gha::latent_tile_tokens(), std::max(c_kv->ss, k_rope->ss), 2, 1LL << 31))
     return fail(GHA_ERR_SHAPE, "one sequence of the cache spans 2 GiB or more (L_cap=%d)", L_cap);
   const size_t need = latent_absorb_decode_workspace_bytes(B, h_q, s_q, L_max_hint, r_kv);
   if (workspace == nullptr || workspace_bytes < need)
@@ -763,6 +846,7 @@ gha_status latent_absorb_decode(const gha_tensor* q_lat, const gha_tensor* q_rop
                                             workspace_bytes);
   if (s != GHA_OK) return s;
   if ((s = check_device()) != GHA_OK) return s;
+  if ((s = check_lengths_on_device(seqlens_k, B, s_q, L_cap, workspace, stream, "latent_absorb_decode")) != GHA_OK) return s;
 
   gha::LatentArgs a{};
   a.q = q_lat->ptr; a.q_sb = q_lat->sb; a.q_sh = q_lat->sh; a.q_ss = q_lat->ss;
@@ -804,6 +888,7 @@ gha_status gqla_absorb_decode(const gha_tensor* q_c, const gha_tensor* q_rope, c
                               size_t workspace_bytes, void* stream) {
   if (B < 1 || h_q < 1 || g < 1 || s_q < 1 || L_cap < 1 || L_max_hint < 1)
     return fail(GHA_ERR_SHAPE, "sizes must be positive");
+  if (!within_limits(B, h_q, g, s_q, L_cap, L_max_hint)) return limits_fail();
   if (h_q % g) return fail(GHA_ERR_GROUPING, "h_q=%d is not a multiple of g=%d", h_q, g);
   if (d_h != 128 || r_kv != 512 || d_r != 64)
     return fail(GHA_ERR_HEAD_DIM, "need d_h == 128, r_kv == 512 and d_r == 64 (got %d, %d, %d)", d_h, r_kv, d_r);
@@ -837,6 +922,7 @@ gha_status gqla_absorb_decode(const gha_tensor* q_c, const gha_tensor* q_rope, c
                                       L_max_hint, r_kv, d_r, in_dtype, GHA_BF16, scale, base, lat_ws)) != GHA_OK)
     return s;
   if ((s = check_device()) != GHA_OK) return s;
+  if ((s = check_lengths_on_device(seqlens_k, B, s_q, L_cap, base, stream, "gqla_absorb_decode")) != GHA_OK) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   gha::AbsorbArgs ab{};
   ab.in = q_c->ptr; ab.in_sb = q_c->sb; ab.in_sh = q_c->sh; ab.in_ss = q_c->ss;

@@ -485,9 +485,8 @@ bool gta_layout_supported(const PrefillArgs& a, int d_qk, int d_v) {
   // one (batch, group) K or (batch, head) V sequence must span less than 2^31
   // bytes (32-bit buffer offsets and range) and rows must not overlap, so that
   // the range check cuts exactly at the last position
-  const int64_t span_k = ((int64_t)a.S_q + 2 * KB) * a.k_ss * 2;
-  const int64_t span_v = ((int64_t)a.S_q + 2 * KB) * a.v_ss * 2;
-  return a.k_ss >= d_qk && a.v_ss >= d_v && span_k < ((int64_t)1 << 31) && span_v < ((int64_t)1 << 31);
+  return a.k_ss >= d_qk && a.v_ss >= d_v && span_below((int64_t)a.S_q + 2 * KB, a.k_ss, 2, (int64_t)1 << 31) &&
+         span_below((int64_t)a.S_q + 2 * KB, a.v_ss, 2, (int64_t)1 << 31);
 }
 
 hipError_t launch_gta(const PrefillArgs& a, int d_qk, int sources, bool out_f32, hipStream_t st) {

@@ -81,28 +81,15 @@ __global__ __launch_bounds__(64 * NW, 2) void gta_fused_kernel(PrefillArgs a) {
   const int li = lane & 15, lg = lane >> 4;
 
   // ---- which positions of which group --------------------------------------
-  // Causal q-block qb walks 2 qb + 2 key tiles.  When the grid is exactly two
-  // work-groups per CU, the dispatcher places work-group b and b + n_cus on
-  // one CU (and b on XCD b % 8): the (batch, group) units are spread over the
-  // XCDs (unit u on XCD u % 8, so a unit's K/V meets in one L2) and, inside
-  // an XCD, the first slots take its blocks heaviest first and the second
-  // slots lightest first, so that each CU carries the same work.  Otherwise
-  // the blocks go heaviest first over the whole grid, and the dispatcher's
-  // later rounds fill in behind them.
+  // Causal q-block qb walks 2 qb + 2 key tiles.  The blocks go heaviest first
+  // over the whole grid (every unit's last q-block, then the one before, ...),
+  // so that the dispatcher's later rounds fill in behind the heavy ones.
   const int b_id = blockIdx.x;
   if (b_id >= a.n_blocks) return;
   const int n_qb = a.n_qblocks;
   const int n_units = a.n_blocks / n_qb;
-  int unit, qb;
-  if (a.wg_order == 1) {
-    const int x = b_id & 7, j = b_id >> 3, cx = a.n_cus >> 3, ux = n_units >> 3;
-    const int rho = j < cx ? j : 3 * cx - 1 - j;  // rank within the XCD, heaviest first
-    qb = n_qb - 1 - rho / ux;
-    unit = x + 8 * (rho % ux);
-  } else {
-    qb = n_qb - 1 - b_id / n_units;
-    unit = b_id % n_units;
-  }
+  int qb = n_qb - 1 - b_id / n_units;
+  int unit = b_id % n_units;
   qb = __builtin_amdgcn_readfirstlane(qb);
   unit = __builtin_amdgcn_readfirstlane(unit);
   const int grp = __builtin_amdgcn_readfirstlane(unit % a.h_kv);
@@ -376,21 +363,11 @@ __global__ __launch_bounds__(64 * NW, 2) void gta_fused_kernel(PrefillArgs a) {
 
 template <int DQK, int NV>
 hipError_t launch_nv(const PrefillArgs& args, bool out_f32, hipStream_t st) {
-  using Ly = GfLayout<DQK, NV>;
-  PrefillArgs a = args;
-  // complementary pairs need exactly two resident work-groups per CU, whole
-  // units per XCD and whole CU pairs per XCD
-  const int cus = device_cus();
-  const int n_units = a.n_blocks / a.n_qblocks;
-  a.n_cus = cus;
-  a.wg_order = (a.causal && cus > 0 && cus % 8 == 0 && a.n_blocks == 2 * cus && n_units % 8 == 0 &&
-                2 * Ly::BYTES <= 160 * 1024)
-                   ? 1 : 0;
-  const uint32_t padded = (uint32_t)((a.n_blocks + 7) / 8 * 8);
+  const uint32_t grid = (uint32_t)args.n_blocks;
   if (out_f32)
-    hipLaunchKernelGGL((gta_fused_kernel<DQK, NV, true>), dim3(padded), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((gta_fused_kernel<DQK, NV, true>), dim3(grid), dim3(64 * NW), 0, st, args);
   else
-    hipLaunchKernelGGL((gta_fused_kernel<DQK, NV, false>), dim3(padded), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((gta_fused_kernel<DQK, NV, false>), dim3(grid), dim3(64 * NW), 0, st, args);
   return hipGetLastError();
 }
 

@@ -8,6 +8,13 @@
 
 namespace gha {
 
+// rows * stride * elem_bytes < limit for non-negative operands, with no
+// intermediate overflow (a product that overflows is not below any limit)
+inline bool span_below(int64_t rows, int64_t stride, int64_t elem_bytes, int64_t limit) {
+  int64_t p = 0;
+  return !__builtin_mul_overflow(rows, stride, &p) && !__builtin_mul_overflow(p, elem_bytes, &p) && p < limit;
+}
+
 struct PrefillArgs {
   const void* q; int64_t q_sb, q_sh, q_ss;
   const void* k; int64_t k_sb, k_sh, k_ss;
@@ -33,10 +40,6 @@ struct PrefillArgs {
   // the kernel's value source s of group j is columns 64 (s % v_sph) .. + 63
   // of head j v_hpg + s / v_sph
   int v_hpg, v_sph;
-  // GTA one-stream kernel: 1 when the grid is exactly two work-groups per CU
-  // (n_cus CUs); then work-group b shares its CU with b + n_cus and the pair
-  // takes complementary causal blocks.  0: heaviest blocks first.
-  int wg_order, n_cus;
   const void* q2; int64_t q2_sb, q2_sh, q2_ss;
   const void* k2; int64_t k2_sb, k2_sh, k2_ss;
 };
@@ -138,6 +141,9 @@ int prefill_bf16_waves(const PrefillArgs& a, int d);  // waves per work-group of
 int device_cus();
 // sets the detail string gha_last_error() returns (defined in abi.cpp)
 void set_last_error(const char* msg);
+// debug checks: tests lo <= seqlens[b] <= hi for b < B on the device and
+// writes out[0] = the first failing b (-1 if none) and out[1] = its length
+hipError_t launch_check_lengths(const int32_t* seqlens, int B, int lo, int hi, int32_t* out, hipStream_t st);
 // the workspace gqa_decode needs for these cache views (defined in abi.cpp)
 size_t gqa_decode_path_workspace(const gha_tensor* k_cache, const gha_tensor* v_cache, int B, int h_q, int h_kv,
                                  int s_q, int L_cap, int L_max_hint, int d);

@@ -426,8 +426,8 @@ bool prefill_d128_supported(const PrefillArgs& a) {
   // that the range check cuts exactly at the last key
   int64_t ss = a.k_ss > a.v_ss ? a.k_ss : a.v_ss;
   if (a.dk2 > 0) ss = ss > a.k2_ss ? ss : a.k2_ss;
-  const int64_t span = ((int64_t)a.S_k + 4 * KB) * ss * 2;
-  return a.k_ss >= 128 && a.v_ss >= 128 && (a.dk2 == 0 || a.k2_ss >= a.dk2) && span < ((int64_t)1 << 31);
+  return a.k_ss >= 128 && a.v_ss >= 128 && (a.dk2 == 0 || a.k2_ss >= a.dk2) &&
+         span_below((int64_t)a.S_k + 4 * KB, ss, 2, (int64_t)1 << 31);
 }
 
 int device_cus() {

@@ -1,9 +1,9 @@
 /* gha.h - C ABI of the grouped-head attention library for AMD Instinct MI355X
  * (gfx950).
  *
- * Six operations, all exact causal scaled dot-product attention
- * o = softmax(scale * q k^T) v with fp32 accumulation, differing in which heads
- * share what:
+ * Every operation is exact causal scaled dot-product attention
+ * o = softmax(scale * q k^T) v with fp32 accumulation; they differ in which
+ * heads share what.  Six kinds:
  *
  *   gqa_prefill               grouped-query attention over a whole sequence:
  *                             consecutive groups of h_q/h_kv query heads share
@@ -34,6 +34,13 @@
  *                             k^R (width d_r); the value is the latent itself.
  *                             ("GQLA: Group-Query Latent Attention ...",
  *                             section 1, section 3.1 Eq. (1), Figure 2 right.)
+ *
+ * and their variants, each declared with its own contract below:
+ * gqa_decode_paged (block-table KV cache, optional sliding window),
+ * gqa_decode_fp8 (E4M3 caches with per-tensor scales), gqla_gqa_prefill (the
+ * GQLA expand path over a whole sequence), gqla_absorb_decode (GQLA absorbed
+ * into the latent on the device) and gqa_decode_noalloc (gqa_decode with
+ * library-owned scratch, for callers that cannot allocate).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -84,7 +91,8 @@ typedef enum {
   GHA_ERR_DTYPE = 6,     /* unsupported input/output element types */
   GHA_ERR_HEAD_DIM = 7,  /* unsupported head / latent width */
   GHA_ERR_WORKSPACE = 8, /* workspace missing or too small */
-  GHA_ERR_HIP = 9        /* no usable device, or a launch failed */
+  GHA_ERR_HIP = 9,       /* no usable device, or a launch failed */
+  GHA_ERR_PRECONDITION = 10 /* debug checks: a sequence length outside [s_q, L_cap] */
 } gha_status;
 
 typedef enum { GHA_F32 = 0, GHA_BF16 = 1, GHA_FP8_E4M3 = 2 } gha_dtype;  /* E4M3: caches of gqa_decode_fp8 */
@@ -346,6 +354,33 @@ gha_status gqa_decode_noalloc(const gha_tensor* q, const gha_tensor* k_cache,
 size_t gqa_decode_noalloc_scratch_bytes(void);
 
 /* Status name, thread-local detail of the last error, library version. */
+/* Debug checks of the decode length precondition on the device.
+ *
+ * Every decode entry point relies on s_q <= seqlens_k[b] <= L_cap for each
+ * sequence b: the new tokens are the last s_q cached positions (bottom-right
+ * alignment) and each step reads the whole cached history ("GQLA: Group-Query
+ * Latent Attention ...", section 1).  The lengths live in device memory, so the
+ * host validation cannot see them; without debug checks the kernels clamp a
+ * length to [0, L_cap] and a row with no visible key gets zeros (lse -inf).
+ *
+ * With debug checks on, each decode entry point, after its host validation,
+ * first launches a one-work-group kernel that tests every seqlens_k[b] on the
+ * call's stream, waits for the stream, and returns GHA_ERR_PRECONDITION
+ * (gha_last_error names the first failing b and its length) without
+ * launching anything else when a length is out of range.  The kernel writes
+ * its answer into the first 8 bytes of the call's workspace (for
+ * gqa_decode_noalloc, of its scratch array).  Because the call then waits on
+ * the stream, debug checks are for debugging: not for timing and not under
+ * graph capture.
+ *
+ * gha_set_debug_checks(on) switches them on (non-zero) or off for the whole
+ * process; until it is first called, they are on when the environment
+ * variable GHA_DEBUG_CHECKS holds a non-zero integer.  gha_debug_checks()
+ * returns 1 when they are on, else 0.  Prefill calls have no lengths and are
+ * not affected. */
+void gha_set_debug_checks(int on);
+int gha_debug_checks(void);
+
 const char* gha_status_string(gha_status s);
 const char* gha_last_error(void);
 int gha_version(void);

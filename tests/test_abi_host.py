@@ -5,6 +5,8 @@ argument checks, which fail first."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -41,6 +43,32 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), n
     assert lib.gha_version() >= 100
     assert lib.gha_status_string(3) == b"GHA_ERR_GROUPING"
+
+
+def test_debug_checks_switch(lib):
+    assert lib.gha_status_string(10) == b"GHA_ERR_PRECONDITION"
+    before = lib.gha_debug_checks()
+    try:
+        lib.gha_set_debug_checks(1)
+        assert lib.gha_debug_checks() == 1 and gha.debug_checks()
+        lib.gha_set_debug_checks(0)
+        assert lib.gha_debug_checks() == 0 and not gha.debug_checks()
+        gha.set_debug_checks(True)
+        assert lib.gha_debug_checks() == 1
+    finally:
+        lib.gha_set_debug_checks(before)
+
+
+@pytest.mark.parametrize("env,want", [("1", "True"), ("0", "False"), (None, "False")])
+def test_debug_checks_follow_the_environment_until_set(lib, env, want):
+    e = {k: v for k, v in os.environ.items() if k != "GHA_DEBUG_CHECKS"}
+    if env is not None:
+        e["GHA_DEBUG_CHECKS"] = env
+    code = ("import grouped_head_latent_amd as g; a = g.debug_checks(); g.set_debug_checks(not a); "
+            "print(a, g.debug_checks())")
+    r = subprocess.run([sys.executable, "-c", code], env=e, cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == [want, str(want != "True")]
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
