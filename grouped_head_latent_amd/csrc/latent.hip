@@ -27,8 +27,14 @@
 // k mod 16; its RoPE row (8 chunks) at 128 k in a separate ring with chunk c
 // at position c ^ ((k / 2) mod 8).  One DMA instruction moves one token's
 // 1 KiB latent row (or the RoPE rows of 8 tokens) from contiguous HBM.
-// Score reads (16 tokens, one chunk) and transposing reads (4 tokens x 32 B
-// per 16 lanes, 8 tokens per half-wave) land in distinct banks.
+// The transposing value reads (4 tokens x 32 B per 16 lanes) are free of
+// bank conflicts.  The score reads (16 tokens, one chunk) are not: gfx950's
+// LDS maps rows 1 KiB apart onto its banks so that every 4-bit permutation
+// of k mod 16 leaves them two-way conflicted (an LDS probe of this pattern
+// counts 3.9 conflict cycles per read; the kernel's counters show about two
+// per LDS instruction).  Swizzles that the probe measured conflict-free for
+// both kinds of read (e.g. sw(k) = 2 (k2 + 2 k0 + 4 (k1 ^ k2)) from the bits
+// of k) made this kernel 1-3% slower at s_q = 1 and 2, so this one is kept.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "lds_pipe.hpp"
