@@ -130,6 +130,10 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// a 16-byte global load marked non-temporal (data read once: it need not stay in L2)
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Work-group id remapped so that consecutive logical ids run on the same

@@ -129,11 +129,11 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
   for (int qt = 0; qt < QT; ++qt) {
     const int pos = min(pos0 + qt * 16 + li, a.S_q - 1);
 #pragma unroll
-    for (int s = 0; s < DS1; ++s) qf[qt][s] = ld16(qbase + (int64_t)pos * a.q_ss + 32 * s + 8 * lg);
+    for (int s = 0; s < DS1; ++s) qf[qt][s] = ld16_stream(qbase + (int64_t)pos * a.q_ss + 32 * s + 8 * lg);
     if constexpr (DK2 > 0) {
       const __bf16* q2p = (const __bf16*)a.q2 + (int64_t)b * a.q2_sb + (int64_t)qhead * a.q2_sh + (int64_t)pos * a.q2_ss;
 #pragma unroll
-      for (int s = DS1; s < DS; ++s) qf[qt][s] = ld16(q2p + 32 * (s - DS1) + 8 * lg);
+      for (int s = DS1; s < DS; ++s) qf[qt][s] = ld16_stream(q2p + 32 * (s - DS1) + 8 * lg);
     }
   }
 
@@ -394,26 +394,54 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
   for (int t = t_mask; t < n_kb; ++t) iteration(t, std::true_type{});
 
   // ---- epilogue --------------------------------------------------------------
+  // bf16 rows go out through LDS: this wave's slice of K buffer qt (rows
+  // 16 w .. 16 w + 15, written only by this wave's DMAs, idle after the last
+  // barrier) holds q-tile qt as 16 rows of 256 B, and each 16 lanes then
+  // store one whole row.  The output is never read again, so the stores (like
+  // the query loads) are non-temporal: they stream past L2 instead of
+  // evicting the K/V tiles that other work-groups of the head still read.
+  static_assert(QT <= 2, "q-tile qt is staged in K buffer qt");
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int qpos = pos0 + qt * 16 + li;
     const float l = lacc[qt][0];
-    if (qpos >= a.S_q) continue;
-    const float inv = 1.f / l;
-    if (a.lse != nullptr && lg == 0) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (qpos < a.S_q && a.lse != nullptr && lg == 0) {
       a.lse[((int64_t)b * a.lse_heads + qhead) * a.S_q + qpos] = (m2[qt] + fast_log2(l)) * kLn2;
     }
+    if constexpr (OUT_F32) {
+      if (qpos < a.S_q) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 16 * dt + 4 * lg;
-      const int64_t obase = (int64_t)b * a.o_sb + (int64_t)qhead * a.o_sh + (int64_t)qpos * a.o_ss + d;
-      const f32x4 v = oacc[dt][qt] * inv;
-      if constexpr (OUT_F32) {
-        *reinterpret_cast<f32x4*>((float*)a.o + obase) = v;
-      } else {
-        *reinterpret_cast<u32x2*>((__bf16*)a.o + obase) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        for (int dt = 0; dt < DT; ++dt) {
+          const int64_t obase = (int64_t)b * a.o_sb + (int64_t)qhead * a.o_sh + (int64_t)qpos * a.o_ss + 16 * dt + 4 * lg;
+          *reinterpret_cast<f32x4*>((float*)a.o + obase) = oacc[dt][qt] * inv;
+        }
+      }
+    } else {
+      unsigned char* stage = smem + qt * TILEB + wave * 16 * ROWB + li * ROWB;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 v = oacc[dt][qt] * inv;
+        *reinterpret_cast<u32x2*>(stage + 2 * (16 * dt + 4 * lg)) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
       }
     }
+  }
+  if constexpr (!OUT_F32) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + (lane >> 4);  // row of the q-tile
+        const int qpos = pos0 + qt * 16 + r;
+        const u32x4 v = ld16(smem + qt * TILEB + wave * 16 * ROWB + r * ROWB + 16 * (lane & 15));
+        if (qpos < a.S_q) {
+          const int64_t obase = (int64_t)b * a.o_sb + (int64_t)qhead * a.o_sh + (int64_t)qpos * a.o_ss + 8 * (lane & 15);
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>((__bf16*)a.o + obase));
+        }
+      }
+    }
+    // every staging read has returned before a second pass's DMAs refill the slice
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
   }  // pass
 }
