@@ -396,8 +396,9 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
   // ---- epilogue --------------------------------------------------------------
   // bf16 rows go out through LDS: this wave's slice of K buffer qt (rows
   // 16 w .. 16 w + 15, written only by this wave's DMAs, idle after the last
-  // barrier) holds q-tile qt as 16 rows of 256 B, and each 16 lanes then
-  // store one whole row.  The output is never read again, so the stores (like
+  // barrier) holds q-tile qt as 16 rows of 256 B (16-byte unit u of row r at
+  // u ^ r, so that neither the 8-byte writes nor the row reads conflict in
+  // the banks), and each 16 lanes then store one whole row.  The output is never read again, so the stores (like
   // the query loads) are non-temporal: they stream past L2 instead of
   // evicting the K/V tiles that other work-groups of the head still read.
   static_assert(QT <= 2, "q-tile qt is staged in K buffer qt");
@@ -422,7 +423,8 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const f32x4 v = oacc[dt][qt] * inv;
-        *reinterpret_cast<u32x2*>(stage + 2 * (16 * dt + 4 * lg)) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(stage + 16 * ((2 * dt + (lg >> 1)) ^ li) + 8 * (lg & 1)) =
+            u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
       }
     }
   }
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * i + (lane >> 4);  // row of the q-tile
         const int qpos = pos0 + qt * 16 + r;
-        const u32x4 v = ld16(smem + qt * TILEB + wave * 16 * ROWB + r * ROWB + 16 * (lane & 15));
+        const u32x4 v = ld16(smem + qt * TILEB + wave * 16 * ROWB + r * ROWB + 16 * ((lane & 15) ^ r));
         if (qpos < a.S_q) {
           const int64_t obase = (int64_t)b * a.o_sb + (int64_t)qhead * a.o_sh + (int64_t)qpos * a.o_ss + 8 * (lane & 15);
           __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>((__bf16*)a.o + obase));
