@@ -274,6 +274,35 @@ def test_gqa_decode_full_size(gha_lib, s_q):
         check(f"full decode lse b={b}", lse[b:b + 1], ref_lse)
 
 
+# The streaming decode kernel addresses one (sequence, KV head) cache slice
+# through a buffer with 32-bit offsets: it takes a slice while L_cap + 64
+# token rows span less than 2 GiB; gqa_decode gives longer ones to the
+# register-fed kernel (64-bit addresses).
+LONGEST_STREAMED = (1 << 31) // (2 * 128) - 64 - 1  # 8388543 tokens at d = 128
+
+
+@pytest.mark.parametrize("L", [LONGEST_STREAMED, LONGEST_STREAMED + 1])
+def test_gqa_decode_longest_sequences(gha_lib, L):
+    """One sequence of L = L_cap tokens: the last length the streaming
+    kernel's offsets cover, and the first past them.  The new tokens' visible
+    keys run to the last row of a 2 GiB cache slice; output and lse against
+    the oracle."""
+    B, h_q, h_kv, s_q, d = 1, 4, 1, 2, 128
+    say(f"longest decode L={L}")
+    seqlens = np.array([L], dtype=np.int32)
+    qb, kb, vb = decode_case(B, h_q, h_kv, s_q, L, seqlens, d, 43)
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    sl = torch.from_numpy(seqlens).cuda()
+    o, lse = gha_lib.gqa_decode(q, k, v, sl, out_dtype=torch.float32, return_lse=True)
+    all_finite("longest decode", o)
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    del q, k, v
+    torch.cuda.empty_cache()
+    ref, ref_lse = oracle.gqa_decode(widen(qb), widen(kb), widen(vb), seqlens)
+    check(f"longest decode L={L}", o, ref)
+    check(f"longest decode lse L={L}", lse, ref_lse)
+
+
 # ------------------------------------------------ paged and windowed decode
 
 PAGED_CASES = [
@@ -823,6 +852,38 @@ def test_latent_absorb_decode(gha_lib, B, h_q, s_q, L_cap, seqlens):
     check("latent fp32", o32.cpu().numpy(), ref)
     check("latent bf16", o16.float().cpu().numpy(), ref, bf16_out=True)
     check("latent lse", lse.cpu().numpy(), ref_lse)
+
+
+# The latent kernel reads a sequence's 1152-byte cache rows through a buffer
+# with 32-bit offsets: L_cap + 32 rows must span less than 2 GiB.
+LONGEST_LATENT = (1 << 31) // 1152 - 32  # 1864103 tokens
+
+
+def test_latent_absorb_decode_longest_sequence(gha_lib):
+    """One sequence of the longest cache the latent kernel takes, against the
+    oracle; one token more is refused before anything is launched."""
+    B, h_q, s_q, L = 1, 16, 1, LONGEST_LATENT
+    say(f"longest latent L={L}")
+    seqlens = np.array([L], dtype=np.int32)
+    q_c, q_r, cache, w_uk, w_uv, q_lat = latent_inputs(B, s_q, h_q, L, seqlens, 47, g=1)
+    dcache = bf16_to_torch(cache)
+    scale = 1 / math.sqrt(128 + 64)
+    dq, dr, sl = bf16_to_torch(q_lat), bf16_to_torch(q_r), torch.from_numpy(seqlens).cuda()
+    o32, lse = gha_lib.latent_absorb_decode(dq, dr, dcache[..., :512], dcache[..., 512:], sl, scale=scale,
+                                            out_dtype=torch.float32, return_lse=True)
+    all_finite("longest latent", o32)
+    o32, lse = o32.cpu().numpy(), lse.cpu().numpy()
+    longer = torch.empty((B, L + 1, 576), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gha_lib.GhaError) as e:
+        gha_lib.latent_absorb_decode(dq, dr, longer[..., :512], longer[..., 512:], sl, scale=scale)
+    assert e.value.status == gha_lib.STATUS.index("GHA_ERR_SHAPE")
+    del dcache, longer
+    torch.cuda.empty_cache()
+    c = widen(cache)
+    ref, ref_lse = oracle.latent_absorb_decode(widen(q_lat), widen(q_r), c[..., :512], c[..., 512:], seqlens,
+                                               scale=scale)
+    check("longest latent", o32, ref)
+    check("longest latent lse", lse, ref_lse)
 
 
 @pytest.mark.parametrize("heads", [None, (5, 77, 126)])
