@@ -130,6 +130,31 @@ def test_gqa_prefill_bf16(gha_lib, B, h_q, h_kv, S_q, S_k, d, causal):
     check("lse", lse.cpu().numpy(), ref_lse)
 
 
+# The d = 128 prefill kernel reads a (batch, KV head) key or value slice
+# through a buffer with 32-bit offsets: it takes S_k while S_k + 256 rows span
+# less than 2 GiB; longer ones go to the generic bf16 kernel.
+LONGEST_PREFILL_KEYS = (1 << 31) // (2 * 128) - 256 - 1  # 8388351 keys
+
+
+@pytest.mark.parametrize("S_k", [LONGEST_PREFILL_KEYS, LONGEST_PREFILL_KEYS + 1])
+def test_gqa_prefill_longest_keys(gha_lib, S_k):
+    """16 causal queries (bottom-right) over the longest key slice the d = 128
+    kernel's offsets cover, and one key more (generic kernel); output and lse
+    against the oracle."""
+    B, h_q, h_kv, S_q, d = 1, 4, 1, 16, 128
+    say(f"longest prefill S_k={S_k}")
+    qb, kb, vb = gen((B, h_q, S_q, d), 45, 1), gen((B, h_kv, S_k, d), 45, 2), gen((B, h_kv, S_k, d), 45, 3)
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    o, lse = gha_lib.gqa_prefill(q, k, v, causal=True, out_dtype=torch.float32, return_lse=True)
+    all_finite("longest prefill", o)
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    del q, k, v
+    torch.cuda.empty_cache()
+    ref, ref_lse = oracle.gqa_prefill(widen(qb), widen(kb), widen(vb), causal=True)
+    check(f"longest prefill S_k={S_k}", o, ref)
+    check(f"longest prefill lse S_k={S_k}", lse, ref_lse)
+
+
 def test_gqa_prefill_strided_bshd_layout(gha_lib):
     """(B, S, H, D) memory order passed through the strides."""
     say("bf16 prefill BSHD strides")
