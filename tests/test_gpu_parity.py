@@ -86,15 +86,26 @@ def test_tiny_gqa_fp32_matches_oracle_and_repeated_heads(gha_lib):
     assert torch.equal(o, o_mha)
 
 
-@pytest.mark.parametrize("B,h_q,h_kv,S,d", [(2, 4, 2, 150, 128), (1, 2, 1, 65, 64)])
-def test_fp32_prefill_ragged(gha_lib, B, h_q, h_kv, S, d):
-    say(f"fp32 prefill B={B} h={h_q}/{h_kv} S={S} d={d}")
-    q = synth.normal_f32((B, h_q, S, d), 7, 1)
-    k = synth.normal_f32((B, h_kv, S, d), 7, 2)
-    v = synth.normal_f32((B, h_kv, S, d), 7, 3)
-    o = gha_lib.gqa_prefill(*(torch.from_numpy(x).cuda() for x in (q, k, v)))
-    ref, _ = oracle.gqa_prefill(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64))
-    assert np.abs(o.cpu().numpy() - ref).max() <= 1e-5
+@pytest.mark.parametrize("B,h_q,h_kv,S_q,S_k,d,causal", [
+    (2, 4, 2, 150, 150, 128, True),   # ragged: 10 q-tiles, the last of 6 rows
+    (1, 2, 1, 65, 65, 64, True),
+    (1, 8, 2, 20, 173, 64, True),     # chunked prefill: bottom-right causal
+    (2, 3, 3, 40, 33, 128, False),    # MHA, no mask, a key tile of one key
+    (1, 4, 1, 1, 1, 64, True),        # one token
+])
+def test_fp32_prefill_ragged(gha_lib, B, h_q, h_kv, S_q, S_k, d, causal):
+    say(f"fp32 prefill B={B} h={h_q}/{h_kv} S_q={S_q} S_k={S_k} d={d} causal={causal}")
+    q = synth.normal_f32((B, h_q, S_q, d), 7, 1)
+    k = synth.normal_f32((B, h_kv, S_k, d), 7, 2)
+    v = synth.normal_f32((B, h_kv, S_k, d), 7, 3)
+    o, lse = twice("fp32 prefill", lambda: gha_lib.gqa_prefill(*(torch.from_numpy(x).cuda() for x in (q, k, v)),
+                                                               causal=causal, return_lse=True))
+    ref, ref_lse = oracle.gqa_prefill(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                      causal=causal)
+    err = np.abs(o.cpu().numpy() - ref).max()
+    say(f"fp32 max_abs={err:.3e}")
+    assert err <= 1e-5
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-5
 
 
 # ------------------------------------------------------------- bf16 prefill
