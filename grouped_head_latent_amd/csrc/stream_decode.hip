@@ -52,8 +52,9 @@ namespace {
 // T keys per tile: 32 (one 16x16x32 value MFMA step) or 16 (one 16x16x16
 // step), whichever lets a wave keep more tiles in flight.  EB is the bytes
 // per cached element: 2 (bf16 tiles feed the MFMAs straight from the ring)
-// or 1 (8-bit tiles land in the ring and are expanded into one bf16 tile per
-// wave before use).
+// or 1 (8-bit tiles land in the ring; their keys are converted to bf16 in
+// registers as the score MFMAs read them, their values expanded into one
+// bf16 stage per wave for the transposing reads).
 template <int DK1, int DK2, int DVW, int NVS, int T, int EB = 2>
 struct SdLayout {
   // the bf16 tile the MFMAs read (swizzled rows)
@@ -64,7 +65,9 @@ struct SdLayout {
   static constexpr int RK1ROW = EB * DK1, RK2ROW = EB * DK2, RVROW = EB * DVW;
   static constexpr int RK1B = T * RK1ROW, RK2B = T * RK2ROW, RVB = T * RVROW;
   static constexpr int SLOT = RK1B + RK2B + NVS * RVB;          // one ring slot
-  static constexpr int STAGE = EB == 2 ? 0 : TILE;              // the expanded tile
+  // 8-bit tiles: the keys feed the score MFMAs straight from the ring
+  // (converted in registers); only the values are expanded into a bf16 stage
+  static constexpr int STAGE = EB == 2 ? 0 : NVS * VB;
   // LDS per work-group: all of a CU's for 16-bit tiles (one work-group per
   // CU); half for 8-bit ones, so that two work-groups share a CU and one's
   // expansion and softmax run beside the other's MFMAs
@@ -120,6 +123,9 @@ __device__ __forceinline__ int scalar_load_i32(const int32_t* p) {
 // unit swizzles (see above)
 __device__ __forceinline__ int key_swz(int row_bytes, int r) { return row_bytes == 128 ? ((r >> 1) & 7) : (r & 15); }
 __device__ __forceinline__ int val_swz(int row_bytes, int r) { return row_bytes == 128 ? 2 * ((r >> 1) & 3) : 2 * (r & 7); }
+// 8-bit key rows (128 or 64 B): 16-byte unit u of row r at u ^ k8_swz; an
+// 8-byte fragment read of 16 rows then covers distinct banks
+__device__ __forceinline__ int k8_swz(int row_bytes, int r) { return row_bytes == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 
 template <int DK1, int DK2, int DVW, int NVS, int T, int QT, int EB>
 __global__ __launch_bounds__((64 * SdLayout<DK1, DK2, DVW, NVS, T, EB>::NW), 1)
@@ -239,12 +245,12 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
         0,
         (int)(lastk * vrow + (uint32_t)Ly::RVROW), kBufferFlags);
   // per-lane offsets of the instructions of one tile (they repeat every tile)
-  // (8-bit tiles are stored unswizzled: they are only read row-major, by the
-  // expansion into the bf16 tile)
+  // (8-bit value tiles are stored unswizzled: they are only read row-major,
+  // by the expansion into the bf16 stage)
   auto lane_ofs = [&](int row_bytes, uint32_t gl_row, int n, bool is_key) -> uint32_t {
     const int upr = row_bytes / 16, rpi = 1024 / row_bytes;
     const int r = n * rpi + lane / upr;  // row in the tile
-    const int sw = EB == 1 ? 0 : is_key ? key_swz(row_bytes, r) : val_swz(row_bytes, r);
+    const int sw = EB == 1 ? (is_key ? k8_swz(row_bytes, r) : 0) : is_key ? key_swz(row_bytes, r) : val_swz(row_bytes, r);
     return (uint32_t)r * gl_row + 16u * (uint32_t)((lane % upr) ^ sw);
   };
   uint32_t k1o[Ly::NK1], k2o[Ly::NK2 > 0 ? Ly::NK2 : 1], vo[Ly::NV];
@@ -342,23 +348,23 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
     issue_tile(i + NSLOT - 1);                       // into the slot of tile i - 1
     wait_vmem_at_most<Ly::NDMA * (NSLOT - 1)>();     // tile i has landed
     const unsigned char* sl = smem + wave * Ly::WAVE + (i % NSLOT) * Ly::SLOT;
-    // expand part `part` (0: keys, 1: values) of the 8-bit tile into this
-    // wave's bf16 tile, row by row in 16-code chunks (exact: every E4M3
-    // value is a bf16 value), into the swizzled layout the MFMA reads expect
+    // expand the values of the 8-bit tile into this wave's bf16 stage, row by
+    // row in 16-code chunks (exact: every E4M3 value is a bf16 value), into
+    // the swizzled layout the transposing reads expect
     unsigned char* st = smem + wave * Ly::WAVE + NSLOT * Ly::SLOT;
     const unsigned char* sl8 = sl;
-    auto expand = [&](int part) __attribute__((always_inline)) {
-      constexpr int CPR = DK1 / 16;  // 16-code chunks per row (keys and values alike)
-      auto cvt_lo = [](uint32_t w) -> uint32_t {  // codes 0, 1 of the word
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-      };
-      auto cvt_hi = [](uint32_t w) -> uint32_t {  // codes 2, 3
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-      };
+    auto cvt_lo = [](uint32_t w) -> uint32_t {  // E4M3 codes 0, 1 of the word as two bf16
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    };
+    auto cvt_hi = [](uint32_t w) -> uint32_t {  // codes 2, 3
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    };
+    auto expand_values = [&]() __attribute__((always_inline)) {
+      constexpr int CPR = DVW / 16;  // 16-code chunks per row
 #pragma unroll
         for (int c0 = 0; c0 < T * CPR; c0 += 64) {
           const int c = c0 + lane, r = c / CPR, u8 = c % CPR;
-          const u32x4 w = ld16(sl8 + part * Ly::RK1B + 16 * c);
+          const u32x4 w = ld16(sl8 + Ly::RK1B + 16 * c);
           // a chunk becomes units 2 u8 (codes 0..7) and 2 u8 + 1 (codes
           // 8..15) of its row; lanes with bit 2 set store their odd unit
           // first, so that the eight lanes of each store that share a
@@ -369,8 +375,8 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
           const uint32_t b0 = e ? w[0] : w[2], b1 = e ? w[1] : w[3];
           const u32x4 first = {cvt_lo(a0), cvt_hi(a0), cvt_lo(a1), cvt_hi(a1)};
           const u32x4 second = {cvt_lo(b0), cvt_hi(b0), cvt_lo(b1), cvt_hi(b1)};
-          const int sw = part == 0 ? key_swz(Ly::K1ROW, r) : val_swz(Ly::VROW, r);
-          unsigned char* row = st + part * Ly::K1B + r * Ly::K1ROW;
+          const int sw = val_swz(Ly::VROW, r);
+          unsigned char* row = st + r * Ly::VROW;
           st16(row + 16 * ((2 * u8 + e) ^ sw), first);
           st16(row + 16 * ((2 * u8 + 1 - e) ^ sw), second);
         }
@@ -379,13 +385,6 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
       // address it cannot relate (another lane's)
       asm volatile("" ::: "memory");
     };
-    // keys now; values once the score MFMAs are issued, so that their
-    // expansion runs while the matrix core works (and its stores do not sit
-    // in the wave's LDS queue ahead of the key reads)
-    if constexpr (EB == 1) {
-      expand(0);
-      sl = st;
-    }
     const int key0 = start + (i * NWAVE + wave) * T;
 
     // S^T = K Q^T: keys key0 + 16 kt + 4 lg + r in sacc[kt][qt][r]
@@ -395,8 +394,18 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
       u32x4 kf[KT];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        if (s < DS1) kf[kt] = ld16(sl + kt * 16 * Ly::K1ROW + (kf1 ^ (64u * s)));
-        else kf[kt] = ld16(sl + Ly::K1B + kt * 16 * Ly::K2ROW + (kf2 ^ (64u * (s - DS1))));
+        if constexpr (EB == 1) {
+          // 8 codes of key row 16 kt + li (dims 32 s + 8 lg ..): unit
+          // 2 s + lg / 2 of the 8-bit row, half lg % 2, converted in registers
+          const int r = 16 * kt + li;
+          const u32x2 w = *reinterpret_cast<const u32x2*>(
+              sl + r * Ly::RK1ROW + 16 * ((2 * s + (lg >> 1)) ^ k8_swz(Ly::RK1ROW, r)) + 8 * (lg & 1));
+          kf[kt] = u32x4{cvt_lo(w[0]), cvt_hi(w[0]), cvt_lo(w[1]), cvt_hi(w[1])};
+        } else if (s < DS1) {
+          kf[kt] = ld16(sl + kt * 16 * Ly::K1ROW + (kf1 ^ (64u * s)));
+        } else {
+          kf[kt] = ld16(sl + Ly::K1B + kt * 16 * Ly::K2ROW + (kf2 ^ (64u * (s - DS1))));
+        }
       }
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
@@ -405,7 +414,7 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
           sacc[kt][qt] = mfma_bf16(kf[kt], qf[qt][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kt][qt]);
     }
 
-    if constexpr (EB == 1) expand(1);
+    if constexpr (EB == 1) expand_values();
 
     // online softmax per row, running maximum moved lazily (log2 units); the
     // bf16 probabilities of a row are the value MFMA's P^T operand as they lie
@@ -453,7 +462,7 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
     for (int vs = 0; vs < NVS; ++vs)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const unsigned char* vp = sl + Ly::K1B + Ly::K2B + vs * Ly::VB + (vfrag ^ (32u * ct));
+        const unsigned char* vp = (EB == 1 ? st : sl + Ly::K1B + Ly::K2B) + vs * Ly::VB + (vfrag ^ (32u * ct));
         const u32x2 h0 = ld_tr(vp);
         if constexpr (T == 32) {
           const u32x2 h1 = ld_tr(vp + 16 * Ly::VROW);
