@@ -46,6 +46,15 @@ __device__ __forceinline__ u32x2 ld_tr(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
 }
 
+// ds_read_b64_tr_b8: within each 16-lane group, destination lane t receives
+// as byte j the byte t % 8 of the 8 bytes that source lane 2 j + t / 8
+// points at (the layout an LDS probe of the instruction showed).
+typedef int i32x2_lds __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_lds lds_i32x2;
+__device__ __forceinline__ u32x2 ld_tr8(const unsigned char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p));
+}
+
 // s_waitcnt with only the vector-memory counter limited to N (N < 64)
 template <int N>
 __device__ __forceinline__ void wait_vmem_at_most() {

@@ -52,9 +52,9 @@ namespace {
 // T keys per tile: 32 (one 16x16x32 value MFMA step) or 16 (one 16x16x16
 // step), whichever lets a wave keep more tiles in flight.  EB is the bytes
 // per cached element: 2 (bf16 tiles feed the MFMAs straight from the ring)
-// or 1 (8-bit tiles land in the ring; their keys are converted to bf16 in
-// registers as the score MFMAs read them, their values expanded into one
-// bf16 stage per wave for the transposing reads).
+// or 1 (8-bit tiles land in the ring and are converted to bf16 in registers
+// as the MFMAs read them: keys by plain reads, values by 8-bit transposing
+// reads).
 template <int DK1, int DK2, int DVW, int NVS, int T, int EB = 2>
 struct SdLayout {
   // the bf16 tile the MFMAs read (swizzled rows)
@@ -65,12 +65,10 @@ struct SdLayout {
   static constexpr int RK1ROW = EB * DK1, RK2ROW = EB * DK2, RVROW = EB * DVW;
   static constexpr int RK1B = T * RK1ROW, RK2B = T * RK2ROW, RVB = T * RVROW;
   static constexpr int SLOT = RK1B + RK2B + NVS * RVB;          // one ring slot
-  // 8-bit tiles: the keys feed the score MFMAs straight from the ring
-  // (converted in registers); only the values are expanded into a bf16 stage
-  static constexpr int STAGE = EB == 2 ? 0 : NVS * VB;
+  static constexpr int STAGE = 0;  // (no staging: every tile is read where it lands)
   // LDS per work-group: all of a CU's for 16-bit tiles (one work-group per
   // CU); half for 8-bit ones, so that two work-groups share a CU and one's
-  // expansion and softmax run beside the other's MFMAs
+  // conversions and softmax run beside the other's MFMAs
   static constexpr int BUDGET = EB == 1 ? 80 * 1024 : 160 * 1024;
   // four waves per work-group when each can keep two tiles, else two
   static constexpr int NW = 4 * (2 * SLOT + STAGE) <= BUDGET ? 4 : 2;
@@ -126,6 +124,9 @@ __device__ __forceinline__ int val_swz(int row_bytes, int r) { return row_bytes 
 // 8-bit key rows (128 or 64 B): 16-byte unit u of row r at u ^ k8_swz; an
 // 8-byte fragment read of 16 rows then covers distinct banks
 __device__ __forceinline__ int k8_swz(int row_bytes, int r) { return row_bytes == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+// 8-bit value rows: unit u of row r at u ^ v8_swz; a transposing read takes
+// 32 B (two units) from each of 8 rows per half-wave, in distinct banks
+__device__ __forceinline__ int v8_swz(int row_bytes, int r) { return row_bytes == 128 ? 2 * ((r >> 1) & 3) : 2 * ((r >> 2) & 1); }
 
 template <int DK1, int DK2, int DVW, int NVS, int T, int QT, int EB>
 __global__ __launch_bounds__((64 * SdLayout<DK1, DK2, DVW, NVS, T, EB>::NW), 1)
@@ -245,12 +246,11 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
         0,
         (int)(lastk * vrow + (uint32_t)Ly::RVROW), kBufferFlags);
   // per-lane offsets of the instructions of one tile (they repeat every tile)
-  // (8-bit value tiles are stored unswizzled: they are only read row-major,
-  // by the expansion into the bf16 stage)
   auto lane_ofs = [&](int row_bytes, uint32_t gl_row, int n, bool is_key) -> uint32_t {
     const int upr = row_bytes / 16, rpi = 1024 / row_bytes;
     const int r = n * rpi + lane / upr;  // row in the tile
-    const int sw = EB == 1 ? (is_key ? k8_swz(row_bytes, r) : 0) : is_key ? key_swz(row_bytes, r) : val_swz(row_bytes, r);
+    const int sw = EB == 1 ? (is_key ? k8_swz(row_bytes, r) : v8_swz(row_bytes, r))
+                           : (is_key ? key_swz(row_bytes, r) : val_swz(row_bytes, r));
     return (uint32_t)r * gl_row + 16u * (uint32_t)((lane % upr) ^ sw);
   };
   uint32_t k1o[Ly::NK1], k2o[Ly::NK2 > 0 ? Ly::NK2 : 1], vo[Ly::NV];
@@ -348,42 +348,11 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
     issue_tile(i + NSLOT - 1);                       // into the slot of tile i - 1
     wait_vmem_at_most<Ly::NDMA * (NSLOT - 1)>();     // tile i has landed
     const unsigned char* sl = smem + wave * Ly::WAVE + (i % NSLOT) * Ly::SLOT;
-    // expand the values of the 8-bit tile into this wave's bf16 stage, row by
-    // row in 16-code chunks (exact: every E4M3 value is a bf16 value), into
-    // the swizzled layout the transposing reads expect
-    unsigned char* st = smem + wave * Ly::WAVE + NSLOT * Ly::SLOT;
-    const unsigned char* sl8 = sl;
     auto cvt_lo = [](uint32_t w) -> uint32_t {  // E4M3 codes 0, 1 of the word as two bf16
       return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
     };
     auto cvt_hi = [](uint32_t w) -> uint32_t {  // codes 2, 3
       return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-    };
-    auto expand_values = [&]() __attribute__((always_inline)) {
-      constexpr int CPR = DVW / 16;  // 16-code chunks per row
-#pragma unroll
-        for (int c0 = 0; c0 < T * CPR; c0 += 64) {
-          const int c = c0 + lane, r = c / CPR, u8 = c % CPR;
-          const u32x4 w = ld16(sl8 + Ly::RK1B + 16 * c);
-          // a chunk becomes units 2 u8 (codes 0..7) and 2 u8 + 1 (codes
-          // 8..15) of its row; lanes with bit 2 set store their odd unit
-          // first, so that the eight lanes of each store that share a
-          // 128-byte bank window hit eight distinct 16-byte slots (an LDS
-          // probe counted 7.75 conflict cycles per store without this)
-          const int e = (lane >> 2) & 1;
-          const uint32_t a0 = e ? w[2] : w[0], a1 = e ? w[3] : w[1];
-          const uint32_t b0 = e ? w[0] : w[2], b1 = e ? w[1] : w[3];
-          const u32x4 first = {cvt_lo(a0), cvt_hi(a0), cvt_lo(a1), cvt_hi(a1)};
-          const u32x4 second = {cvt_lo(b0), cvt_hi(b0), cvt_lo(b1), cvt_hi(b1)};
-          const int sw = val_swz(Ly::VROW, r);
-          unsigned char* row = st + r * Ly::VROW;
-          st16(row + 16 * ((2 * u8 + e) ^ sw), first);
-          st16(row + 16 * ((2 * u8 + 1 - e) ^ sw), second);
-        }
-      // the wave's LDS operations run in order, so its later reads see these
-      // writes; keep the compiler from moving a read above a write whose
-      // address it cannot relate (another lane's)
-      asm volatile("" ::: "memory");
     };
     const int key0 = start + (i * NWAVE + wave) * T;
 
@@ -414,7 +383,6 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
           sacc[kt][qt] = mfma_bf16(kf[kt], qf[qt][s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kt][qt]);
     }
 
-    if constexpr (EB == 1) expand_values();
 
     // online softmax per row, running maximum moved lazily (log2 units); the
     // bf16 probabilities of a row are the value MFMA's P^T operand as they lie
@@ -458,22 +426,48 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
     }
 
     // O^T += V^T P^T for every value source and column tile
+    if constexpr (EB == 1) {
+      // 8-bit values (one source, 16-key tiles): one transposing read per
+      // pair of column tiles.  Within each 16-lane group g, ds_read_b64_tr_b8
+      // hands destination lane t, as byte j, byte t % 8 of the 8 bytes that
+      // source lane 2 j + t / 8 points at.  Source lane 2 j + p of group g
+      // points at key row 4 g + j % 4, dims c + 8 p, c = 16 ct for j < 4 and
+      // 16 (ct + 1) for j >= 4; lane t so receives keys 4 g .. 4 g + 3 of dim
+      // 16 ct + t (bytes 0..3) and of dim 16 (ct + 1) + t (bytes 4..7): the
+      // A operands of both tiles, converted in registers.
+      static_assert(T == 16 && NVS == 1 && NCT % 2 == 0, "8-bit values");
+      const int j = li >> 1;
+      const int vrow = 4 * lg + (j & 3);
+      const unsigned char* vbase = sl + Ly::RK1B + vrow * Ly::RVROW + 8 * (li & 1);
+      const int vsw = v8_swz(Ly::RVROW, vrow);
 #pragma unroll
-    for (int vs = 0; vs < NVS; ++vs)
+      for (int ct = 0; ct < NCT; ct += 2) {
+        const u32x2 w = ld_tr8(vbase + 16 * ((ct + (j >> 2)) ^ vsw));
+        const u32x2 a0 = {cvt_lo(w[0]), cvt_hi(w[0])}, a1 = {cvt_lo(w[1]), cvt_hi(w[1])};
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const unsigned char* vp = (EB == 1 ? st : sl + Ly::K1B + Ly::K2B) + vs * Ly::VB + (vfrag ^ (32u * ct));
-        const u32x2 h0 = ld_tr(vp);
-        if constexpr (T == 32) {
-          const u32x2 h1 = ld_tr(vp + 16 * Ly::VROW);
-          const u32x4 vt = {h0[0], h0[1], h1[0], h1[1]};
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) oacc[vs][ct][qt] = mfma_bf16(vt, pf[qt], oacc[vs][ct][qt]);
-        } else {
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) oacc[vs][ct][qt] = mfma_k16(h0, pf[qt], oacc[vs][ct][qt]);
+        for (int qt = 0; qt < QT; ++qt) {
+          oacc[0][ct][qt] = mfma_k16(a0, pf[qt], oacc[0][ct][qt]);
+          oacc[0][ct + 1][qt] = mfma_k16(a1, pf[qt], oacc[0][ct + 1][qt]);
         }
       }
+    } else {
+#pragma unroll
+      for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const unsigned char* vp = sl + Ly::K1B + Ly::K2B + vs * Ly::VB + (vfrag ^ (32u * ct));
+          const u32x2 h0 = ld_tr(vp);
+          if constexpr (T == 32) {
+            const u32x2 h1 = ld_tr(vp + 16 * Ly::VROW);
+            const u32x4 vt = {h0[0], h0[1], h1[0], h1[1]};
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) oacc[vs][ct][qt] = mfma_bf16(vt, pf[qt], oacc[vs][ct][qt]);
+          } else {
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) oacc[vs][ct][qt] = mfma_k16(h0, pf[qt], oacc[vs][ct][qt]);
+          }
+        }
+    }
   }
   // no DMA of this wave may still land in the ring, which now holds the
   // combination buffers
