@@ -827,7 +827,7 @@ gha_status latent_absorb_decode_check(const gha_tensor* q_lat, const gha_tensor*
     return fail(GHA_ERR_ALIGN, "workspace not 16-byte aligned");
   const int T = gha::latent_tile_tokens();
   if ((int64_t)B * latent_row_blocks(h_q, s_q) * (gha::latent_rows_per_wg() / 4) > (1LL << 30) ||
-      (int64_t)B * ((L_cap + T - 1) / T) >= (1LL << 31))
+      (int64_t)B * ((L_cap + T - 1) / T + gha::latent_segment_start_tiles()) >= (1LL << 31))
     return fail(GHA_ERR_SHAPE, "problem too large for one launch");
   return GHA_OK;
 }

@@ -86,6 +86,21 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 __device__ __forceinline__ float group4_max(float x) { return xor32_max(xor16_max(x)); }
+
+// Maxima of finite or infinite floats as single instructions.  Written as
+// inline asm because fmaxf on values the compiler cannot prove canonical
+// (MFMA results, asm outputs) costs an extra v_max per operand in IEEE mode;
+// neither helper is meant for NaN inputs.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float group4_sum(float x) { return xor32_sum(xor16_sum(x)); }
 
 // An MFMA A operand of all-ones bf16: multiplying it into P^T sums P over the

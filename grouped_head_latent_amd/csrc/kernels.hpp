@@ -72,7 +72,7 @@ struct LatentArgs {
   float* lse;         // dense (B, s_q, h_q) or null
   float* ws_o;        // (n_rb, n_wg + B, rows per work-group, r_kv) partials
   float* ws_lse;      // (n_rb, n_wg + B, rows per work-group)
-  int32_t* ws_tiles;  // (B + 1) prefix sums of the tiles per sequence
+  int32_t* ws_tiles;  // (B + 1) prefix sums of the split positions per sequence
   int B, h_q, s_q, L_cap;
   int n_rb;           // row blocks (of latent_rows_per_wg()) over s_q * h_q rows
   int n_wg;           // work-groups per row block, each takes 1/n_wg of all tiles
@@ -162,6 +162,7 @@ int stream_decode_chunk();  // keys per scheduling chunk of the streaming decode
 hipError_t launch_latent_decode(const LatentArgs& a, bool out_f32, hipStream_t st);
 int latent_rows_per_wg();    // query rows per work-group of the split kernel
 int latent_tile_tokens();    // tokens per tile
+int latent_segment_start_tiles();  // placeholder positions per sequence in the split (at most)
 // work-groups per row block for n_rb row blocks and at most max_tiles tiles
 int latent_plan_wgs(int n_rb, int64_t max_tiles);
 

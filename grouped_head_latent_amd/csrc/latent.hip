@@ -60,12 +60,14 @@ constexpr int RBASE = NLS * LTILE;
 constexpr int PBASE = RBASE + NRS * RTILE;
 constexpr int LDS_BYTES = PBASE + 2 * PBUF;       // 156 KiB
 constexpr float kLatentSlack = 96.f;              // see the running state below
-#ifndef GHA_LAT_SOFT_SLOTS
-#define GHA_LAT_SOFT_SLOTS 48
-#endif
-constexpr int kSoftSlots = GHA_LAT_SOFT_SLOTS;     // value MFMAs that carry the softmax (< 64)
-// the value MFMA after the last softmax slot publishes P^T, so one must follow
-static_assert(kSoftSlots > 0 && kSoftSlots < 64, "softmax slots must leave a value MFMA to publish after");
+// the cost of starting a segment (loading 128 query rows, writing a 256 KiB
+// partial: some 400 KiB of traffic at a work-group's share of the bandwidth,
+// plus latency), in tiles of 36 KiB; measured at about 30 us against 1.9 us
+// per tile on the 128-head workload
+constexpr int kSegStartTiles = 16;
+// the value MFMA after which P^T is published (after the last softmax step,
+// with value MFMAs left to cover the LDS writes before the barrier)
+constexpr int kPublishSlot = 44;
 
 // chunk swizzles of the LDS rows (see the layout above)
 __host__ __device__ constexpr int lat_sw(int k) { return ((k & 7) << 1) | ((k >> 3) & 1); }
@@ -94,20 +96,28 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(lid / a.n_rb);
 
   // ---- this work-group's share of the tiles of all sequences ----------------
-  // The tiles of sequences 0 .. B - 1 are numbered one after another (NT in
-  // all) and work-group w takes tiles [w NT / n_wg, (w + 1) NT / n_wg): equal
-  // shares whatever the length mix.  Each sequence it touches is a segment
-  // with its own partial, in slot w + b (unique: along the segments either w
-  // or b grows).
+  // The tiles of sequences 0 .. B - 1 (NT in all) are numbered one after
+  // another, each sequence's preceded by X placeholder positions that stand
+  // for the cost of starting a segment there (loading the queries, writing a
+  // partial): X = kSegStartTiles, at most the mean share NT / n_wg.
+  // Work-group w takes the positions [w NV / n_wg, (w + 1) NV / n_wg) of
+  // the NV = NT + X B, i.e. the tiles among them: equal costs whatever the
+  // length mix, a share that opens a second sequence holding X tiles fewer.
+  // Each sequence it touches is a segment with its own partial, in slot
+  // w + b (unique: along the segments either w or b grows).
   int NT = 0;
   for (int c0 = 0; c0 < a.B; c0 += 64)
     NT += __builtin_amdgcn_readlane(wave_incl_scan(latent_tiles(a, c0 + lane)), 63);
-  const int lo = (int)((int64_t)w * NT / a.n_wg), hi = (int)((int64_t)(w + 1) * NT / a.n_wg);
-  // one work-group publishes the prefix sums for the merge
+  const int X = __builtin_amdgcn_readfirstlane(min(kSegStartTiles, NT / a.n_wg));
+  // positions of sequence b: X placeholders, then its tiles (none past the batch)
+  auto positions = [&](int b) __attribute__((always_inline)) { return b < a.B ? latent_tiles(a, b) + X : 0; };
+  const int NV = NT + X * a.B;  // below 2^31: checked on the host
+  const int lo = (int)((int64_t)w * NV / a.n_wg), hi = (int)((int64_t)(w + 1) * NV / a.n_wg);
+  // one work-group publishes the prefix sums of the positions for the merge
   if (lid == 0 && wave == 0) {
     int run = 0;
     for (int c0 = 0; c0 < a.B; c0 += 64) {
-      const int t = latent_tiles(a, c0 + lane);
+      const int t = positions(c0 + lane);
       const int incl = wave_incl_scan(t) + run;
       if (c0 + lane < a.B) a.ws_tiles[c0 + lane] = incl - t;
       run = __builtin_amdgcn_readlane(incl, 63);
@@ -116,10 +126,10 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   }
 
   if (lo >= hi) return;
-  // first sequence with tiles at or after lo, and the tiles before it
+  // first sequence with positions at or after lo, and the positions before it
   int b0 = 0, P = 0;
   for (int c0 = 0;; c0 += 64) {
-    const int t = latent_tiles(a, c0 + lane);
+    const int t = positions(c0 + lane);
     const int incl = wave_incl_scan(t) + P;
     const uint64_t m = __builtin_amdgcn_ballot_w64(incl > lo);
     if (m != 0) {
@@ -213,6 +223,8 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   // either way.
   f32x4 oacc[8][8], lacc[2];  // oacc[column tile][q-tile of the work-group] (AGPRs)
   float m2[2] = {kNegInf, kNegInf};
+  float m2s[2] = {kNegInf, kNegInf};  // m2 + slack: the restart threshold
+  float msub[2] = {0.f, 0.f};         // m2, or 0 while the row has seen nothing
   u32x4 pall[8];              // P^T of all 8 q-tiles of the previous tile
 
   // Tiles wholly before `end` and before every row's causal limit need no
@@ -296,14 +308,21 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
     });
 
     // ---- phase B: softmax per row (= per lane and q-tile) against a fixed
-    // reference, in 32 small stages; sacc[kt][qt][r] is token
-    // k0 + 16 kt + 4 lg + r and becomes its probability in place ----
-    float mx[2], msub[2];
+    // reference, in small stages; sacc[kt][qt][r] is token k0 + 16 kt + 4 lg + r
+    // and becomes its probability in place.  A lane compares the largest of
+    // its own eight scores with the row's threshold m2 + slack (-inf while
+    // the row has seen nothing): only when some lane of the wave exceeds it
+    // (a row's first visible scores, or a restart) is the row maximum formed
+    // across the four lane groups; otherwise the reference stands and no
+    // lanes need to talk.  The decisions are those of the full maximum. ----
+    float lm[2], lm2[2];
     u32x4 pf[2];
     bool restart_row = false;
-    auto stage = [&](auto K_) __attribute__((always_inline)) {
-      constexpr int k = decltype(K_)::value;
-      constexpr int qt = k / 16, st = k % 16;
+    // stages of q-tile qt: 0, 1 mask key tiles 0, 1 (masked tiles only);
+    // 2 .. 5 lane maximum, scaled; 6 .. 9 shift by the reference (two scores
+    // each); 10 .. 17 exp2 (one score each); 18, 19 bf16 packing
+    auto stage = [&](auto QT_, auto ST_) __attribute__((always_inline)) {
+      constexpr int qt = decltype(QT_)::value, st = decltype(ST_)::value;
       if constexpr (st <= 1) {
         if constexpr (kMasked) {
           const int kmax = min(end - 1, kvis[qt]);
@@ -312,35 +331,57 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
             if (k0 + 16 * st + 4 * lg + r > kmax) sacc[st][qt][r] = kNegInf;
         }
       } else if constexpr (st == 2) {
-        mx[qt] = fmaxf(fmaxf(sacc[0][qt][0], sacc[0][qt][1]), fmaxf(sacc[0][qt][2], sacc[0][qt][3]));
+        lm[qt] = max3f(sacc[0][qt][0], sacc[0][qt][1], sacc[0][qt][2]);
+        lm2[qt] = max3f(sacc[0][qt][3], sacc[1][qt][0], sacc[1][qt][1]);
       } else if constexpr (st == 3) {
-        mx[qt] = fmaxf(mx[qt], fmaxf(fmaxf(sacc[1][qt][0], sacc[1][qt][1]), fmaxf(sacc[1][qt][2], sacc[1][qt][3])));
+        lm[qt] = max3f(sacc[1][qt][2], sacc[1][qt][3], lm[qt]);
       } else if constexpr (st == 4) {
-        mx[qt] = xor16_max(mx[qt]);
+        lm[qt] = max2f(lm[qt], lm2[qt]);
       } else if constexpr (st == 5) {
-        mx[qt] = xor32_max(mx[qt]) * c2;
-      } else if constexpr (st == 6) {
-        // the first visible scores of a row fix its reference; a tile that
-        // outgrows it by more than the slack asks for a restart
-        const bool first = m2[qt] == kNegInf;
-        const bool grow = !first && mx[qt] > m2[qt] + kLatentSlack;
-        restart_row = restart_row || grow;
-        m2[qt] = (first || grow) ? mx[qt] : m2[qt];
-        msub[qt] = (m2[qt] == kNegInf) ? 0.f : m2[qt];
-      } else if constexpr (st == 7 || st == 10) {
-        constexpr int kt = st == 7 ? 0 : 1;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sacc[kt][qt][r] = __builtin_fmaf(sacc[kt][qt][r], c2, -msub[qt]);
-      } else if constexpr (st == 8 || st == 9 || st == 11 || st == 12) {
-        constexpr int kt = st < 10 ? 0 : 1, r0 = (st == 8 || st == 11) ? 0 : 2;
-        sacc[kt][qt][r0] = fast_exp2(sacc[kt][qt][r0]);
-        sacc[kt][qt][r0 + 1] = fast_exp2(sacc[kt][qt][r0 + 1]);
-      } else if constexpr (st == 13) {
-        pf[qt] = u32x4{pack_bf16(sacc[0][qt][0], sacc[0][qt][1]), pack_bf16(sacc[0][qt][2], sacc[0][qt][3]),
-                       pack_bf16(sacc[1][qt][0], sacc[1][qt][1]), pack_bf16(sacc[1][qt][2], sacc[1][qt][3])};
+        lm[qt] = lm[qt] * c2;  // = the largest scaled score (scaling is monotone)
+      } else if constexpr (st >= 6 && st <= 9) {
+        constexpr int kt = (st - 6) / 2, r0 = 2 * ((st - 6) % 2);
+        sacc[kt][qt][r0] = __builtin_fmaf(sacc[kt][qt][r0], c2, -msub[qt]);
+        sacc[kt][qt][r0 + 1] = __builtin_fmaf(sacc[kt][qt][r0 + 1], c2, -msub[qt]);
+      } else if constexpr (st >= 10 && st <= 17) {
+        constexpr int kt = (st - 10) / 4, r = (st - 10) % 4;
+        sacc[kt][qt][r] = fast_exp2(sacc[kt][qt][r]);
+      } else if constexpr (st == 18) {
+        pf[qt][0] = pack_bf16(sacc[0][qt][0], sacc[0][qt][1]);
+        pf[qt][1] = pack_bf16(sacc[0][qt][2], sacc[0][qt][3]);
+      } else if constexpr (st == 19) {
+        pf[qt][2] = pack_bf16(sacc[1][qt][0], sacc[1][qt][1]);
+        pf[qt][3] = pack_bf16(sacc[1][qt][2], sacc[1][qt][3]);
       }
     };
-    constexpr int NST = 32;
+    // after stage 5 of both q-tiles: the wave-uniform check, and the row
+    // maxima when some lane asks for them.  A row's first visible scores fix
+    // its reference; a tile that outgrows it by more than the slack asks for
+    // a restart.
+    auto check = [&]() __attribute__((always_inline)) {
+      if (wave_any(lm[0] > m2s[0] || lm[1] > m2s[1])) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const float mx = group4_max(lm[qt]);
+          const bool first = m2[qt] == kNegInf;
+          const bool grow = !first && mx > m2s[qt];
+          restart_row = restart_row || grow;
+          m2[qt] = (first || grow) ? mx : m2[qt];
+          m2s[qt] = m2[qt] + kLatentSlack;
+          msub[qt] = (m2[qt] == kNegInf) ? 0.f : m2[qt];
+        }
+      }
+    };
+    // the softmax as a list of steps: stages 0 .. 5 of both q-tiles
+    // alternating, the check, stages 6 .. 19 alternating
+    constexpr int NSTEP = 2 * 6 + 1 + 2 * 14;
+    static_assert(NSTEP < kPublishSlot && kPublishSlot < 64, "P^T is published after the last softmax step");
+    auto step = [&](auto J_) __attribute__((always_inline)) {
+      constexpr int j = decltype(J_)::value;
+      if constexpr (j < 12) stage(std::integral_constant<int, j % 2>{}, std::integral_constant<int, j / 2>{});
+      else if constexpr (j == 12) check();
+      else stage(std::integral_constant<int, (j - 13) % 2>{}, std::integral_constant<int, 6 + (j - 13) / 2>{});
+    };
     // the scores must retire before the softmax reads them
     auto scores_retire = [&]() __attribute__((always_inline)) {
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(sacc[0][0]), "+v"(sacc[0][1]), "+v"(sacc[1][0]), "+v"(sacc[1][1]));
@@ -364,8 +405,7 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
       if (lane == 0) restart_flag[it & 1][wave] = any_restart ? 1 : 0;
     };
     if constexpr (kPV) {
-      constexpr int NB = 64;         // value MFMAs
-      constexpr int NBS = kSoftSlots;  // the softmax stages share the first NBS of them
+      constexpr int NB = 64;  // value MFMAs; step j of the softmax follows MFMA j + 1
       static_for<0, NB>([&](auto M_) __attribute__((always_inline)) {
         constexpr int m = decltype(M_)::value;
         constexpr int dt = m / 8, qt = m % 8;
@@ -374,13 +414,13 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
         mfma_acc(oacc[dt][qt], vf[dt & 1], pall[qt]);
         __builtin_amdgcn_sched_barrier(0);
         if (m == 0) scores_retire();
-        if constexpr (m < NBS) static_for<m * NST / NBS, (m + 1) * NST / NBS>(stage);
-        if (m == NBS) publish();
+        if constexpr (m >= 1 && m <= NSTEP) step(std::integral_constant<int, m - 1>{});
+        if (m == kPublishSlot) publish();
         __builtin_amdgcn_sched_barrier(0);
       });
     } else {
       scores_retire();
-      static_for<0, NST>(stage);
+      static_for<0, NSTEP>(step);
 #pragma unroll
       for (int j = 5; j < 9; ++j) dma(dt2, j);
       publish();
@@ -470,9 +510,10 @@ __global__ __launch_bounds__(256, 1) void latent_split_kernel(LatentArgs a) {
   for (int b = b0; b < a.B && P < hi; ++b) {
     const int L = __builtin_amdgcn_readfirstlane(min(max(a.seqlens[b], 0), a.L_cap));
     const int nt = (L + T - 1) / T;
-    const int t0 = max(lo, P) - P, t1 = min(hi, P + nt) - P;
+    const int first = P + X;  // position of the sequence's tile 0
+    const int t0 = max(lo, first) - first, t1 = min(hi, first + nt) - first;
     if (t0 < t1) segment(b, L, t0 * T, min(L, t1 * T), w + b);
-    P += nt;
+    P = first + nt;
   }
 }
 
@@ -489,16 +530,18 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
   const int f = (tid & 63) * 8;
   const int R = rb * ROWS + row;
   if (R >= a.s_q * a.h_q) return;
-  // the work-groups whose tile range meets this sequence's tiles [p0, p1)
-  const int p0 = a.ws_tiles[b], p1 = a.ws_tiles[b + 1], NT = a.ws_tiles[a.B];
+  // the work-groups whose share of the positions meets this sequence's
+  // tiles [p0, p1) (its last positions: the split kernel numbers each
+  // sequence's placeholders, then its tiles)
+  const int p1 = a.ws_tiles[b + 1], p0 = p1 - latent_tiles(a, b), NV = a.ws_tiles[a.B];
   const int64_t n = a.n_wg;
   int w_first = 0, w_last = -1;
   if (p0 < p1) {
-    w_first = (int)(((int64_t)(p0 + 1) * n - 1) / NT);  // last w with w NT / n <= p0
-    w_last = (int)(((int64_t)p1 * n - 1) / NT);         // last w with w NT / n < p1
+    w_first = (int)(((int64_t)(p0 + 1) * n - 1) / NV);  // last w with w NV / n <= p0
+    w_last = (int)(((int64_t)p1 * n - 1) / NV);         // last w with w NV / n < p1
   }
   auto meets = [&](int w) {
-    const int lo = (int)(w * (int64_t)NT / n), hi = (int)((w + 1) * (int64_t)NT / n);
+    const int lo = (int)(w * (int64_t)NV / n), hi = (int)((w + 1) * (int64_t)NV / n);
     return max(lo, p0) < min(hi, p1);
   };
   const int64_t base = (int64_t)rb * (a.n_wg + a.B) * ROWS + row;
@@ -538,6 +581,7 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
 
 int latent_rows_per_wg() { return ROWS; }
 int latent_tile_tokens() { return T; }
+int latent_segment_start_tiles() { return kSegStartTiles; }
 
 int latent_plan_wgs(int n_rb, int64_t max_tiles) {
   // one work-group per CU in a single round: equal tile shares then finish
