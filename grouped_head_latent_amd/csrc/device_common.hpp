@@ -90,15 +90,17 @@ __device__ __forceinline__ float group4_max(float x) { return xor32_max(xor16_ma
 // Maxima of finite or infinite floats as single instructions.  Written as
 // inline asm because fmaxf on values the compiler cannot prove canonical
 // (MFMA results, asm outputs) costs an extra v_max per operand in IEEE mode;
-// neither helper is meant for NaN inputs.
+// neither helper is meant for NaN inputs.  Volatile, so that a maximum
+// woven between MFMAs stays where it is written: moved to its use, it would
+// keep the raw scores it reads alive beside the probabilities made from them.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
 __device__ __forceinline__ float max2f(float a, float b) {
   float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  asm volatile("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
 __device__ __forceinline__ float group4_sum(float x) { return xor32_sum(xor16_sum(x)); }

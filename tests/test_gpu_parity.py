@@ -166,6 +166,40 @@ def test_gqa_prefill_longest_keys(gha_lib, S_k):
     check(f"longest prefill lse S_k={S_k}", lse, ref_lse)
 
 
+@pytest.mark.parametrize("heads", [None, (1, 6)])
+def test_gqa_prefill_growing_scores(gha_lib, heads):
+    """Keys whose scores jump far above the first tile's maximum, twice (key
+    rows of three magnitudes, the jumps over 96 in log2 units): a prefill
+    kernel that fixes each row's reference from its first tile must replace
+    it and start the row block again, and the result is still the softmax.
+    With `heads`, only those query heads see the jump; the others have a zero
+    query and flat scores."""
+    say(f"bf16 prefill growing scores, heads={heads}")
+    B, h_q, h_kv, S, d = 1, 8, 2, 600, 128
+    kb = gen((B, h_kv, S, d), 46, 2)
+    vb = gen((B, h_kv, S, d), 46, 3)
+    eight = np.float32(8.0).view(np.uint32) >> 16
+    sixteen = np.float32(16.0).view(np.uint32) >> 16
+    one = np.float32(1.0).view(np.uint32) >> 16
+    kb[:, :, 200:400] = eight
+    kb[:, :, 400:] = sixteen
+    qb = np.full((B, h_q, S, d), one, dtype=np.uint16)
+    if heads is not None:
+        qb[:] = 0
+        qb[:, list(heads)] = one
+    q, k, v = (bf16_to_torch(x) for x in (qb, kb, vb))
+    o, lse = gha_lib.gqa_prefill(q, k, v, causal=True, out_dtype=torch.float32, return_lse=True)
+    ref, ref_lse = oracle.gqa_prefill(widen(qb), widen(kb), widen(vb), causal=True)
+    check("growing scores", o.cpu().numpy(), ref)
+    check("growing scores lse", lse.cpu().numpy(), ref_lse)
+    # rows past key 400 of the jumping heads average the values of keys 400 ..
+    jumped = list(heads) if heads is not None else list(range(h_q))
+    v32 = widen(vb)
+    for hq in jumped:
+        want = v32[0, hq // 4, 400:451].mean(axis=0)
+        assert np.allclose(ref[0, hq, 450], want, atol=1e-6)
+
+
 def test_gqa_prefill_strided_bshd_layout(gha_lib):
     """(B, S, H, D) memory order passed through the strides."""
     say("bf16 prefill BSHD strides")
