@@ -333,6 +333,12 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
       for (int j = 0; j < GHA_PF_PFD; ++j) load_step(step_at(j), t, fr[j]);  // in flight during the softmax
       __builtin_amdgcn_sched_barrier(0);
       u32x4 pf[QT][2];
+      // Each lane scales the largest of its own scores of a row; only when
+      // some lane exceeds its row's reference by more than the slack does the
+      // wave form the row maxima across the four lane groups and move the
+      // reference (the decisions of a full reduction, without it most tiles).
+      float mxl[QT];
+      bool grow = false;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         if (kMasked) {
@@ -344,23 +350,32 @@ __global__ __launch_bounds__(256, GHA_PF_MIN_WG) void prefill_d128_kernel(Prefil
             for (int r = 0; r < 4; ++r)
               if (key0 + 16 * kt + 4 * lg + r > kmax) sacc[kt][qt][r] = kNegInf;
         }
-        float mx = fmaxf(fmaxf(sacc[0][qt][0], sacc[0][qt][1]), sacc[0][qt][2]);
-        mx = fmaxf(fmaxf(mx, sacc[0][qt][3]), sacc[1][qt][0]);
-        mx = fmaxf(fmaxf(mx, sacc[1][qt][1]), sacc[1][qt][2]);
-        mx = fmaxf(fmaxf(mx, sacc[1][qt][3]), sacc[2][qt][0]);
-        mx = fmaxf(fmaxf(mx, sacc[2][qt][1]), sacc[2][qt][2]);
-        mx = fmaxf(fmaxf(mx, sacc[2][qt][3]), sacc[3][qt][0]);
-        mx = fmaxf(fmaxf(mx, sacc[3][qt][1]), sacc[3][qt][2]);
-        mx = fmaxf(mx, sacc[3][qt][3]);
-        const float mx2 = group4_max(mx) * c2;
-        if (wave_any(mx2 > m2[qt] + kRescaleSlack)) {
-          const float mnew = fmaxf(m2[qt], mx2);
-          const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2[qt] - mnew);
-          m2[qt] = mnew;
-          lacc[qt] *= alpha;
+        float mx = max3f(sacc[0][qt][0], sacc[0][qt][1], sacc[0][qt][2]);
+        mx = max3f(mx, sacc[0][qt][3], sacc[1][qt][0]);
+        mx = max3f(mx, sacc[1][qt][1], sacc[1][qt][2]);
+        mx = max3f(mx, sacc[1][qt][3], sacc[2][qt][0]);
+        mx = max3f(mx, sacc[2][qt][1], sacc[2][qt][2]);
+        mx = max3f(mx, sacc[2][qt][3], sacc[3][qt][0]);
+        mx = max3f(mx, sacc[3][qt][1], sacc[3][qt][2]);
+        mxl[qt] = max2f(mx, sacc[3][qt][3]) * c2;  // = the largest scaled score (scaling is monotone)
+        grow = grow || mxl[qt] > m2[qt] + kRescaleSlack;
+      }
+      if (wave_any(grow)) {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+        for (int qt = 0; qt < QT; ++qt) {
+          const float mx2 = group4_max(mxl[qt]);
+          if (wave_any(mx2 > m2[qt] + kRescaleSlack)) {
+            const float mnew = fmaxf(m2[qt], mx2);
+            const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m2[qt] - mnew);
+            m2[qt] = mnew;
+            lacc[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+          }
         }
+      }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
         const float msub = (m2[qt] == kNegInf) ? 0.f : m2[qt];
         float p[4][4];
 #pragma unroll
