@@ -344,7 +344,10 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
 
 #pragma unroll
   for (int i = 0; i < NSLOT - 1; ++i) issue_tile(i);
-  for (int i = 0; i < n_my; ++i) {
+  // tile i of this wave: keys start + (i NWAVE + wave) T ..; the mask is
+  // applied only where some row may not see a key of the tile
+  auto tile = [&](int i, auto masked_) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked_)::value;
     issue_tile(i + NSLOT - 1);                       // into the slot of tile i - 1
     wait_vmem_at_most<Ly::NDMA * (NSLOT - 1)>();     // tile i has landed
     const unsigned char* sl = smem + wave * Ly::WAVE + (i % NSLOT) * Ly::SLOT;
@@ -395,7 +398,7 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = key0 + 16 * kt + 4 * lg + r;
-          if (key >= end || key > kvis[qt] || key < kmin[qt]) sacc[kt][qt][r] = kNegInf;
+          if (kMasked && (key >= end || key > kvis[qt] || key < kmin[qt])) sacc[kt][qt][r] = kNegInf;
           mx = fmaxf(mx, sacc[kt][qt][r]);
         }
       const float mx2 = group4_max(mx) * c2;
@@ -468,6 +471,23 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
           }
         }
     }
+  };
+  // Keys below safe_end are visible to every row (s_q new tokens: row t sees
+  // up to L - s_q + t) and inside the segment; keys from kmin_top on are
+  // inside every row's window.  The tiles wholly in [kmin_top, safe_end) are
+  // consecutive for each wave and skip the mask.
+  {
+    const int safe_end = min(end, L - a.s_q + 1);
+    const int kmin_top = a.window > 0 ? L - a.window : 0;
+    const int step = NWAVE * T, first = start + wave * T;  // key0 of tile i: first + i step
+    int i_lo = kmin_top > first ? (kmin_top - first + step - 1) / step : 0;
+    int i_hi = safe_end - first - T >= 0 ? (safe_end - first - T) / step + 1 : 0;
+    i_lo = __builtin_amdgcn_readfirstlane(min(i_lo, n_my));
+    i_hi = __builtin_amdgcn_readfirstlane(max(i_lo, min(i_hi, n_my)));
+    int i = 0;
+    for (; i < i_lo; ++i) tile(i, std::true_type{});
+    for (; i < i_hi; ++i) tile(i, std::false_type{});
+    for (; i < n_my; ++i) tile(i, std::true_type{});
   }
   // no DMA of this wave may still land in the ring, which now holds the
   // combination buffers
