@@ -25,7 +25,8 @@
 // segment with its own partial; inside a segment every wave walks its own
 // tiles (tiles w, w + 4, ...).
 // A wave moves its tiles from HBM into a private LDS ring by buffer DMA
-// (buffer_load ... lds; no VGPR staging), keeps NSLOT - 1 tiles in flight
+// (buffer_load ... lds; no VGPR staging; non-temporal, as every tile of a
+// group's key and value is read once per step), keeps NSLOT - 1 tiles in flight
 // while it computes on the oldest, and never waits for another wave until the
 // end.  Per tile, with all query rows of the group (the query heads times the
 // s_q new tokens, padded to 16 or 32) in one wave:
@@ -289,16 +290,17 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
             rows > 0 ? (int)((uint32_t)(rows - 1) * vrow + (uint32_t)Ly::RVROW) : 0, kBufferFlags);
 #pragma unroll
         for (int n = 0; n < Ly::NK1; ++n)
-          lds_dma16(kp, dst + 1024 * n, k1o[n], ok ? (uint32_t)u * k1row : kOutOfRange);
+          lds_dma16_stream(kp, dst + 1024 * n, k1o[n], ok ? (uint32_t)u * k1row : kOutOfRange);
 #pragma unroll
         for (int n = 0; n < Ly::NV; ++n)
-          lds_dma16(vp, dst + Ly::RK1B + 1024 * n, vo[n], ok ? (uint32_t)u * vrow : kOutOfRange);
+          lds_dma16_stream(vp, dst + Ly::RK1B + 1024 * n, vo[n], ok ? (uint32_t)u * vrow : kOutOfRange);
         return;
       }
     }
 #pragma unroll
     for (int n = 0; n < Ly::NK1; ++n)
-      lds_dma16(k1rs, dst + 1024 * n, k1o[n], ok ? (uint32_t)key0 * k1row : kOutOfRange);
+      lds_dma16_stream(k1rs, dst + 1024 * n, k1o[n], ok ? (uint32_t)key0 * k1row : kOutOfRange);
+    // the shared key part is read by every group of the team through L2
 #pragma unroll
     for (int n = 0; n < Ly::NK2; ++n)
       lds_dma16(k2rs, dst + Ly::RK1B + 1024 * n, k2o[n], ok ? (uint32_t)key0 * k2row : kOutOfRange);
@@ -306,7 +308,7 @@ void stream_decode_split_kernel(StreamDecodeArgs a) {
     for (int vs = 0; vs < NVS; ++vs)
 #pragma unroll
       for (int n = 0; n < Ly::NV; ++n)
-        lds_dma16(vrs[vs], dst + Ly::RK1B + Ly::RK2B + vs * Ly::RVB + 1024 * n, vo[n], ok ? (uint32_t)key0 * vrow : kOutOfRange);
+        lds_dma16_stream(vrs[vs], dst + Ly::RK1B + Ly::RK2B + vs * Ly::RVB + 1024 * n, vo[n], ok ? (uint32_t)key0 * vrow : kOutOfRange);
   };
 
   // ---- fragment addresses ----------------------------------------------------------
