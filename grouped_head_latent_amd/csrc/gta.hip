@@ -38,6 +38,18 @@
 // of tile it - 1 with the softmax of tile it spread between them (VALU and
 // matrix core run side by side), then P^T(it) to LDS and one barrier.
 //
+// Specialised form (SPEC, the one built): waves 0..3 only score (32
+// positions each: K is read by four waves instead of eight) and waves 4..7
+// only apply values (with four sources, wave 4 + h takes source h for all 128
+// positions: each V tile is read once).  Wave w and wave w + 4 share a SIMD,
+// so one's softmax runs beside the other's value MFMAs; the iteration
+// structure, the rings, the P^T exchange and the restart are those above.
+// The iteration is bound by LDS throughput: per iteration and CU the
+// specialised form moves about 184 KiB through the LDS (K, V^T and P^T reads,
+// P^T and DMA writes) against 248 KiB.  Each role runs a loop of its own with
+// its epilogue inside, so that neither keeps the other's registers live and
+// no accumulator outlives the loop.
+//
 // LDS rows, 16-byte units swizzled so that every fragment read touches
 // distinct banks:
 //   K row r (d_qk = 64: 8 units) keeps unit u at u ^ ((r / 2) % 8); score
@@ -61,9 +73,8 @@ constexpr int PFRAG = 1024;             // one P^T operand fragment: 64 lanes x 
 constexpr int PBUF = 16 * PFRAG;        // P^T of 8 row tiles x 2 contraction steps
 constexpr float kSlack = 96.f;
 constexpr int NW = 8;                   // waves per work-group
-constexpr int QT = ROWS / (16 * NW);    // 16-position score tiles per wave
 
-template <int DQK, int H>
+template <int DQK, int H, bool SPEC>
 struct GtaLayout {
   static constexpr int KROW = 2 * DQK;          // bytes per K row
   static constexpr int KTILE = KB * KROW;
@@ -76,27 +87,39 @@ struct GtaLayout {
   static constexpr int STATS = PBASE + 2 * PBUF;  // 128 floats, then 2 x 8 restart flags
   static constexpr int FLAGS = STATS + 4 * ROWS;
   static constexpr int BYTES = FLAGS + 16;
-  static constexpr int KDMA = KTILE / 1024 / NW;  // DMA instructions per wave per K tile
-  static constexpr int VDMA = VTILE / 1024 / NW;  // ... per V tile
-  static constexpr int NDMA = KDMA + VDMA;
+  // DMA instructions per wave per K tile (by the score waves) and per V
+  // tile (by the value waves); every wave does both unless specialised
+  static constexpr int KDMA = KTILE / 1024 / (SPEC ? NW / 2 : NW);
+  static constexpr int VDMA = VTILE / 1024 / (SPEC ? NW / 2 : NW);
   static constexpr int RPD = 1024 / KROW;         // K rows per DMA instruction
 };
 
 __host__ __device__ constexpr int k_swz(int dqk, int r) { return dqk == 64 ? ((r >> 1) & 7) : (r & 15); }
+// a pointer that is the same in every lane, kept in scalar registers (the
+// buffer descriptors built from it are scalar operands)
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (P*)(((uint64_t)hi << 32) | lo);
+}
 
-template <int DQK, int H, bool OUT_F32>
+template <int DQK, int H, bool OUT_F32, bool SPEC>
 __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
-  using Ly = GtaLayout<DQK, H>;
+  using Ly = GtaLayout<DQK, H, SPEC>;
   constexpr int DS = DQK / 32;      // score contraction steps
-  constexpr int HW = NW / H;        // waves per head in the value phase
-  constexpr int RT = 8 / HW;        // row tiles per wave in the value phase
+  constexpr int NSW = SPEC ? NW / 2 : NW;  // score waves
+  constexpr int NVW = SPEC ? NW / 2 : NW;  // value waves
+  constexpr int QT = ROWS / (16 * NSW);    // 16-position score tiles per score wave
+  constexpr int HW = NVW / H;       // value waves per head
+  constexpr int RT = 8 / HW;        // row tiles per value wave
   constexpr int NB = 8 * RT;        // value MFMAs per tile: 2 steps x 4 column tiles x RT
-  constexpr int NBS = 3 * NB / 4;   // the softmax shares the first NBS of them
+  constexpr int NBS = 3 * NB / 4;   // the softmax shares the first NBS of them (unspecialised)
   constexpr int U = Ly::KROW / 16;  // 16-byte units per K row
   constexpr int NS = Ly::NS;
   static_assert(H == 1 || H == 2 || H == 4, "value sources per work-group");
-  static_assert(QT == 1, "one score tile per wave");
-  static_assert(RT == 1 || RT == 2 || RT == 4, "row tiles per wave");
+  static_assert(QT == 1 || QT == 2, "score tiles per wave");
+  static_assert(RT == 1 || RT == 2 || RT == 4 || RT == 8, "row tiles per wave");
   static_assert(Ly::KDMA >= 1 && Ly::KDMA <= DS && Ly::VDMA >= 1 && NB % Ly::VDMA == 0, "DMA slots");
   static_assert(Ly::BYTES <= 160 * 1024, "LDS");
 
@@ -105,6 +128,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
+  // roles (wave-uniform): every wave scores and applies values unless specialised
+  const bool scorer = !SPEC || wave < NSW;
+  const bool valuer = !SPEC || wave >= NW - NVW;
+  const int sw = SPEC ? min(wave, NSW - 1) : wave;         // index among the score waves
+  const int vw = SPEC ? max(wave - (NW - NVW), 0) : wave;  // ... among the value waves
 
   // ---- which positions of which group -----------------------------------------
   // Work-groups start in blockIdx order as CUs free up, and causal q-blocks
@@ -121,8 +149,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
   const int b = __builtin_amdgcn_readfirstlane((int)(lid % n_bg) / a.h_kv);
   const int S = a.S_q;
   const int pos_wg = qb * ROWS;
-  const int hv = wave / HW;          // value phase: head hv of the group
-  const int rt0 = (wave % HW) * RT;  //   and its first row tile
+  const int hv = vw / HW;          // value phase: head hv of the group
+  const int rt0 = (vw % HW) * RT;  //   and its first row tile
 
   // tiles to visit; tiles from t_mask on need the mask (diagonal or ragged)
   int n_kb, t_mask;
@@ -137,17 +165,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
   t_mask = __builtin_amdgcn_readfirstlane(min(t_mask, n_kb));
 
   const __bf16* qbase = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)grp * a.q_sh;
-  const __bf16* kbase = (const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)grp * a.k_sh;
+  const __bf16* kbase = uniform_ptr((const __bf16*)a.k + (int64_t)b * a.k_sb + (int64_t)grp * a.k_sh);
   // value source hv: columns 64 (hv % v_sph) .. + 63 of head grp v_hpg + hv / v_sph
   const int vhead = grp * a.v_hpg + hv / a.v_sph, vcol = 64 * (hv % a.v_sph);
-  const __bf16* vbase = (const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)vhead * a.v_sh + vcol;
+  const __bf16* vbase = uniform_ptr((const __bf16*)a.v + (int64_t)b * a.v_sb + (int64_t)vhead * a.v_sh + vcol);
 
   // ---- Q^T fragments of this wave's score rows ----------------------------------
   u32x4 qf[QT][DS];
   int kmax[QT];  // last key each lane's row sees
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const int pos = pos_wg + 16 * (QT * wave + qt) + li;
+    const int pos = pos_wg + 16 * (QT * sw + qt) + li;
     const int pc = min(pos, S - 1);
     kmax[qt] = a.causal ? pc : S - 1;
 #pragma unroll
@@ -157,11 +185,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
   const float c2 = a.scale * kLog2e;
 
   // ---- tile DMAs -----------------------------------------------------------------
-  // K: wave w moves rows RPD (w KDMA + j) .. + RPD - 1 with its j-th
-  // instruction (lane l: row l / U, unit position l % U).  V: wave w moves
-  // rows 8 n .. 8 n + 7 of its value head with instruction j, n = (w VDMA + j)
-  // mod 8 (lane l: row l / 8, position l % 8).  Offsets of tiles past the
-  // last read as zeros.
+  // K: score wave w moves rows RPD (w KDMA + j) .. + RPD - 1 with its j-th
+  // instruction (lane l: row l / U, unit position l % U).  V: value wave w
+  // moves rows 8 n .. 8 n + 7 of its value head with instruction j,
+  // n = (w VDMA + j) mod 8 (lane l: row l / 8, position l % 8).  Offsets of
+  // tiles past the last read as zeros.
   const uint32_t krow = (uint32_t)a.k_ss * 2u, vrow = (uint32_t)a.v_ss * 2u;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)kbase, 0, (int)((uint32_t)(S - 1) * krow + (uint32_t)Ly::KROW), kBufferFlags);
@@ -170,18 +198,18 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
   uint32_t kofs[Ly::KDMA];
 #pragma unroll
   for (int j = 0; j < Ly::KDMA; ++j) {
-    const int r = (wave * Ly::KDMA + j) * Ly::RPD + lane / U;
+    const int r = (sw * Ly::KDMA + j) * Ly::RPD + lane / U;
     kofs[j] = (uint32_t)(lane / U) * krow + 16u * ((lane % U) ^ k_swz(DQK, r));
   }
   const uint32_t vofs = (uint32_t)(lane >> 3) * vrow + 16u * ((lane & 7) ^ (2 * ((lane >> 4) & 3)));
   const uint32_t lds0 = lds_offset(smem);
   auto issue_k = [&](int t, int j) __attribute__((always_inline)) {
-    const int n = wave * Ly::KDMA + j;
+    const int n = sw * Ly::KDMA + j;
     const uint32_t so = t < n_kb ? (uint32_t)(t * KB + n * Ly::RPD) * krow : kOutOfRange;
     lds_dma16(krs, lds0 + Ly::KBASE + (t % NS) * Ly::KTILE + n * 1024, kofs[j], so);
   };
   auto issue_v = [&](int t, int j) __attribute__((always_inline)) {
-    const int n = (wave * Ly::VDMA + j) & 7;
+    const int n = (vw * Ly::VDMA + j) & 7;
     const uint32_t so = t < n_kb ? (uint32_t)(t * KB + 8 * n) * vrow : kOutOfRange;
     lds_dma16(vrs, lds0 + Ly::VBASE + (t % NS) * Ly::VTILE + hv * VHEAD + n * 1024, vofs, so);
   };
@@ -223,6 +251,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
   // of an iteration), those MFMAs must retire.  The nops are tied to them.
   auto value_retire = [&]() __attribute__((always_inline)) {
 #define GHA_RETIRE "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+    if constexpr (SPEC) {
+      // accumulators in VGPRs (see the value MFMAs of the specialised form)
+      if constexpr (RT == 2)
+        asm volatile(GHA_RETIRE : "+v"(oacc[3][0]), "+v"(oacc[3][RT - 1]), "+v"(oacc[2][0]), "+v"(oacc[2][RT - 1]));
+      if constexpr (RT == 4)
+        asm volatile(GHA_RETIRE : "+v"(oacc[3][0]), "+v"(oacc[3][1]), "+v"(oacc[3][2]), "+v"(oacc[3][RT - 1]));
+      if constexpr (RT == 8)
+        asm volatile(GHA_RETIRE : "+v"(oacc[3][0]), "+v"(oacc[3][1]), "+v"(oacc[3][2]), "+v"(oacc[3][3]),
+                     "+v"(oacc[3][4]), "+v"(oacc[3][5]), "+v"(oacc[3][6]), "+v"(oacc[3][RT - 1]));
+      return;
+    }
     if constexpr (RT == 1) asm volatile(GHA_RETIRE : "+a"(oacc[3][0]), "+a"(oacc[2][0]), "+a"(oacc[1][0]));
     if constexpr (RT == 2)
       asm volatile(GHA_RETIRE : "+a"(oacc[3][0]), "+a"(oacc[3][RT - 1]), "+a"(oacc[2][0]), "+a"(oacc[2][RT - 1]));
@@ -231,10 +270,25 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
 #undef GHA_RETIRE
   };
 
-  auto iter = [&](int it, auto masked, auto has_score, auto has_pv) __attribute__((always_inline)) -> bool {
+  // Roles as compile-time constants: 0 every wave does both (unspecialised),
+  // 1 score waves, 2 value waves.  The specialised roles run loops of their
+  // own, so that neither keeps the other's registers live.
+  using Both = std::integral_constant<int, 0>;
+  using Scorer = std::integral_constant<int, 1>;
+  using Valuer = std::integral_constant<int, 2>;
+  // wait until at most one iteration's DMAs of this wave (NS - 2 tiles of them) are in flight
+  auto wait_this_iteration_dmas = [&](auto role) __attribute__((always_inline)) {
+    constexpr int kRole = decltype(role)::value;
+    if constexpr (kRole == 0) wait_vmem_at_most<(Ly::KDMA + Ly::VDMA) * (NS - 2)>();
+    if constexpr (kRole == 1) wait_vmem_at_most<Ly::KDMA * (NS - 2)>();
+    if constexpr (kRole == 2) wait_vmem_at_most<Ly::VDMA * (NS - 2)>();
+  };
+
+  auto iter = [&](int it, auto masked, auto has_score, auto has_pv, auto role) __attribute__((always_inline)) -> bool {
     constexpr bool kMasked = decltype(masked)::value;
     constexpr bool kS = decltype(has_score)::value;
     constexpr bool kP = decltype(has_pv)::value;
+    constexpr int kRole = decltype(role)::value;
     const int k0 = it * KB;
     // slot bases of this iteration, kept opaque so that each fragment address
     // is one add of a scalar to a loop-invariant lane offset
@@ -257,6 +311,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
 
     // ---- phase A: S^T of tile it for this wave's rows ----
     f32x4 sacc[4][QT];
+    auto phase_a = [&]() __attribute__((always_inline)) {
     if constexpr (kS) {
       u32x4 kf[2][4];
       auto load_k = [&](int s, u32x4 (&f)[4]) __attribute__((always_inline)) {
@@ -268,7 +323,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
         constexpr int s = decltype(S_)::value;
         if (s + 1 < DS) load_k(s + 1, kf[(s + 1) & 1]);
         if (s < Ly::KDMA) issue_k(dk, s);
-        if (kP && s == DS - 1) {
+        if (!SPEC && kP && s == DS - 1) {
           load_p(0);
           load_v(0, vf[0]);
         }
@@ -287,6 +342,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
       load_p(0);
       load_v(0, vf[0]);
     }
+    };
 
     // ---- phase B: softmax of tile it in 23 small stages per score row (=
     // lane and q-tile); sacc[kt][qt][r] is key k0 + 16 kt + 4 lg + r and
@@ -342,13 +398,18 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
     auto scores_retire = [&]() __attribute__((always_inline)) {
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
                    : "+v"(sacc[0][0]), "+v"(sacc[1][0]), "+v"(sacc[2][0]), "+v"(sacc[3][0]));
+      if constexpr (QT == 2)
+        asm volatile("" : "+v"(sacc[0][QT - 1]), "+v"(sacc[1][QT - 1]), "+v"(sacc[2][QT - 1]), "+v"(sacc[3][QT - 1]));
     };
     // P^T of this wave's rows to LDS with their normaliser (two wait states
     // after the VALU writes of the MFMA operands, accumulator included), and
     // the restart request
     auto publish = [&]() __attribute__((always_inline)) {
       u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
-      asm volatile("s_nop 1" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(lacc[0]), "+v"(ones));
+      if constexpr (QT == 1) asm volatile("s_nop 1" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(lacc[0]), "+v"(ones));
+      if constexpr (QT == 2)
+        asm volatile("s_nop 1" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(pf[QT - 1][0]), "+v"(pf[QT - 1][1]),
+                     "+v"(lacc[0]), "+v"(lacc[QT - 1]), "+v"(ones));
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -357,123 +418,215 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) st16(pw + (2 * (QT * wave + qt) + ks) * PFRAG, pf[qt][ks]);
+        for (int ks = 0; ks < 2; ++ks) st16(pw + (2 * (QT * sw + qt) + ks) * PFRAG, pf[qt][ks]);
       // a wave whose rows outgrew their reference asks the whole work-group to
       // start again (every wave must run the same tiles and barriers)
       const bool any_restart = wave_any(restart_row);  // all lanes vote, outside the lane-0 branch
       if (lane == 0) flag_s[NW * (it & 1) + wave] = any_restart ? 1 : 0;
     };
 
-    if constexpr (kP) {
-      // O^T += V^T P^T of tile it - 1: step = 4 ks + ct, RT MFMAs per step
-      static_for<0, NB>([&](auto M_) __attribute__((always_inline)) {
-        constexpr int m = decltype(M_)::value;
-        constexpr int step = m / RT, rt = m % RT, ks = step / 4, ct = step % 4;
-        if (rt == 0 && step + 1 < 8) load_v(step + 1, vf[(step + 1) & 1]);
-        if (NPB == 2 && m == 1) load_p(1);
-        if (m % (NB / Ly::VDMA) == NB / Ly::VDMA / 2) issue_v(dv, m / (NB / Ly::VDMA));
-        mfma_acc(oacc[ct][rt], vf[step & 1], pall[ks % NPB][rt]);
-        // a single set of P^T fragments is refilled once its last reader has issued
-        if (NPB == 1 && m == 4 * RT - 1) load_p(1);
-        __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kRole != 0) {
+      if constexpr (kRole == 1) {
         if constexpr (kS) {
-          if (m == 0) scores_retire();
-          if constexpr (m < NBS) static_for<m * NST / NBS, (m + 1) * NST / NBS>(stage);
-          if (m == NBS) publish();
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      value_retire();
-    } else {
-      scores_retire();
-      static_for<0, NST>(stage);
+          // the score chain sets the pace: its MFMAs and VALU work go ahead of
+          // the value wave's MFMA stream on the shared SIMD
+          __builtin_amdgcn_s_setprio(3);
+          phase_a();
+          scores_retire();
+          static_for<0, NST>(stage);
+          publish();
+          __builtin_amdgcn_s_setprio(0);
+        } else {
 #pragma unroll
-      for (int j = 0; j < Ly::VDMA; ++j) issue_v(dv, j);
-      publish();
+          for (int j = 0; j < Ly::KDMA; ++j) issue_k(dk, j);
+        }
+      }
+      if constexpr (kRole == 2) {
+        if constexpr (kP) {
+          load_p(0);
+          load_v(0, vf[0]);
+          // O^T += V^T P^T of tile it - 1 (as below, without the softmax)
+          static_for<0, NB>([&](auto M_) __attribute__((always_inline)) {
+            constexpr int m = decltype(M_)::value;
+            constexpr int step = m / RT, rt = m % RT, ks = step / 4, ct = step % 4;
+            if (rt == 0 && step + 1 < 8) load_v(step + 1, vf[(step + 1) & 1]);
+            if (NPB == 2 && m == 1) load_p(1);
+            if (m % (NB / Ly::VDMA) == NB / Ly::VDMA / 2) issue_v(dv, m / (NB / Ly::VDMA));
+            // accumulators in VGPRs: without AGPRs in use the compiler can give
+            // either role up to 256 registers (with 128 AGPRs of accumulators it
+            // splits them 128 / 128 and the score role spills)
+            mfma_v(oacc[ct][rt], vf[step & 1], pall[ks % NPB][rt]);
+            if (NPB == 1 && m == 4 * RT - 1) load_p(1);
+            __builtin_amdgcn_sched_barrier(0);
+          });
+          value_retire();
+        } else {
+#pragma unroll
+          for (int j = 0; j < Ly::VDMA; ++j) issue_v(dv, j);
+        }
+      }
+    } else {
+      phase_a();
+      if constexpr (kP) {
+        // O^T += V^T P^T of tile it - 1: step = 4 ks + ct, RT MFMAs per step
+        static_for<0, NB>([&](auto M_) __attribute__((always_inline)) {
+          constexpr int m = decltype(M_)::value;
+          constexpr int step = m / RT, rt = m % RT, ks = step / 4, ct = step % 4;
+          if (rt == 0 && step + 1 < 8) load_v(step + 1, vf[(step + 1) & 1]);
+          if (NPB == 2 && m == 1) load_p(1);
+          if (m % (NB / Ly::VDMA) == NB / Ly::VDMA / 2) issue_v(dv, m / (NB / Ly::VDMA));
+          mfma_acc(oacc[ct][rt], vf[step & 1], pall[ks % NPB][rt]);
+          // a single set of P^T fragments is refilled once its last reader has issued
+          if (NPB == 1 && m == 4 * RT - 1) load_p(1);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (kS) {
+            if (m == 0) scores_retire();
+            if constexpr (m < NBS) static_for<m * NST / NBS, (m + 1) * NST / NBS>(stage);
+            if (m == NBS) publish();
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        value_retire();
+      } else {
+        scores_retire();
+        static_for<0, NST>(stage);
+  #pragma unroll
+        for (int j = 0; j < Ly::VDMA; ++j) issue_v(dv, j);
+        publish();
+      }
     }
 
     // a restart raised at the previous barrier: nothing since is kept
     if (__builtin_amdgcn_readfirstlane((uint32_t)(flags | (flags >> 32))) != 0) return true;
     // the tiles of the next iteration have landed (this one's DMAs may fly on)
-    wait_vmem_at_most<Ly::NDMA * (NS - 2)>();
+    wait_this_iteration_dmas(role);
     __syncthreads();
     if constexpr (kS) flags = *reinterpret_cast<const uint64_t*>(flag_s + NW * (it & 1));
     return false;
   };
 
-  for (;;) {
+  // run(role, done): the tile loop of a role, restarted until no wave asks for
+  // it, then done() (the role's epilogue) inside the loop, so that no
+  // accumulator lives on past the loop's exit
+  auto run = [&](auto role, auto&& done) __attribute__((always_inline)) {
+    constexpr int kRole = decltype(role)::value;
+    for (;;) {
+      if constexpr (kRole != 2) {
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qt = 0; qt < QT; ++qt) lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      if constexpr (kRole != 1) {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) oacc[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    flags = 0;
-    // K of tiles 0 .. NS - 2 and V of tiles 0 .. NS - 3, in that order
+          for (int rt = 0; rt < RT; ++rt) oacc[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      flags = 0;
+      // K of tiles 0 .. NS - 2 and V of tiles 0 .. NS - 3, in that order
+      if constexpr (kRole != 2) {
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
+        for (int t = 0; t < NS - 1; ++t)
 #pragma unroll
-      for (int j = 0; j < Ly::KDMA; ++j) issue_k(t, j);
+          for (int j = 0; j < Ly::KDMA; ++j) issue_k(t, j);
+      }
+      if constexpr (kRole != 1) {
 #pragma unroll
-    for (int t = 0; t < NS - 2; ++t)
+        for (int t = 0; t < NS - 2; ++t)
 #pragma unroll
-      for (int j = 0; j < Ly::VDMA; ++j) issue_v(t, j);
-    wait_vmem_at_most<Ly::NDMA * (NS - 2)>();
-    __syncthreads();
-    bool restart = t_mask > 0 ? iter(0, std::false_type{}, std::true_type{}, std::false_type{})
-                              : iter(0, std::true_type{}, std::true_type{}, std::false_type{});
-    int it = 1;
-    for (; it < t_mask && !restart; ++it)
-      restart = iter(it, std::false_type{}, std::true_type{}, std::true_type{});
-    for (; it < n_kb && !restart; ++it)
-      restart = iter(it, std::true_type{}, std::true_type{}, std::true_type{});
-    if (!restart) restart = iter(n_kb, std::false_type{}, std::false_type{}, std::true_type{});
-    // no DMA may still target a slot that is about to be reused
-    wait_vmem_all();
-    if (!restart) break;
-    __syncthreads();
-  }
+          for (int j = 0; j < Ly::VDMA; ++j) issue_v(t, j);
+      }
+      // a value wave never publishes a restart request: its flag bytes stay zero
+      if (lane == 0) {
+        flag_s[wave] = 0;
+        flag_s[NW + wave] = 0;
+      }
+      wait_this_iteration_dmas(role);
+      __syncthreads();
+      bool restart = t_mask > 0 ? iter(0, std::false_type{}, std::true_type{}, std::false_type{}, role)
+                                : iter(0, std::true_type{}, std::true_type{}, std::false_type{}, role);
+      int it = 1;
+      for (; it < t_mask && !restart; ++it)
+        restart = iter(it, std::false_type{}, std::true_type{}, std::true_type{}, role);
+      for (; it < n_kb && !restart; ++it)
+        restart = iter(it, std::true_type{}, std::true_type{}, std::true_type{}, role);
+      if (!restart) restart = iter(n_kb, std::false_type{}, std::false_type{}, std::true_type{}, role);
+      // no DMA may still target a slot that is about to be reused
+      wait_vmem_all();
+      if (!restart) {
+        done();
+        return;
+      }
+      __syncthreads();
+    }
+  };
 
   // ---- epilogue: 1 / l of every row through LDS, then O = O^T / l ------------------
   float* stats = reinterpret_cast<float*>(smem + Ly::STATS);
+  auto write_stats = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float l = lacc[qt][0];
-    const int row = 16 * (QT * wave + qt) + li;
-    const int pos = pos_wg + row;
-    if (lg == 0) {
-      stats[row] = 1.f / l;
-      if (a.lse != nullptr && pos < S)
-        a.lse[((int64_t)b * a.lse_heads + grp) * S + pos] = (m2[qt] + fast_log2(l)) * kLn2;
+    for (int qt = 0; qt < QT; ++qt) {
+      const float l = lacc[qt][0];
+      const int row = 16 * (QT * sw + qt) + li;
+      const int pos = pos_wg + row;
+      if (lg == 0) {
+        stats[row] = 1.f / l;
+        if (a.lse != nullptr && pos < S)
+          a.lse[((int64_t)b * a.lse_heads + grp) * S + pos] = (m2[qt] + fast_log2(l)) * kLn2;
+      }
     }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = 16 * (rt0 + rt) + li;
-    const int pos = pos_wg + row;
-    if (pos >= S) continue;
-    const float inv = stats[row];
-    const int64_t obase = (int64_t)b * a.o_sb + (int64_t)vhead * a.o_sh + (int64_t)pos * a.o_ss + vcol + 4 * lg;
-    // oacc[ct][rt][r] is feature 16 ct + 4 lg + r of this row
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const f32x4 v = oacc[ct][rt] * inv;
-      if constexpr (OUT_F32)
-        *reinterpret_cast<f32x4*>((float*)a.o + obase + 16 * ct) = v;
-      else
-        *reinterpret_cast<u32x2*>((__bf16*)a.o + obase + 16 * ct) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+  };
+  auto write_outputs = [&]() __attribute__((always_inline)) {
+  #pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = 16 * (rt0 + rt) + li;
+      const int pos = pos_wg + row;
+      if (pos >= S) continue;
+      const float inv = stats[row];
+      const int64_t obase = (int64_t)b * a.o_sb + (int64_t)vhead * a.o_sh + (int64_t)pos * a.o_ss + vcol + 4 * lg;
+      // oacc[ct][rt][r] is feature 16 ct + 4 lg + r of this row
+  #pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const f32x4 v = oacc[ct][rt] * inv;
+        if constexpr (OUT_F32)
+          *reinterpret_cast<f32x4*>((float*)a.o + obase + 16 * ct) = v;
+        else
+          *reinterpret_cast<u32x2*>((__bf16*)a.o + obase + 16 * ct) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      }
     }
+  };
+  if constexpr (SPEC) {
+    if (scorer) {
+      run(Scorer{}, [&]() __attribute__((always_inline)) {
+        write_stats();
+        __syncthreads();
+      });
+    } else {
+      run(Valuer{}, [&]() __attribute__((always_inline)) {
+        __syncthreads();
+        write_outputs();
+      });
+    }
+  } else {
+    run(Both{}, [&]() __attribute__((always_inline)) {
+      write_stats();
+      __syncthreads();
+      write_outputs();
+    });
   }
 }
+
+#ifndef GHA_GTA_SPEC
+#define GHA_GTA_SPEC 1  // score and value waves specialised
+#endif
 
 template <int DQK, int H>
 hipError_t launch_h(const PrefillArgs& a, bool out_f32, hipStream_t st) {
   const uint32_t padded = (uint32_t)((a.n_blocks + 7) / 8 * 8);
+  constexpr bool kSpec = GHA_GTA_SPEC != 0;
   if (out_f32)
-    hipLaunchKernelGGL((gta_kernel<DQK, H, true>), dim3(padded), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((gta_kernel<DQK, H, true, kSpec>), dim3(padded), dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((gta_kernel<DQK, H, false>), dim3(padded), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((gta_kernel<DQK, H, false, kSpec>), dim3(padded), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
