@@ -424,18 +424,34 @@ __global__ __launch_bounds__(64 * NW, 1) void gta_kernel(PrefillArgs a) {
       const bool any_restart = wave_any(restart_row);  // all lanes vote, outside the lane-0 branch
       if (lane == 0) flag_s[NW * (it & 1) + wave] = any_restart ? 1 : 0;
     };
+    // the same per score tile (specialised form): tile qt's P^T goes to LDS as
+    // soon as its softmax is done, so that its writes drain while the next
+    // tile's softmax runs (the value waves' reads keep the LDS busy)
+    auto publish_qt = [&](auto Q_) __attribute__((always_inline)) {
+      constexpr int qt = decltype(Q_)::value;
+      u32x4 ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+      asm volatile("s_nop 1" : "+v"(pf[qt][0]), "+v"(pf[qt][1]), "+v"(lacc[qt]), "+v"(ones));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) mfma_v(lacc[qt], ones, pf[qt][ks]);
+      unsigned char* pw = smem + Ly::PBASE + (it & 1) * PBUF + 16 * lane;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) st16(pw + (2 * (QT * sw + qt) + ks) * PFRAG, pf[qt][ks]);
+      if constexpr (qt == QT - 1) {
+        const bool any_restart = wave_any(restart_row);  // all lanes vote, outside the lane-0 branch
+        if (lane == 0) flag_s[NW * (it & 1) + wave] = any_restart ? 1 : 0;
+      }
+    };
 
     if constexpr (kRole != 0) {
       if constexpr (kRole == 1) {
         if constexpr (kS) {
-          // the score chain sets the pace: its MFMAs and VALU work go ahead of
-          // the value wave's MFMA stream on the shared SIMD
-          __builtin_amdgcn_s_setprio(3);
           phase_a();
           scores_retire();
-          static_for<0, NST>(stage);
-          publish();
-          __builtin_amdgcn_s_setprio(0);
+          static_for<0, NST>([&](auto K_) __attribute__((always_inline)) {
+            constexpr int k = decltype(K_)::value;
+            stage(K_);
+            if constexpr (k % NSQ == NSQ - 1) publish_qt(std::integral_constant<int, k / NSQ>{});
+          });
         } else {
 #pragma unroll
           for (int j = 0; j < Ly::KDMA; ++j) issue_k(dk, j);
