@@ -785,6 +785,10 @@ GTA_CASES = [
     (1, 4, 4, 150, 64, 256),  # one head of 256: 4 sources
     (1, 8, 2, 130, 128, 256), # 16 sources, four launches, d_qk 128
     (1, 6, 2, 100, 64, 128),  # 6 sources, three launches of 2
+    # d_qk 128 with fewer sources (two value waves per source, four per
+    # source), ragged against the 64-key tiles
+    (1, 4, 2, 150, 128, 64),  # two heads per group: two sources
+    (2, 2, 2, 90, 128, 64),   # one head per group: one source
 ]
 
 
