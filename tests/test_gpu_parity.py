@@ -789,6 +789,9 @@ GTA_CASES = [
     # source), ragged against the 64-key tiles
     (1, 4, 2, 150, 128, 64),  # two heads per group: two sources
     (2, 2, 2, 90, 128, 64),   # one head per group: one source
+    # shorter than one key tile; one position (its output is v_0)
+    (2, 8, 2, 40, 64, 64),
+    (1, 8, 2, 1, 64, 64),
 ]
 
 
