@@ -9,17 +9,19 @@
 // four sources is covered by several launches, each recomputing the scores.
 //
 // One work-group (eight waves, two per SIMD) owns 128 positions of one group
-// and walks the keys in tiles of 64:
-//   score: wave w computes S^T = K Q^T for positions 16 w .. 16 w + 15 (K
-//          from LDS, Q^T resident in VGPRs), runs their softmax and publishes
-//          the bf16 probabilities as P^T operand fragments in LDS;
-//   value: the waves split the value sources and positions (with four
-//          sources, wave w takes source w / 2 for positions 64 (w % 2) .. + 63)
-//          and accumulate O^T += V^T P^T: V^T fragments come from transposing
-//          LDS reads of the source's V tile, P^T fragments from LDS.
-// So the score matrix is computed once per group and every K or V tile is
-// fetched once per work-group.  Two waves per SIMD let one wave's softmax and
-// LDS traffic overlap the other's matrix work.
+// and walks the keys in tiles of 64.  Its waves split the work by role:
+//   score waves 0..3: wave w computes S^T = K Q^T for positions 32 w ..
+//          32 w + 31 (K from LDS, Q^T resident in VGPRs), runs their softmax
+//          and publishes the bf16 probabilities as P^T operand fragments in
+//          LDS;
+//   value waves 4..7: they split the value sources (with four sources, wave
+//          4 + h takes source h for all 128 positions) and accumulate
+//          O^T += V^T P^T: V^T fragments come from transposing LDS reads of
+//          the source's V tile, P^T fragments from LDS, one tile behind.
+// So the score matrix is computed once per group, every K or V tile is
+// fetched once per work-group, K is read by four waves and each V tile by one.
+// Wave w and wave w + 4 share a SIMD, so one's softmax runs beside the
+// other's value MFMAs.
 //
 // Tiles reach LDS by buffer DMA (buffer_load ... lds, no VGPR staging) into
 // rings of NS slots: the DMAs of an iteration fetch the K tile NS - 1 ahead of
@@ -34,21 +36,17 @@
 // makes the work-group start again with the larger reference; the result is
 // the same softmax either way.
 //
-// Iteration it: phase A, the score MFMAs of tile it; phase B, the value MFMAs
-// of tile it - 1 with the softmax of tile it spread between them (VALU and
-// matrix core run side by side), then P^T(it) to LDS and one barrier.
-//
-// Specialised form (SPEC, the one built): waves 0..3 only score (32
-// positions each: K is read by four waves instead of eight) and waves 4..7
-// only apply values (with four sources, wave 4 + h takes source h for all 128
-// positions: each V tile is read once).  Wave w and wave w + 4 share a SIMD,
-// so one's softmax runs beside the other's value MFMAs; the iteration
-// structure, the rings, the P^T exchange and the restart are those above.
-// The iteration is bound by LDS throughput: per iteration and CU the
-// specialised form moves about 184 KiB through the LDS (K, V^T and P^T reads,
-// P^T and DMA writes) against 248 KiB.  Each role runs a loop of its own with
+// Iteration it: the score waves score tile it and publish P^T(it); the value
+// waves apply P^T(it - 1) to V(it - 1); one barrier.  The iteration is bound
+// by LDS throughput: per iteration and CU the LDS moves about 184 KiB (K, V^T
+// and P^T reads, P^T and DMA writes).  Each role runs a loop of its own with
 // its epilogue inside, so that neither keeps the other's registers live and
 // no accumulator outlives the loop.
+//
+// Unspecialised form (SPEC = false, built with GHA_GTA_SPEC=0): every wave
+// scores 16 positions and applies one source to 64 positions, the softmax of
+// tile it woven between its value MFMAs of tile it - 1; the LDS then moves
+// about 248 KiB per iteration and CU, and the iteration takes ~12% longer.
 //
 // LDS rows, 16-byte units swizzled so that every fragment read touches
 // distinct banks:
